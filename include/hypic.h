@@ -1,0 +1,326 @@
+/*
+ * hypic.h -- C ABI of libhypic: linear-attention state composition for
+ * position-independent caching, on AMD MI355X (gfx950).
+ *
+ * Sources (the HYPIC pages):
+ *   [news]   HYPIC news article, news.aibase.com/tw/news/29683
+ *   [readme] HYPIC project README ("PIC modes", "Key techniques")
+ *   [arxiv]  abstract of arXiv 2607.01299
+ *
+ * Conventions used by every call
+ *   - A chain is one (layer, value-head) recurrence.  Its state S is d_k x d_v,
+ *     a transition T is d_k x d_k and acts from the left: composing segment C1
+ *     and then C2 gives S(C1.C2) = T(C2) S(C1) + S(C2) ([news], paragraph on
+ *     linear layers and the cached transition operator).
+ *   - Dense kind, the gated delta rule (Yang, Kautz & Hatamizadeh, ICLR 2025):
+ *       S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,
+ *     the write not decayed at its own step; DeltaNet is log_alpha == 0.
+ *     Diagonal kind (GLA):  S_t = diag(alpha_t) S_{t-1} + k_t v_t^T.
+ *     Scalar kind (RetNet gamma, Mamba2): S_t = alpha_t S_{t-1} + k_t v_t^T.
+ *     These are the decaying families [news] names in the same paragraph.
+ *   - Per-token output o_t = S_t^T q_t, with S_t the state after token t.
+ *     No 1/sqrt(d) scale is applied: the caller pre-scales q.
+ *   - T is returned as T_hat * 2^T_exp: T_hat float32 with one int32 exponent
+ *     per (segment, chain), because the product of hundreds of decaying
+ *     transitions leaves float32's range.  The pair is not unique; only the
+ *     represented value is meaningful.
+ *   - Grouped-query attention: value head h reads key/query head
+ *     floor(h * h_k / h_v).  log_alpha and beta are per value head.
+ *   - All tensors are dense, C-contiguous, caller-owned DEVICE memory unless
+ *     marked "host".  Layouts are given per field.  The library never
+ *     allocates device memory and keeps no pointer after a call returns.
+ *   - Every call validates all arguments on the host BEFORE any HIP call.  On
+ *     failure nothing is enqueued, the call returns a status != HYPIC_OK and
+ *     hypic_last_error() (thread-local) describes the problem.  A launch
+ *     failure returns HYPIC_ERR_DEVICE.  Device faults surface at the caller's
+ *     next synchronisation.  Every call is asynchronous on `stream`
+ *     (NULL = the null stream); host arrays may be freed when the call returns.
+ *   - NaN/Inf inputs propagate; they are not checked.
+ *   - Supported shapes: d_k == d_v in {64, 128}; chunk == 64; conv width 4.
+ *     Anything else returns HYPIC_ERR_UNSUPPORTED.
+ *   - Outputs are bitwise reproducible run to run and independent of the
+ *     schedule (no atomics in any reduction).
+ */
+#ifndef HYPIC_H
+#define HYPIC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HYPIC_VERSION 1
+
+typedef struct ihipStream_t* hypic_stream_t; /* a hipStream_t */
+
+typedef enum {
+    HYPIC_OK = 0,
+    HYPIC_ERR_INVALID_ARGUMENT = 1,
+    HYPIC_ERR_UNSUPPORTED = 2,
+    HYPIC_ERR_WORKSPACE_TOO_SMALL = 3,
+    HYPIC_ERR_DEVICE = 4
+} hypic_status;
+
+/* element type of q/k/v (inputs) and of o / conv outputs */
+typedef enum { HYPIC_F32 = 0, HYPIC_BF16 = 1 } hypic_dtype;
+
+typedef enum {
+    HYPIC_DENSE_DELTA = 0, /* A_t = alpha_t (I - beta_t k_t k_t^T)  (GDN, DeltaNet) */
+    HYPIC_DIAG = 1,        /* A_t = diag(alpha_t)                   (GLA)          */
+    HYPIC_SCALAR = 2       /* A_t = alpha_t I                       (RetNet, Mamba2) */
+} hypic_kind;
+
+/* Order in which (segment, chain) build tasks are handed to the compute units.
+ * Segment parallelism with longest-processing-time-first balancing is the
+ * [news] paragraph on segment parallelism; here the workers are the GPU's
+ * compute units instead of serving instances. */
+typedef enum {
+    HYPIC_SCHED_NATURAL = 0, /* segment-major task order, hardware dispatch          */
+    HYPIC_SCHED_LPT = 1,     /* longest segments first, hardware dispatch (greedy list
+                                scheduling = LPT)                                     */
+    HYPIC_SCHED_RR = 2       /* persistent workgroups, task i -> slot i mod n_slots   */
+} hypic_schedule;
+
+/* Operand precision of the dense build's matrix-core products.  Accumulation
+ * is always float32.  AUTO: F32 for float32 inputs, F16 for bf16 inputs. */
+typedef enum {
+    HYPIC_PREC_AUTO = 0,
+    HYPIC_PREC_F32 = 1, /* float32 operands (fp32 matrix cores), for fp32 inputs   */
+    HYPIC_PREC_F16 = 2  /* f16 operands, power-of-two renormalised T columns        */
+} hypic_precision;
+
+typedef enum {
+    HYPIC_COMPOSE_AUTO = 0,     /* FOLD for few elements per chain, else SCAN      */
+    HYPIC_COMPOSE_FOLD = 1,     /* sequential S <- T_i S + S_i per chain            */
+    HYPIC_COMPOSE_SCAN = 2,     /* blocked reduce, scan of block aggregates, re-fold */
+    HYPIC_COMPOSE_NAIVE_ADD = 3 /* S <- S + S_i: the "addition" PIC mode of [readme],
+                                   exact only without decay ([news])               */
+} hypic_compose_mode;
+
+typedef enum { HYPIC_ACT_NONE = 0, HYPIC_ACT_SILU = 1 } hypic_activation;
+
+/* ------------------------------------------------------------------------------------
+ * hypic_segment_build -- per-segment transition T_C and zero-start end state S(C|0).
+ *
+ * [news], linear-layer paragraph: both depend only on the segment's own
+ * tokens, so they are computed once when the segment is first prefilled and
+ * cached.  T_C is the ordered product of the segment's per-token transitions;
+ * S(C|0) is the state after the segment from S = 0.  The dense kind uses the
+ * chunked WY/UT form of the gated delta rule with T carried as extra state
+ * columns; the diagonal and scalar kinds use their closed forms.
+ *
+ * Segment s covers tokens [cu_seqlens[s] + skip_head, cu_seqlens[s+1]) of the
+ * packed token axis (skip_head >= 0 leaves the seam window out of the cache
+ * entry; a segment no longer than skip_head is empty: T = I, S = 0).
+ *
+ * Layouts (B = n_batch, typically layers; N = n_tokens):
+ *   k           [B, N, h_k, d_k]   in_dtype
+ *   v           [B, N, h_v, d_v]   in_dtype
+ *   log_alpha   float32, <= 0: DENSE/SCALAR [B, N, h_v]; DIAG [B, N, h_v, d_k]
+ *   beta        float32 [B, N, h_v] (DENSE only; must be NULL otherwise)
+ *   T_hat       float32 (NULL = skip T, plain state pass):
+ *                 DENSE [n_seg, B, h_v, d_k, d_k]; DIAG [n_seg, B, h_v, d_k];
+ *                 SCALAR [n_seg, B, h_v]
+ *   T_exp       int32 [n_seg, B, h_v] (required iff T_hat)
+ *   S           float32 [n_seg, B, h_v, d_k, d_v]
+ * Outputs are segment-major so that they serve directly as the element store
+ * of hypic_compose (slot = segment, chain = b * h_v + h).
+ * Requires a workspace of hypic_segment_build_workspace_bytes() bytes
+ * (device memory, 256-byte aligned) that stays untouched until the call's
+ * work on `stream` has finished.
+ * ---------------------------------------------------------------------------------- */
+typedef struct {
+    hypic_kind kind;
+    hypic_dtype in_dtype;
+    int32_t n_batch;
+    int64_t n_tokens;
+    int32_t h_k, h_v, d_k, d_v;
+    int32_t chunk;              /* must be 64 */
+    int32_t n_seg;
+    const int64_t* cu_seqlens;  /* host [n_seg + 1], cu[0] = 0, non-decreasing, cu[n_seg] <= N */
+    int32_t skip_head;          /* >= 0 */
+    int32_t qk_l2norm;          /* 1: k is scaled to unit L2 norm per token and head on load */
+    const void* k;
+    const void* v;
+    const float* log_alpha;
+    const float* beta;
+    float* T_hat;
+    int32_t* T_exp;
+    float* S;
+    hypic_schedule schedule;
+    hypic_precision precision;
+    void* workspace;
+    size_t workspace_bytes;
+} hypic_build_desc;
+
+hypic_status hypic_segment_build(const hypic_build_desc* desc, hypic_stream_t stream);
+size_t hypic_segment_build_workspace_bytes(const hypic_build_desc* desc);
+
+/* ------------------------------------------------------------------------------------
+ * hypic_compose -- constant-time composition of cached segments.
+ *
+ * [news], linear-layer paragraph: on reuse the running state is left-
+ * multiplied by the cached T_C and the cached S(C|0) added, in request order:
+ *   S <- T_{slot[i]} S + S_{slot[i]},  i = 0 .. n_elem-1,  starting from S0.
+ * FOLD runs this sequentially per chain; SCAN uses the associative operator
+ * (T2,S2) o (T1,S1) = (T2 T1, T2 S1 + S2) with identity (I, 0) in a blocked
+ * reduce / scan / re-fold.  NAIVE_ADD is the straw-man S <- S + S_i.
+ *
+ * Layouts (C = n_chain):
+ *   slot        device int32 [n_elem], values in [0, n_slot); NULL = identity
+ *               (then n_slot >= n_elem)
+ *   T_hat       float32 element store: DENSE [n_slot, C, d_k, d_k];
+ *               DIAG [n_slot, C, d_k]; SCALAR [n_slot, C]  (unused by NAIVE_ADD)
+ *   T_exp       int32 [n_slot, C]
+ *   S           float32 [n_slot, C, d_k, d_v]
+ *   S0          float32 [C, d_k, d_v] or NULL (zero)
+ *   S_final     float32 [C, d_k, d_v]
+ *   S_prefix    float32 [n_elem, C, d_k, d_v] or NULL: the state ENTERING element i
+ *   T_total     float32 like one element of T_hat, or NULL; T_total_exp int32 [C]
+ * SCAN needs hypic_compose_workspace_bytes() of device workspace; FOLD and
+ * NAIVE_ADD need none.
+ * ---------------------------------------------------------------------------------- */
+typedef struct {
+    hypic_kind kind;
+    int32_t n_chain;
+    int32_t d_k, d_v;
+    int32_t n_elem;
+    int32_t n_slot;
+    const int32_t* slot;
+    const float* T_hat;
+    const int32_t* T_exp;
+    const float* S;
+    const float* S0;
+    float* S_final;
+    float* S_prefix;
+    float* T_total;
+    int32_t* T_total_exp;
+    hypic_compose_mode mode;
+    int32_t scan_block;         /* elements per block for SCAN; 0 = automatic */
+    void* workspace;
+    size_t workspace_bytes;
+} hypic_compose_desc;
+
+hypic_status hypic_compose(const hypic_compose_desc* desc, hypic_stream_t stream);
+size_t hypic_compose_workspace_bytes(const hypic_compose_desc* desc);
+
+/* ------------------------------------------------------------------------------------
+ * hypic_seam_advance -- seam tokens through the running state (dense kind).
+ *
+ * [news], seam-window paragraph: the first w tokens of a reused segment are
+ * not cached; on reuse they are recomputed under the full prefix, so the
+ * linear layers compute the seam's own T and S on the fly, advance the
+ * running state, and hand each seam token's output to the layers above.
+ * [readme], "PIC modes": the window width is a runtime knob, default 8.
+ *
+ * Seam s covers tokens [cu_seam[s], cu_seam[s+1]) of the packed seam axis
+ * (any length; w <= 64 runs as a single chunk).  Needs
+ * hypic_seam_advance_workspace_bytes() of device workspace (the seam table).
+ * Layouts (B = n_batch, N = n_tokens = packed seam tokens):
+ *   q, k        [B, N, h_k, d_k]  in_dtype;   v [B, N, h_v, d_v] in_dtype
+ *   log_alpha, beta  float32 [B, N, h_v]
+ *   S_in        float32, seam s at S_in + s * state_stride: [B, h_v, d_k, d_v];
+ *               NULL = zero.  state_stride 0 means B*h_v*d_k*d_v.
+ *   o           [B, N, h_v, d_v] out_dtype, or NULL
+ *   S_out       float32, same addressing as S_in (may alias S_in), or NULL
+ *   T_hat       float32 [n_seam, B, h_v, d_k, d_k] or NULL; T_exp int32 [n_seam, B, h_v]
+ *   S_seam      float32 [n_seam, B, h_v, d_k, d_v] or NULL: the seam's zero-start state
+ * ---------------------------------------------------------------------------------- */
+typedef struct {
+    hypic_dtype in_dtype;
+    hypic_dtype out_dtype;
+    int32_t n_batch;
+    int64_t n_tokens;
+    int32_t h_k, h_v, d_k, d_v;
+    int32_t n_seam;
+    const int64_t* cu_seam;     /* host [n_seam + 1] */
+    int32_t qk_l2norm;          /* 1: q and k scaled to unit L2 norm per token and head */
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* log_alpha;
+    const float* beta;
+    const float* S_in;
+    int64_t state_stride;       /* floats between consecutive seams in S_in / S_out */
+    void* o;
+    float* S_out;
+    float* T_hat;
+    int32_t* T_exp;
+    float* S_seam;
+    hypic_precision precision;
+    void* workspace;
+    size_t workspace_bytes;
+} hypic_seam_desc;
+
+hypic_status hypic_seam_advance(const hypic_seam_desc* desc, hypic_stream_t stream);
+size_t hypic_seam_advance_workspace_bytes(const hypic_seam_desc* desc);
+
+/* ------------------------------------------------------------------------------------
+ * hypic_conv_warmup -- depthwise causal convolution with the state carried
+ * across a segment boundary ([news], linear-layer paragraph: conv-state
+ * warm-up aligns variants that run a causal conv before the recurrence).
+ *
+ *   y_t[c] = act( bias[c] + sum_{j=0}^{W-1} weight[c, j] * xx_{t+j}[c] )
+ * where xx is the segment's W-1 carried inputs followed by its x rows, so
+ * tap W-1 multiplies the current token (PyTorch Conv1d cross-correlation with
+ * left padding W-1).  state_out receives the segment's last W-1 rows of xx.
+ * Layouts (B = n_batch, N = n_tokens, C = channels, W = width = 4):
+ *   x          [B, N, C] in_dtype
+ *   state_in   [n_state, B, W-1, C] in_dtype, or NULL (zero state)
+ *   state_index device int32 [n_seg]: row of state_in for segment s, -1 = zero;
+ *               NULL = identity (segment s uses state_in[s], n_state >= n_seg)
+ *   weight     float32 [C, W];  bias float32 [C] or NULL
+ *   y          [B, N, C] out_dtype
+ *   state_out  [n_seg, B, W-1, C] in_dtype, or NULL
+ * channels must be a multiple of 8.  Needs hypic_conv_warmup_workspace_bytes()
+ * of device workspace (the segment table).
+ * ---------------------------------------------------------------------------------- */
+typedef struct {
+    hypic_dtype in_dtype;
+    hypic_dtype out_dtype;
+    int32_t n_batch;
+    int64_t n_tokens;
+    int32_t channels;
+    int32_t width;
+    int32_t n_seg;
+    const int64_t* cu_seqlens;  /* host [n_seg + 1] */
+    const void* x;
+    const void* state_in;
+    int32_t n_state;
+    const int32_t* state_index;
+    const float* weight;
+    const float* bias;
+    hypic_activation activation;
+    void* y;
+    void* state_out;
+    void* workspace;
+    size_t workspace_bytes;
+} hypic_conv_desc;
+
+hypic_status hypic_conv_warmup(const hypic_conv_desc* desc, hypic_stream_t stream);
+size_t hypic_conv_warmup_workspace_bytes(const hypic_conv_desc* desc);
+
+/* ------------------------------------------------------------------------------------
+ * hypic_plan_schedule -- host-only planner behind HYPIC_SCHED_* (no GPU use).
+ *
+ * Assigns n tasks of integer weight (chunks) to `groups` workers.  LPT: tasks in
+ * order of decreasing weight (ties: lower index first), each to the least-loaded
+ * worker (ties: lower worker), Graham's longest-processing-time rule.  RR: task
+ * i to worker i mod groups.  Writes order[n] (LPT processing order; identity
+ * for RR), assign[n] and *makespan (max worker load).  Either output array may
+ * be NULL.  Returns HYPIC_ERR_INVALID_ARGUMENT on negative weights, n < 0 or
+ * groups < 1.
+ * ---------------------------------------------------------------------------------- */
+hypic_status hypic_plan_schedule(const int64_t* weights, int32_t n, int32_t groups,
+                                 hypic_schedule schedule, int32_t* order, int32_t* assign,
+                                 int64_t* makespan);
+
+const char* hypic_last_error(void);
+int hypic_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HYPIC_H */

@@ -1,0 +1,671 @@
+// libhypic C ABI: argument validation, workspace layout, schedule planning, launches.
+//
+// Every entry point validates all of its arguments on the host before touching the
+// HIP runtime; on failure it enqueues nothing and returns a status with a message in
+// the thread-local hypic_last_error().
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <numeric>
+#include <string>
+#include <vector>
+
+#include "../../include/hypic.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+hypic_status fail(hypic_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+hypic_status ok() {
+    g_err.clear();
+    return HYPIC_OK;
+}
+
+hypic_status device_fail(const char* what, hipError_t e) {
+    return fail(HYPIC_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Validate a host offset table: cu[0] = 0, non-decreasing, cu[n] <= limit.
+hypic_status check_offsets(const int64_t* cu, int32_t n, int64_t limit, const char* name) {
+    if (n < 0) return fail(HYPIC_ERR_INVALID_ARGUMENT, "%s: negative segment count %d", name, n);
+    if (!cu) return fail(HYPIC_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+    if (cu[0] != 0) return fail(HYPIC_ERR_INVALID_ARGUMENT, "%s[0] = %lld, must be 0", name, (long long)cu[0]);
+    for (int32_t i = 0; i < n; ++i)
+        if (cu[i + 1] < cu[i])
+            return fail(HYPIC_ERR_INVALID_ARGUMENT, "%s is decreasing at %d (%lld > %lld)", name, i,
+                        (long long)cu[i], (long long)cu[i + 1]);
+    if (cu[n] > limit)
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "%s[%d] = %lld exceeds n_tokens = %lld", name, n, (long long)cu[n],
+                    (long long)limit);
+    return HYPIC_OK;
+}
+
+// Segment table uploaded to the workspace: starts (int64), lengths (int32), task order.
+struct SegTable {
+    size_t off_start = 0, off_len = 0, off_order = 0, bytes = 0;
+};
+
+SegTable seg_table_layout(int32_t n_seg, int64_t n_order) {
+    SegTable t;
+    t.off_start = 0;
+    t.off_len = align_up(sizeof(int64_t) * std::max<int64_t>(n_seg, 1));
+    t.off_order = t.off_len + align_up(sizeof(int32_t) * std::max<int64_t>(n_seg, 1));
+    t.bytes = t.off_order + align_up(sizeof(int32_t) * std::max<int64_t>(n_order, 0));
+    return t;
+}
+
+// host image of the segment table, copied in one transfer
+hipError_t upload_seg_table(const SegTable& L, void* ws, const std::vector<int64_t>& start,
+                            const std::vector<int32_t>& len, const std::vector<int32_t>& order, hipStream_t s) {
+    std::vector<unsigned char> img(L.bytes, 0);
+    if (!start.empty()) memcpy(img.data() + L.off_start, start.data(), start.size() * sizeof(int64_t));
+    if (!len.empty()) memcpy(img.data() + L.off_len, len.data(), len.size() * sizeof(int32_t));
+    if (!order.empty()) memcpy(img.data() + L.off_order, order.data(), order.size() * sizeof(int32_t));
+    // pageable source: the runtime stages it before returning, so img may die afterwards
+    return hipMemcpyAsync(ws, img.data(), L.bytes, hipMemcpyHostToDevice, s);
+}
+
+bool supported_d(int d) { return d == 64 || d == 128; }
+
+int64_t build_tasks(const hypic_build_desc* d) { return (int64_t)d->n_seg * d->n_batch * d->h_v; }
+
+hypic_status validate_build(const hypic_build_desc* d) {
+    if (!d) return fail(HYPIC_ERR_INVALID_ARGUMENT, "build: desc is NULL");
+    if (d->kind < HYPIC_DENSE_DELTA || d->kind > HYPIC_SCALAR)
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "build: unknown kind %d", (int)d->kind);
+    if (d->in_dtype != HYPIC_F32 && d->in_dtype != HYPIC_BF16)
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "build: unknown in_dtype %d", (int)d->in_dtype);
+    if (d->n_batch < 1 || d->n_tokens < 0 || d->h_k < 1 || d->h_v < 1)
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "build: bad geometry n_batch=%d n_tokens=%lld h_k=%d h_v=%d",
+                    d->n_batch, (long long)d->n_tokens, d->h_k, d->h_v);
+    if (d->h_v % d->h_k != 0)
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "build: h_v=%d is not a multiple of h_k=%d", d->h_v, d->h_k);
+    if (d->d_k != d->d_v || !supported_d(d->d_k))
+        return fail(HYPIC_ERR_UNSUPPORTED, "build: d_k=%d d_v=%d (supported: d_k == d_v in {64, 128})", d->d_k, d->d_v);
+    if (d->chunk != 64) return fail(HYPIC_ERR_UNSUPPORTED, "build: chunk=%d (supported: 64)", d->chunk);
+    if (d->skip_head < 0) return fail(HYPIC_ERR_INVALID_ARGUMENT, "build: skip_head=%d < 0", d->skip_head);
+    if (d->qk_l2norm != 0 && d->qk_l2norm != 1)
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "build: qk_l2norm=%d must be 0 or 1", d->qk_l2norm);
+    if (d->qk_l2norm && d->kind != HYPIC_DENSE_DELTA)
+        return fail(HYPIC_ERR_UNSUPPORTED, "build: qk_l2norm is supported for the dense kind only");
+    hypic_status st = check_offsets(d->cu_seqlens, d->n_seg, d->n_tokens, "build: cu_seqlens");
+    if (st != HYPIC_OK) return st;
+    for (int32_t i = 0; i < d->n_seg; ++i)
+        if (d->cu_seqlens[i + 1] - d->cu_seqlens[i] > (int64_t)1 << 30)
+            return fail(HYPIC_ERR_UNSUPPORTED, "build: segment %d longer than 2^30 tokens", i);
+    if (build_tasks(d) > INT32_MAX) return fail(HYPIC_ERR_UNSUPPORTED, "build: too many (segment, chain) tasks");
+    if (d->n_seg > 0 && d->n_tokens > 0) {
+        if (!d->k || !d->v || !d->log_alpha)
+            return fail(HYPIC_ERR_INVALID_ARGUMENT, "build: k, v and log_alpha are required");
+        if (!aligned16(d->k) || !aligned16(d->v))
+            return fail(HYPIC_ERR_INVALID_ARGUMENT, "build: k and v must be 16-byte aligned");
+    }
+    if (d->kind == HYPIC_DENSE_DELTA) {
+        if (d->n_seg > 0 && d->n_tokens > 0 && !d->beta)
+            return fail(HYPIC_ERR_INVALID_ARGUMENT, "build: beta is required for the dense kind");
+    } else if (d->beta) {
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "build: beta must be NULL for the diagonal and scalar kinds");
+    }
+    if (d->n_seg > 0 && !d->S) return fail(HYPIC_ERR_INVALID_ARGUMENT, "build: S is NULL");
+    if ((d->T_hat == nullptr) != (d->T_exp == nullptr))
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "build: T_hat and T_exp must be both set or both NULL");
+    if (d->schedule < HYPIC_SCHED_NATURAL || d->schedule > HYPIC_SCHED_RR)
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "build: unknown schedule %d", (int)d->schedule);
+    if (d->precision < HYPIC_PREC_AUTO || d->precision > HYPIC_PREC_F16)
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "build: unknown precision %d", (int)d->precision);
+    if (d->kind == HYPIC_DENSE_DELTA) {
+        const bool f32 = d->precision == HYPIC_PREC_F32 ||
+                         (d->precision == HYPIC_PREC_AUTO && d->in_dtype == HYPIC_F32 && d->d_k == 64);
+        if (f32 && d->d_k != 64)
+            return fail(HYPIC_ERR_UNSUPPORTED, "build: the F32 operand plan supports d = 64 only");
+    }
+    return HYPIC_OK;
+}
+
+bool build_prec_f32(const hypic_build_desc* d) {
+    return d->precision == HYPIC_PREC_F32 ||
+           (d->precision == HYPIC_PREC_AUTO && d->in_dtype == HYPIC_F32 && d->d_k == 64);
+}
+
+int device_cu_count() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    return n;
+}
+
+// LPT order of segments (longest first, ties by index), expanded to tasks.
+std::vector<int32_t> lpt_task_order(const std::vector<int32_t>& len, int32_t per_seg) {
+    std::vector<int32_t> segs(len.size());
+    std::iota(segs.begin(), segs.end(), 0);
+    std::stable_sort(segs.begin(), segs.end(), [&](int32_t a, int32_t b) { return len[a] > len[b]; });
+    std::vector<int32_t> order;
+    order.reserve(segs.size() * per_seg);
+    for (int32_t s : segs)
+        for (int32_t j = 0; j < per_seg; ++j) order.push_back(s * per_seg + j);
+    return order;
+}
+
+}  // namespace
+
+// The public functions take C linkage from their declarations in hypic.h.
+
+const char* hypic_last_error(void) { return g_err.c_str(); }
+int hypic_version(void) { return HYPIC_VERSION; }
+
+hypic_status hypic_plan_schedule(const int64_t* weights, int32_t n, int32_t groups, hypic_schedule schedule,
+                                 int32_t* order, int32_t* assign, int64_t* makespan) {
+    if (n < 0) return fail(HYPIC_ERR_INVALID_ARGUMENT, "plan: n = %d < 0", n);
+    if (groups < 1) return fail(HYPIC_ERR_INVALID_ARGUMENT, "plan: groups = %d < 1", groups);
+    if (n > 0 && !weights) return fail(HYPIC_ERR_INVALID_ARGUMENT, "plan: weights is NULL");
+    for (int32_t i = 0; i < n; ++i)
+        if (weights[i] < 0) return fail(HYPIC_ERR_INVALID_ARGUMENT, "plan: weight %d is negative", i);
+    if (schedule != HYPIC_SCHED_LPT && schedule != HYPIC_SCHED_RR && schedule != HYPIC_SCHED_NATURAL)
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "plan: unknown schedule %d", (int)schedule);
+    std::vector<int32_t> ord(n);
+    std::iota(ord.begin(), ord.end(), 0);
+    std::vector<int64_t> load(groups, 0);
+    std::vector<int32_t> asg(n, 0);
+    if (schedule == HYPIC_SCHED_LPT) {
+        std::stable_sort(ord.begin(), ord.end(), [&](int32_t a, int32_t b) { return weights[a] > weights[b]; });
+        for (int32_t i : ord) {
+            int32_t g = 0;
+            for (int32_t j = 1; j < groups; ++j)
+                if (load[j] < load[g]) g = j;
+            asg[i] = g;
+            load[g] += weights[i];
+        }
+    } else {
+        for (int32_t i = 0; i < n; ++i) {
+            asg[i] = i % groups;
+            load[i % groups] += weights[i];
+        }
+    }
+    if (order) std::copy(ord.begin(), ord.end(), order);
+    if (assign) std::copy(asg.begin(), asg.end(), assign);
+    if (makespan) *makespan = n ? *std::max_element(load.begin(), load.end()) : 0;
+    return ok();
+}
+
+// ------------------------------------------------------------------------------------------
+// segment build
+
+size_t hypic_segment_build_workspace_bytes(const hypic_build_desc* d) {
+    if (!d || d->n_seg < 0) return 0;
+    const int64_t n_order = d->schedule == HYPIC_SCHED_LPT ? build_tasks(d) : 0;
+    return seg_table_layout(d->n_seg, n_order).bytes;
+}
+
+hypic_status hypic_segment_build(const hypic_build_desc* d, hypic_stream_t stream) {
+    hypic_status st = validate_build(d);
+    if (st != HYPIC_OK) return st;
+    const int64_t n_tasks = build_tasks(d);
+    if (n_tasks == 0) return ok();
+    const SegTable L = seg_table_layout(d->n_seg, d->schedule == HYPIC_SCHED_LPT ? n_tasks : 0);
+    if (!d->workspace || d->workspace_bytes < L.bytes)
+        return fail(HYPIC_ERR_WORKSPACE_TOO_SMALL, "build: workspace of %zu bytes needed, %zu given", L.bytes,
+                    d->workspace ? d->workspace_bytes : (size_t)0);
+    if (reinterpret_cast<uintptr_t>(d->workspace) % kAlign)
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "build: workspace must be 256-byte aligned");
+
+    std::vector<int64_t> start(d->n_seg);
+    std::vector<int32_t> len(d->n_seg);
+    for (int32_t i = 0; i < d->n_seg; ++i) {
+        start[i] = d->cu_seqlens[i] + d->skip_head;
+        len[i] = (int32_t)std::max<int64_t>(0, d->cu_seqlens[i + 1] - start[i]);
+    }
+    std::vector<int32_t> order;
+    if (d->schedule == HYPIC_SCHED_LPT) order = lpt_task_order(len, d->n_batch * d->h_v);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = upload_seg_table(L, d->workspace, start, len, order, s);
+    if (e != hipSuccess) return device_fail("build: segment table upload", e);
+    unsigned char* ws = static_cast<unsigned char*>(d->workspace);
+    const long long* dstart = reinterpret_cast<const long long*>(ws + L.off_start);
+    const int* dlen = reinterpret_cast<const int*>(ws + L.off_len);
+    const int* dorder = order.empty() ? nullptr : reinterpret_cast<const int*>(ws + L.off_order);
+
+    if (d->kind == HYPIC_DENSE_DELTA) {
+        hypic::EngineArgs a{};
+        a.n_batch = d->n_batch;
+        a.n_tokens = d->n_tokens;
+        a.h_k = d->h_k;
+        a.h_v = d->h_v;
+        a.n_seg = d->n_seg;
+        a.qk_l2norm = d->qk_l2norm;
+        a.in_bf16 = d->in_dtype == HYPIC_BF16;
+        a.seg_start = dstart;
+        a.seg_len = dlen;
+        a.order = dorder;
+        a.n_tasks = (int)n_tasks;
+        a.k = d->k;
+        a.v = d->v;
+        a.log_alpha = d->log_alpha;
+        a.beta = d->beta;
+        a.S_out = d->S;
+        a.out_stride = (long long)d->n_batch * d->h_v * d->d_k * d->d_v;
+        a.T_hat = d->T_hat;
+        a.T_exp = d->T_exp;
+        int grid = (int)n_tasks;
+        if (d->schedule == HYPIC_SCHED_RR) {
+            const int cus = device_cu_count();
+            if (cus <= 0) return fail(HYPIC_ERR_DEVICE, "build: cannot query the device's compute units");
+            a.persistent = 1;
+            grid = (int)std::min<int64_t>(n_tasks, cus);
+        }
+        e = hypic::launch_dense_engine(a, d->d_k, build_prec_f32(d) ? 1 : 0, grid, s);
+        if (e != hipSuccess) return device_fail("build: dense engine launch", e);
+    } else {
+        hypic::DiagArgs a{};
+        a.n_batch = d->n_batch;
+        a.n_tokens = d->n_tokens;
+        a.h_k = d->h_k;
+        a.h_v = d->h_v;
+        a.n_seg = d->n_seg;
+        a.scalar = d->kind == HYPIC_SCALAR;
+        a.in_bf16 = d->in_dtype == HYPIC_BF16;
+        a.seg_start = dstart;
+        a.seg_len = dlen;
+        a.order = dorder;
+        a.n_tasks = (int)n_tasks;
+        a.k = d->k;
+        a.v = d->v;
+        a.log_alpha = d->log_alpha;
+        a.T_hat = d->T_hat;
+        a.T_exp = d->T_exp;
+        a.S = d->S;
+        if (d->schedule == HYPIC_SCHED_RR)
+            return fail(HYPIC_ERR_UNSUPPORTED, "build: RR schedule is implemented for the dense kind only");
+        e = hypic::launch_diag_build(a, d->d_k, s);
+        if (e != hipSuccess) return device_fail("build: diagonal build launch", e);
+    }
+    return ok();
+}
+
+// ------------------------------------------------------------------------------------------
+// compose
+
+namespace {
+
+int scan_block_size(const hypic_compose_desc* d) {
+    if (d->scan_block > 0) return d->scan_block;
+    int b = 1;
+    while (b * b < d->n_elem) ++b;  // ~sqrt(n): balances the two sequential phases
+    return std::max(b, 2);
+}
+
+hypic_compose_mode resolve_mode(const hypic_compose_desc* d) {
+    if (d->mode != HYPIC_COMPOSE_AUTO) return d->mode;
+    // few chains cannot fill the GPU with one block per chain: use the blocked scan
+    return (d->n_elem >= 16 && (int64_t)d->n_chain * 4 < 1024) ? HYPIC_COMPOSE_SCAN : HYPIC_COMPOSE_FOLD;
+}
+
+struct ScanLayout {
+    size_t aggT = 0, aggE = 0, aggS = 0, pre = 0, bytes = 0;
+};
+
+ScanLayout scan_layout(const hypic_compose_desc* d, int nblk) {
+    const int64_t C = d->n_chain, D = d->d_k;
+    const int64_t tlen = d->kind == HYPIC_DENSE_DELTA ? D * D : (d->kind == HYPIC_DIAG ? D : 1);
+    ScanLayout L;
+    L.aggT = 0;
+    L.aggE = L.aggT + align_up(sizeof(float) * nblk * C * tlen);
+    L.aggS = L.aggE + align_up(sizeof(int32_t) * nblk * C);
+    L.pre = L.aggS + align_up(sizeof(float) * nblk * C * D * D);
+    L.bytes = L.pre + (d->S_prefix ? align_up(sizeof(float) * nblk * C * D * D) : 0);
+    return L;
+}
+
+hypic_status validate_compose(const hypic_compose_desc* d) {
+    if (!d) return fail(HYPIC_ERR_INVALID_ARGUMENT, "compose: desc is NULL");
+    if (d->kind < HYPIC_DENSE_DELTA || d->kind > HYPIC_SCALAR)
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "compose: unknown kind %d", (int)d->kind);
+    if (d->mode < HYPIC_COMPOSE_AUTO || d->mode > HYPIC_COMPOSE_NAIVE_ADD)
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "compose: unknown mode %d", (int)d->mode);
+    if (d->n_chain < 1 || d->n_elem < 0 || d->n_slot < 0)
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "compose: bad n_chain=%d n_elem=%d n_slot=%d", d->n_chain, d->n_elem,
+                    d->n_slot);
+    if (d->d_k != d->d_v || !supported_d(d->d_k))
+        return fail(HYPIC_ERR_UNSUPPORTED, "compose: d_k=%d d_v=%d (supported: d_k == d_v in {64, 128})", d->d_k,
+                    d->d_v);
+    if (!d->slot && d->n_slot < d->n_elem)
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "compose: slot is NULL but n_slot=%d < n_elem=%d", d->n_slot,
+                    d->n_elem);
+    if (!d->S_final) return fail(HYPIC_ERR_INVALID_ARGUMENT, "compose: S_final is NULL");
+    if (d->n_elem > 0 && !d->S) return fail(HYPIC_ERR_INVALID_ARGUMENT, "compose: S is NULL");
+    const hypic_compose_mode m = resolve_mode(d);
+    if (m != HYPIC_COMPOSE_NAIVE_ADD && d->n_elem > 0 && (!d->T_hat || !d->T_exp))
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "compose: T_hat and T_exp are required");
+    if ((d->T_total == nullptr) != (d->T_total_exp == nullptr))
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "compose: T_total and T_total_exp must be both set or both NULL");
+    if (m == HYPIC_COMPOSE_NAIVE_ADD && d->T_total)
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "compose: NAIVE_ADD has no transition; T_total must be NULL");
+    if (d->T_hat && !aligned16(d->T_hat))
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "compose: T_hat must be 16-byte aligned");
+    if (d->scan_block < 0) return fail(HYPIC_ERR_INVALID_ARGUMENT, "compose: scan_block < 0");
+    if ((int64_t)d->n_chain * d->n_elem > INT32_MAX || d->n_chain > 65535 * 1024)
+        return fail(HYPIC_ERR_UNSUPPORTED, "compose: too many chains x elements");
+    return HYPIC_OK;
+}
+
+}  // namespace
+
+size_t hypic_compose_workspace_bytes(const hypic_compose_desc* d) {
+    if (!d || d->n_elem <= 0 || d->n_chain <= 0) return 0;
+    if (resolve_mode(d) != HYPIC_COMPOSE_SCAN) return 0;
+    const int B = scan_block_size(d);
+    return scan_layout(d, (d->n_elem + B - 1) / B).bytes;
+}
+
+hypic_status hypic_compose(const hypic_compose_desc* d, hypic_stream_t stream) {
+    hypic_status st = validate_compose(d);
+    if (st != HYPIC_OK) return st;
+    const hypic_compose_mode m = resolve_mode(d);
+    const int kind = d->kind == HYPIC_DENSE_DELTA ? 0 : (d->kind == HYPIC_DIAG ? 1 : 2);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const int D = d->d_k;
+    const bool wantT = d->T_total != nullptr;
+    int nblk = 1, B = d->n_elem;
+    ScanLayout L;
+    if (m == HYPIC_COMPOSE_SCAN && d->n_elem > 0) {
+        B = scan_block_size(d);
+        nblk = (d->n_elem + B - 1) / B;
+        L = scan_layout(d, nblk);
+        if (!d->workspace || d->workspace_bytes < L.bytes)
+            return fail(HYPIC_ERR_WORKSPACE_TOO_SMALL, "compose: workspace of %zu bytes needed, %zu given", L.bytes,
+                        d->workspace ? d->workspace_bytes : (size_t)0);
+        if (reinterpret_cast<uintptr_t>(d->workspace) % kAlign)
+            return fail(HYPIC_ERR_INVALID_ARGUMENT, "compose: workspace must be 256-byte aligned");
+    }
+    hipError_t e;
+    if (m != HYPIC_COMPOSE_SCAN || d->n_elem == 0) {
+        hypic::FoldArgs a{};
+        a.kind = kind;
+        a.n_chain = d->n_chain;
+        a.n_elem = d->n_elem;
+        a.per_block = std::max(1, d->n_elem);
+        a.n_block = 1;
+        a.slot = d->slot;
+        a.T_hat = d->T_hat;
+        a.T_exp = d->T_exp;
+        a.S = d->S;
+        a.init_S = d->S0;
+        a.out_S = d->S_final;
+        a.out_T = d->T_total;
+        a.out_e = d->T_total_exp;
+        a.prefix = d->S_prefix;
+        a.naive = m == HYPIC_COMPOSE_NAIVE_ADD;
+        e = hypic::launch_fold(a, D, wantT ? 1 : 0, s);
+        if (e != hipSuccess) return device_fail("compose: fold launch", e);
+        return ok();
+    }
+    unsigned char* ws = static_cast<unsigned char*>(d->workspace);
+    float* aggT = reinterpret_cast<float*>(ws + L.aggT);
+    int* aggE = reinterpret_cast<int*>(ws + L.aggE);
+    float* aggS = reinterpret_cast<float*>(ws + L.aggS);
+    float* pre = d->S_prefix ? reinterpret_cast<float*>(ws + L.pre) : nullptr;
+    // 1) block aggregates (T_b, S_b) from (I, 0)
+    hypic::FoldArgs a{};
+    a.kind = kind;
+    a.n_chain = d->n_chain;
+    a.n_elem = d->n_elem;
+    a.per_block = B;
+    a.n_block = nblk;
+    a.slot = d->slot;
+    a.T_hat = d->T_hat;
+    a.T_exp = d->T_exp;
+    a.S = d->S;
+    a.out_S = aggS;
+    a.out_T = aggT;
+    a.out_e = aggE;
+    e = hypic::launch_fold(a, D, 1, s);
+    if (e != hipSuccess) return device_fail("compose: scan reduce launch", e);
+    // 2) fold over the block aggregates from S0: final state, block-entry states
+    hypic::FoldArgs b{};
+    b.kind = kind;
+    b.n_chain = d->n_chain;
+    b.n_elem = nblk;
+    b.per_block = nblk;
+    b.n_block = 1;
+    b.T_hat = aggT;
+    b.T_exp = aggE;
+    b.S = aggS;
+    b.init_S = d->S0;
+    b.out_S = d->S_final;
+    b.out_T = d->T_total;
+    b.out_e = d->T_total_exp;
+    b.prefix = pre;
+    e = hypic::launch_fold(b, D, wantT ? 1 : 0, s);
+    if (e != hipSuccess) return device_fail("compose: scan of block aggregates launch", e);
+    // 3) re-fold each block from its entry state, writing the per-element states
+    if (d->S_prefix) {
+        hypic::FoldArgs c{};
+        c.kind = kind;
+        c.n_chain = d->n_chain;
+        c.n_elem = d->n_elem;
+        c.per_block = B;
+        c.n_block = nblk;
+        c.slot = d->slot;
+        c.T_hat = d->T_hat;
+        c.T_exp = d->T_exp;
+        c.S = d->S;
+        c.init_S = pre;
+        c.prefix = d->S_prefix;
+        e = hypic::launch_fold(c, D, 0, s);
+        if (e != hipSuccess) return device_fail("compose: scan re-fold launch", e);
+    }
+    return ok();
+}
+
+// ------------------------------------------------------------------------------------------
+// seam advance
+
+namespace {
+
+hypic_status validate_seam(const hypic_seam_desc* d) {
+    if (!d) return fail(HYPIC_ERR_INVALID_ARGUMENT, "seam: desc is NULL");
+    if (d->in_dtype != HYPIC_F32 && d->in_dtype != HYPIC_BF16)
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "seam: unknown in_dtype %d", (int)d->in_dtype);
+    if (d->out_dtype != HYPIC_F32 && d->out_dtype != HYPIC_BF16)
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "seam: unknown out_dtype %d", (int)d->out_dtype);
+    if (d->n_batch < 1 || d->n_tokens < 0 || d->h_k < 1 || d->h_v < 1 || d->h_v % d->h_k)
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "seam: bad geometry");
+    if (d->d_k != d->d_v || !supported_d(d->d_k))
+        return fail(HYPIC_ERR_UNSUPPORTED, "seam: d_k=%d d_v=%d (supported: d_k == d_v in {64, 128})", d->d_k, d->d_v);
+    if (d->qk_l2norm != 0 && d->qk_l2norm != 1) return fail(HYPIC_ERR_INVALID_ARGUMENT, "seam: qk_l2norm must be 0/1");
+    hypic_status st = check_offsets(d->cu_seam, d->n_seam, d->n_tokens, "seam: cu_seam");
+    if (st != HYPIC_OK) return st;
+    if ((int64_t)d->n_seam * d->n_batch * d->h_v > INT32_MAX) return fail(HYPIC_ERR_UNSUPPORTED, "seam: too many tasks");
+    if (d->n_tokens > 0 && d->n_seam > 0) {
+        if (!d->k || !d->v || !d->log_alpha || !d->beta)
+            return fail(HYPIC_ERR_INVALID_ARGUMENT, "seam: k, v, log_alpha and beta are required");
+        if (!aligned16(d->k) || !aligned16(d->v) || (d->q && !aligned16(d->q)))
+            return fail(HYPIC_ERR_INVALID_ARGUMENT, "seam: q, k and v must be 16-byte aligned");
+    }
+    if (d->o && !d->q) return fail(HYPIC_ERR_INVALID_ARGUMENT, "seam: o requested without q");
+    if ((d->T_hat == nullptr) != (d->T_exp == nullptr))
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "seam: T_hat and T_exp must be both set or both NULL");
+    const int64_t dense = (int64_t)d->n_batch * d->h_v * d->d_k * d->d_v;
+    if (d->state_stride != 0 && d->state_stride < dense)
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "seam: state_stride %lld overlaps seams (minimum %lld)",
+                    (long long)d->state_stride, (long long)dense);
+    if (d->precision < HYPIC_PREC_AUTO || d->precision > HYPIC_PREC_F16)
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "seam: unknown precision");
+    const bool f32 = d->precision == HYPIC_PREC_F32 ||
+                     (d->precision == HYPIC_PREC_AUTO && d->in_dtype == HYPIC_F32 && d->d_k == 64);
+    if (f32 && d->d_k != 64) return fail(HYPIC_ERR_UNSUPPORTED, "seam: the F32 operand plan supports d = 64 only");
+    return HYPIC_OK;
+}
+
+}  // namespace
+
+size_t hypic_seam_advance_workspace_bytes(const hypic_seam_desc* d) {
+    if (!d || d->n_seam < 0) return 0;
+    return seg_table_layout(d->n_seam, 0).bytes;
+}
+
+hypic_status hypic_seam_advance(const hypic_seam_desc* d, hypic_stream_t stream) {
+    hypic_status st = validate_seam(d);
+    if (st != HYPIC_OK) return st;
+    const int64_t n_tasks = (int64_t)d->n_seam * d->n_batch * d->h_v;
+    if (n_tasks == 0) return ok();
+    const SegTable L = seg_table_layout(d->n_seam, 0);
+    if (!d->workspace || d->workspace_bytes < L.bytes)
+        return fail(HYPIC_ERR_WORKSPACE_TOO_SMALL, "seam: workspace of %zu bytes needed, %zu given", L.bytes,
+                    d->workspace ? d->workspace_bytes : (size_t)0);
+    if (reinterpret_cast<uintptr_t>(d->workspace) % kAlign)
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "seam: workspace must be 256-byte aligned");
+    std::vector<int64_t> start(d->n_seam);
+    std::vector<int32_t> len(d->n_seam);
+    for (int32_t i = 0; i < d->n_seam; ++i) {
+        start[i] = d->cu_seam[i];
+        len[i] = (int32_t)(d->cu_seam[i + 1] - d->cu_seam[i]);
+    }
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = upload_seg_table(L, d->workspace, start, len, {}, s);
+    if (e != hipSuccess) return device_fail("seam: table upload", e);
+    unsigned char* ws = static_cast<unsigned char*>(d->workspace);
+    const int64_t dense = (int64_t)d->n_batch * d->h_v * d->d_k * d->d_v;
+    const bool f32 = d->precision == HYPIC_PREC_F32 ||
+                     (d->precision == HYPIC_PREC_AUTO && d->in_dtype == HYPIC_F32 && d->d_k == 64);
+    hypic::EngineArgs a{};
+    a.n_batch = d->n_batch;
+    a.n_tokens = d->n_tokens;
+    a.h_k = d->h_k;
+    a.h_v = d->h_v;
+    a.n_seg = d->n_seam;
+    a.qk_l2norm = d->qk_l2norm;
+    a.in_bf16 = d->in_dtype == HYPIC_BF16;
+    a.out_bf16 = d->out_dtype == HYPIC_BF16;
+    a.seg_start = reinterpret_cast<const long long*>(ws + L.off_start);
+    a.seg_len = reinterpret_cast<const int*>(ws + L.off_len);
+    a.n_tasks = (int)n_tasks;
+    a.k = d->k;
+    a.v = d->v;
+    a.log_alpha = d->log_alpha;
+    a.beta = d->beta;
+    if (d->o || d->S_out || d->T_hat) {
+        hypic::EngineArgs r = a;
+        r.q = d->o ? d->q : nullptr;
+        r.o = d->o;
+        r.S_in = d->S_in;
+        r.in_stride = d->state_stride ? d->state_stride : dense;
+        r.S_out = d->S_out;
+        r.out_stride = d->state_stride ? d->state_stride : dense;
+        r.T_hat = d->T_hat;
+        r.T_exp = d->T_exp;
+        e = hypic::launch_dense_engine(r, d->d_k, f32 ? 1 : 0, (int)n_tasks, s);
+        if (e != hipSuccess) return device_fail("seam: engine launch", e);
+    }
+    if (d->S_seam) {
+        // the seam's own zero-start state (its transition comes from the run above)
+        hypic::EngineArgs r = a;
+        r.S_out = d->S_seam;
+        r.out_stride = dense;
+        e = hypic::launch_dense_engine(r, d->d_k, f32 ? 1 : 0, (int)n_tasks, s);
+        if (e != hipSuccess) return device_fail("seam: zero-start engine launch", e);
+    }
+    return ok();
+}
+
+// ------------------------------------------------------------------------------------------
+// conv warm-up
+
+namespace {
+
+hypic_status validate_conv(const hypic_conv_desc* d) {
+    if (!d) return fail(HYPIC_ERR_INVALID_ARGUMENT, "conv: desc is NULL");
+    if ((d->in_dtype != HYPIC_F32 && d->in_dtype != HYPIC_BF16) ||
+        (d->out_dtype != HYPIC_F32 && d->out_dtype != HYPIC_BF16))
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "conv: unknown dtype");
+    if (d->width != 4) return fail(HYPIC_ERR_UNSUPPORTED, "conv: width=%d (supported: 4)", d->width);
+    if (d->n_batch < 1 || d->n_tokens < 0 || d->channels < 1)
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "conv: bad geometry");
+    if (d->channels % 8) return fail(HYPIC_ERR_UNSUPPORTED, "conv: channels=%d is not a multiple of 8", d->channels);
+    if (d->activation != HYPIC_ACT_NONE && d->activation != HYPIC_ACT_SILU)
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "conv: unknown activation");
+    hypic_status st = check_offsets(d->cu_seqlens, d->n_seg, d->n_tokens, "conv: cu_seqlens");
+    if (st != HYPIC_OK) return st;
+    if (d->n_seg > 65535 || d->n_batch > 65535) return fail(HYPIC_ERR_UNSUPPORTED, "conv: too many segments/batches");
+    if (d->n_seg > 0) {
+        if (!d->weight) return fail(HYPIC_ERR_INVALID_ARGUMENT, "conv: weight is NULL");
+        if (d->n_tokens > 0 && (!d->x || !d->y)) return fail(HYPIC_ERR_INVALID_ARGUMENT, "conv: x and y are required");
+        if ((d->x && !aligned16(d->x)) || (d->y && !aligned16(d->y)) || (d->state_in && !aligned16(d->state_in)) ||
+            (d->state_out && !aligned16(d->state_out)))
+            return fail(HYPIC_ERR_INVALID_ARGUMENT, "conv: x, y and states must be 16-byte aligned");
+        if (d->state_in && !d->state_index && d->n_state < d->n_seg)
+            return fail(HYPIC_ERR_INVALID_ARGUMENT, "conv: state_index is NULL but n_state=%d < n_seg=%d", d->n_state,
+                        d->n_seg);
+    }
+    return HYPIC_OK;
+}
+
+}  // namespace
+
+size_t hypic_conv_warmup_workspace_bytes(const hypic_conv_desc* d) {
+    if (!d || d->n_seg < 0) return 0;
+    return seg_table_layout(d->n_seg, 0).bytes;
+}
+
+hypic_status hypic_conv_warmup(const hypic_conv_desc* d, hypic_stream_t stream) {
+    hypic_status st = validate_conv(d);
+    if (st != HYPIC_OK) return st;
+    if (d->n_seg == 0) return ok();
+    const SegTable L = seg_table_layout(d->n_seg, 0);
+    if (!d->workspace || d->workspace_bytes < L.bytes)
+        return fail(HYPIC_ERR_WORKSPACE_TOO_SMALL, "conv: workspace of %zu bytes needed, %zu given", L.bytes,
+                    d->workspace ? d->workspace_bytes : (size_t)0);
+    if (reinterpret_cast<uintptr_t>(d->workspace) % kAlign)
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "conv: workspace must be 256-byte aligned");
+    std::vector<int64_t> start(d->n_seg);
+    std::vector<int32_t> len(d->n_seg);
+    int64_t span = 3;
+    for (int32_t i = 0; i < d->n_seg; ++i) {
+        start[i] = d->cu_seqlens[i];
+        len[i] = (int32_t)(d->cu_seqlens[i + 1] - d->cu_seqlens[i]);
+        span = std::max<int64_t>(span, len[i]);
+    }
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = upload_seg_table(L, d->workspace, start, len, {}, s);
+    if (e != hipSuccess) return device_fail("conv: table upload", e);
+    unsigned char* ws = static_cast<unsigned char*>(d->workspace);
+    hypic::ConvArgs a{};
+    a.n_batch = d->n_batch;
+    a.n_tokens = d->n_tokens;
+    a.channels = d->channels;
+    a.n_seg = d->n_seg;
+    a.in_bf16 = d->in_dtype == HYPIC_BF16;
+    a.out_bf16 = d->out_dtype == HYPIC_BF16;
+    a.silu = d->activation == HYPIC_ACT_SILU;
+    a.seg_start = reinterpret_cast<const long long*>(ws + L.off_start);
+    a.seg_len = reinterpret_cast<const int*>(ws + L.off_len);
+    a.x = d->x;
+    a.state_in = d->state_in;
+    a.n_state = d->n_state;
+    a.state_index = d->state_index;
+    a.weight = d->weight;
+    a.bias = d->bias;
+    a.y = d->y;
+    a.state_out = d->state_out;
+    e = hypic::launch_conv(a, span, s);
+    if (e != hipSuccess) return device_fail("conv: launch", e);
+    return ok();
+}

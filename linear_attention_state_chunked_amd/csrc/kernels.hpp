@@ -1,0 +1,111 @@
+// Internal launcher interface between the C-ABI host layer and the HIP kernels.
+// Not part of the public API (include/hypic.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hypic {
+
+// One dense (gated delta rule) chunk-engine launch.  Each task is one
+// (segment, batch, value head) chain; it runs the segment's tokens chunk by chunk
+// from X = [I | S_in] and emits T_hat/T_exp (if T_hat), the end state and, with q,
+// the per-token outputs.
+struct EngineArgs {
+    int n_batch;
+    long long n_tokens;
+    int h_k, h_v;
+    int n_seg;
+    int qk_l2norm;
+    int in_bf16;
+    int out_bf16;
+    const long long* seg_start;  // device [n_seg], first token of the segment's covered range
+    const int* seg_len;          // device [n_seg], covered tokens
+    const int* order;            // device [n_tasks] task order, or null (natural)
+    int n_tasks;
+    int persistent;              // 1: grid-stride over tasks (static round robin)
+    const void* k;
+    const void* v;
+    const void* q;               // null: no outputs
+    const float* log_alpha;
+    const float* beta;
+    const float* S_in;           // null: zero
+    long long in_stride;         // floats between segments' state blocks in S_in
+    float* S_out;                // may be null
+    long long out_stride;
+    float* T_hat;                // null: T columns skipped
+    int* T_exp;
+    void* o;
+};
+
+// kind: 0 diagonal (GLA, per-channel log_alpha), 1 scalar
+struct DiagArgs {
+    int n_batch;
+    long long n_tokens;
+    int h_k, h_v;
+    int n_seg;
+    int scalar;
+    int in_bf16;
+    int qk_l2norm;
+    const long long* seg_start;
+    const int* seg_len;
+    const int* order;
+    int n_tasks;
+    const void* k;
+    const void* v;
+    const float* log_alpha;
+    float* T_hat;
+    int* T_exp;
+    float* S;
+};
+
+// One fold launch: grid (chain, block).  Block `blk` folds elements
+// [blk*per_block, min(n_elem, (blk+1)*per_block)) in order, from the state
+// init_S[blk] (or zero) and transition I.
+struct FoldArgs {
+    int kind;                 // 0 dense, 1 diag, 2 scalar
+    int n_chain;
+    int n_elem;
+    int per_block;
+    int n_block;
+    const int* slot;          // element -> slot, or null
+    const float* T_hat;       // element store [n_slot, n_chain, ...]
+    const int* T_exp;
+    const float* S;
+    const float* init_S;      // [n_block, n_chain, dk, dv] or null
+    float* out_S;             // [n_block, n_chain, dk, dv] or null
+    float* out_T;             // [n_block, n_chain, ...] or null
+    int* out_e;               // [n_block, n_chain] or null
+    float* prefix;            // [n_elem, n_chain, dk, dv] or null
+    int naive;                // 1: S <- S + S_i
+};
+
+struct ConvArgs {
+    int n_batch;
+    long long n_tokens;
+    int channels;
+    int n_seg;
+    int in_bf16, out_bf16;
+    int silu;
+    const long long* seg_start;
+    const int* seg_len;
+    const int* seg_of_token_block;  // unused (reserved)
+    const void* x;
+    const void* state_in;
+    int n_state;
+    const int* state_index;
+    const float* weight;
+    const float* bias;
+    void* y;
+    void* state_out;
+};
+
+hipError_t launch_dense_engine(const EngineArgs& a, int d, int prec_f32, int grid, hipStream_t s);
+hipError_t launch_diag_build(const DiagArgs& a, int d, hipStream_t s);
+hipError_t launch_fold(const FoldArgs& a, int d, int with_T, hipStream_t s);
+hipError_t launch_conv(const ConvArgs& a, long long total_tokens, hipStream_t s);
+
+// resident workgroups per CU for the dense engine (for persistent grids)
+int dense_engine_max_lds(int d, int prec_f32, int with_q);
+
+}  // namespace hypic

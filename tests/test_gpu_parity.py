@@ -1,0 +1,289 @@
+"""GPU parity: libhypic (through the C ABI) against the fp64 oracle.
+
+Tolerances: relative Frobenius error per output block (one T, S or o matrix per
+segment or seam and chain), 1e-5 for float32 inputs and 2e-3 for bf16 inputs
+with float32 state and T.  T is compared exponent-aligned; an exactly-zero
+reference block must be exactly zero on the device.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import linear_attention_state_chunked_amd as H
+import oracle as O
+from synth import WORKLOADS, chain_inputs, segment_lengths
+from tests.gpu_util import cu_of, dev_tensor, max_err, oracle_segments
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 1e-5
+TOL_BF16 = 2e-3
+
+
+def _dense_inputs(wl, n, h_v, layer=0, raw_keys=False):
+    """Device inputs [1, n, h, d] for value heads 0..h_v-1 of workload wl, plus the
+    per-chain numpy arrays for the oracle."""
+    h_k = max(1, (h_v * wl.h_k) // wl.h_v)
+    chains = [chain_inputs(wl, layer, h, n) for h in range(h_v)]
+    dt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+    kk = np.stack([chains[(kh * wl.h_v) // wl.h_k]["k"] for kh in range(h_k)], axis=1)
+    qq = np.stack([chains[(kh * wl.h_v) // wl.h_k]["q"] for kh in range(h_k)], axis=1)
+    if raw_keys:
+        rng = np.random.default_rng(99)
+        scale = rng.uniform(0.5, 3.0, size=kk.shape[:2] + (1,)).astype(np.float32)
+        kk = kk * scale
+        qq = qq * scale
+        if wl.dtype == "bf16":
+            from synth import rne_bf16
+            kk, qq = rne_bf16(kk), rne_bf16(qq)
+    dev = {
+        "k": dev_tensor(kk[None], dt),
+        "q": dev_tensor(qq[None], dt),
+        "v": dev_tensor(np.stack([c["v"] for c in chains], axis=1)[None], dt),
+        "log_alpha": dev_tensor(np.stack([c["log_alpha"] for c in chains], axis=1)[None]),
+    }
+    if wl.kind == "dense":
+        dev["beta"] = dev_tensor(np.stack([c["beta"] for c in chains], axis=1)[None])
+    for h, c in enumerate(chains):
+        kh = (h * h_k) // h_v
+        c["k"] = kk[:, kh].astype(np.float32)
+        c["q"] = qq[:, kh].astype(np.float32)
+    return dev, chains
+
+
+def _check_build(out, chains, lens, kind, tol, skip=0, normalise=False):
+    errs_T, errs_S = [], []
+    for h, c in enumerate(chains):
+        k = O.l2_normalise(c["k"]) if normalise else c["k"]
+        ref = oracle_segments(kind, k, c["v"], c["log_alpha"], c.get("beta"), lens, skip=skip)
+        for s, r in enumerate(ref):
+            S = out["S"][s, 0, h].cpu().numpy()
+            if np.all(r["S"] == 0):
+                assert np.all(S == 0), (s, h)
+            else:
+                errs_S.append(float(O.rel_err(S, r["S"])))
+            if out["T_hat"] is not None:
+                Th = out["T_hat"][s, 0, h].cpu().numpy()
+                errs_T.append(float(O.rel_err_T(kind, Th, int(out["T_exp"][s, 0, h]), r["T_hat"], r["T_exp"])))
+    assert max_err(errs_S) < tol, max_err(errs_S)
+    assert max_err(errs_T) < tol, max_err(errs_T)
+    return max_err(errs_T), max_err(errs_S)
+
+
+# ----------------------------------------------------------------------------------------
+# tiny fp32 gated-delta head: 4 x 256 tokens, build + compose against the 1024-token run
+
+
+@pytest.mark.parametrize("name", ["tiny_gdn_f32", "tiny_gdn_f32_slow"])
+def test_tiny_fp32_build_and_compose(gpu, name):
+    wl = WORKLOADS[name]
+    lens = segment_lengths(wl)
+    n = sum(lens)
+    dev, chains = _dense_inputs(wl, n, 1)
+    out = H.hypic_segment_build(dev["k"], dev["v"], dev["log_alpha"], cu_of(lens), beta=dev["beta"])
+    torch.cuda.synchronize()
+    _check_build(out, chains, lens, "dense", TOL_F32)
+    c = chains[0]
+    full = O.dense_recurrence(c["k"], c["v"], c["log_alpha"], c["beta"])
+    cuts = cu_of(lens)
+    n_seg = len(lens)
+    for mode in ("fold", "scan"):
+        comp = H.hypic_compose(out["T_hat"].reshape(n_seg, 1, 64, 64), out["T_exp"].reshape(n_seg, 1),
+                               out["S"].reshape(n_seg, 1, 64, 64), mode=mode, want_T=True, want_prefix=True,
+                               scan_block=2)
+        torch.cuda.synchronize()
+        assert O.rel_err(comp["S_final"][0].cpu().numpy(), full["S"]) < TOL_F32, mode
+        assert O.rel_err_T("dense", comp["T_total"][0].cpu().numpy(), int(comp["T_total_exp"][0]),
+                           full["T_hat"], full["T_exp"]) < TOL_F32, mode
+        for i in range(1, n_seg):
+            lo = cuts[i]
+            pre = O.dense_recurrence(c["k"][:lo], c["v"][:lo], c["log_alpha"][:lo], c["beta"][:lo])["S"]
+            assert O.rel_err(comp["S_prefix"][i, 0].cpu().numpy(), pre) < TOL_F32, (mode, i)
+        assert torch.all(comp["S_prefix"][0] == 0)
+
+
+# ----------------------------------------------------------------------------------------
+# bf16 dense build: ragged segments spanning several chunks, empty segments, GQA
+
+
+RAGGED = [1, 63, 64, 65, 130, 0, 300, 700]
+
+
+@pytest.fixture(scope="module")
+def ragged_dense(gpu):
+    wl = WORKLOADS["gdn64k_bf16"]
+    return (wl,) + _dense_inputs(wl, sum(RAGGED), 4)
+
+
+def test_dense_bf16_ragged_build(ragged_dense):
+    wl, dev, chains = ragged_dense
+    out = H.hypic_segment_build(dev["k"], dev["v"], dev["log_alpha"], cu_of(RAGGED), beta=dev["beta"])
+    torch.cuda.synchronize()
+    eT, eS = _check_build(out, chains, RAGGED, "dense", TOL_BF16)
+    print(f"ragged dense bf16: max T err {eT:.2e}, max S err {eS:.2e}")
+    # the empty segment is the identity element
+    e = RAGGED.index(0)
+    Te = torch.ldexp(out["T_hat"][e, 0], out["T_exp"][e, 0][:, None, None].float())
+    assert torch.equal(Te, torch.eye(128, device=Te.device).expand_as(Te))
+
+
+def test_dense_bf16_skip_head_and_no_T(ragged_dense):
+    wl, dev, chains = ragged_dense
+    out = H.hypic_segment_build(dev["k"], dev["v"], dev["log_alpha"], cu_of(RAGGED), beta=dev["beta"], skip_head=8)
+    plain = H.hypic_segment_build(dev["k"], dev["v"], dev["log_alpha"], cu_of(RAGGED), beta=dev["beta"],
+                                  skip_head=8, with_T=False)
+    torch.cuda.synchronize()
+    _check_build(out, chains, RAGGED, "dense", TOL_BF16, skip=8)
+    # the T columns never feed the S columns: the plain state pass is bitwise the same
+    assert torch.equal(plain["S"], out["S"])
+
+
+def test_dense_bf16_l2norm_on_load(gpu):
+    wl = WORKLOADS["gdn64k_bf16"]
+    lens = [100, 64, 37]
+    dev, chains = _dense_inputs(wl, sum(lens), 2, raw_keys=True)
+    out = H.hypic_segment_build(dev["k"], dev["v"], dev["log_alpha"], cu_of(lens), beta=dev["beta"], qk_l2norm=True)
+    torch.cuda.synchronize()
+    _check_build(out, chains, lens, "dense", TOL_BF16, normalise=True)
+
+
+def test_schedules_are_bitwise_identical(ragged_dense):
+    wl, dev, chains = ragged_dense
+    outs = []
+    for sched in ("natural", "lpt", "rr", "natural"):
+        o = H.hypic_segment_build(dev["k"], dev["v"], dev["log_alpha"], cu_of(RAGGED), beta=dev["beta"],
+                                  schedule=sched)
+        torch.cuda.synchronize()
+        outs.append(o)
+    for o in outs[1:]:
+        assert torch.equal(o["S"], outs[0]["S"])
+        assert torch.equal(o["T_hat"], outs[0]["T_hat"])
+        assert torch.equal(o["T_exp"], outs[0]["T_exp"])
+
+
+# ----------------------------------------------------------------------------------------
+# diagonal (GLA) and scalar (RetNet) decay families
+
+
+@pytest.mark.parametrize("name,kind", [("retnet_bf16", "scalar"), ("gla_bf16", "diag")])
+def test_diag_scalar_build_compose_and_naive(gpu, name, kind):
+    wl = WORKLOADS[name]
+    lens = list(segment_lengths(wl))
+    n, h = sum(lens), wl.h_v
+    chains = [chain_inputs(wl, 0, i, n) for i in range(h)]
+    k = dev_tensor(np.stack([c["k"] for c in chains], 1)[None], torch.bfloat16)
+    v = dev_tensor(np.stack([c["v"] for c in chains], 1)[None], torch.bfloat16)
+    la = dev_tensor(np.stack([c["log_alpha"] for c in chains], 1)[None])
+    out = H.hypic_segment_build(k, v, la, cu_of(lens), kind=kind)
+    torch.cuda.synchronize()
+    # per-segment parity on 4 heads spread over the decay range
+    sel = [0, 5, 10, 15]
+    sub = {"S": out["S"][:, :, sel], "T_hat": out["T_hat"][:, :, sel], "T_exp": out["T_exp"][:, :, sel]}
+    _check_build(sub, [chains[i] for i in sel], lens, kind, TOL_BF16)
+    n_seg = len(lens)
+    tshape = (n_seg, h, 128) if kind == "diag" else (n_seg, h)
+    comp = H.hypic_compose(out["T_hat"].reshape(tshape), out["T_exp"].reshape(n_seg, h),
+                           out["S"].reshape(n_seg, h, 128, 128), kind=kind, mode="fold")
+    naive = H.hypic_compose(None, None, out["S"].reshape(n_seg, h, 128, 128), kind=kind, mode="naive_add")
+    torch.cuda.synchronize()
+    fn = O.diag_recurrence if kind == "diag" else O.scalar_recurrence
+    for i in sel:
+        c = chains[i]
+        full = fn(c["k"], c["v"], c["log_alpha"])["S"]
+        err = float(O.rel_err(comp["S_final"][i].cpu().numpy(), full))
+        naive_err = float(O.rel_err(naive["S_final"][i].cpu().numpy(), full))
+        print(f"{name} head {i}: transition-compose err {err:.2e}, naive-addition err {naive_err:.3f}")
+        assert err < TOL_BF16
+        assert naive_err > 10 * TOL_BF16   # decay makes naive addition structurally wrong
+
+
+# ----------------------------------------------------------------------------------------
+# seam advance
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_seam_advance(gpu, dtype):
+    wl = WORKLOADS["gdn64k_bf16" if dtype == "bf16" else "tiny_gdn_f32"]
+    d = wl.d
+    ws = [1, 8, 8, 33, 64, 0, 70]
+    n = sum(ws)
+    h_v = 2 if dtype == "bf16" else 1
+    dev, chains = _dense_inputs(wl, n, h_v)
+    rng = np.random.default_rng(5)
+    S_in = rng.standard_normal((len(ws), 1, h_v, d, d)).astype(np.float32)
+    res = H.hypic_seam_advance(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"], cu_of(ws),
+                               S_in=dev_tensor(S_in), want_T=True, want_S_seam=True, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    tol = TOL_BF16 if dtype == "bf16" else TOL_F32
+    cuts = cu_of(ws)
+    errs = {"o": [], "S_out": [], "T": [], "S_seam": []}
+    for h, c in enumerate(chains):
+        for s in range(len(ws)):
+            lo, hi = cuts[s], cuts[s + 1]
+            r = O.seam_advance(c["q"][lo:hi], c["k"][lo:hi], c["v"][lo:hi], c["log_alpha"][lo:hi],
+                               c["beta"][lo:hi], S_in[s, 0, h])
+            if hi > lo:
+                errs["o"].append(float(O.rel_err(res["o"][0, lo:hi, h].cpu().numpy(), r["o"])))
+            errs["S_out"].append(float(O.rel_err(res["S_out"][s, 0, h].cpu().numpy(), r["S_out"])))
+            errs["T"].append(float(O.rel_err_T("dense", res["T_hat"][s, 0, h].cpu().numpy(),
+                                               int(res["T_exp"][s, 0, h]), r["T_hat"], r["T_exp"])))
+            S_seam = res["S_seam"][s, 0, h].cpu().numpy()
+            if hi == lo:
+                assert np.all(S_seam == 0)
+            else:
+                errs["S_seam"].append(float(O.rel_err(S_seam, r["S_seam"])))
+    for key, e in errs.items():
+        print(f"seam {dtype} {key}: max err {max_err(e):.2e}")
+        assert max_err(e) < tol, key
+
+
+def test_seam_in_place_and_strided(gpu):
+    wl = WORKLOADS["gdn64k_bf16"]
+    ws = [8, 8, 8]
+    dev, chains = _dense_inputs(wl, sum(ws), 2)
+    rng = np.random.default_rng(6)
+    # states of 3 seams interleaved with 3 other blocks (stride = 2 dense blocks)
+    buf = dev_tensor(rng.standard_normal((6, 1, 2, 128, 128)).astype(np.float32))
+    orig = buf.clone()
+    ref_in = buf[0::2].clone()
+    stride = 2 * 2 * 128 * 128
+    a = H.hypic_seam_advance(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"], cu_of(ws),
+                             S_in=ref_in, want_o=False)
+    b = H.hypic_seam_advance(dev["q"], dev["k"], dev["v"], dev["log_alpha"], dev["beta"], cu_of(ws),
+                             S_in=buf, S_out=buf, state_stride=stride, want_o=False)
+    torch.cuda.synchronize()
+    assert torch.equal(buf[0::2], a["S_out"])
+    assert torch.equal(buf[1::2], orig[1::2])   # blocks between the seams untouched
+
+
+# ----------------------------------------------------------------------------------------
+# conv warm-up
+
+
+@pytest.mark.parametrize("act,out_dtype", [("none", torch.float32), ("silu", torch.float32), ("none", torch.bfloat16)])
+def test_conv_warmup(gpu, act, out_dtype):
+    from synth import rne_bf16
+    rng = np.random.default_rng(7)
+    lens = [1, 2, 3, 8, 50, 0]
+    n, C = sum(lens), 256
+    x = rne_bf16(rng.standard_normal((n, C)).astype(np.float32))
+    w = (0.5 * rng.standard_normal((C, 4))).astype(np.float32)
+    bias = rng.standard_normal(C).astype(np.float32)
+    states = rne_bf16(rng.standard_normal((4, 1, 3, C)).astype(np.float32))
+    idx = np.array([-1, 0, 2, 1, 3, 0], np.int32)
+    res = H.hypic_conv_warmup(dev_tensor(x[None], torch.bfloat16), dev_tensor(w), cu_of(lens),
+                              state_in=dev_tensor(states, torch.bfloat16),
+                              state_index=torch.from_numpy(idx).to(gpu), bias=dev_tensor(bias), activation=act,
+                              out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    cuts = cu_of(lens)
+    tol = TOL_F32 if out_dtype == torch.float32 else TOL_BF16
+    for s in range(len(lens)):
+        lo, hi = cuts[s], cuts[s + 1]
+        st = None if idx[s] < 0 else states[idx[s], 0]
+        y, so = O.causal_conv(x[lo:hi], w, bias=bias, state=st, activation=act)
+        if hi > lo:
+            assert O.rel_err(res["y"][0, lo:hi].float().cpu().numpy(), y) < tol, s
+        # the carried state is a copy: bit-exact
+        assert np.array_equal(res["state_out"][s, 0].float().cpu().numpy(), so.astype(np.float32)), s
