@@ -53,7 +53,22 @@ struct EngineLayout {
     static constexpr int total = Misc + 32 * 4;
 };
 
-template <int D, class Op, bool WITH_Q>
+// Row-major load / store of one 32x32 accumulator tile (row stride LD floats) from a
+// per-lane base pointer, so that every element address is base + constant.
+template <int LD>
+__device__ __forceinline__ void store_tile(float* p, const floatx16& x, int half, int l32) {
+    float* q = p + (4 * half) * LD + l32;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) q[(8 * (j >> 2) + (j & 3)) * LD] = x[j];
+}
+template <int LD>
+__device__ __forceinline__ void load_tile(const float* p, floatx16& x, int half, int l32) {
+    const float* q = p + (4 * half) * LD + l32;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) x[j] = q[(8 * (j >> 2) + (j & 3)) * LD];
+}
+
+template <int D, class Op, bool WITH_Q, bool PERSIST>
 __global__ __launch_bounds__(D * 4) void dense_engine_kernel(EngineArgs a) {
     using E = typename Op::elem;
     using LY = EngineLayout<D, Op, WITH_Q>;
@@ -65,24 +80,7 @@ __global__ __launch_bounds__(D * 4) void dense_engine_kernel(EngineArgs a) {
     constexpr int RS_D = LY::RS_D, RS_T = LY::RS_T, LS = LY::LS;
     constexpr int G8 = D / 8;        // 8-element groups per row
 
-    __shared__ __align__(16) unsigned char smem[LY::total];
-    E* sKr = reinterpret_cast<E*>(smem + LY::Kr);
-    E* sKt = reinterpret_cast<E*>(smem + LY::Kt);
-    E* sVt = reinterpret_cast<E*>(smem + LY::Vt);
-    E* sQq = reinterpret_cast<E*>(smem + LY::Qq);
-    E* sTgA = reinterpret_cast<E*>(smem + LY::TgA);
-    E* sTgG = reinterpret_cast<E*>(smem + LY::TgG);
-    float* sL = reinterpret_cast<float*>(smem + LY::Lm);
-    E* sWq = reinterpret_cast<E*>(smem + LY::Lm);
-    float* sInv = reinterpret_cast<float*>(smem + LY::Inv);
-    E* sMq = reinterpret_cast<E*>(smem + LY::Inv);
-    float* sP = reinterpret_cast<float*>(smem + LY::P);
-    float* sG = reinterpret_cast<float*>(smem + LY::Vec);
-    float* sGam = sG + 64;
-    float* sBeta = sG + 128;
-    float* sSc = sG + 192;
-    float* sMisc = reinterpret_cast<float*>(smem + LY::Misc);
-    int* sEw = reinterpret_cast<int*>(sMisc + 1);
+    __shared__ __align__(16) unsigned char smem_raw[LY::total];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6, half = lane >> 5, l32 = lane & 31;
@@ -92,8 +90,8 @@ __global__ __launch_bounds__(D * 4) void dense_engine_kernel(EngineArgs a) {
     const bool in_bf16 = a.in_bf16 != 0;
     const long long N = a.n_tokens;
 
-    const int stride = a.persistent ? (int)gridDim.x : a.n_tasks;
-    for (int it = blockIdx.x; it < a.n_tasks; it += stride) {
+    // one task per workgroup, or a grid-stride loop over tasks (static round robin)
+    for (int it = blockIdx.x; it < a.n_tasks; it += PERSIST ? (int)gridDim.x : a.n_tasks) {
         const int task = a.order ? a.order[it] : it;
         const int per_seg = a.n_batch * a.h_v;
         const int seg = task / per_seg;
@@ -114,12 +112,9 @@ __global__ __launch_bounds__(D * 4) void dense_engine_kernel(EngineArgs a) {
                 for (int j = 0; j < 16; ++j)
                     X[xb][j] = (32 * xb + acc_row(half, j) == col0 + l32) ? 1.f : 0.f;
         } else if (a.S_in) {
-            const float* src = a.S_in + seg * a.in_stride + chain_off * D * D;
+            const float* src = a.S_in + seg * a.in_stride + chain_off * D * D + col0;
 #pragma unroll
-            for (int xb = 0; xb < NB; ++xb)
-#pragma unroll
-                for (int j = 0; j < 16; ++j)
-                    X[xb][j] = src[(32 * xb + acc_row(half, j)) * D + col0 + l32];
+            for (int xb = 0; xb < NB; ++xb) load_tile<D>(src + 32 * xb * D, X[xb], half, l32);
         } else {
 #pragma unroll
             for (int xb = 0; xb < NB; ++xb) X[xb] = zero16();
@@ -129,6 +124,27 @@ __global__ __launch_bounds__(D * 4) void dense_engine_kernel(EngineArgs a) {
         for (int c0 = 0; c0 < len; c0 += kChunk) {
             const int valid = min(kChunk, len - c0);
             const long long tok0 = start + c0;
+            // LDS views from an opaque zero offset: stops the compiler from hoisting every
+            // per-lane LDS address out of the chunk loop into long-lived registers.
+            int lz = 0;
+            asm volatile("" : "+s"(lz));
+            unsigned char* smem = smem_raw + lz;
+            E* sKr = reinterpret_cast<E*>(smem + LY::Kr);
+            E* sKt = reinterpret_cast<E*>(smem + LY::Kt);
+            E* sVt = reinterpret_cast<E*>(smem + LY::Vt);
+            E* sQq = reinterpret_cast<E*>(smem + LY::Qq);
+            E* sTgA = reinterpret_cast<E*>(smem + LY::TgA);
+            E* sTgG = reinterpret_cast<E*>(smem + LY::TgG);
+            float* sL = reinterpret_cast<float*>(smem + LY::Lm);
+            E* sWq = reinterpret_cast<E*>(smem + LY::Lm);
+            float* sInv = reinterpret_cast<float*>(smem + LY::Inv);
+            E* sMq = reinterpret_cast<E*>(smem + LY::Inv);
+            float* sP = reinterpret_cast<float*>(smem + LY::P);
+            float* sG = reinterpret_cast<float*>(smem + LY::Vec);
+            float* sGam = sG + 64;
+            float* sBeta = sG + 128;
+            float* sSc = sG + 192;
+            float* sMisc = reinterpret_cast<float*>(smem + LY::Misc);
 
             // ---------------- phase 1: stage the chunk in LDS, gate prefix
             for (int i = tid; i < 64 * G8; i += NT) {
@@ -396,25 +412,25 @@ __global__ __launch_bounds__(D * 4) void dense_engine_kernel(EngineArgs a) {
         }
 
         // ---- epilogue: align the T waves' exponents, write T_hat / T_exp / S
+        int* sEw = reinterpret_cast<int*>(smem_raw + LY::Misc) + 1;
         if (t_wave && do_T && lane == 0) sEw[wave] = ew;
         __syncthreads();
         if (t_wave && do_T) {
             int emax = sEw[0];
             for (int w = 1; w < NW / 2; ++w) emax = max(emax, sEw[w]);
-            float* dst = a.T_hat + ((long long)seg * a.n_batch * a.h_v + chain_off) * D * D;
+            float* dst = a.T_hat + ((long long)seg * a.n_batch * a.h_v + chain_off) * D * D + col0;
 #pragma unroll
-            for (int xb = 0; xb < NB; ++xb)
+            for (int xb = 0; xb < NB; ++xb) {
 #pragma unroll
-                for (int j = 0; j < 16; ++j)
-                    dst[(32 * xb + acc_row(half, j)) * D + col0 + l32] = ldexpf(X[xb][j], ew - emax);
+                for (int j = 0; j < 16; ++j) X[xb][j] = ldexpf(X[xb][j], ew - emax);
+                store_tile<D>(dst + 32 * xb * D, X[xb], half, l32);
+            }
             if (tid == 0) a.T_exp[(long long)seg * a.n_batch * a.h_v + chain_off] = emax;
         }
         if (!t_wave && a.S_out) {
-            float* dst = a.S_out + seg * a.out_stride + chain_off * D * D;
+            float* dst = a.S_out + seg * a.out_stride + chain_off * D * D + col0;
 #pragma unroll
-            for (int xb = 0; xb < NB; ++xb)
-#pragma unroll
-                for (int j = 0; j < 16; ++j) dst[(32 * xb + acc_row(half, j)) * D + col0 + l32] = X[xb][j];
+            for (int xb = 0; xb < NB; ++xb) store_tile<D>(dst + 32 * xb * D, X[xb], half, l32);
         }
         __syncthreads();
     }
@@ -422,7 +438,10 @@ __global__ __launch_bounds__(D * 4) void dense_engine_kernel(EngineArgs a) {
 
 template <int D, class Op, bool WITH_Q>
 static hipError_t launch_one(const EngineArgs& a, int grid, hipStream_t s) {
-    hipLaunchKernelGGL((dense_engine_kernel<D, Op, WITH_Q>), dim3(grid), dim3(D * 4), 0, s, a);
+    if (a.persistent)
+        hipLaunchKernelGGL((dense_engine_kernel<D, Op, WITH_Q, true>), dim3(grid), dim3(D * 4), 0, s, a);
+    else
+        hipLaunchKernelGGL((dense_engine_kernel<D, Op, WITH_Q, false>), dim3(grid), dim3(D * 4), 0, s, a);
     return hipGetLastError();
 }
 
