@@ -20,6 +20,8 @@ hold them exactly, so the CPU reference sees exactly what the device sees.
 
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -187,7 +189,7 @@ def chain_inputs(wl: Workload, layer: int, vhead: int, n: int | None = None) -> 
     return out
 
 
-def layer_inputs(wl: Workload, layer: int, heads: range | None = None) -> dict:
+def layer_inputs(wl: Workload, layer: int, heads: range | None = None, with_q: bool = True) -> dict:
     """All chains of one layer in token-major layout.
 
     k, q: [N, H_k, d]; v: [N, H_v, d]; beta: [N, H_v]; log_alpha: [N, H_v]
@@ -198,20 +200,28 @@ def layer_inputs(wl: Workload, layer: int, heads: range | None = None) -> dict:
     hv = range(wl.h_v) if heads is None else heads
     khs = sorted({wl.khead(h) for h in hv})
     k = np.empty((n, wl.h_k, wl.d), np.float32)
-    q = np.empty((n, wl.h_k, wl.d), np.float32)
-    for kh in khs:
-        k[:, kh] = _key_like(wl, layer, kh, n, "k")
-        q[:, kh] = _key_like(wl, layer, kh, n, "q")
+    q = np.empty((n, wl.h_k, wl.d), np.float32) if with_q else None
     v = np.empty((n, wl.h_v, wl.d), np.float32)
     la_shape = (n, wl.h_v, wl.d) if wl.kind == "diag" else (n, wl.h_v)
     la = np.zeros(la_shape, np.float32)
     beta = np.zeros((n, wl.h_v), np.float32)
-    for h in hv:
+
+    def key_job(kh):
+        k[:, kh] = _key_like(wl, layer, kh, n, "k")
+        if with_q:
+            q[:, kh] = _key_like(wl, layer, kh, n, "q")
+
+    def value_job(h):
         c = _value_side(wl, layer, h, n)
         v[:, h] = c["v"]
         la[:, h] = c["log_alpha"]
         if "beta" in c:
             beta[:, h] = c["beta"]
+
+    # heads are independent streams: fill them concurrently (numpy releases the GIL)
+    with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        list(ex.map(key_job, khs))
+        list(ex.map(value_job, hv))
     return {"k": k, "q": q, "v": v, "log_alpha": la, "beta": beta}
 
 
