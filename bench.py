@@ -27,10 +27,10 @@ sys.path.insert(0, ROOT)
 METRIC = "segment-build tokens/s for (T_C,S|0) + compose µs/segment, % MFMA/HBM peak"
 PEAK_MFMA_F16 = 2.5e15        # MI355X dense f16/bf16 matrix peak, FLOP/s
 PEAK_HBM = 8.0e12             # MI355X HBM3E, B/s
-D, C = 128, 64
+D, CHUNK = 128, 64
 
 
-def build_flops_per_chunk(d=D, c=C, r=2):
+def build_flops_per_chunk(d=D, c=CHUNK, r=2):
     """Algorithmic flops of one 64-token chunk of one value head (dense build with T):
     gram K K^T shared by r value heads, UT solve, W' and U, and the [T | S] carry."""
     return 2 * c * c * d / r + c ** 3 / 3 + 4 * c * c * d + 4 * c * d * (d + d)

@@ -271,8 +271,8 @@ hypic_status hypic_segment_build(const hypic_build_desc* d, hypic_stream_t strea
             a.persistent = 1;
             grid = (int)std::min<int64_t>(n_tasks, cus);
         }
-        e = hypic::launch_dense_engine(a, d->d_k, build_prec_f32(d) ? 1 : 0, grid, s);
-        if (e != hipSuccess) return device_fail("build: dense engine launch", e);
+        e = hypic::launch_gdn_build(a, d->d_k, build_prec_f32(d) ? 1 : 0, grid, s);
+        if (e != hipSuccess) return device_fail("build: dense build launch", e);
     } else {
         hypic::DiagArgs a{};
         a.n_batch = d->n_batch;

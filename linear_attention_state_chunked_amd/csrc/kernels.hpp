@@ -101,6 +101,8 @@ struct ConvArgs {
 };
 
 hipError_t launch_dense_engine(const EngineArgs& a, int d, int prec_f32, int grid, hipStream_t s);
+// warp-specialised segment build (X = [I | 0] start, no outputs); T columns iff a.T_hat
+hipError_t launch_gdn_build(const EngineArgs& a, int d, int prec_f32, int grid, hipStream_t s);
 hipError_t launch_diag_build(const DiagArgs& a, int d, hipStream_t s);
 hipError_t launch_fold(const FoldArgs& a, int d, int with_T, hipStream_t s);
 hipError_t launch_conv(const ConvArgs& a, long long total_tokens, hipStream_t s);
