@@ -271,7 +271,8 @@ size_t hypic_seam_advance_workspace_bytes(const hypic_seam_desc* desc);
  *   state_in   [n_state, B, W-1, C] in_dtype, or NULL (zero state)
  *   state_index device int32 [n_seg]: row of state_in for segment s, -1 = zero;
  *               NULL = identity (segment s uses state_in[s], n_state >= n_seg)
- *   weight     float32 [C, W];  bias float32 [C] or NULL
+ *   weight     float32 [B, C, W] (each batch entry, e.g. each layer, has its own
+ *              taps);  bias float32 [B, C] or NULL
  *   y          [B, N, C] out_dtype
  *   state_out  [n_seg, B, W-1, C] in_dtype, or NULL
  * channels must be a multiple of 8.  Needs hypic_conv_warmup_workspace_bytes()

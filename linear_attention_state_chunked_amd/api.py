@@ -48,18 +48,29 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
+def _out(out, name, shape, dtype, device):
+    """Caller-provided output tensor `out[name]` (checked), else a new one."""
+    t = (out or {}).get(name)
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != device or not t.is_contiguous():
+        raise ValueError(f"out[{name!r}] must be a contiguous {dtype} tensor of shape {tuple(shape)} on {device}")
+    return t
+
+
 def _as4(x):
     return x if x.dim() == 4 else x.unsqueeze(0)
 
 
 def hypic_segment_build(k, v, log_alpha, cu_seqlens, beta=None, *, kind="dense", with_T=True, skip_head=0,
-                        qk_l2norm=False, schedule="natural", precision="auto"):
+                        qk_l2norm=False, schedule="natural", precision="auto", out=None):
     """Per-segment (T_hat, T_exp, S) for every (segment, batch, value head).
 
     k [B,N,h_k,d] (or [N,h_k,d]), v [B,N,h_v,d]; log_alpha [B,N,h_v] (diag:
     [B,N,h_v,d]); beta [B,N,h_v] (dense).  Returns a dict with T_hat
     (dense [n_seg,B,h_v,d,d], diag [n_seg,B,h_v,d], scalar [n_seg,B,h_v]) or None,
     T_exp [n_seg,B,h_v] int32 or None, and S [n_seg,B,h_v,d,d] float32.
+    `out` may hold preallocated "T_hat", "T_exp", "S" tensors of those shapes.
     """
     k, v = _contig(_as4(k), "k"), _contig(_as4(v), "v")
     kd = A.KIND[kind]
@@ -70,12 +81,12 @@ def hypic_segment_build(k, v, log_alpha, cu_seqlens, beta=None, *, kind="dense",
     cu = _host_offsets(cu_seqlens)
     n_seg = len(cu) - 1
     dev = k.device
-    S = torch.empty((n_seg, B, h_v, d, d), dtype=torch.float32, device=dev)
+    S = _out(out, "S", (n_seg, B, h_v, d, d), torch.float32, dev)
     T_hat = T_exp = None
     if with_T:
         tshape = {A.DENSE: (n_seg, B, h_v, d, d), A.DIAG: (n_seg, B, h_v, d), A.SCALAR: (n_seg, B, h_v)}[kd]
-        T_hat = torch.empty(tshape, dtype=torch.float32, device=dev)
-        T_exp = torch.empty((n_seg, B, h_v), dtype=torch.int32, device=dev)
+        T_hat = _out(out, "T_hat", tshape, torch.float32, dev)
+        T_exp = _out(out, "T_exp", (n_seg, B, h_v), torch.int32, dev)
     desc = A.BuildDesc(kind=kd, in_dtype=_dtype(k), n_batch=B, n_tokens=N, h_k=h_k, h_v=h_v, d_k=d, d_v=v.shape[3],
                        chunk=64, n_seg=n_seg, cu_seqlens=cu.ctypes.data, skip_head=skip_head,
                        qk_l2norm=int(bool(qk_l2norm)), k=_ptr(k), v=_ptr(v), log_alpha=_ptr(la), beta=_ptr(bt),
@@ -127,13 +138,14 @@ def hypic_compose(T_hat, T_exp, S, *, kind="dense", slot=None, S0=None, mode="au
 
 def hypic_seam_advance(q, k, v, log_alpha, beta, cu_seam, *, S_in=None, state_stride=0, want_o=True,
                        S_out="new", want_T=False, want_S_seam=False, out_dtype=None, qk_l2norm=False,
-                       precision="auto"):
+                       precision="auto", out=None):
     """Seam tokens through the running state.
 
     q, k [B,N,h_k,d]; v [B,N,h_v,d]; log_alpha, beta [B,N,h_v]; S_in float32
     with seam s at offset s*state_stride (0 = dense [n_seam,B,h_v,d,d]) or None.
     S_out: "new" (allocate), a tensor (may be S_in) or None.  Returns o
-    [B,N,h_v,d], S_out, T_hat/T_exp [n_seam,B,h_v,d,d], S_seam.
+    [B,N,h_v,d], S_out, T_hat/T_exp [n_seam,B,h_v,d,d], S_seam.  `out` may hold
+    preallocated "o", "T_hat", "T_exp", "S_seam" tensors of those shapes.
     """
     q, k, v = _contig(_as4(q), "q"), _contig(_as4(k), "k"), _contig(_as4(v), "v")
     B, N, h_k, d = k.shape
@@ -144,12 +156,12 @@ def hypic_seam_advance(q, k, v, log_alpha, beta, cu_seam, *, S_in=None, state_st
     la = _contig(log_alpha.reshape(B, N, h_v), "log_alpha")
     bt = _contig(beta.reshape(B, N, h_v), "beta")
     out_dtype = out_dtype or k.dtype
-    o = torch.empty((B, N, h_v, d), dtype=out_dtype, device=dev) if want_o else None
+    o = _out(out, "o", (B, N, h_v, d), out_dtype, dev) if want_o else None
     if isinstance(S_out, str):
         S_out = torch.empty((n_seam, B, h_v, d, d), dtype=torch.float32, device=dev) if state_stride == 0 else None
-    T_hat = torch.empty((n_seam, B, h_v, d, d), dtype=torch.float32, device=dev) if want_T else None
-    T_exp = torch.empty((n_seam, B, h_v), dtype=torch.int32, device=dev) if want_T else None
-    S_seam = torch.empty((n_seam, B, h_v, d, d), dtype=torch.float32, device=dev) if want_S_seam else None
+    T_hat = _out(out, "T_hat", (n_seam, B, h_v, d, d), torch.float32, dev) if want_T else None
+    T_exp = _out(out, "T_exp", (n_seam, B, h_v), torch.int32, dev) if want_T else None
+    S_seam = _out(out, "S_seam", (n_seam, B, h_v, d, d), torch.float32, dev) if want_S_seam else None
     desc = A.SeamDesc(in_dtype=_dtype(k), out_dtype=_dtype(o) if o is not None else A.F32, n_batch=B, n_tokens=N,
                       h_k=h_k, h_v=h_v, d_k=d, d_v=v.shape[3], n_seam=n_seam, cu_seam=cu.ctypes.data,
                       qk_l2norm=int(bool(qk_l2norm)), q=_ptr(q), k=_ptr(k), v=_ptr(v), log_alpha=_ptr(la),
@@ -167,12 +179,19 @@ def hypic_conv_warmup(x, weight, cu_seqlens, *, state_in=None, state_index=None,
                       out_dtype=None, want_state=True):
     """Depthwise causal conv (width 4) with carried state.
 
-    x [B,N,C] (or [N,C]); weight [C,4] float32; state_in [n_state,B,3,C] (x's
-    dtype) or None; state_index device int32 [n_seg] or None.  Returns y
-    [B,N,C] and state_out [n_seg,B,3,C] (or None).
+    x [B,N,C] (or [N,C]); weight [B,C,4] float32 ([C,4] when B = 1); bias [B,C]
+    ([C] when B = 1) or None; state_in [n_state,B,3,C] (x's dtype) or None;
+    state_index device int32 [n_seg] or None.  Returns y [B,N,C] and state_out
+    [n_seg,B,3,C] (or None).
     """
     x = _contig(x if x.dim() == 3 else x.unsqueeze(0), "x")
     B, N, Cc = x.shape
+    if weight.dim() == 2:
+        weight = weight.unsqueeze(0)
+    if bias is not None and bias.dim() == 1:
+        bias = bias.unsqueeze(0)
+    if weight.shape[0] != B or weight.shape[1] != Cc or (bias is not None and tuple(bias.shape) != (B, Cc)):
+        raise ValueError("weight must be [B, C, W] and bias [B, C] (per batch entry)")
     cu = _host_offsets(cu_seqlens)
     n_seg = len(cu) - 1
     dev = x.device
@@ -180,7 +199,7 @@ def hypic_conv_warmup(x, weight, cu_seqlens, *, state_in=None, state_index=None,
     st_out = torch.empty((n_seg, B, 3, Cc), dtype=x.dtype, device=dev) if want_state else None
     for t, nm in ((weight, "weight"), (state_in, "state_in"), (state_index, "state_index"), (bias, "bias")):
         _contig(t, nm)
-    desc = A.ConvDesc(in_dtype=_dtype(x), out_dtype=_dtype(y), n_batch=B, n_tokens=N, channels=Cc, width=weight.shape[1],
+    desc = A.ConvDesc(in_dtype=_dtype(x), out_dtype=_dtype(y), n_batch=B, n_tokens=N, channels=Cc, width=weight.shape[2],
                       n_seg=n_seg, cu_seqlens=cu.ctypes.data, x=_ptr(x), state_in=_ptr(state_in),
                       n_state=state_in.shape[0] if state_in is not None else 0, state_index=_ptr(state_index),
                       weight=_ptr(weight), bias=_ptr(bias), activation=A.ACT[activation], y=_ptr(y),

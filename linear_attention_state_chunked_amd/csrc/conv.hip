@@ -56,15 +56,16 @@ __global__ __launch_bounds__(256) void conv_kernel(ConvArgs a) {
     };
 
     if (t < len) {
+        const float* wb = a.weight + (long long)b * C * kConvW;  // this batch entry's taps
         float y[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) y[u] = a.bias ? a.bias[c0 + u] : 0.f;
+        for (int u = 0; u < 8; ++u) y[u] = a.bias ? a.bias[(long long)b * C + c0 + u] : 0.f;
 #pragma unroll
         for (int j = 0; j < kConvW; ++j) {
             float x[8];
             fetch(t + j, x);
 #pragma unroll
-            for (int u = 0; u < 8; ++u) y[u] += a.weight[(c0 + u) * kConvW + j] * x[u];
+            for (int u = 0; u < 8; ++u) y[u] += wb[(c0 + u) * kConvW + j] * x[u];
         }
         if (a.silu) {
 #pragma unroll

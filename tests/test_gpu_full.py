@@ -1,0 +1,302 @@
+"""GPU parity at full workload sizes, checked on sampled chains.
+
+The device runs every chain of the workload in the launch configuration the
+benchmark uses; the fp64 oracle recomputes a seeded sample of chains one by one
+(on a process pool, overlapped with the device work).  Sampled chains take their
+inputs from their own numpy streams; the remaining chains are filled on the
+device with the same distributions.  Tolerance: 2e-3 relative Frobenius error
+per output block (bf16 inputs, fp32 state and T); T compared exponent-aligned.
+"""
+
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import linear_attention_state_chunked_amd as H
+import oracle as O
+from synth import WORKLOADS, chain_inputs, conv_chain_inputs, layer_inputs, request_order, segment_lengths
+from synth.device_fill import fill_dense_layer_, fill_preconv_layer_
+from tests.gpu_util import cu_of, dev_tensor
+from tests.oracle_jobs import dense_segments_job, start_pool, warm_chain_job
+
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
+
+TOL = 2e-3
+DEV = "cuda:0"
+
+
+def tol_T_total(n_elem):
+    """Bound for a composed transition of n elements: each factor carries the
+    per-block bar, and errors of independent factors add in quadrature."""
+    return TOL * np.sqrt(n_elem)
+
+
+def log(msg):
+    print(f"[full] {msg}", flush=True)
+
+
+def sampled_chains(seed, n_layers, h_v, n):
+    rng = np.random.default_rng([seed, 7777])
+    flat = sorted(int(f) for f in rng.choice(n_layers * h_v, size=n, replace=False))
+    return [(f // h_v, f % h_v) for f in flat]
+
+
+def _host(t):
+    return t.detach().cpu().numpy()
+
+
+def _collect(pool, res, timeout=800):
+    try:
+        return res.get(timeout=timeout)
+    finally:
+        pool.terminate()
+        pool.join()
+
+
+def _check_T_S(label, T_hat, T_exp, S, ref):
+    """T_hat [d,d] f32, T_exp int, S [d,d] against an oracle (T_hat, T_exp, S)."""
+    eT = float(O.rel_err_T("dense", T_hat, T_exp, ref[0], ref[1]))
+    eS = float(O.rel_err(S, ref[2]))
+    assert eT <= TOL and eS <= TOL, f"{label}: T err {eT:.3e}, S err {eS:.3e}"
+    return eT, eS
+
+
+# ----------------------------------------------------------------------------------------
+# 64k-token GDN layer: 64 segments x 1024 tokens, 32 value heads on 16 key heads
+
+
+def test_gdn64k_full_build_and_compose(gpu):
+    wl = WORKLOADS["gdn64k_bf16"]
+    lens = segment_lengths(wl)
+    cu = cu_of(lens)
+    n_seg, h_v, d = len(lens), wl.h_v, wl.d
+    final_heads = [5, 26]
+    seg_heads = {0: [0, 1, 31, 63], 13: [2, 40, 62], 22: [7, 33, 63], 31: [0, 17, 50, 62]}
+    jobs = [("gdn64k_bf16", 0, h, None, True) for h in final_heads]
+    jobs += [("gdn64k_bf16", 0, h, segs, False) for h, segs in seg_heads.items()]
+    pool, res = start_pool(dense_segments_job, jobs)
+    t0 = time.time()
+    x = layer_inputs(wl, 0, with_q=False)
+    k = dev_tensor(x["k"][None], torch.bfloat16)
+    v = dev_tensor(x["v"][None], torch.bfloat16)
+    beta = dev_tensor(x["beta"][None])
+    la = dev_tensor(x["log_alpha"][None])
+    del x
+    log(f"gdn64k inputs resident ({time.time() - t0:.1f} s); build + compose")
+    b = H.hypic_segment_build(k, v, la, cu, beta, schedule="natural")
+    E_T = b["T_hat"].reshape(n_seg, h_v, d, d)
+    E_e = b["T_exp"].reshape(n_seg, h_v)
+    E_S = b["S"].reshape(n_seg, h_v, d, d)
+    c_auto = H.hypic_compose(E_T, E_e, E_S, mode="auto")
+    c_fold = H.hypic_compose(E_T, E_e, E_S, mode="fold", want_T=True)
+    torch.cuda.synchronize()
+    Th, Te, Sh = _host(E_T), _host(E_e), _host(E_S)
+    Sa, Sf = _host(c_auto["S_final"]), _host(c_fold["S_final"])
+    Tt, Tte = _host(c_fold["T_total"]), _host(c_fold["T_total_exp"])
+    log("device done; waiting for the oracle")
+    outs = _collect(pool, res)
+    worst = [0.0, 0.0, 0.0, 0.0]
+    for (name, layer, h, segs, fold), r in zip(jobs, outs):
+        for s, ref in r["seg"].items():
+            eT, eS = _check_T_S(f"head {h} segment {s}", Th[s, h], Te[s, h], Sh[s, h], ref)
+            worst[0], worst[1] = max(worst[0], eT), max(worst[1], eS)
+        if fold:
+            for lab, Sx in (("auto", Sa), ("fold", Sf)):
+                e = float(O.rel_err(Sx[h], r["S_final"]))
+                assert e <= TOL, f"head {h} composed state ({lab}): {e:.3e}"
+                worst[2] = max(worst[2], e)
+            e = float(O.rel_err_T("dense", Tt[h], Tte[h], r["T_hat"], r["T_exp"]))
+            assert e <= tol_T_total(n_seg), f"head {h} composed T: {e:.3e}"
+            worst[3] = max(worst[3], e)
+    log(f"gdn64k: max T {worst[0]:.2e}, S {worst[1]:.2e}, S_final {worst[2]:.2e}, T_total {worst[3]:.2e}")
+
+
+# ----------------------------------------------------------------------------------------
+# cold 100k-token request: 20 uneven segments x 30 layers x 32 value heads
+
+
+def test_cold100k_full_schedules_scan_and_single_pass(gpu):
+    wl = WORKLOADS["cold100k_bf16"]
+    lens = segment_lengths(wl)
+    cu = cu_of(lens)
+    N, L, n_seg, h_k, h_v, d = int(cu[-1]), wl.n_layers, len(lens), wl.h_k, wl.h_v, wl.d
+    chains = sampled_chains(wl.seed, L, h_v, 8)
+    pool, res = start_pool(dense_segments_job, [("cold100k_bf16", l, h, None, True) for l, h in chains])
+    t0 = time.time()
+    k = torch.empty((L, N, h_k, d), dtype=torch.bfloat16, device=DEV)
+    v = torch.empty((L, N, h_v, d), dtype=torch.bfloat16, device=DEV)
+    beta = torch.empty((L, N, h_v), dtype=torch.float32, device=DEV)
+    la = torch.empty((L, N, h_v), dtype=torch.float32, device=DEV)
+    for layer in range(L):
+        fill_dense_layer_(wl, layer, k[layer], v[layer], beta[layer], la[layer])
+    for layer, h in chains:
+        c = chain_inputs(wl, layer, h)
+        k[layer, :, wl.khead(h)] = dev_tensor(c["k"], torch.bfloat16)
+        v[layer, :, h] = dev_tensor(c["v"], torch.bfloat16)
+        beta[layer, :, h] = dev_tensor(c["beta"])
+        la[layer, :, h] = dev_tensor(c["log_alpha"])
+    torch.cuda.synchronize()
+    log(f"cold100k inputs resident ({time.time() - t0:.1f} s, {L} layers x {N} tokens); builds")
+
+    b = H.hypic_segment_build(k, v, la, cu, beta, schedule="lpt")
+    for sched in ("rr", "natural"):
+        o = H.hypic_segment_build(k, v, la, cu, beta, schedule=sched)
+        for key in ("T_hat", "T_exp", "S"):
+            assert torch.equal(o[key], b[key]), f"{sched} schedule changed {key}"
+        del o
+    n_chain = L * h_v
+    E_T = b["T_hat"].reshape(n_seg, n_chain, d, d)
+    E_e = b["T_exp"].reshape(n_seg, n_chain)
+    E_S = b["S"].reshape(n_seg, n_chain, d, d)
+    c = H.hypic_compose(E_T, E_e, E_S, mode="scan", want_T=True)
+    single = H.hypic_segment_build(k, v, la, [0, N], beta, with_T=False)["S"].reshape(n_chain, d, d)
+    # the composed state equals the single sequential pass for every chain
+    num = torch.linalg.vector_norm((c["S_final"] - single).reshape(n_chain, -1).double(), dim=1)
+    den = torch.linalg.vector_norm(single.reshape(n_chain, -1).double(), dim=1)
+    e_all = float((num / den).max())
+    log(f"cold100k: composed vs single pass, max over {n_chain} chains {e_all:.2e}")
+    assert e_all <= TOL
+    idx = [layer * h_v + h for layer, h in chains]
+    Th = _host(E_T[:, idx])
+    Te = _host(E_e[:, idx])
+    Sh = _host(E_S[:, idx])
+    Sc = _host(c["S_final"][idx])
+    Ss = _host(single[idx])
+    Tt, Tte = _host(c["T_total"][idx]), _host(c["T_total_exp"][idx])
+    del k, v, b, c, single
+    log("device done; waiting for the oracle")
+    outs = _collect(pool, res)
+    worst = [0.0, 0.0, 0.0]
+    worst_T = 0.0
+    for j, ((layer, h), r) in enumerate(zip(chains, outs)):
+        for s, ref in r["seg"].items():
+            eT, eS = _check_T_S(f"layer {layer} head {h} segment {s}", Th[s, j], Te[s, j], Sh[s, j], ref)
+            worst[0], worst[1] = max(worst[0], eT), max(worst[1], eS)
+        for lab, Sx in (("scan", Sc[j]), ("single pass", Ss[j])):
+            e = float(O.rel_err(Sx, r["S_final"]))
+            assert e <= TOL, f"layer {layer} head {h} final state ({lab}): {e:.3e}"
+            worst[2] = max(worst[2], e)
+        e = float(O.rel_err_T("dense", Tt[j], Tte[j], r["T_hat"], r["T_exp"]))
+        assert e <= tol_T_total(n_seg), f"layer {layer} head {h} composed T: {e:.3e}"
+        worst_T = max(worst_T, e)
+    log(f"cold100k: max T {worst[0]:.2e}, S {worst[1]:.2e}, final {worst[2]:.2e}, T_total {worst_T:.2e}")
+
+
+# ----------------------------------------------------------------------------------------
+# warm hit: 128 cached segments (lognormal lengths) x 30 layers x 32 value heads,
+# seam window 8, conv width 4 with the carried state
+
+
+def test_warm30_full_conv_seam_compose(gpu):
+    wl = WORKLOADS["warm30_bf16"]
+    lens = np.asarray(segment_lengths(wl))
+    order = request_order(wl)
+    cu = cu_of(lens)
+    N, L, n_slot, h_k, h_v, d, w = int(cu[-1]), wl.n_layers, len(lens), wl.h_k, wl.h_v, wl.d, wl.seam
+    W = wl.conv_width
+    chains = sampled_chains(wl.seed, L, h_v, 8)
+    pool, res = start_pool(warm_chain_job, chains)
+    t0 = time.time()
+    bf = torch.bfloat16
+    xq = torch.empty((L, N, h_k * d), dtype=bf, device=DEV)
+    xk = torch.empty((L, N, h_k * d), dtype=bf, device=DEV)
+    xv = torch.empty((L, N, h_v * d), dtype=bf, device=DEV)
+    wq = torch.empty((L, h_k * d, W), dtype=torch.float32, device=DEV)
+    wk = torch.empty((L, h_k * d, W), dtype=torch.float32, device=DEV)
+    wv = torch.empty((L, h_v * d, W), dtype=torch.float32, device=DEV)
+    beta = torch.empty((L, N, h_v), dtype=torch.float32, device=DEV)
+    la = torch.empty((L, N, h_v), dtype=torch.float32, device=DEV)
+    for layer in range(L):
+        fill_preconv_layer_(wl, layer, xq[layer], xk[layer], xv[layer], wq[layer], wk[layer], wv[layer],
+                            beta[layer], la[layer])
+    for layer, h in chains:
+        x = conv_chain_inputs(wl, layer, h)
+        kh = wl.khead(h)
+        xq[layer, :, kh * d:(kh + 1) * d] = dev_tensor(x["xq"], bf)
+        xk[layer, :, kh * d:(kh + 1) * d] = dev_tensor(x["xk"], bf)
+        xv[layer, :, h * d:(h + 1) * d] = dev_tensor(x["xv"], bf)
+        wq[layer, kh * d:(kh + 1) * d] = dev_tensor(x["wq"])
+        wk[layer, kh * d:(kh + 1) * d] = dev_tensor(x["wk"])
+        wv[layer, h * d:(h + 1) * d] = dev_tensor(x["wv"])
+        beta[layer, :, h] = dev_tensor(x["beta"])
+        la[layer, :, h] = dev_tensor(x["log_alpha"])
+    torch.cuda.synchronize()
+    log(f"warm30 pre-conv inputs resident ({time.time() - t0:.1f} s, {L} layers x {N} tokens)")
+
+    # --- cache fill (first prefill of every slot, storage order): conv from a zero
+    # state, then the segment build of tokens [w, n) (the seam is recomputed at reuse)
+    n_chain = L * h_v
+    E_T = torch.empty((2 * n_slot, n_chain, d, d), dtype=torch.float32, device=DEV)
+    E_e = torch.empty((2 * n_slot, n_chain), dtype=torch.int32, device=DEV)
+    E_S = torch.empty((2 * n_slot, n_chain, d, d), dtype=torch.float32, device=DEV)
+    conv_state = {nm: torch.empty((n_slot, L, W - 1, x.shape[2]), dtype=bf, device=DEV)
+                  for nm, x in (("q", xq), ("k", xk), ("v", xv))}
+    for layer in range(L):
+        # conv outputs stay float32 up to the recurrence (its loader rounds operands once)
+        y = {}
+        for nm, xx, ww in (("k", xk, wk), ("v", xv, wv), ("q", xq, wq)):
+            r = H.hypic_conv_warmup(xx[layer], ww[layer], cu, out_dtype=torch.float32, want_state=True)
+            y[nm] = r["y"]
+            conv_state[nm][:, layer] = r["state_out"][:, 0]
+        part = H.hypic_segment_build(y["k"].view(1, N, h_k, d), y["v"].view(1, N, h_v, d), la[layer:layer + 1],
+                                     cu, beta[layer:layer + 1], skip_head=w, qk_l2norm=True)
+        E_T[:n_slot].view(n_slot, L, h_v, d, d)[:, layer] = part["T_hat"][:, 0]
+        E_e[:n_slot].view(n_slot, L, h_v)[:, layer] = part["T_exp"][:, 0]
+        E_S[:n_slot].view(n_slot, L, h_v, d, d)[:, layer] = part["S"][:, 0]
+        del y, part
+    torch.cuda.synchronize()
+    log("cache filled; warm path")
+
+    # --- warm hit, request order: seam tokens = first w tokens of each requested slot
+    seam_tok = np.concatenate([np.arange(cu[s], cu[s] + w) for s in order])
+    cu_seam = np.arange(0, w * n_slot + 1, w, dtype=np.int64)
+    ti = torch.from_numpy(seam_tok).to(DEV)
+    prev = np.concatenate([[-1], order[:-1]]).astype(np.int32)      # conv state: previous requested slot
+    sidx = torch.from_numpy(prev).to(DEV)
+    y = {}
+    for nm, xx, ww in (("q", xq, wq), ("k", xk, wk), ("v", xv, wv)):
+        y[nm] = H.hypic_conv_warmup(xx.index_select(1, ti).contiguous(), ww, cu_seam, state_in=conv_state[nm],
+                                    state_index=sidx, out_dtype=torch.float32, want_state=False)["y"]
+    sq = y["q"].view(L, -1, h_k, d)
+    sk = y["k"].view(L, -1, h_k, d)
+    sv = y["v"].view(L, -1, h_v, d)
+    sb = beta.index_select(1, ti).contiguous()
+    sl = la.index_select(1, ti).contiguous()
+    # seam elements (zero start) into the second half of the element store
+    H.hypic_seam_advance(sq, sk, sv, sl, sb, cu_seam, want_o=False, S_out=None, want_T=True, want_S_seam=True,
+                         qk_l2norm=True,
+                         out={"T_hat": E_T[n_slot:].view(n_slot, L, h_v, d, d),
+                              "T_exp": E_e[n_slot:].view(n_slot, L, h_v),
+                              "S_seam": E_S[n_slot:].view(n_slot, L, h_v, d, d)})
+    slot = np.empty(2 * n_slot, np.int32)
+    slot[0::2] = n_slot + np.arange(n_slot)      # seam of request position p
+    slot[1::2] = order                           # then the cached rest of that slot
+    slot_d = torch.from_numpy(slot).to(DEV)
+    c = H.hypic_compose(E_T, E_e, E_S, slot=slot_d, mode="scan", want_prefix=True)
+    cf = H.hypic_compose(E_T, E_e, E_S, slot=slot_d, mode="fold")
+    # outputs of the seam tokens from the state entering each segment
+    pre = c["S_prefix"]
+    sa = H.hypic_seam_advance(sq, sk, sv, sl, sb, cu_seam, S_in=pre, state_stride=2 * n_chain * d * d,
+                              S_out=None, qk_l2norm=True, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    idx = [layer * h_v + h for layer, h in chains]
+    S_start = _host(pre[0::2][:, idx])                                  # [n_slot, 8, d, d]
+    o = sa["o"]                                                         # [L, n_slot*w, h_v, d]
+    o_s = np.stack([_host(o[layer, :, h]) for layer, h in chains], 1)    # [n_slot*w, 8, d]
+    S_fin = _host(c["S_final"][idx])
+    S_fin_fold = _host(cf["S_final"][idx])
+    del xq, xk, xv, E_T, E_S, c, cf, pre, sa
+    log("device done; waiting for the oracle")
+    outs = _collect(pool, res)
+    worst = [0.0, 0.0, 0.0]
+    for j, ((layer, h), r) in enumerate(zip(chains, outs)):
+        e_start = O.rel_err(S_start[:, j], r["S_start"])
+        e_o = O.rel_err(o_s[:, j].reshape(n_slot, w, d), r["o_seam"])
+        e_f = max(float(O.rel_err(S_fin[j], r["S_final"])), float(O.rel_err(S_fin_fold[j], r["S_final"])))
+        worst = [max(worst[0], float(np.max(e_start))), max(worst[1], float(np.max(e_o))), max(worst[2], e_f)]
+        assert np.max(e_start) <= TOL, f"layer {layer} head {h}: segment-start state err {np.max(e_start):.3e}"
+        assert np.max(e_o) <= TOL, f"layer {layer} head {h}: seam output err {np.max(e_o):.3e}"
+        assert e_f <= TOL, f"layer {layer} head {h}: final state err {e_f:.3e}"
+    log(f"warm30: max segment-start state {worst[0]:.2e}, seam o {worst[1]:.2e}, final {worst[2]:.2e}")
