@@ -8,47 +8,126 @@
 // per chain; SCAN is a blocked reduce (aggregates), a fold over the block aggregates,
 // and a re-fold that writes the per-element states.
 //
-// Dense kind: each wave owns 32 columns of X = [T | S] in matrix-core accumulators
-// and computes T_i X with f16 hi/lo operand splits (three products, ~22-bit operand
-// precision) after scaling its column block by an exact power of two; T_i is staged in
-// LDS as hi/lo f16 with its contraction axis in accumulator order.
+// Dense kind: each wave owns 32 columns of S (and, for the composed transition, of
+// T) in matrix-core accumulators and computes T_i X with f16 hi/lo operand splits
+// (three products, ~22-bit operand precision) after scaling its column block by an
+// exact power of two; T_i is staged row-major in LDS as hi/lo f16 by loader waves,
+// one element ahead.
 // Diagonal / scalar kinds: elementwise, one thread per state entry stripe.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
 namespace hypic {
 
-__device__ __forceinline__ void split_hilo(const floatx16& x, int st, halfx8& hi, halfx8& lo) {
+__device__ __forceinline__ void split_hilo(const floatx16& x, int st, float scale, halfx8& hi, halfx8& lo) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const float v = x[8 * st + i];
+        const float v = x[8 * st + i] * scale;
         const _Float16 h = (_Float16)v;
         hi[i] = h;
         lo[i] = (_Float16)(v - (float)h);
     }
 }
 
-template <int D, bool WITH_T>
-__global__ __launch_bounds__((WITH_T ? 2 : 1) * D * 2) void fold_dense_kernel(FoldArgs a) {
-    constexpr int NWS = D / 32;                     // S waves
-    constexpr int NW = (WITH_T ? 2 : 1) * NWS;
-    constexpr int NB = D / 32;
-    constexpr int RS = D + 8;
-    __shared__ __align__(16) _Float16 sThi[D * RS];
-    __shared__ __align__(16) _Float16 sTlo[D * RS];
-    __shared__ int sE;
-    __shared__ int sEw[8];
+// A fragment of T_i for output row `row`, contraction block kb, step st: the 8
+// contraction indices a lane half h supplies in accumulator order are
+// 32kb + 16st + 4h + {0..3} and 32kb + 16st + 8 + 4h + {0..3}, two 8-byte runs of
+// the row-major staged tile.
+__device__ __forceinline__ halfx8 t_frag(const _Float16* base) {
+    typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+    const half4 x = *reinterpret_cast<const half4*>(base);
+    const half4 y = *reinterpret_cast<const half4*>(base + 8);
+    halfx8 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r[i] = x[i];
+        r[4 + i] = y[i];
+    }
+    return r;
+}
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, l32 = lane & 31;
-    const bool t_wave = WITH_T && wave < NWS;
-    const int col0 = (t_wave ? wave : (WITH_T ? wave - NWS : wave)) * 32;
+// Dense kind.  One workgroup per (chain, element block, role); role 0 composes S,
+// role 1 (launched only when the composed transition is wanted) composes T.  D/32
+// compute waves each keep 32 columns of the running S (or T) in accumulators; D/32
+// loader waves hold the next element's (T_i, S_i) in registers, loaded from HBM
+// while the current element is multiplied, and write them into LDS (T_i as hi/lo
+// f16, S_i as fp32, row-major) between two workgroup barriers.
+template <int D>
+__global__ __launch_bounds__(D * 4) void fold_dense_kernel(FoldArgs a) {
+    constexpr int NB = D / 32;                        // compute waves = loader waves
+    constexpr int NLT = NB * 64;                      // loader threads
+    constexpr int RS = D + 8;                         // staged row stride (halves)
+    constexpr int TPL = D * D / (4 * NLT);            // float4 of T_i per loader thread
+    static_assert(TPL * 4 * NLT == D * D, "staging split");
+    constexpr int RSS = D + 4;                        // staged S_i row stride (floats)
+    __shared__ __align__(16) _Float16 sT[2][D * RS];      // hi, lo
+    __shared__ __align__(16) float sS[D * RSS];
+    __shared__ int sE;
+    __shared__ int sEw[NB];
+
+    const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool loader = wave >= NB;
+    const bool t_role = blockIdx.z == 1;
     const int chain = blockIdx.x, blk = blockIdx.y;
     const int e0 = blk * a.per_block;
     const int e1 = min(a.n_elem, e0 + a.per_block);
     const long long DD = (long long)D * D;
+    auto elem = [&](int el) __attribute__((always_inline)) -> long long {
+        const int sl = a.slot ? a.slot[el] : el;
+        return (long long)sl * a.n_chain + chain;
+    };
 
+    if (loader) {
+        const int lt = tid - NB * 64;
+        typedef float f4 __attribute__((ext_vector_type(4)));
+        f4 tr[TPL], ts[TPL];
+        int ei = 0;
+        auto load = [&](int el) __attribute__((always_inline)) {
+            const long long so = elem(el);
+            const f4* src = reinterpret_cast<const f4*>(a.T_hat + so * DD);
+#pragma unroll
+            for (int r = 0; r < TPL; ++r) tr[r] = src[lt + NLT * r];
+            // (the transition role stages a second copy of T_i, from cache, in place of S_i)
+            const f4* srs = reinterpret_cast<const f4*>((t_role ? a.T_hat : a.S) + so * DD);
+#pragma unroll
+            for (int r = 0; r < TPL; ++r) ts[r] = srs[lt + NLT * r];
+            ei = a.T_exp[so];
+        };
+        auto stage = [&]() __attribute__((always_inline)) {
+            typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+            for (int r = 0; r < TPL; ++r) {
+                const int f = 4 * (lt + NLT * r);
+                const int row = f / D, col = f % D;
+                const f4 v = tr[r];
+                half4 h, l;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    h[u] = (_Float16)v[u];
+                    l[u] = (_Float16)(v[u] - (float)h[u]);
+                }
+                *reinterpret_cast<half4*>(&sT[0][row * RS + col]) = h;
+                *reinterpret_cast<half4*>(&sT[1][row * RS + col]) = l;
+                *reinterpret_cast<f4*>(&sS[row * RSS + col]) = ts[r];
+            }
+            if (lt == 0) sE = ei;
+        };
+        if (e0 < e1) load(e0);
+        for (int el = e0; el < e1; ++el) {
+            stage();
+            __syncthreads();  // element el staged
+            if (el + 1 < e1) load(el + 1);
+            __syncthreads();  // element el consumed
+        }
+        __syncthreads();  // epilogue exponent exchange
+        return;
+    }
+
+    // ---------------------------------- compute waves ----------------------------------
+    const int col0 = 32 * wave;
     floatx16 X[NB];
-    if (t_wave) {
+    if (t_role) {
 #pragma unroll
         for (int xb = 0; xb < NB; ++xb)
 #pragma unroll
@@ -63,115 +142,87 @@ __global__ __launch_bounds__((WITH_T ? 2 : 1) * D * 2) void fold_dense_kernel(Fo
 #pragma unroll
         for (int xb = 0; xb < NB; ++xb) X[xb] = zero16();
     }
-    int ew = 0;
 
+    int ew = 0;
     for (int el = e0; el < e1; ++el) {
-        const int slot = a.slot ? a.slot[el] : el;
-        const long long so = (long long)slot * a.n_chain + chain;
-        if (a.prefix && !t_wave) {
-            float* dst = a.prefix + ((long long)el * a.n_chain + chain) * DD;
-#pragma unroll
-            for (int xb = 0; xb < NB; ++xb)
-#pragma unroll
-                for (int j = 0; j < 16; ++j) dst[(32 * xb + acc_row(half, j)) * D + col0 + l32] = X[xb][j];
-        }
-        const float* Si = a.S + so * DD;
-        if (a.naive) {
-            if (!t_wave) {
+        const _Float16* Th = sT[0];
+        const _Float16* Tl = sT[1];
+        if (!t_role && a.prefix) {
+            {
+                float* dst = a.prefix + ((long long)el * a.n_chain + chain) * DD;
 #pragma unroll
                 for (int xb = 0; xb < NB; ++xb)
 #pragma unroll
-                    for (int j = 0; j < 16; ++j) X[xb][j] += Si[(32 * xb + acc_row(half, j)) * D + col0 + l32];
-            }
-            continue;
-        }
-        // stage T_i as hi/lo f16, rows = output rows, columns in accumulator order
-        const float* Ti = a.T_hat + so * DD;
-        for (int i = tid; i < D * D / 4; i += NW * 64) {
-            const int r = (4 * i) / D, c = (4 * i) % D;
-            const float4 v = reinterpret_cast<const float4*>(Ti)[i];
-            const float vv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const _Float16 hv = (_Float16)vv[u];
-                sThi[r * RS + acc_pos(c + u)] = hv;
-                sTlo[r * RS + acc_pos(c + u)] = (_Float16)(vv[u] - (float)hv);
+                    for (int j = 0; j < 16; ++j) dst[(32 * xb + acc_row(half, j)) * D + col0 + l32] = X[xb][j];
             }
         }
-        if (tid == 0) sE = a.T_exp[so];
-        __syncthreads();
-        const int ei = sE;
-        // scale this wave's column block to max |x| in [0.5, 1) before splitting
+        __syncthreads();  // element el staged
+        const int ecur = sE;
+        // scale this wave's columns to max |x| in [0.5, 1) before the hi/lo split
         float m = 0.f;
 #pragma unroll
         for (int xb = 0; xb < NB; ++xb)
 #pragma unroll
             for (int j = 0; j < 16; ++j) m = fmaxf(m, fabsf(X[xb][j]));
         const int sx = exp2_of(wave_max(m));
-        halfx8 bh[NB][2], bl[NB][2];
+        const float sc = ldexpf(1.f, -sx);
+        floatx16 acc[NB];
+#pragma unroll
+        for (int ob = 0; ob < NB; ++ob) acc[ob] = zero16();
 #pragma unroll
         for (int kb = 0; kb < NB; ++kb) {
-            floatx16 xs;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) xs[j] = ldexpf(X[kb][j], -sx);
-            split_hilo(xs, 0, bh[kb][0], bl[kb][0]);
-            split_hilo(xs, 1, bh[kb][1], bl[kb][1]);
-        }
+            for (int st = 0; st < 2; ++st) {
+                halfx8 bh, bl;
+                split_hilo(X[kb], st, sc, bh, bl);
 #pragma unroll
-        for (int ob = 0; ob < NB; ++ob) {
-            floatx16 acc = zero16();
-#pragma unroll
-            for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-                for (int st = 0; st < 2; ++st) {
-                    const int off = (32 * ob + l32) * RS + 32 * kb + 16 * half + 8 * st;
-                    const halfx8 ah = *reinterpret_cast<const halfx8*>(sThi + off);
-                    const halfx8 al = *reinterpret_cast<const halfx8*>(sTlo + off);
-                    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, bh[kb][st], acc, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bl[kb][st], acc, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bh[kb][st], acc, 0, 0, 0);
+                for (int ob = 0; ob < NB; ++ob) {
+                    const int off = (32 * ob + l32) * RS + 32 * kb + 16 * st + 4 * half;
+                    const halfx8 ah = t_frag(Th + off);
+                    const halfx8 al = t_frag(Tl + off);
+                    acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, bh, acc[ob], 0, 0, 0);
+                    acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bl, acc[ob], 0, 0, 0);
+                    acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bh, acc[ob], 0, 0, 0);
                 }
-            if (t_wave) {
-                X[ob] = acc;  // T columns: exponent tracked separately
-            } else {
-#pragma unroll
-                for (int j = 0; j < 16; ++j)
-                    X[ob][j] = ldexpf(acc[j], sx + ei) + Si[(32 * ob + acc_row(half, j)) * D + col0 + l32];
             }
         }
-        if (t_wave) {
-            // X holds T_i * (X * 2^-sx): exponent += sx + ei, then renormalise
+        if (t_role) {
+            // X = T_i (X 2^-sx): exponent += sx + e_i, then renormalise
             float mm = 0.f;
 #pragma unroll
             for (int xb = 0; xb < NB; ++xb)
 #pragma unroll
-                for (int j = 0; j < 16; ++j) mm = fmaxf(mm, fabsf(X[xb][j]));
+                for (int j = 0; j < 16; ++j) mm = fmaxf(mm, fabsf(acc[xb][j]));
             const int e = exp2_of(wave_max(mm));
+            const float r = ldexpf(1.f, -e);
 #pragma unroll
             for (int xb = 0; xb < NB; ++xb)
 #pragma unroll
-                for (int j = 0; j < 16; ++j) X[xb][j] = ldexpf(X[xb][j], -e);
-            ew += sx + ei + e;
-        }
-        __syncthreads();
-    }
-
-    if (WITH_T && a.out_T) {
-        if (t_wave && lane == 0) sEw[wave] = ew;
-        __syncthreads();
-        if (t_wave) {
-            int emax = sEw[0];
-            for (int w = 1; w < NWS; ++w) emax = max(emax, sEw[w]);
-            float* dst = a.out_T + ((long long)blk * a.n_chain + chain) * DD;
+                for (int j = 0; j < 16; ++j) X[xb][j] = acc[xb][j] * r;
+            ew += sx + ecur + e;
+        } else {
 #pragma unroll
             for (int xb = 0; xb < NB; ++xb)
 #pragma unroll
                 for (int j = 0; j < 16; ++j)
-                    dst[(32 * xb + acc_row(half, j)) * D + col0 + l32] = ldexpf(X[xb][j], ew - emax);
-            if (tid == 0) a.out_e[(long long)blk * a.n_chain + chain] = emax;
+                    X[xb][j] = ldexpf(acc[xb][j], sx + ecur) + sS[(32 * xb + acc_row(half, j)) * RSS + col0 + l32];
         }
+        __syncthreads();  // element el consumed
     }
-    if (!t_wave && a.out_S) {
+
+    if (t_role && lane == 0) sEw[wave] = ew;
+    __syncthreads();  // epilogue exponent exchange
+    if (t_role) {
+        int emax = sEw[0];
+        for (int w = 1; w < NB; ++w) emax = max(emax, sEw[w]);
+        float* dst = a.out_T + ((long long)blk * a.n_chain + chain) * DD;
+#pragma unroll
+        for (int xb = 0; xb < NB; ++xb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                dst[(32 * xb + acc_row(half, j)) * D + col0 + l32] = ldexpf(X[xb][j], ew - emax);
+        if (tid == 0) a.out_e[(long long)blk * a.n_chain + chain] = emax;
+    } else if (a.out_S) {
         float* dst = a.out_S + ((long long)blk * a.n_chain + chain) * DD;
 #pragma unroll
         for (int xb = 0; xb < NB; ++xb)
@@ -258,15 +309,11 @@ __global__ __launch_bounds__(256) void fold_diag_kernel(FoldArgs a) {
 hipError_t launch_fold(const FoldArgs& a, int d, int with_T, hipStream_t s) {
     const dim3 grid(a.n_chain, a.n_block);
     if (a.kind == 0 && !a.naive) {
-        if (d == 128) {
-            if (with_T) hipLaunchKernelGGL((fold_dense_kernel<128, true>), grid, dim3(512), 0, s, a);
-            else hipLaunchKernelGGL((fold_dense_kernel<128, false>), grid, dim3(256), 0, s, a);
-        } else if (d == 64) {
-            if (with_T) hipLaunchKernelGGL((fold_dense_kernel<64, true>), grid, dim3(256), 0, s, a);
-            else hipLaunchKernelGGL((fold_dense_kernel<64, false>), grid, dim3(128), 0, s, a);
-        } else {
-            return hipErrorInvalidValue;
-        }
+        // role 1 (the composed transition) only when its outputs are wanted
+        const dim3 g3(a.n_chain, a.n_block, (with_T && a.out_T) ? 2 : 1);
+        if (d == 128) hipLaunchKernelGGL((fold_dense_kernel<128>), g3, dim3(512), 0, s, a);
+        else if (d == 64) hipLaunchKernelGGL((fold_dense_kernel<64>), g3, dim3(256), 0, s, a);
+        else return hipErrorInvalidValue;
     } else {
         // naive addition of any kind, and the diagonal / scalar kinds
         if (d == 128) hipLaunchKernelGGL((fold_diag_kernel<128>), grid, dim3(256), 0, s, a);

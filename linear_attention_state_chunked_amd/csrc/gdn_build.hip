@@ -177,7 +177,8 @@ struct GLayout {
     static constexpr int IVl = IVh + sz_V32;
     static constexpr int TgA = IVl + sz_V32;           // Tg
     static constexpr int TgG = TgA + sz_T64;           // Tg diag(gamma)
-    static constexpr int Gv = TgG + sz_T64;            // G, gamma, beta (fp32)
+    static constexpr int TgGl = TgG + sz_T64;          // its low part (precise-T plan)
+    static constexpr int Gv = TgGl + sz_T64;           // G, gamma, beta (fp32)
     static constexpr int Misc = Gv + 3 * 64 * 4;       // counter, exponents
     static constexpr int total = Misc + 32 * 4;
     // regions that must start at zero and are only partly written
@@ -196,7 +197,7 @@ __device__ __forceinline__ void prep_barrier(int* cnt, int target, int lane) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
-template <int D, bool WITH_T, bool IN_BF16, bool PERSIST>
+template <int D, bool WITH_T, bool IN_BF16, bool PERSIST, bool PT>
 __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_build_kernel(EngineArgs a) {
     using LY = GLayout<D>;
     using E = _Float16;
@@ -283,7 +284,13 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
 #pragma unroll
                                 for (int st = 0; st < 2; ++st) {
                                     const halfx8 fa = ld8(Wf + (((mt * NB + kb) * 2 + st) * 64 + ln) * 8);
-                                    Vn[mt] = OpF16::mma(fa, OpF16::from_acc(X[kb], st), Vn[mt]);
+                                    if (PT && TR) {
+                                        const HL xb = split_acc(X[kb], st);
+                                        Vn[mt] = OpF16::mma(fa, xb.lo, Vn[mt]);
+                                        Vn[mt] = OpF16::mma(fa, xb.hi, Vn[mt]);
+                                    } else {
+                                        Vn[mt] = OpF16::mma(fa, OpF16::from_acc(X[kb], st), Vn[mt]);
+                                    }
                                 }
                             const float4* s4 = reinterpret_cast<const float4*>(Sc + 32 * mt + 4 * hf);
 #pragma unroll
@@ -305,7 +312,13 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
 #pragma unroll
                                 for (int st = 0; st < 2; ++st) {
                                     const halfx8 fa = colfrag_acc(Kn, RK, 32 * mt, 32 * xb, st, ln);
-                                    X[xb] = OpF16::mma(fa, OpF16::from_acc(Vn[mt], st), X[xb]);
+                                    if (PT && TR) {
+                                        const HL vb = split_acc(Vn[mt], st);
+                                        X[xb] = OpF16::mma(fa, vb.lo, X[xb]);
+                                        X[xb] = OpF16::mma(fa, vb.hi, X[xb]);
+                                    } else {
+                                        X[xb] = OpF16::mma(fa, OpF16::from_acc(Vn[mt], st), X[xb]);
+                                    }
                                 }
                         }
                         if (TR) {
@@ -329,6 +342,7 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                         const E* Kn1 = reinterpret_cast<const E*>(sm + LY::Kn + pn * LY::sz_K);
                         const E* TgA = reinterpret_cast<const E*>(sm + LY::TgA);
                         const E* TgG = reinterpret_cast<const E*>(sm + LY::TgG);
+                        const E* TgGl = reinterpret_cast<const E*>(sm + LY::TgGl);
                         const E* Vn1 = reinterpret_cast<const E*>(sm + LY::Vn);
                         E* Wf1 = reinterpret_cast<E*>(sm + LY::Wf + pn * LY::sz_Wf);
                         // -W'^T tiles (d rows, token columns): their accumulators are the operand
@@ -342,6 +356,10 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                                 for (int kk = 0; kk < 4; ++kk) {
                                     const halfx8 fa = colfrag_nat(Kn1, RK, 0, 32 * dt, kk, ln);
                                     const halfx8 fb = ld8(TgG + (32 * mt + lq) * RT + 16 * kk + 8 * hf);
+                                    if (PT) {
+                                        const halfx8 fl = ld8(TgGl + (32 * mt + lq) * RT + 16 * kk + 8 * hf);
+                                        acc = OpF16::mma(fa, fl, acc);
+                                    }
                                     acc = OpF16::mma(fa, fb, acc);
                                 }
 #pragma unroll
@@ -448,6 +466,7 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                         E* IVl = reinterpret_cast<E*>(sm + LY::IVl);
                         E* TgA = reinterpret_cast<E*>(sm + LY::TgA);
                         E* TgG = reinterpret_cast<E*>(sm + LY::TgG);
+                        E* TgGl = reinterpret_cast<E*>(sm + LY::TgGl);
                         float* sG = reinterpret_cast<float*>(sm + LY::Gv);
                         float* sGam = sG + 64;
                         float* sBeta = sG + 128;
@@ -580,14 +599,17 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                                         const float4 g4 = *reinterpret_cast<const float4*>(sGam + t0);
                                         const float bt[4] = {b4.x, b4.y, b4.z, b4.w};
                                         const float gm[4] = {g4.x, g4.y, g4.z, g4.w};
-                                        halfx4 ta, tg;
+                                        halfx4 ta, tg, tl;
 #pragma unroll
                                         for (int u = 0; u < 4; ++u) {
                                             ta[u] = (_Float16)(y[4 * q4 + u] * bt[u]);
-                                            tg[u] = (_Float16)(y[4 * q4 + u] * bt[u] * gm[u]);
+                                            const float g = y[4 * q4 + u] * bt[u] * gm[u];
+                                            tg[u] = (_Float16)g;
+                                            tl[u] = (_Float16)(g - (float)tg[u]);
                                         }
                                         st4h(TgA + (16 * bb + cr) * RT + t0, ta);
                                         st4h(TgG + (16 * bb + cr) * RT + t0, tg);
+                                        if (PT) st4h(TgGl + (16 * bb + cr) * RT + t0, tl);
                                     }
                                 }
                             }
@@ -625,14 +647,17 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                                     const float4 g4 = *reinterpret_cast<const float4*>(sGam + t0);
                                     const float bt[4] = {b4.x, b4.y, b4.z, b4.w};
                                     const float gm[4] = {g4.x, g4.y, g4.z, g4.w};
-                                    halfx4 ta, tg;
+                                    halfx4 ta, tg, tgl;
 #pragma unroll
                                     for (int u = 0; u < 4; ++u) {
                                         ta[u] = (_Float16)(v[u] * bt[u]);
-                                        tg[u] = (_Float16)(v[u] * bt[u] * gm[u]);
+                                        const float g = v[u] * bt[u] * gm[u];
+                                        tg[u] = (_Float16)g;
+                                        tgl[u] = (_Float16)(g - (float)tg[u]);
                                     }
                                     st4h(TgA + m * RT + t0, ta);
                                     st4h(TgG + m * RT + t0, tg);
+                                    if (PT) st4h(TgGl + m * RT + t0, tgl);
                                 }
                             }
                         }
@@ -667,15 +692,18 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                                 const float4 g4 = *reinterpret_cast<const float4*>(sGam + t0);
                                 const float bt[4] = {b4.x, b4.y, b4.z, b4.w};
                                 const float gm[4] = {g4.x, g4.y, g4.z, g4.w};
-                                halfx4 ta, tg;
+                                halfx4 ta, tg, tl;
 #pragma unroll
                                 for (int u = 0; u < 4; ++u) {
                                     const float v = -R2[4 * q4 + u];
                                     ta[u] = (_Float16)(v * bt[u]);
-                                    tg[u] = (_Float16)(v * bt[u] * gm[u]);
+                                    const float g = v * bt[u] * gm[u];
+                                    tg[u] = (_Float16)g;
+                                    tl[u] = (_Float16)(g - (float)tg[u]);
                                 }
                                 st4h(TgA + m * RT + t0, ta);
                                 st4h(TgG + m * RT + t0, tg);
+                                if (PT) st4h(TgGl + m * RT + t0, tl);
                             }
                         }
                     }
@@ -694,19 +722,20 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
     }
 }
 
-template <int D, bool WITH_T, bool IN_BF16>
+template <int D, bool WITH_T, bool IN_BF16, bool PT>
 static hipError_t launch_v(const EngineArgs& a, int grid, hipStream_t s) {
     constexpr int nt = ((WITH_T ? 2 : 1) * D / 32 + 4) * 64;
     if (a.persistent)
-        hipLaunchKernelGGL((gdn_build_kernel<D, WITH_T, IN_BF16, true>), dim3(grid), dim3(nt), 0, s, a);
+        hipLaunchKernelGGL((gdn_build_kernel<D, WITH_T, IN_BF16, true, PT>), dim3(grid), dim3(nt), 0, s, a);
     else
-        hipLaunchKernelGGL((gdn_build_kernel<D, WITH_T, IN_BF16, false>), dim3(grid), dim3(nt), 0, s, a);
+        hipLaunchKernelGGL((gdn_build_kernel<D, WITH_T, IN_BF16, false, PT>), dim3(grid), dim3(nt), 0, s, a);
     return hipGetLastError();
 }
 
 template <int D, bool IN_BF16>
 static hipError_t launch_t(const EngineArgs& a, int grid, hipStream_t s) {
-    return a.T_hat ? launch_v<D, true, IN_BF16>(a, grid, s) : launch_v<D, false, IN_BF16>(a, grid, s);
+    if (!a.T_hat) return launch_v<D, false, IN_BF16, false>(a, grid, s);
+    return a.precise_T ? launch_v<D, true, IN_BF16, true>(a, grid, s) : launch_v<D, true, IN_BF16, false>(a, grid, s);
 }
 
 hipError_t launch_gdn_build(const EngineArgs& a, int d, int prec_f32, int grid, hipStream_t s) {

@@ -40,6 +40,8 @@ hypic_status device_fail(const char* what, hipError_t e) {
 }
 
 constexpr size_t kAlign = 256;
+constexpr int32_t kPreciseTTokens = 2048;
+
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -264,6 +266,10 @@ hypic_status hypic_segment_build(const hypic_build_desc* d, hypic_stream_t strea
         a.out_stride = (long long)d->n_batch * d->h_v * d->d_k * d->d_v;
         a.T_hat = d->T_hat;
         a.T_exp = d->T_exp;
+        // f16 operand rounding errors of the T columns add up over a segment's chunks
+        // (relative error ~ 2.4e-4 * sqrt(chunks) for bf16 inputs): past 2048 tokens the
+        // T columns switch to hi/lo operands so long segments stay well inside 2e-3
+        a.precise_T = *std::max_element(len.begin(), len.end()) > kPreciseTTokens ? 1 : 0;
         int grid = (int)n_tasks;
         if (d->schedule == HYPIC_SCHED_RR) {
             const int cus = device_cu_count();
@@ -305,15 +311,52 @@ hypic_status hypic_segment_build(const hypic_build_desc* d, hypic_stream_t strea
 
 namespace {
 
+// Dense compose cost model in element steps, one workgroup per compute unit (LDS-bound):
+// FOLD runs one workgroup per chain (two with the composed T) for n steps; SCAN's block
+// reduce runs two per (chain, block) for B steps, the scan of the aggregates one (two)
+// per chain for n/B steps, and the optional re-fold one per (chain, block) for B steps.
+int64_t dense_rounds(int64_t wgs) {
+    int cus = device_cu_count();
+    if (cus <= 0) cus = 256;
+    return (wgs + cus - 1) / cus;
+}
+
+int64_t dense_fold_cost(const hypic_compose_desc* d) {
+    return dense_rounds((int64_t)d->n_chain * (d->T_total ? 2 : 1)) * d->n_elem;
+}
+
+int64_t dense_scan_cost(const hypic_compose_desc* d, int64_t b) {
+    const int64_t C = d->n_chain, nb = (d->n_elem + b - 1) / b;
+    int64_t cost = dense_rounds(2 * C * nb) * b + dense_rounds(C * (d->T_total ? 2 : 1)) * nb;
+    if (d->S_prefix) cost += dense_rounds(C * nb) * b;
+    return cost;
+}
+
 int scan_block_size(const hypic_compose_desc* d) {
     if (d->scan_block > 0) return d->scan_block;
-    int b = 1;
-    while (b * b < d->n_elem) ++b;  // ~sqrt(n): balances the two sequential phases
-    return std::max(b, 2);
+    const int64_t n = d->n_elem;
+    if (d->kind != HYPIC_DENSE_DELTA) {
+        int b = 1;
+        while ((int64_t)b * b < n) ++b;  // ~sqrt(n): balances the two sequential phases
+        return std::max(b, 2);
+    }
+    int best = 2;
+    int64_t best_cost = dense_scan_cost(d, 2);
+    for (int64_t b = 3; b <= n; ++b) {
+        const int64_t c = dense_scan_cost(d, b);
+        if (c < best_cost) {
+            best_cost = c;
+            best = (int)b;
+        }
+    }
+    return best;
 }
 
 hypic_compose_mode resolve_mode(const hypic_compose_desc* d) {
     if (d->mode != HYPIC_COMPOSE_AUTO) return d->mode;
+    if (d->kind == HYPIC_DENSE_DELTA)
+        return (d->n_elem >= 4 && dense_scan_cost(d, scan_block_size(d)) < dense_fold_cost(d)) ? HYPIC_COMPOSE_SCAN
+                                                                                                  : HYPIC_COMPOSE_FOLD;
     // few chains cannot fill the GPU with one block per chain: use the blocked scan
     return (d->n_elem >= 16 && (int64_t)d->n_chain * 4 < 1024) ? HYPIC_COMPOSE_SCAN : HYPIC_COMPOSE_FOLD;
 }

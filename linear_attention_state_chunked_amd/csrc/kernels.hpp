@@ -36,6 +36,7 @@ struct EngineArgs {
     float* T_hat;                // null: T columns skipped
     int* T_exp;
     void* o;
+    int precise_T;               // T columns with hi/lo operands (long segments)
 };
 
 // kind: 0 diagonal (GLA, per-channel log_alpha), 1 scalar

@@ -13,6 +13,7 @@ from .workloads import (  # noqa: F401
     conv_chain_inputs,
     layer_inputs,
     layer_conv_inputs,
+    random_elements,
     rne_bf16,
     request_order,
     segment_lengths,

@@ -282,3 +282,24 @@ def layer_conv_inputs(wl: Workload, layer: int) -> dict:
         beta[:, h] = c["beta"]
         la[:, h] = c["log_alpha"]
     return {"x": x, "w": w, "beta": beta, "log_alpha": la}
+
+
+# ----------------------------------------------------------------------------------------
+# synthetic element stores for the composition (well-conditioned transitions)
+
+
+def random_elements(seed: int, n_slot: int, n_chain: int, d: int) -> dict:
+    """A cache of n_slot elements for n_chain chains: T_hat = c Q (Q orthogonal from
+    the QR factor of a Gaussian matrix, c ~ U[0.6, 1]), T_exp in {-1, 0}, S ~ N(0,1).
+    Represented transitions have norm <= 1 and no preferred direction, so every
+    product T_i X carries weight in the composed state.  float32 values."""
+    rng = np.random.default_rng([seed, 0, 0, 13])
+    T = np.empty((n_slot, n_chain, d, d), np.float32)
+    for i in range(n_slot):
+        for c in range(n_chain):
+            q, r = np.linalg.qr(rng.standard_normal((d, d)))
+            q = q * np.sign(np.diag(r))[None, :]
+            T[i, c] = (rng.uniform(0.6, 1.0) * q).astype(np.float32)
+    e = rng.integers(-1, 1, size=(n_slot, n_chain), endpoint=True).astype(np.int32)
+    S = rng.standard_normal((n_slot, n_chain, d, d)).astype(np.float32)
+    return {"T_hat": T, "T_exp": e, "S": S}

@@ -104,6 +104,36 @@ def test_tiny_fp32_build_and_compose(gpu, name):
 
 
 # ----------------------------------------------------------------------------------------
+# composition of synthetic elements: well-conditioned transitions, request order by slot
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_compose_random_elements(gpu, d):
+    from synth import random_elements
+
+    n_slot, n_chain, n_elem = 23, 3, 37
+    el = random_elements(11 + d, n_slot, n_chain, d)
+    slot = np.random.default_rng([11, d]).integers(0, n_slot, size=n_elem).astype(np.int32)
+    S0 = np.random.default_rng([12, d]).standard_normal((n_chain, d, d)).astype(np.float32)
+    refs = []
+    for c in range(n_chain):
+        elems = [{"T_hat": el["T_hat"][s, c], "T_exp": el["T_exp"][s, c], "S": el["S"][s, c]} for s in slot]
+        refs.append(O.compose_fold("dense", elems, S0=S0[c]))
+    Td, ed, Sd = dev_tensor(el["T_hat"]), dev_tensor(el["T_exp"], torch.int32), dev_tensor(el["S"])
+    sd, S0d = dev_tensor(slot, torch.int32), dev_tensor(S0)
+    for mode, blk in (("fold", 0), ("scan", 0), ("scan", 5), ("auto", 0)):
+        r = H.hypic_compose(Td, ed, Sd, slot=sd, S0=S0d, mode=mode, want_T=True, want_prefix=True, scan_block=blk)
+        torch.cuda.synchronize()
+        for c in range(n_chain):
+            ref = refs[c]
+            eS = float(O.rel_err(r["S_final"][c].cpu().numpy(), ref["S_final"]))
+            eT = float(O.rel_err_T("dense", r["T_total"][c].cpu().numpy(), int(r["T_total_exp"][c]),
+                                   ref["T_hat"], ref["T_exp"]))
+            eP = float(np.max(O.rel_err(r["S_prefix"][:, c].cpu().numpy(), ref["S_prefix"])))
+            assert max(eS, eT, eP) < TOL_F32, (mode, blk, c, eS, eT, eP)
+
+
+# ----------------------------------------------------------------------------------------
 # bf16 dense build: ragged segments spanning several chunks, empty segments, GQA
 
 
