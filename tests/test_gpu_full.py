@@ -29,8 +29,9 @@ DEV = "cuda:0"
 
 def tol_T_total(n_elem):
     """Bound for a composed transition of n elements: each factor carries the
-    per-block bar, and errors of independent factors add in quadrature."""
-    return TOL * np.sqrt(n_elem)
+    per-block bar, and to first order the relative error of a product is at most
+    the sum of its factors' relative errors."""
+    return TOL * n_elem
 
 
 def log(msg):
