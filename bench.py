@@ -7,13 +7,24 @@ all 2,048 segment-heads in one launch), then the composition of the 64 cached
 segments into one running state per head.  Inputs are resident in HBM before
 the timed region.  Prints one JSON line.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Beside the headline line's fields, "rows" times every other step of the path on
+its own workload shape (inputs filled on the device; the timing does not depend on
+the values): the diagonal/scalar build (16 x 512 tokens, 16 RetNet + 16 GLA
+heads), the warm 30-layer path (conv warm-up of the seam tokens, seam advance,
+compose of 128 segments x 960 chains with prefix states), and the cold 100k-token
+30-layer build in LPT, round-robin and natural order with the single sequential
+pass beside it.  Each carries its algorithmic bytes or flops and the fraction of
+the matching MI355X peak.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-rows]
+  python bench.py --calibrate-copy      (a plain 1 GiB device copy, for HBM counters)
 """
 
 from __future__ import annotations
 
 import argparse
 import ctypes as C
+import hashlib
 import json
 import os
 import sys
@@ -103,6 +114,46 @@ class Path:
         self.compose()
 
 
+def engine_source_sha256():
+    path = os.path.join(ROOT, "linear_attention_state_chunked_amd", "csrc", "gdn_build.hip")
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per build launch from the committed rocprofv3 counter summary, if it
+    was taken on the current build engine source; else None."""
+    path = os.path.join(ROOT, "profiles", "gdn_build_gdn64k_hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and line.startswith("- "):
+                k, v = line[2:].split(":", 1)
+                kv[k.strip()] = v.strip().strip("`")
+    if kv.get("engine source sha256") != engine_source_sha256():
+        return None
+    try:
+        return float(kv["HBM bytes per launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def calibrate_copy():
+    """A plain device copy of known size: what FETCH_SIZE / WRITE_SIZE read for it
+    gives the scale of the counters."""
+    import torch
+
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}))
+
+
 def time_events(fn, reps, stream):
     import torch
 
@@ -113,6 +164,165 @@ def time_events(fn, reps, stream):
         e1.record(stream)
     torch.cuda.synchronize()
     return [e0.elapsed_time(e1) * 1e-3 for e0, e1 in evs]
+
+
+def _median_time(fn, reps=5, warm=2):
+    import torch
+
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    return float(np.median(time_events(fn, reps, torch.cuda.current_stream())))
+
+
+def _hbm(nbytes, t):
+    return {"s": t, "bytes": nbytes, "TB_per_s": nbytes / t / 1e12, "hbm_frac": nbytes / t / PEAK_HBM}
+
+
+def _mfma(flops, t):
+    return {"s": t, "flops": flops, "TFLOP_per_s": flops / t / 1e12, "mfma_frac": flops / t / PEAK_MFMA_F16}
+
+
+def row_diag(dev):
+    """Diagonal / scalar-decay build and compose: 16 x 512 tokens, 16 RetNet heads
+    (scalar) and 16 GLA heads (per-channel), d = 128, bf16 k and v."""
+    import torch
+    import torch.nn.functional as F
+
+    from linear_attention_state_chunked_amd import api as H
+
+    g = torch.Generator(device=dev)
+    g.manual_seed(1)
+    N, h, d, n_seg = 8192, 16, 128, 16
+    cu = np.arange(0, N + 1, N // n_seg, dtype=np.int64)
+    k = F.normalize(torch.randn(1, N, h, d, device=dev, generator=g), dim=-1).bfloat16()
+    v = torch.randn(1, N, h, d, device=dev, generator=g).bfloat16()
+    gam = 1.0 - 2.0 ** -(5.0 + 4.0 * torch.arange(h, device=dev) / 15.0)
+    la_s = torch.log(gam)[None, None, :].expand(1, N, h).contiguous().float()
+    la_g = (-F.softplus(-(2.0 + torch.randn(1, N, h, d, device=dev, generator=g))) / 16.0).float()
+    out = {}
+    for kind, la in (("scalar", la_s), ("diag", la_g)):
+        t = _median_time(lambda: H.hypic_segment_build(k, v, la, cu, kind=kind))
+        b = H.hypic_segment_build(k, v, la, cu, kind=kind)
+        tlen = d if kind == "diag" else 1
+        nbytes = 2 * k.numel() * 2 + la.numel() * 4 + n_seg * h * (d * d + tlen + 1) * 4
+        row = _hbm(nbytes, t)
+        row["flops"] = 2 * N * h * d * d
+        Tn = b["T_hat"].reshape((n_seg, h) + ((d,) if kind == "diag" else ()))
+        tc = _median_time(lambda: H.hypic_compose(Tn, b["T_exp"].reshape(n_seg, h), b["S"].reshape(n_seg, h, d, d),
+                                                  kind=kind, mode="fold"))
+        row["compose"] = _hbm(n_seg * h * (d * d + tlen + 1) * 4, tc)
+        out[kind] = row
+    return out
+
+
+def row_warm(dev):
+    """Warm 30-layer path, 128 cached segments x 32 value heads (16 key heads), seam
+    w = 8: conv warm-up of the 1,024 seam tokens per layer with the carried conv
+    state, seam build (T, S from zero), compose of the 256 interleaved (seam, rest)
+    elements per chain with prefix states, seam outputs from the composed states."""
+    import torch
+
+    from linear_attention_state_chunked_amd import api as H
+
+    L, hk, hv, d, n_slot, w = 30, 16, 32, 128, 128, 8
+    nw, nc = n_slot * w, L * hv
+    g = torch.Generator(device=dev)
+    g.manual_seed(3)
+    rnd = lambda *sh, dt=torch.float32: torch.randn(*sh, device=dev, generator=g).to(dt)
+    xs = {"q": rnd(L, nw, hk * d, dt=torch.bfloat16), "k": rnd(L, nw, hk * d, dt=torch.bfloat16),
+          "v": rnd(L, nw, hv * d, dt=torch.bfloat16)}
+    ws = {n: 0.5 * rnd(L, x.shape[2], 4) for n, x in xs.items()}
+    st = {n: rnd(n_slot, L, 3, x.shape[2], dt=torch.bfloat16) for n, x in xs.items()}
+    sidx = torch.from_numpy(np.concatenate([[-1], np.random.default_rng(3).permutation(n_slot)[:-1]]).astype(np.int32)).to(dev)
+    cu_seam = np.arange(0, nw + 1, w, dtype=np.int64)
+    beta = torch.sigmoid(rnd(L, nw, hv))
+    la = -0.05 * torch.nn.functional.softplus(rnd(L, nw, hv))
+    y = {}
+
+    def conv():
+        for n in ("q", "k", "v"):
+            y[n] = H.hypic_conv_warmup(xs[n], ws[n], cu_seam, state_in=st[n], state_index=sidx,
+                                       out_dtype=torch.float32, want_state=False)["y"]
+
+    t_conv = _median_time(conv)
+    conv()
+    conv_bytes = sum(x.numel() * 2 + x.numel() * 4 + n_slot * L * 3 * x.shape[2] * 2 for x in xs.values())
+    sq, sk, sv = y["q"].view(L, nw, hk, d), y["k"].view(L, nw, hk, d), y["v"].view(L, nw, hv, d)
+    E_T = torch.empty((2 * n_slot, nc, d, d), device=dev)
+    E_e = torch.full((2 * n_slot, nc), -60, dtype=torch.int32, device=dev)
+    E_S = torch.empty((2 * n_slot, nc, d, d), device=dev)
+    E_T[:n_slot].normal_(generator=g).mul_(0.05)
+    E_S[:n_slot].normal_(generator=g)
+    seam_out = {"T_hat": E_T[n_slot:].view(n_slot, L, hv, d, d), "T_exp": E_e[n_slot:].view(n_slot, L, hv),
+                "S_seam": E_S[n_slot:].view(n_slot, L, hv, d, d)}
+    seam1 = lambda: H.hypic_seam_advance(sq, sk, sv, la, beta, cu_seam, want_o=False, S_out=None, want_T=True,
+                                         want_S_seam=True, qk_l2norm=True, out=seam_out)
+    t_seam1 = _median_time(seam1)
+    seam1()
+    slot = np.empty(2 * n_slot, np.int32)
+    slot[0::2] = n_slot + np.arange(n_slot)
+    slot[1::2] = np.random.default_rng(3).permutation(n_slot)
+    slot_d = torch.from_numpy(slot).to(dev)
+    res = {}
+
+    def compose():
+        res["c"] = H.hypic_compose(E_T, E_e, E_S, slot=slot_d, mode="auto", want_prefix=True)
+
+    t_comp = _median_time(compose, reps=3)
+    pre = res["c"]["S_prefix"]
+    seam2 = lambda: H.hypic_seam_advance(sq, sk, sv, la, beta, cu_seam, S_in=pre, state_stride=2 * nc * d * d,
+                                         S_out=None, qk_l2norm=True, out_dtype=torch.float32)
+    t_seam2 = _median_time(seam2)
+    tok_bytes = (2 * hk + hv) * d * 4 * L * nw + 2 * hv * 4 * L * nw
+    seam1_bytes = tok_bytes + 2 * n_slot * nc * d * d * 4 + n_slot * nc * 4
+    comp_bytes = 2 * n_slot * nc * (2 * d * d * 4 + 4) + 2 * n_slot * nc * d * d * 4
+    seam2_bytes = tok_bytes + n_slot * nc * d * d * 4 + L * nw * hv * d * 4
+    return {"conv_warmup": _hbm(conv_bytes, t_conv),
+            "seam_build": _hbm(seam1_bytes, t_seam1),
+            "compose_fold_prefix": dict(_hbm(comp_bytes, t_comp), us_per_segment=t_comp * 1e6 / n_slot),
+            "seam_outputs": _hbm(seam2_bytes, t_seam2),
+            "total_ms": (t_conv + t_seam1 + t_comp + t_seam2) * 1e3}
+
+
+def row_cold(dev):
+    """Cold 100,000-token request, 30 layers x 32 value heads (16 key heads), 20
+    segments of uneven length: the build of all 19,200 segment-heads in LPT,
+    round-robin and natural task order, and the single sequential pass (no T)."""
+    import torch
+
+    from linear_attention_state_chunked_amd import api as H
+    from synth import WORKLOADS, segment_lengths
+    from synth.device_fill import fill_dense_layer_
+
+    wl = WORKLOADS["cold100k_bf16"]
+    lens = segment_lengths(wl)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    N, L, hk, hv, d = int(cu[-1]), wl.n_layers, wl.h_k, wl.h_v, wl.d
+    k = torch.empty((L, N, hk, d), dtype=torch.bfloat16, device=dev)
+    v = torch.empty((L, N, hv, d), dtype=torch.bfloat16, device=dev)
+    beta = torch.empty((L, N, hv), device=dev)
+    la = torch.empty((L, N, hv), device=dev)
+    for layer in range(L):
+        fill_dense_layer_(wl, layer, k[layer], v[layer], beta[layer], la[layer])
+    n_seg = len(lens)
+    out = {"T_hat": torch.empty((n_seg, L, hv, d, d), device=dev),
+           "T_exp": torch.empty((n_seg, L, hv), dtype=torch.int32, device=dev),
+           "S": torch.empty((n_seg, L, hv, d, d), device=dev)}
+    chunks = sum((n + CHUNK - 1) // CHUNK for n in lens)
+    flops = build_flops_per_chunk() * chunks * L * hv
+    res = {}
+    for sched in ("lpt", "rr", "natural"):
+        t = _median_time(lambda: H.hypic_segment_build(k, v, la, cu, beta, schedule=sched, out=out), reps=3)
+        res[sched] = _mfma(flops, t)
+    single_flops = (2 * CHUNK * CHUNK * d / 2 + CHUNK ** 3 / 3 + 4 * CHUNK * CHUNK * d + 4 * CHUNK * d * d) \
+        * ((N + CHUNK - 1) // CHUNK) * L * hv
+    t = _median_time(lambda: H.hypic_segment_build(k, v, la, [0, N], beta, with_T=False), reps=3)
+    res["single_pass_no_T"] = _mfma(single_flops, t)
+    E = (out["T_hat"].view(n_seg, L * hv, d, d), out["T_exp"].view(n_seg, L * hv), out["S"].view(n_seg, L * hv, d, d))
+    tc = _median_time(lambda: H.hypic_compose(*E, mode="scan"), reps=3)
+    res["compose_scan"] = dict(_hbm(n_seg * L * hv * (2 * d * d * 4 + 4), tc), us_per_segment=tc * 1e6 / n_seg)
+    return res
 
 
 def _oracle_chain(args):
@@ -164,7 +374,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--no-rows", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
@@ -197,6 +412,7 @@ def main():
     flops = build_flops_per_chunk() * n_chunks * path.h_v
     achieved = flops / t_build
     comp_bytes = path.n_seg * path.h_v * (2 * D * D * 4)     # read T_hat and S per element
+    traffic = measured_traffic()
     out = {
         "metric": METRIC,
         "value": value,
@@ -220,8 +436,17 @@ def main():
         "compose_us_per_segment": t_comp * 1e6 / path.n_seg,
         "compose_hbm_frac": comp_bytes / t_comp / PEAK_HBM,
         "roofline": {"bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK_MFMA_F16 / 1e12,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_MFMA_F16, "traffic": None},
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_MFMA_F16, "traffic": traffic},
     }
+    if not args.no_rows:
+        del path, inp
+        torch.cuda.empty_cache()
+        rows = {}
+        for name, fn in (("diag_scalar_build_16x512", row_diag), ("warm30_seam_compose", row_warm),
+                         ("cold100k_build", row_cold)):
+            rows[name] = fn(dev)
+            torch.cuda.empty_cache()
+        out["rows"] = rows
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_budget)
     print(json.dumps(out))
