@@ -589,6 +589,36 @@ hypic_status hypic_seam_advance(const hypic_seam_desc* d, hypic_stream_t stream)
     const int64_t dense = (int64_t)d->n_batch * d->h_v * d->d_k * d->d_v;
     const bool f32 = d->precision == HYPIC_PREC_F32 ||
                      (d->precision == HYPIC_PREC_AUTO && d->in_dtype == HYPIC_F32 && d->d_k == 64);
+    if (*std::max_element(len.begin(), len.end()) <= hypic::kSeamShort && d->d_k == d->d_v) {
+        // short seams: closed rank-w form, fp32 arithmetic, every output in one launch
+        hypic::SeamArgs q{};
+        q.n_batch = d->n_batch;
+        q.n_tokens = d->n_tokens;
+        q.h_k = d->h_k;
+        q.h_v = d->h_v;
+        q.qk_l2norm = d->qk_l2norm;
+        q.in_bf16 = d->in_dtype == HYPIC_BF16;
+        q.out_bf16 = d->out_dtype == HYPIC_BF16;
+        q.seg_start = reinterpret_cast<const long long*>(ws + L.off_start);
+        q.seg_len = reinterpret_cast<const int*>(ws + L.off_len);
+        q.n_tasks = (int)n_tasks;
+        q.q = d->q;
+        q.k = d->k;
+        q.v = d->v;
+        q.log_alpha = d->log_alpha;
+        q.beta = d->beta;
+        q.S_in = d->S_in;
+        q.in_stride = d->state_stride ? d->state_stride : dense;
+        q.S_out = d->S_out;
+        q.out_stride = d->state_stride ? d->state_stride : dense;
+        q.o = d->o;
+        q.T_hat = d->T_hat;
+        q.T_exp = d->T_exp;
+        q.S_seam = d->S_seam;
+        e = hypic::launch_seam(q, d->d_k, s);
+        if (e != hipSuccess) return device_fail("seam: short-seam launch", e);
+        return ok();
+    }
     hypic::EngineArgs a{};
     a.n_batch = d->n_batch;
     a.n_tokens = d->n_tokens;

@@ -81,6 +81,32 @@ struct FoldArgs {
     int naive;                // 1: S <- S + S_i
 };
 
+// One short-seam launch (every seam <= 16 tokens): one workgroup per (seam, batch,
+// value head); computes whichever of o, S_out, T_hat/T_exp, S_seam are non-null.
+struct SeamArgs {
+    int n_batch;
+    long long n_tokens;
+    int h_k, h_v;
+    int qk_l2norm;
+    int in_bf16, out_bf16;
+    const long long* seg_start;  // device [n_seam]
+    const int* seg_len;          // device [n_seam]
+    int n_tasks;
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* log_alpha;
+    const float* beta;
+    const float* S_in;           // null: zero
+    long long in_stride;         // floats between seams' state blocks
+    float* S_out;
+    long long out_stride;
+    void* o;
+    float* T_hat;
+    int* T_exp;
+    float* S_seam;
+};
+
 struct ConvArgs {
     int n_batch;
     long long n_tokens;
@@ -107,6 +133,9 @@ hipError_t launch_gdn_build(const EngineArgs& a, int d, int prec_f32, int grid, 
 hipError_t launch_diag_build(const DiagArgs& a, int d, hipStream_t s);
 hipError_t launch_fold(const FoldArgs& a, int d, int with_T, hipStream_t s);
 hipError_t launch_conv(const ConvArgs& a, long long total_tokens, hipStream_t s);
+// seams of at most kSeamShort tokens
+constexpr int kSeamShort = 16;
+hipError_t launch_seam(const SeamArgs& a, int d, hipStream_t s);
 
 // resident workgroups per CU for the dense engine (for persistent grids)
 int dense_engine_max_lds(int d, int prec_f32, int with_q);

@@ -232,11 +232,16 @@ def test_diag_scalar_build_compose_and_naive(gpu, name, kind):
 # seam advance
 
 
+SEAM_WIDTHS = {"short": [1, 8, 16, 0, 5, 12, 3],          # all <= 16: closed rank-w kernel
+               "long": [1, 8, 8, 33, 64, 0, 70]}          # some > 16: chunked engine
+
+
+@pytest.mark.parametrize("widths", ["short", "long"])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_seam_advance(gpu, dtype):
+def test_seam_advance(gpu, dtype, widths):
     wl = WORKLOADS["gdn64k_bf16" if dtype == "bf16" else "tiny_gdn_f32"]
     d = wl.d
-    ws = [1, 8, 8, 33, 64, 0, 70]
+    ws = SEAM_WIDTHS[widths]
     n = sum(ws)
     h_v = 2 if dtype == "bf16" else 1
     dev, chains = _dense_inputs(wl, n, h_v)
@@ -264,7 +269,7 @@ def test_seam_advance(gpu, dtype):
             else:
                 errs["S_seam"].append(float(O.rel_err(S_seam, r["S_seam"])))
     for key, e in errs.items():
-        print(f"seam {dtype} {key}: max err {max_err(e):.2e}")
+        print(f"seam {dtype} {widths} {key}: max err {max_err(e):.2e}")
         assert max_err(e) < tol, key
 
 
