@@ -63,7 +63,8 @@ def _as4(x):
 
 
 def hypic_segment_build(k, v, log_alpha, cu_seqlens, beta=None, *, kind="dense", with_T=True, skip_head=0,
-                        qk_l2norm=False, schedule="natural", precision="auto", out=None):
+                        qk_l2norm=False, schedule="natural", precision="auto", out=None, workspace_bytes=None,
+                        workspace=None):
     """Per-segment (T_hat, T_exp, S) for every (segment, batch, value head).
 
     k [B,N,h_k,d] (or [N,h_k,d]), v [B,N,h_v,d]; log_alpha [B,N,h_v] (diag:
@@ -71,6 +72,9 @@ def hypic_segment_build(k, v, log_alpha, cu_seqlens, beta=None, *, kind="dense",
     (dense [n_seg,B,h_v,d,d], diag [n_seg,B,h_v,d], scalar [n_seg,B,h_v]) or None,
     T_exp [n_seg,B,h_v] int32 or None, and S [n_seg,B,h_v,d,d] float32.
     `out` may hold preallocated "T_hat", "T_exp", "S" tensors of those shapes.
+    workspace_bytes overrides the queried workspace size (a smaller one that still
+    holds the segment table selects the single-launch engine); workspace passes a
+    caller-owned uint8 device tensor instead.
     """
     k, v = _contig(_as4(k), "k"), _contig(_as4(v), "v")
     kd = A.KIND[kind]
@@ -93,8 +97,11 @@ def hypic_segment_build(k, v, log_alpha, cu_seqlens, beta=None, *, kind="dense",
                        T_hat=_ptr(T_hat), T_exp=_ptr(T_exp), S=_ptr(S), schedule=A.SCHED[schedule],
                        precision=A.PREC[precision])
     L = A.lib()
-    nbytes = L.hypic_segment_build_workspace_bytes(C.byref(desc))
-    ws = _workspace(nbytes, dev)
+    if workspace is not None:
+        ws = _contig(workspace, "workspace")
+    else:
+        nbytes = L.hypic_segment_build_workspace_bytes(C.byref(desc)) if workspace_bytes is None else workspace_bytes
+        ws = _workspace(nbytes, dev)
     desc.workspace, desc.workspace_bytes = ws.data_ptr(), ws.numel()
     A.check(L.hypic_segment_build(C.byref(desc), _stream()))
     return {"T_hat": T_hat, "T_exp": T_exp, "S": S, "_workspace": ws}

@@ -197,6 +197,210 @@ __device__ __forceinline__ void prep_barrier(int* cnt, int target, int lane) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
+// Chunk-local UT transform on four cooperating waves (pw = 0..3): from the staged K rows
+// (f16, row stride D + 8) and the gate prefix, the gram K K^T, L = strictly-lower(
+// beta_i e^{G_i - G_j} K K^T) and Tg = (I + L)^-1 diag(beta).  Tg leaves through
+// out(row, col0, Tg[row][col0..+3], (Tg diag(gamma))[row][col0..+3] hi, lo) as f16; only
+// the lower 16x16 blocks are written.  pbar() orders the four waves between the stages.
+template <int D, bool PT, class Bar, class Out>
+__device__ __forceinline__ void ut_solve(const _Float16* Kn1, const float* sG, const float* sGam, const float* sBeta,
+                                         float* Ld, _Float16* LTh, _Float16* LTl, _Float16* DVh, _Float16* DVl,
+                                         _Float16* IVh, _Float16* IVl, int pw, int ln, Bar&& pbar, Out&& out) {
+    constexpr int RK = D + 8, RT = 64 + 8, RV = 32 + 8;
+    const int hf = ln >> 5, lq = ln & 31;
+    // ---- gram K K^T (three lower 32x32 tiles) -> L^T rows (hi/lo) and
+    //      the fp32 diagonal 16x16 blocks of L
+    if (pw < 3) {
+        const int ti = pw == 0 ? 0 : 1, tj = pw == 2 ? 1 : 0;
+        floatx16 acc = zero16();
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            const halfx8 fa = ld8(Kn1 + (32 * ti + lq) * RK + 16 * kk + 8 * hf);
+            const halfx8 fb = ld8(Kn1 + (32 * tj + lq) * RK + 16 * kk + 8 * hf);
+            acc = OpF16::mma(fa, fb, acc);
+        }
+        // lane column j; its registers hold rows i = 32 ti + 8 q + 4 h + 0..3
+        const int j = 32 * tj + lq;
+        const float Gj = sG[j];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int i0 = 32 * ti + 8 * q + 4 * hf;
+            const float4 g4 = *reinterpret_cast<const float4*>(sG + i0);
+            const float4 b4 = *reinterpret_cast<const float4*>(sBeta + i0);
+            const float gi[4] = {g4.x, g4.y, g4.z, g4.w};
+            const float bi[4] = {b4.x, b4.y, b4.z, b4.w};
+            float v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                v[u] = (i0 + u > j) ? bi[u] * fexp(gi[u] - Gj) * acc[4 * q + u] : 0.f;
+            halfx4 vh, vl;
+            split4(v, vh, vl);
+            st4h(LTh + j * RT + i0, vh);
+            st4h(LTl + j * RT + i0, vl);
+            if (ti == tj && ((i0 >> 4) == (j >> 4))) {
+                // L_bb[i][m] with m = j: column j of the diagonal block
+                float* ld = Ld + (i0 >> 4) * (16 * 20) + (j & 15);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) ld[((i0 + u) & 15) * 20] = v[u];
+            }
+        }
+    }
+    pbar(ln);
+
+    // ---- solve, halves q = 0, 1 (one wave each): rows of the 16x16
+    //      diagonal inverses, then Inv' = D' - D' N D'
+    if (pw < 2) {
+        const int q = pw;
+        {   // lanes 0..31: row cr of the diagonal inverse D_bb, bb = 2q + (ln >> 4)
+            const int bb = 2 * q + ((ln >> 4) & 1), cr = ln & 15, o = 16 * (bb & 1);
+            if (ln < 32) {
+                float y[16];
+#pragma unroll
+                for (int m = 0; m < 16; ++m) y[m] = (m == cr) ? 1.f : 0.f;
+                const float* Lb = Ld + bb * (16 * 20);
+                // rows of L_bb, loaded three steps ahead of their use
+                float4 rw[16][4];
+#pragma unroll
+                for (int i = 15; i >= 13; --i)
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4)
+                        if (4 * q4 < i) rw[i][q4] = reinterpret_cast<const float4*>(Lb + i * 20)[q4];
+#pragma unroll
+                for (int i = 15; i >= 1; --i) {
+                    if (i - 3 >= 1) {
+#pragma unroll
+                        for (int q4 = 0; q4 < 4; ++q4)
+                            if (4 * q4 < i - 3)
+                                rw[i - 3][q4] = reinterpret_cast<const float4*>(Lb + (i - 3) * 20)[q4];
+                    }
+                    const float yi = y[i];
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        if (4 * q4 >= i) break;
+                        const float l4[4] = {rw[i][q4].x, rw[i][q4].y, rw[i][q4].z, rw[i][q4].w};
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+                            if (4 * q4 + u < i) y[4 * q4 + u] -= yi * l4[u];
+                    }
+                }
+                // y = row cr of D_bb: D' and Inv' rows (hi/lo), Tg rows
+                const int rloc = o + cr;
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    halfx4 vh, vl;
+                    split4(y + 4 * q4, vh, vl);
+                    st4h(DVh + (32 * q + rloc) * RV + o + 4 * q4, vh);
+                    st4h(DVl + (32 * q + rloc) * RV + o + 4 * q4, vl);
+                    st4h(IVh + (32 * q + rloc) * RV + o + 4 * q4, vh);
+                    st4h(IVl + (32 * q + rloc) * RV + o + 4 * q4, vl);
+                    const int t0 = 16 * bb + 4 * q4;
+                    const float4 b4 = *reinterpret_cast<const float4*>(sBeta + t0);
+                    const float4 g4 = *reinterpret_cast<const float4*>(sGam + t0);
+                    const float bt[4] = {b4.x, b4.y, b4.z, b4.w};
+                    const float gm[4] = {g4.x, g4.y, g4.z, g4.w};
+                    halfx4 ta, tg, tl;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        ta[u] = (_Float16)(y[4 * q4 + u] * bt[u]);
+                        const float g = y[4 * q4 + u] * bt[u] * gm[u];
+                        tg[u] = (_Float16)g;
+                        tl[u] = (_Float16)(g - (float)tg[u]);
+                    }
+                    out(16 * bb + cr, t0, ta, tg, tl);
+                }
+            }
+        }
+        // Q = N^T D'^T: only contraction k = 16..31 and rows r < 16 of N^T are nonzero
+        HL fa, fb;
+        if (lq < 16) {
+            fa.hi = ld8(LTh + (32 * q + lq) * RT + 32 * q + 16 + 8 * hf);
+            fa.lo = ld8(LTl + (32 * q + lq) * RT + 32 * q + 16 + 8 * hf);
+        } else {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) fa.hi[u] = fa.lo[u] = (_Float16)0.f;
+        }
+        fb.hi = ld8(DVh + (32 * q + lq) * RV + 16 + 8 * hf);
+        fb.lo = ld8(DVl + (32 * q + lq) * RV + 16 + 8 * hf);
+        const floatx16 Qt = mma3(fa, fb, zero16());
+        // R^T = D'^T Q: Q has rows k < 16 only, i.e. contraction step 0 in
+        // accumulator order
+        HL da;
+        da.hi = colfrag_acc(DVh + 32 * q * RV, RV, 0, 0, 0, ln);
+        da.lo = colfrag_acc(DVl + 32 * q * RV, RV, 0, 0, 0, ln);
+        const floatx16 Rt = mma3(da, split_acc(Qt, 0), zero16());
+        // lane column m holds R[m][t], t = acc_row(h, j); nonzero for m >= 16, t < 16
+        if (lq >= 16) {
+            const int m = 32 * q + lq;
+#pragma unroll
+            for (int q4 = 0; q4 < 2; ++q4) {
+                const int tl = 8 * q4 + 4 * hf;   // rows acc_row(h, 4 q4 + 0..3)
+                float v[4] = {-Rt[4 * q4], -Rt[4 * q4 + 1], -Rt[4 * q4 + 2], -Rt[4 * q4 + 3]};
+                halfx4 vh, vl;
+                split4(v, vh, vl);
+                st4h(IVh + m * RV + tl, vh);
+                st4h(IVl + m * RV + tl, vl);
+                const int t0 = 32 * q + tl;
+                const float4 b4 = *reinterpret_cast<const float4*>(sBeta + t0);
+                const float4 g4 = *reinterpret_cast<const float4*>(sGam + t0);
+                const float bt[4] = {b4.x, b4.y, b4.z, b4.w};
+                const float gm[4] = {g4.x, g4.y, g4.z, g4.w};
+                halfx4 ta, tg, tgl;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    ta[u] = (_Float16)(v[u] * bt[u]);
+                    const float g = v[u] * bt[u] * gm[u];
+                    tg[u] = (_Float16)g;
+                    tgl[u] = (_Float16)(g - (float)tg[u]);
+                }
+                out(m, t0, ta, tg, tgl);
+            }
+        }
+    }
+    pbar(ln);
+
+    // ---- solve, lower-left 32x32 block: -Inv'_1 L'_10 Inv'_0, computed as
+    //      its transpose Inv'_0^T (L'_10^T Inv'_1^T)
+    if (pw == 0) {
+        floatx16 Q2 = zero16();
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            HL fa, fb;
+            fa.hi = ld8(LTh + lq * RT + 32 + 16 * kk + 8 * hf);
+            fa.lo = ld8(LTl + lq * RT + 32 + 16 * kk + 8 * hf);
+            fb.hi = ld8(IVh + (32 + lq) * RV + 16 * kk + 8 * hf);
+            fb.lo = ld8(IVl + (32 + lq) * RV + 16 * kk + 8 * hf);
+            Q2 = mma3(fa, fb, Q2);
+        }
+        floatx16 R2 = zero16();
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            HL da;
+            da.hi = colfrag_acc(IVh, RV, 0, 0, st, ln);
+            da.lo = colfrag_acc(IVl, RV, 0, 0, st, ln);
+            R2 = mma3(da, split_acc(Q2, st), R2);
+        }
+        const int m = 32 + lq;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const int t0 = 8 * q4 + 4 * hf;
+            const float4 b4 = *reinterpret_cast<const float4*>(sBeta + t0);
+            const float4 g4 = *reinterpret_cast<const float4*>(sGam + t0);
+            const float bt[4] = {b4.x, b4.y, b4.z, b4.w};
+            const float gm[4] = {g4.x, g4.y, g4.z, g4.w};
+            halfx4 ta, tg, tl;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float v = -R2[4 * q4 + u];
+                ta[u] = (_Float16)(v * bt[u]);
+                const float g = v * bt[u] * gm[u];
+                tg[u] = (_Float16)g;
+                tl[u] = (_Float16)(g - (float)tg[u]);
+            }
+            out(m, t0, ta, tg, tl);
+        }
+    }
+}
+
 template <int D, bool WITH_T, bool IN_BF16, bool PERSIST, bool PT>
 __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_build_kernel(EngineArgs a) {
     using LY = GLayout<D>;
@@ -509,203 +713,12 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                         if (c + 2 < nc) prefetch(c + 2, ln, pt);
                         pbar(ln);
 
-                        // ---- gram K K^T (three lower 32x32 tiles) -> L^T rows (hi/lo) and
-                        //      the fp32 diagonal 16x16 blocks of L
-                        if (pw < 3) {
-                            const int ti = pw == 0 ? 0 : 1, tj = pw == 2 ? 1 : 0;
-                            floatx16 acc = zero16();
-#pragma unroll
-                            for (int kk = 0; kk < D / 16; ++kk) {
-                                const halfx8 fa = ld8(Kn1 + (32 * ti + lq) * RK + 16 * kk + 8 * hf);
-                                const halfx8 fb = ld8(Kn1 + (32 * tj + lq) * RK + 16 * kk + 8 * hf);
-                                acc = OpF16::mma(fa, fb, acc);
-                            }
-                            // lane column j; its registers hold rows i = 32 ti + 8 q + 4 h + 0..3
-                            const int j = 32 * tj + lq;
-                            const float Gj = sG[j];
-#pragma unroll
-                            for (int q = 0; q < 4; ++q) {
-                                const int i0 = 32 * ti + 8 * q + 4 * hf;
-                                const float4 g4 = *reinterpret_cast<const float4*>(sG + i0);
-                                const float4 b4 = *reinterpret_cast<const float4*>(sBeta + i0);
-                                const float gi[4] = {g4.x, g4.y, g4.z, g4.w};
-                                const float bi[4] = {b4.x, b4.y, b4.z, b4.w};
-                                float v[4];
-#pragma unroll
-                                for (int u = 0; u < 4; ++u)
-                                    v[u] = (i0 + u > j) ? bi[u] * fexp(gi[u] - Gj) * acc[4 * q + u] : 0.f;
-                                halfx4 vh, vl;
-                                split4(v, vh, vl);
-                                st4h(LTh + j * RT + i0, vh);
-                                st4h(LTl + j * RT + i0, vl);
-                                if (ti == tj && ((i0 >> 4) == (j >> 4))) {
-                                    // L_bb[i][m] with m = j: column j of the diagonal block
-                                    float* ld = Ld + (i0 >> 4) * (16 * 20) + (j & 15);
-#pragma unroll
-                                    for (int u = 0; u < 4; ++u) ld[((i0 + u) & 15) * 20] = v[u];
-                                }
-                            }
-                        }
-                        pbar(ln);
-
-                        // ---- solve, halves q = 0, 1 (one wave each): rows of the 16x16
-                        //      diagonal inverses, then Inv' = D' - D' N D'
-                        if (pw < 2) {
-                            const int q = pw;
-                            {   // lanes 0..31: row cr of the diagonal inverse D_bb, bb = 2q + (ln >> 4)
-                                const int bb = 2 * q + ((ln >> 4) & 1), cr = ln & 15, o = 16 * (bb & 1);
-                                if (ln < 32) {
-                                    float y[16];
-#pragma unroll
-                                    for (int m = 0; m < 16; ++m) y[m] = (m == cr) ? 1.f : 0.f;
-                                    const float* Lb = Ld + bb * (16 * 20);
-                                    // rows of L_bb, loaded three steps ahead of their use
-                                    float4 rw[16][4];
-#pragma unroll
-                                    for (int i = 15; i >= 13; --i)
-#pragma unroll
-                                        for (int q4 = 0; q4 < 4; ++q4)
-                                            if (4 * q4 < i) rw[i][q4] = reinterpret_cast<const float4*>(Lb + i * 20)[q4];
-#pragma unroll
-                                    for (int i = 15; i >= 1; --i) {
-                                        if (i - 3 >= 1) {
-#pragma unroll
-                                            for (int q4 = 0; q4 < 4; ++q4)
-                                                if (4 * q4 < i - 3)
-                                                    rw[i - 3][q4] = reinterpret_cast<const float4*>(Lb + (i - 3) * 20)[q4];
-                                        }
-                                        const float yi = y[i];
-#pragma unroll
-                                        for (int q4 = 0; q4 < 4; ++q4) {
-                                            if (4 * q4 >= i) break;
-                                            const float l4[4] = {rw[i][q4].x, rw[i][q4].y, rw[i][q4].z, rw[i][q4].w};
-#pragma unroll
-                                            for (int u = 0; u < 4; ++u)
-                                                if (4 * q4 + u < i) y[4 * q4 + u] -= yi * l4[u];
-                                        }
-                                    }
-                                    // y = row cr of D_bb: D' and Inv' rows (hi/lo), Tg rows
-                                    const int rloc = o + cr;
-#pragma unroll
-                                    for (int q4 = 0; q4 < 4; ++q4) {
-                                        halfx4 vh, vl;
-                                        split4(y + 4 * q4, vh, vl);
-                                        st4h(DVh + (32 * q + rloc) * RV + o + 4 * q4, vh);
-                                        st4h(DVl + (32 * q + rloc) * RV + o + 4 * q4, vl);
-                                        st4h(IVh + (32 * q + rloc) * RV + o + 4 * q4, vh);
-                                        st4h(IVl + (32 * q + rloc) * RV + o + 4 * q4, vl);
-                                        const int t0 = 16 * bb + 4 * q4;
-                                        const float4 b4 = *reinterpret_cast<const float4*>(sBeta + t0);
-                                        const float4 g4 = *reinterpret_cast<const float4*>(sGam + t0);
-                                        const float bt[4] = {b4.x, b4.y, b4.z, b4.w};
-                                        const float gm[4] = {g4.x, g4.y, g4.z, g4.w};
-                                        halfx4 ta, tg, tl;
-#pragma unroll
-                                        for (int u = 0; u < 4; ++u) {
-                                            ta[u] = (_Float16)(y[4 * q4 + u] * bt[u]);
-                                            const float g = y[4 * q4 + u] * bt[u] * gm[u];
-                                            tg[u] = (_Float16)g;
-                                            tl[u] = (_Float16)(g - (float)tg[u]);
-                                        }
-                                        st4h(TgA + (16 * bb + cr) * RT + t0, ta);
-                                        st4h(TgG + (16 * bb + cr) * RT + t0, tg);
-                                        if (PT) st4h(TgGl + (16 * bb + cr) * RT + t0, tl);
-                                    }
-                                }
-                            }
-                            // Q = N^T D'^T: only contraction k = 16..31 and rows r < 16 of N^T are nonzero
-                            HL fa, fb;
-                            if (lq < 16) {
-                                fa.hi = ld8(LTh + (32 * q + lq) * RT + 32 * q + 16 + 8 * hf);
-                                fa.lo = ld8(LTl + (32 * q + lq) * RT + 32 * q + 16 + 8 * hf);
-                            } else {
-#pragma unroll
-                                for (int u = 0; u < 8; ++u) fa.hi[u] = fa.lo[u] = (_Float16)0.f;
-                            }
-                            fb.hi = ld8(DVh + (32 * q + lq) * RV + 16 + 8 * hf);
-                            fb.lo = ld8(DVl + (32 * q + lq) * RV + 16 + 8 * hf);
-                            const floatx16 Qt = mma3(fa, fb, zero16());
-                            // R^T = D'^T Q: Q has rows k < 16 only, i.e. contraction step 0 in
-                            // accumulator order
-                            HL da;
-                            da.hi = colfrag_acc(DVh + 32 * q * RV, RV, 0, 0, 0, ln);
-                            da.lo = colfrag_acc(DVl + 32 * q * RV, RV, 0, 0, 0, ln);
-                            const floatx16 Rt = mma3(da, split_acc(Qt, 0), zero16());
-                            // lane column m holds R[m][t], t = acc_row(h, j); nonzero for m >= 16, t < 16
-                            if (lq >= 16) {
-                                const int m = 32 * q + lq;
-#pragma unroll
-                                for (int q4 = 0; q4 < 2; ++q4) {
-                                    const int tl = 8 * q4 + 4 * hf;   // rows acc_row(h, 4 q4 + 0..3)
-                                    float v[4] = {-Rt[4 * q4], -Rt[4 * q4 + 1], -Rt[4 * q4 + 2], -Rt[4 * q4 + 3]};
-                                    halfx4 vh, vl;
-                                    split4(v, vh, vl);
-                                    st4h(IVh + m * RV + tl, vh);
-                                    st4h(IVl + m * RV + tl, vl);
-                                    const int t0 = 32 * q + tl;
-                                    const float4 b4 = *reinterpret_cast<const float4*>(sBeta + t0);
-                                    const float4 g4 = *reinterpret_cast<const float4*>(sGam + t0);
-                                    const float bt[4] = {b4.x, b4.y, b4.z, b4.w};
-                                    const float gm[4] = {g4.x, g4.y, g4.z, g4.w};
-                                    halfx4 ta, tg, tgl;
-#pragma unroll
-                                    for (int u = 0; u < 4; ++u) {
-                                        ta[u] = (_Float16)(v[u] * bt[u]);
-                                        const float g = v[u] * bt[u] * gm[u];
-                                        tg[u] = (_Float16)g;
-                                        tgl[u] = (_Float16)(g - (float)tg[u]);
-                                    }
-                                    st4h(TgA + m * RT + t0, ta);
-                                    st4h(TgG + m * RT + t0, tg);
-                                    if (PT) st4h(TgGl + m * RT + t0, tgl);
-                                }
-                            }
-                        }
-                        pbar(ln);
-
-                        // ---- solve, lower-left 32x32 block: -Inv'_1 L'_10 Inv'_0, computed as
-                        //      its transpose Inv'_0^T (L'_10^T Inv'_1^T)
-                        if (pw == 0) {
-                            floatx16 Q2 = zero16();
-#pragma unroll
-                            for (int kk = 0; kk < 2; ++kk) {
-                                HL fa, fb;
-                                fa.hi = ld8(LTh + lq * RT + 32 + 16 * kk + 8 * hf);
-                                fa.lo = ld8(LTl + lq * RT + 32 + 16 * kk + 8 * hf);
-                                fb.hi = ld8(IVh + (32 + lq) * RV + 16 * kk + 8 * hf);
-                                fb.lo = ld8(IVl + (32 + lq) * RV + 16 * kk + 8 * hf);
-                                Q2 = mma3(fa, fb, Q2);
-                            }
-                            floatx16 R2 = zero16();
-#pragma unroll
-                            for (int st = 0; st < 2; ++st) {
-                                HL da;
-                                da.hi = colfrag_acc(IVh, RV, 0, 0, st, ln);
-                                da.lo = colfrag_acc(IVl, RV, 0, 0, st, ln);
-                                R2 = mma3(da, split_acc(Q2, st), R2);
-                            }
-                            const int m = 32 + lq;
-#pragma unroll
-                            for (int q4 = 0; q4 < 4; ++q4) {
-                                const int t0 = 8 * q4 + 4 * hf;
-                                const float4 b4 = *reinterpret_cast<const float4*>(sBeta + t0);
-                                const float4 g4 = *reinterpret_cast<const float4*>(sGam + t0);
-                                const float bt[4] = {b4.x, b4.y, b4.z, b4.w};
-                                const float gm[4] = {g4.x, g4.y, g4.z, g4.w};
-                                halfx4 ta, tg, tl;
-#pragma unroll
-                                for (int u = 0; u < 4; ++u) {
-                                    const float v = -R2[4 * q4 + u];
-                                    ta[u] = (_Float16)(v * bt[u]);
-                                    const float g = v * bt[u] * gm[u];
-                                    tg[u] = (_Float16)g;
-                                    tl[u] = (_Float16)(g - (float)tg[u]);
-                                }
-                                st4h(TgA + m * RT + t0, ta);
-                                st4h(TgG + m * RT + t0, tg);
-                                if (PT) st4h(TgGl + m * RT + t0, tl);
-                            }
-                        }
+                        ut_solve<D, PT>(Kn1, sG, sGam, sBeta, Ld, LTh, LTl, DVh, DVl, IVh, IVl, pw, ln, pbar,
+                                        [&](int row, int t0, halfx4 ta, halfx4 tg, halfx4 tl) {
+                                            st4h(TgA + row * RT + t0, ta);
+                                            st4h(TgG + row * RT + t0, tg);
+                                            if (PT) st4h(TgGl + row * RT + t0, tl);
+                                        });
                     }
                     __syncthreads();  // chunk c+1 prepared
                     __syncthreads();  // W'(c+1) written by the carry waves

@@ -104,7 +104,7 @@ def test_build_offsets_and_workspace(L):
     d, cu = _build_desc()
     need = L.hypic_segment_build_workspace_bytes(C.byref(d))
     assert need > 0 and need % 256 == 0
-    d.workspace_bytes = need - 1
+    d.workspace_bytes = 255          # below the segment table itself
     assert L.hypic_segment_build(C.byref(d), None) == A.ERR_WORKSPACE_TOO_SMALL
     d.workspace = None
     d.workspace_bytes = need
