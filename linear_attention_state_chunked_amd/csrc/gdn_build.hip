@@ -96,26 +96,51 @@ __device__ __forceinline__ floatx16 mma3(const HL& a, const HL& b, floatx16 c) {
     c = __builtin_amdgcn_mfma_f32_32x32x16_f16(a.hi, b.lo, c, 0, 0, 0);
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a.hi, b.hi, c, 0, 0, 0);
 }
-__device__ __forceinline__ HL split_acc(const floatx16& a, int st) {
-    HL r;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float v = a[8 * st + i];
-        const _Float16 h = (_Float16)v;
-        r.hi[i] = h;
-        r.lo[i] = (_Float16)(v - (float)h);
-    }
+// hi/lo split of fp32 values into f16 pairs: hi = f16(v), lo = f16(v - hi).  v - hi is
+// exact in fp32, so lo is one fused v_fma_mix step (-1 * hi + v, rounded once) per value
+// instead of an f16 -> f32 conversion, a subtraction and a second conversion.
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ unsigned int pk_f16(float a, float b) {
+    return __builtin_bit_cast(unsigned int, f16x2{(_Float16)a, (_Float16)b});
+}
+__device__ __forceinline__ unsigned int lo_pair(unsigned int hi, float a, float b) {
+    unsigned int r;
+    asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mixhi_f16 %0, %1, -1.0, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+        : "=&v"(r)
+        : "v"(hi), "v"(a), "v"(b));
     return r;
 }
-__device__ __forceinline__ void split4(const float* v, halfx4& hi, halfx4& lo) {
+__device__ __forceinline__ HL split_acc(const floatx16& a, int st) {
+    u32x4 h, l;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const _Float16 h = (_Float16)v[i];
-        hi[i] = h;
-        lo[i] = (_Float16)(v[i] - (float)h);
+        h[i] = pk_f16(a[8 * st + 2 * i], a[8 * st + 2 * i + 1]);
+        l[i] = lo_pair(h[i], a[8 * st + 2 * i], a[8 * st + 2 * i + 1]);
     }
+    return HL{__builtin_bit_cast(halfx8, h), __builtin_bit_cast(halfx8, l)};
+}
+__device__ __forceinline__ void split4(const float* v, halfx4& hi, halfx4& lo) {
+    const unsigned int h0 = pk_f16(v[0], v[1]), h1 = pk_f16(v[2], v[3]);
+    hi = __builtin_bit_cast(halfx4, u32x2{h0, h1});
+    lo = __builtin_bit_cast(halfx4, u32x2{lo_pair(h0, v[0], v[1]), lo_pair(h1, v[2], v[3])});
 }
 __device__ __forceinline__ void st4h(_Float16* p, halfx4 v) { *reinterpret_cast<halfx4*>(p) = v; }
+
+// Four entries y of a row of (I + L)^-1 at token columns t0..t0+3 -> the f16 entries of
+// Tg = (I + L)^-1 diag(beta) and of Tg diag(gamma) (hi and lo parts)
+__device__ __forceinline__ void tg4(const float* y, const float* sBeta, const float* sBG, int t0, halfx4& ta,
+                                    halfx4& tg, halfx4& tl) {
+    const float4 b4 = *reinterpret_cast<const float4*>(sBeta + t0);
+    const float4 g4 = *reinterpret_cast<const float4*>(sBG + t0);
+    const float g[4] = {y[0] * g4.x, y[1] * g4.y, y[2] * g4.z, y[3] * g4.w};
+    ta = __builtin_bit_cast(halfx4, u32x2{pk_f16(y[0] * b4.x, y[1] * b4.y), pk_f16(y[2] * b4.z, y[3] * b4.w)});
+    const unsigned int h0 = pk_f16(g[0], g[1]), h1 = pk_f16(g[2], g[3]);
+    tg = __builtin_bit_cast(halfx4, u32x2{h0, h1});
+    tl = __builtin_bit_cast(halfx4, u32x2{lo_pair(h0, g[0], g[1]), lo_pair(h1, g[2], g[3])});
+}
 
 template <bool BF16>
 struct Raw8;
@@ -125,6 +150,7 @@ struct Raw8<true> {
     __device__ void load(const void* base, long long idx) {
         w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + idx);
     }
+    __device__ void loadp(const unsigned char* p) { w = *reinterpret_cast<const uint4*>(p); }
     __device__ void zero() { w = make_uint4(0, 0, 0, 0); }
     __device__ void get(float (&x)[8]) const {
         const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
@@ -142,6 +168,10 @@ struct Raw8<false> {
         const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + idx);
         a = p[0];
         b = p[1];
+    }
+    __device__ void loadp(const unsigned char* p) {
+        a = reinterpret_cast<const float4*>(p)[0];
+        b = reinterpret_cast<const float4*>(p)[1];
     }
     __device__ void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
     __device__ void get(float (&x)[8]) const {
@@ -178,7 +208,7 @@ struct GLayout {
     static constexpr int TgA = IVl + sz_V32;           // Tg
     static constexpr int TgG = TgA + sz_T64;           // Tg diag(gamma)
     static constexpr int TgGl = TgG + sz_T64;          // its low part (precise-T plan)
-    static constexpr int Gv = TgGl + sz_T64;           // G, gamma, beta (fp32)
+    static constexpr int Gv = TgGl + sz_T64;           // G log2 e, beta, beta gamma (fp32)
     static constexpr int Misc = Gv + 3 * 64 * 4;       // counter, exponents
     static constexpr int total = Misc + 32 * 4;
     // regions that must start at zero and are only partly written
@@ -203,7 +233,7 @@ __device__ __forceinline__ void prep_barrier(int* cnt, int target, int lane) {
 // out(row, col0, Tg[row][col0..+3], (Tg diag(gamma))[row][col0..+3] hi, lo) as f16; only
 // the lower 16x16 blocks are written.  pbar() orders the four waves between the stages.
 template <int D, bool PT, class Bar, class Out>
-__device__ __forceinline__ void ut_solve(const _Float16* Kn1, const float* sG, const float* sGam, const float* sBeta,
+__device__ __forceinline__ void ut_solve(const _Float16* Kn1, const float* sGl, const float* sBeta, const float* sBG,
                                          float* Ld, _Float16* LTh, _Float16* LTl, _Float16* DVh, _Float16* DVl,
                                          _Float16* IVh, _Float16* IVl, int pw, int ln, Bar&& pbar, Out&& out) {
     constexpr int RK = D + 8, RT = 64 + 8, RV = 32 + 8;
@@ -221,18 +251,19 @@ __device__ __forceinline__ void ut_solve(const _Float16* Kn1, const float* sG, c
         }
         // lane column j; its registers hold rows i = 32 ti + 8 q + 4 h + 0..3
         const int j = 32 * tj + lq;
-        const float Gj = sG[j];
+        // e^{G_i - G_j} = 2^{G_i log2 e - G_j log2 e}
+        const float Gj = sGl[j];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int i0 = 32 * ti + 8 * q + 4 * hf;
-            const float4 g4 = *reinterpret_cast<const float4*>(sG + i0);
+            const float4 g4 = *reinterpret_cast<const float4*>(sGl + i0);
             const float4 b4 = *reinterpret_cast<const float4*>(sBeta + i0);
             const float gi[4] = {g4.x, g4.y, g4.z, g4.w};
             const float bi[4] = {b4.x, b4.y, b4.z, b4.w};
             float v[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u)
-                v[u] = (i0 + u > j) ? bi[u] * fexp(gi[u] - Gj) * acc[4 * q + u] : 0.f;
+                v[u] = (i0 + u > j) ? bi[u] * __builtin_amdgcn_exp2f(gi[u] - Gj) * acc[4 * q + u] : 0.f;
             halfx4 vh, vl;
             split4(v, vh, vl);
             st4h(LTh + j * RT + i0, vh);
@@ -294,18 +325,8 @@ __device__ __forceinline__ void ut_solve(const _Float16* Kn1, const float* sG, c
                     st4h(IVh + (32 * q + rloc) * RV + o + 4 * q4, vh);
                     st4h(IVl + (32 * q + rloc) * RV + o + 4 * q4, vl);
                     const int t0 = 16 * bb + 4 * q4;
-                    const float4 b4 = *reinterpret_cast<const float4*>(sBeta + t0);
-                    const float4 g4 = *reinterpret_cast<const float4*>(sGam + t0);
-                    const float bt[4] = {b4.x, b4.y, b4.z, b4.w};
-                    const float gm[4] = {g4.x, g4.y, g4.z, g4.w};
                     halfx4 ta, tg, tl;
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        ta[u] = (_Float16)(y[4 * q4 + u] * bt[u]);
-                        const float g = y[4 * q4 + u] * bt[u] * gm[u];
-                        tg[u] = (_Float16)g;
-                        tl[u] = (_Float16)(g - (float)tg[u]);
-                    }
+                    tg4(y + 4 * q4, sBeta, sBG, t0, ta, tg, tl);
                     out(16 * bb + cr, t0, ta, tg, tl);
                 }
             }
@@ -340,18 +361,8 @@ __device__ __forceinline__ void ut_solve(const _Float16* Kn1, const float* sG, c
                 st4h(IVh + m * RV + tl, vh);
                 st4h(IVl + m * RV + tl, vl);
                 const int t0 = 32 * q + tl;
-                const float4 b4 = *reinterpret_cast<const float4*>(sBeta + t0);
-                const float4 g4 = *reinterpret_cast<const float4*>(sGam + t0);
-                const float bt[4] = {b4.x, b4.y, b4.z, b4.w};
-                const float gm[4] = {g4.x, g4.y, g4.z, g4.w};
                 halfx4 ta, tg, tgl;
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    ta[u] = (_Float16)(v[u] * bt[u]);
-                    const float g = v[u] * bt[u] * gm[u];
-                    tg[u] = (_Float16)g;
-                    tgl[u] = (_Float16)(g - (float)tg[u]);
-                }
+                tg4(v, sBeta, sBG, t0, ta, tg, tgl);
                 out(m, t0, ta, tg, tgl);
             }
         }
@@ -383,19 +394,9 @@ __device__ __forceinline__ void ut_solve(const _Float16* Kn1, const float* sG, c
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
             const int t0 = 8 * q4 + 4 * hf;
-            const float4 b4 = *reinterpret_cast<const float4*>(sBeta + t0);
-            const float4 g4 = *reinterpret_cast<const float4*>(sGam + t0);
-            const float bt[4] = {b4.x, b4.y, b4.z, b4.w};
-            const float gm[4] = {g4.x, g4.y, g4.z, g4.w};
+            const float v[4] = {-R2[4 * q4], -R2[4 * q4 + 1], -R2[4 * q4 + 2], -R2[4 * q4 + 3]};
             halfx4 ta, tg, tl;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float v = -R2[4 * q4 + u];
-                ta[u] = (_Float16)(v * bt[u]);
-                const float g = v * bt[u] * gm[u];
-                tg[u] = (_Float16)g;
-                tl[u] = (_Float16)(g - (float)tg[u]);
-            }
+            tg4(v, sBeta, sBG, t0, ta, tg, tl);
             out(m, t0, ta, tg, tl);
         }
     }
@@ -505,6 +506,7 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                                 Vn[mt][4 * q + 2] *= sv.z;
                                 Vn[mt][4 * q + 3] *= sv.w;
                             }
+                            __builtin_amdgcn_sched_barrier(0);
                         }
                         const float Gamma = Sc[64];
 #pragma unroll
@@ -530,7 +532,7 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
 #pragma unroll
                             for (int xb = 0; xb < NB; ++xb)
 #pragma unroll
-                                for (int j = 0; j < 16; ++j) m = fmaxf(m, fabsf(X[xb][j]));
+                                for (int j = 0; j < 16; j += 2) m = fmaxf(m, fmaxf(fabsf(X[xb][j]), fabsf(X[xb][j + 1])));
                             const int e = exp2_of(wave_max(m));
                             if (e != 0) {
 #pragma unroll
@@ -576,16 +578,14 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                             }
                         }
                         if (!TR) {
+                            // both token halves per V fragment: one fragment live at a time
+                            Un[0] = Un[1] = zero16();
 #pragma unroll
-                            for (int mt = 0; mt < 2; ++mt) {
-                                floatx16 acc = zero16();
+                            for (int kk = 0; kk < 4; ++kk) {
+                                const halfx8 fb = colfrag_nat(Vn1, RK, 0, col0, kk, ln);
 #pragma unroll
-                                for (int kk = 0; kk < 4; ++kk) {
-                                    const halfx8 fa = ld8(TgA + (32 * mt + lq) * RT + 16 * kk + 8 * hf);
-                                    const halfx8 fb = colfrag_nat(Vn1, RK, 0, col0, kk, ln);
-                                    acc = OpF16::mma(fa, fb, acc);
-                                }
-                                Un[mt] = acc;
+                                for (int mt = 0; mt < 2; ++mt)
+                                    Un[mt] = OpF16::mma(ld8(TgA + (32 * mt + lq) * RT + 16 * kk + 8 * hf), fb, Un[mt]);
                             }
                         }
                     }
@@ -620,16 +620,28 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                 const int ptid = tid - NC * 64;
                 Raw8<IN_BF16> pk[NLD], pv[NLD];
                 float pla = 0.f, pbt = 0.f;
+                // uniform 64-bit bases per task and chunk, 32-bit per-lane byte offsets
+                constexpr int ESZ = IN_BF16 ? 2 : 4;
+                const long long row0 = (long long)b * N + start;
+                const unsigned char* kb0 =
+                    reinterpret_cast<const unsigned char*>(a.k) + (row0 * a.h_k + hk) * (D * ESZ);
+                const unsigned char* vb0 =
+                    reinterpret_cast<const unsigned char*>(a.v) + (row0 * a.h_v + h) * (D * ESZ);
+                const float* la0 = a.log_alpha + row0 * a.h_v + h;
+                const float* bt0 = a.beta + row0 * a.h_v + h;
+                const unsigned kstride = (unsigned)a.h_k * (D * ESZ), vstride = (unsigned)a.h_v * (D * ESZ);
                 auto prefetch = [&](int cc, int ln, int pt) {
-                    const long long tok0 = start + 64LL * cc;
                     const int valid = min(64, len - 64 * cc);
+                    const unsigned char* kc = kb0 + (long long)(64 * cc) * kstride;
+                    const unsigned char* vc = vb0 + (long long)(64 * cc) * vstride;
+                    const int t0 = pt / G8;
+                    const unsigned d0b = 8 * ESZ * (pt % G8);
 #pragma unroll
                     for (int r = 0; r < NLD; ++r) {
-                        const int i = pt + NP * 64 * r;
-                        const int t = i / G8, d0 = 8 * (i % G8);
+                        const int t = t0 + (NP * 64 / G8) * r;
                         if (t < valid) {
-                            pk[r].load(a.k, ((b * N + tok0 + t) * a.h_k + hk) * D + d0);
-                            pv[r].load(a.v, ((b * N + tok0 + t) * a.h_v + h) * D + d0);
+                            pk[r].loadp(kc + (t * kstride + d0b));
+                            pv[r].loadp(vc + (t * vstride + d0b));
                         } else {
                             pk[r].zero();
                             pv[r].zero();
@@ -637,9 +649,9 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                     }
                     if (pw == 0) {
                         const bool ok = ln < valid;
-                        const long long gi = (b * N + tok0 + ln) * a.h_v + h;
-                        pla = ok ? a.log_alpha[gi] : 0.f;
-                        pbt = ok ? a.beta[gi] : 0.f;
+                        const unsigned go = (unsigned)ln * a.h_v;
+                        pla = ok ? (la0 + (long long)(64 * cc) * a.h_v)[go] : 0.f;
+                        pbt = ok ? (bt0 + (long long)(64 * cc) * a.h_v)[go] : 0.f;
                     }
                 };
                 auto pbar = [&](int ln) {
@@ -671,15 +683,15 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                         E* TgA = reinterpret_cast<E*>(sm + LY::TgA);
                         E* TgG = reinterpret_cast<E*>(sm + LY::TgG);
                         E* TgGl = reinterpret_cast<E*>(sm + LY::TgGl);
-                        float* sG = reinterpret_cast<float*>(sm + LY::Gv);
-                        float* sGam = sG + 64;
-                        float* sBeta = sG + 128;
+                        float* sGl = reinterpret_cast<float*>(sm + LY::Gv);
+                        float* sBeta = sGl + 64;
+                        float* sBG = sGl + 128;
 
                         // ---- stage chunk c+1: K and V rows, gate prefix
+                        const int st0 = (unsigned)pt / G8, sd0 = 8 * ((unsigned)pt % G8);
 #pragma unroll
                         for (int r = 0; r < NLD; ++r) {
-                            const int i = pt + NP * 64 * r;
-                            const int t = i / G8, d0 = 8 * (i % G8);
+                            const int t = st0 + (NP * 64 / G8) * r, d0 = sd0;
                             float x[8];
                             pk[r].get(x);
                             if (a.qk_l2norm) {
@@ -692,28 +704,28 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
 #pragma unroll
                                 for (int u = 0; u < 8; ++u) x[u] *= sc;
                             }
-                            halfx8 hk8, hv8;
-#pragma unroll
-                            for (int u = 0; u < 8; ++u) hk8[u] = (_Float16)x[u];
+                            const u32x4 hk8 = {pk_f16(x[0], x[1]), pk_f16(x[2], x[3]), pk_f16(x[4], x[5]),
+                                               pk_f16(x[6], x[7])};
                             pv[r].get(x);
-#pragma unroll
-                            for (int u = 0; u < 8; ++u) hv8[u] = (_Float16)x[u];
-                            *reinterpret_cast<halfx8*>(Kn1 + t * RK + d0) = hk8;
-                            *reinterpret_cast<halfx8*>(Vn + t * RK + d0) = hv8;
+                            const u32x4 hv8 = {pk_f16(x[0], x[1]), pk_f16(x[2], x[3]), pk_f16(x[4], x[5]),
+                                               pk_f16(x[6], x[7])};
+                            *reinterpret_cast<u32x4*>(Kn1 + t * RK + d0) = hk8;
+                            *reinterpret_cast<u32x4*>(Vn + t * RK + d0) = hv8;
                         }
                         if (pw == 0) {
                             const float G = wave_scan_dpp(pla);
                             const float Glast = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(G), 63));
-                            sG[ln] = G;
-                            sGam[ln] = fexp(G);
+                            const float Gl = G * 1.4426950408889634f;
+                            sGl[ln] = Gl;
                             sBeta[ln] = pbt;
+                            sBG[ln] = pbt * __builtin_amdgcn_exp2f(Gl);
                             Scn[ln] = fexp(Glast - G);
                             if (ln == 0) Scn[64] = fexp(Glast);
                         }
                         if (c + 2 < nc) prefetch(c + 2, ln, pt);
                         pbar(ln);
 
-                        ut_solve<D, PT>(Kn1, sG, sGam, sBeta, Ld, LTh, LTl, DVh, DVl, IVh, IVl, pw, ln, pbar,
+                        ut_solve<D, PT>(Kn1, sGl, sBeta, sBG, Ld, LTh, LTl, DVh, DVl, IVh, IVl, pw, ln, pbar,
                                         [&](int row, int t0, halfx4 ta, halfx4 tg, halfx4 tl) {
                                             st4h(TgA + row * RT + t0, ta);
                                             st4h(TgG + row * RT + t0, tg);
