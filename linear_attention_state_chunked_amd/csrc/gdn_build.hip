@@ -12,9 +12,11 @@
 // Warp specialisation.  Carry waves own 32 columns of X each (T columns, then S
 // columns), keep them in matrix-core accumulators for the whole segment and run the
 // carry of chunk c; four preparation waves meanwhile stage chunk c+1, form its gram and
-// solve it.  Carry waves then turn the solve into W' (stored as ready-made operand
-// fragments) and U (kept in registers) for chunk c+1.  Two workgroup barriers per chunk;
-// the preparation waves order their own stages with a bounded LDS-counter barrier.
+// solve it.  After the one workgroup barrier per chunk the carry waves turn the solve
+// into W' (stored as ready-made operand fragments) and U (kept in registers) for chunk
+// c+1 while the preparation waves already stage chunk c+2 (K, V and gate buffers are
+// doubled).  Bounded LDS counters order the rest: the preparation waves' own stages,
+// the carry waves' W' hand-off, and the reuse of the Tg buffer.
 //
 // Layout rules.  Every matrix in LDS is a natural row-major f16 tile written with
 // 8- or 16-byte stores.  Row fragments are plain 16-byte reads; column fragments
@@ -97,8 +99,10 @@ __device__ __forceinline__ floatx16 mma3(const HL& a, const HL& b, floatx16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a.hi, b.hi, c, 0, 0, 0);
 }
 // hi/lo split of fp32 values into f16 pairs: hi = f16(v), lo = f16(v - hi).  v - hi is
-// exact in fp32, so lo is one fused v_fma_mix step (-1 * hi + v, rounded once) per value
-// instead of an f16 -> f32 conversion, a subtraction and a second conversion.
+// exact in fp32, so lo can be a fused f16-source fma (-1 * hi + v, rounded once), which
+// the compiler emits as v_fma_mix instead of a conversion, a subtraction and a second
+// conversion.  (Written in C, not inline assembly: the results feed matrix-core operands,
+// and only compiler-visible instructions get the required VALU -> MFMA wait states.)
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -106,12 +110,12 @@ __device__ __forceinline__ unsigned int pk_f16(float a, float b) {
     return __builtin_bit_cast(unsigned int, f16x2{(_Float16)a, (_Float16)b});
 }
 __device__ __forceinline__ unsigned int lo_pair(unsigned int hi, float a, float b) {
-    unsigned int r;
-    asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]\n\t"
-        "v_fma_mixhi_f16 %0, %1, -1.0, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
-        : "=&v"(r)
-        : "v"(hi), "v"(a), "v"(b));
-    return r;
+    // -1 held in a register, so that the compiler selects its fused f16-source fma
+    float m1 = -1.f;
+    asm("" : "+v"(m1));
+    const f16x2 h = __builtin_bit_cast(f16x2, hi);
+    return __builtin_bit_cast(unsigned int, f16x2{(_Float16)__builtin_fmaf((float)h[0], m1, a),
+                                                  (_Float16)__builtin_fmaf((float)h[1], m1, b)});
 }
 __device__ __forceinline__ HL split_acc(const floatx16& a, int st) {
     u32x4 h, l;
@@ -183,39 +187,34 @@ struct Raw8<false> {
 // ---------------------------------------------------------------------------------------
 // LDS layout (bytes); f16 tiles unless noted
 
+constexpr int kXS = 16 + 4;         // row stride (f16) of a column-major 16x16 exchange tile
+constexpr int kXT = 2 * 16 * kXS;   // one exchange slot (f16 elements): hi tile, then lo tile
+
 template <int D>
 struct GLayout {
     static constexpr int NB = D / 32;
     static constexpr int RK = D + 8;                   // K, V rows
-    static constexpr int RT = 64 + 8;                  // 64-wide rows: L^T, Tg
-    static constexpr int RV = 32 + 8;                  // 32-wide rows: D', Inv'
+    static constexpr int RT = 64 + 8;                  // 64-wide rows of the Tg tiles
     static constexpr int sz_K = 64 * RK * 2;
     static constexpr int sz_Wf = 2 * NB * 2 * 64 * 8 * 2;
     static constexpr int sz_Sc = 80 * 4;
     static constexpr int sz_T64 = 64 * RT * 2;
-    static constexpr int sz_V32 = 64 * RV * 2;
     static constexpr int Kn = 0;                       // K rows (x2)
-    static constexpr int Wf = Kn + 2 * sz_K;           // -W'^T operand fragments (x2)
-    static constexpr int Sc = Wf + 2 * sz_Wf;          // Gamma/gamma_i, Gamma (fp32, x2)
-    static constexpr int Vn = Sc + 2 * sz_Sc;          // V rows
-    static constexpr int Ld = Vn + sz_K;               // fp32 diagonal 16x16 blocks of L, [4][16][20]
-    static constexpr int LTh = Ld + 4 * 16 * 20 * 4;   // L^T hi / lo
-    static constexpr int LTl = LTh + sz_T64;
-    static constexpr int DVh = LTl + sz_T64;           // D' (block-diagonal 16x16 inverses per half) hi / lo
-    static constexpr int DVl = DVh + sz_V32;
-    static constexpr int IVh = DVl + sz_V32;           // Inv' (32x32 inverses of the halves) hi / lo
-    static constexpr int IVl = IVh + sz_V32;
-    static constexpr int TgA = IVl + sz_V32;           // Tg
+    static constexpr int Wf = Kn + 2 * sz_K;           // -W'^T operand fragments
+    static constexpr int Sc = Wf + sz_Wf;              // Gamma/gamma_i, Gamma (fp32, x2)
+    static constexpr int Vn = Sc + 2 * sz_Sc;          // V rows (x2)
+    static constexpr int XB = Vn + 2 * sz_K;           // eight 16x16 exchange slots (hi, lo)
+    static constexpr int TgA = XB + 8 * kXT * 2;       // Tg, token-column-major
     static constexpr int TgG = TgA + sz_T64;           // Tg diag(gamma)
     static constexpr int TgGl = TgG + sz_T64;          // its low part (precise-T plan)
     static constexpr int Gv = TgGl + sz_T64;           // G log2 e, beta, beta gamma (fp32)
     static constexpr int Misc = Gv + 3 * 64 * 4;       // counter, exponents
     static constexpr int total = Misc + 32 * 4;
     // regions that must start at zero and are only partly written
-    static constexpr int zero_begin = LTh, zero_end = Gv;
+    static constexpr int zero_begin = TgA, zero_end = Gv;
 };
 
-// bounded LDS-counter barrier among the preparation waves only
+// bounded LDS-counter barrier among a subset of waves (one arrival per wave)
 __device__ __forceinline__ void prep_barrier(int* cnt, int target, int lane) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     if (lane == 0) __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -227,177 +226,199 @@ __device__ __forceinline__ void prep_barrier(int* cnt, int target, int lane) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
-// Chunk-local UT transform on four cooperating waves (pw = 0..3): from the staged K rows
-// (f16, row stride D + 8) and the gate prefix, the gram K K^T, L = strictly-lower(
-// beta_i e^{G_i - G_j} K K^T) and Tg = (I + L)^-1 diag(beta).  Tg leaves through
-// out(row, col0, Tg[row][col0..+3], (Tg diag(gamma))[row][col0..+3] hi, lo) as f16; only
-// the lower 16x16 blocks are written.  pbar() orders the four waves between the stages.
-template <int D, bool PT, class Bar, class Out>
-__device__ __forceinline__ void ut_solve(const _Float16* Kn1, const float* sGl, const float* sBeta, const float* sBG,
-                                         float* Ld, _Float16* LTh, _Float16* LTl, _Float16* DVh, _Float16* DVl,
-                                         _Float16* IVh, _Float16* IVl, int pw, int ln, Bar&& pbar, Out&& out) {
-    constexpr int RK = D + 8, RT = 64 + 8, RV = 32 + 8;
-    const int hf = ln >> 5, lq = ln & 31;
-    // ---- gram K K^T (three lower 32x32 tiles) -> L^T rows (hi/lo) and
-    //      the fp32 diagonal 16x16 blocks of L
-    if (pw < 3) {
-        const int ti = pw == 0 ? 0 : 1, tj = pw == 2 ? 1 : 0;
-        floatx16 acc = zero16();
+// one arrival per wave on an LDS counter, after the wave's earlier LDS accesses
+__device__ __forceinline__ void count_arrival(int* cnt, int lane) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    if (lane == 0) __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// bounded wait until an LDS counter reaches target (the counting side releases)
+__device__ __forceinline__ void wait_count(int* cnt, int target) {
+    int spins = 0;
+    while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins > (1 << 22)) break;  // never hang: a broken invariant gives wrong data, not a hang
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// ---------------------------------------------------------------------------------------
+// 16x16 matrix-core tiles (v_mfma_f32_16x16x16f16, v_mfma_f32_16x16x32_f16).  Accumulator
+// layout: lane l holds column l & 15 and, in register i, row 4 (l >> 4) + i.  That is also
+// the B-operand layout of the 16x16x16 product (contraction index in place of the row), so a
+// result feeds the next product's B operand as it is; as an A operand a matrix X is supplied
+// by the accumulator-layout registers of its transpose.  Tiles exchanged through LDS are
+// stored column-major (each lane writes its four rows as one 8-byte run): a plain 8-byte read
+// returns the B operand, a transposing read the A operand.
+
+struct HL4 {
+    halfx4 hi, lo;
+};
+__device__ __forceinline__ HL4 split4v(floatx4 v) {
+    const unsigned int h0 = pk_f16(v[0], v[1]), h1 = pk_f16(v[2], v[3]);
+    return HL4{__builtin_bit_cast(halfx4, u32x2{h0, h1}),
+               __builtin_bit_cast(halfx4, u32x2{lo_pair(h0, v[0], v[1]), lo_pair(h1, v[2], v[3])})};
+}
+__device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
+// c + a b with hi/lo-split operands (about 22-bit operands; the lo * lo term is dropped)
+__device__ __forceinline__ floatx4 mm16(const HL4& a, const HL4& b, floatx4 c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x16f16(a.lo, b.hi, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x16f16(a.hi, b.lo, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a.hi, b.hi, c, 0, 0, 0);
+}
+__device__ __forceinline__ void st_cm(_Float16* t, floatx4 v, int lane) {
+    const HL4 x = split4v(v);
+    const int o = (lane & 15) * kXS + 4 * (lane >> 4);
+    st4h(t + o, x.hi);
+    st4h(t + 16 * kXS + o, x.lo);
+}
+__device__ __forceinline__ HL4 ld_b(const _Float16* t, int lane) {
+    const int o = (lane & 15) * kXS + 4 * (lane >> 4);
+    return HL4{*reinterpret_cast<const halfx4*>(t + o), *reinterpret_cast<const halfx4*>(t + 16 * kXS + o)};
+}
+__device__ __forceinline__ HL4 ld_a(const _Float16* t, int lane) {
+    const int r0 = 4 * (lane >> 4);
+    return HL4{tr4(t, kXS, r0, 0, lane), tr4(t + 16 * kXS, kXS, r0, 0, lane)};
+}
+
+// Block (b, a) of Tg = (I + L)^-1 diag(beta) and of Tg diag(gamma) (hi, lo) from block (b, a)
+// of (I + L)^-1 in accumulator layout, into the token-column-major Tg tiles (row stride 72).
+__device__ __forceinline__ void st_tg(_Float16* TgAT, _Float16* TgGT, _Float16* TgGlT, bool pt, floatx4 v, int b,
+                                      int a, int lane, const float* sBeta, const float* sBG) {
+    const int tc = 16 * a + (lane & 15);
+    const float bc = sBeta[tc], bgc = sBG[tc];
+    const int o = tc * (64 + 8) + 16 * b + 4 * (lane >> 4);
+    st4h(TgAT + o, __builtin_bit_cast(halfx4, u32x2{pk_f16(v[0] * bc, v[1] * bc), pk_f16(v[2] * bc, v[3] * bc)}));
+    const floatx4 gv = v * bgc;
+    const HL4 x = split4v(gv);
+    st4h(TgGT + o, x.hi);
+    if (pt) st4h(TgGlT + o, x.lo);
+}
+
+// (I - N)^-1 = (I + N)(I + N^2)(I + N^4)(I + N^8) for a strictly lower 16x16 N (N^16 = 0).
+// The factors are polynomials in N and commute.  In: N and N^T; out: the inverse and its
+// transpose, both in accumulator layout.
+__device__ __forceinline__ void inv16(floatx4 n, floatx4 nt, int lane, floatx4& r, floatx4& rt) {
+    floatx4 id;
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-            const halfx8 fa = ld8(Kn1 + (32 * ti + lq) * RK + 16 * kk + 8 * hf);
-            const halfx8 fb = ld8(Kn1 + (32 * tj + lq) * RK + 16 * kk + 8 * hf);
-            acc = OpF16::mma(fa, fb, acc);
-        }
-        // lane column j; its registers hold rows i = 32 ti + 8 q + 4 h + 0..3
-        const int j = 32 * tj + lq;
-        // e^{G_i - G_j} = 2^{G_i log2 e - G_j log2 e}
-        const float Gj = sGl[j];
+    for (int i = 0; i < 4; ++i) id[i] = (4 * (lane >> 4) + i == (lane & 15)) ? 1.f : 0.f;
+    const HL4 N = split4v(n), NT = split4v(nt);
+    const floatx4 p = mm16(NT, N, zero4()), pt = mm16(N, NT, zero4());        // N^2, (N^T)^2
+    const HL4 P = split4v(p), PT = split4v(pt);
+    r = mm16(NT, P, id + n + p);                                              // (I + N)(I + N^2)
+    rt = mm16(P, NT, id + nt + pt);
+    const floatx4 p4 = mm16(PT, P, zero4()), p4t = mm16(P, PT, zero4());      // N^4, (N^T)^4
+    const HL4 P4 = split4v(p4), P4T = split4v(p4t);
+    HL4 R = split4v(r), RT = split4v(rt);
+    r = mm16(RT, P4, r);                                                      // ... (I + N^4)
+    rt = mm16(P4, RT, rt);
+    const HL4 P8 = split4v(mm16(P4T, P4, zero4()));                           // N^8
+    R = split4v(r);
+    RT = split4v(rt);
+    r = mm16(RT, P8, r);                                                      // ... (I + N^8)
+    rt = mm16(P8, RT, rt);
+}
+
+// Chunk-local UT transform, wave pw of four owning token block pw: from the staged K rows
+// (f16, row stride D + 8; the wave's own block also in registers as the gram operand) and
+// the gate vectors (G log2 e, beta, beta gamma), L = strictly-lower(beta_i e^{G_i - G_j}
+// K K^T) and Tg = (I + L)^-1 diag(beta), written as its ten lower 16x16 blocks.
+//   D_b = (I + L_bb)^-1 (each wave its own), then the halves Inv_10 = -D_1 L_10 D_0 and
+//   Inv_32 = -D_3 L_32 D_2, then the lower-left quarter -Inv1 (L'_10 Inv0) with
+//   Q_b0 = L_b0 D_0 + L_b1 Inv_10, Q_b1 = L_b1 D_1 (b = 2, 3), block row 2 = -D_2 Q_2.,
+//   block row 3 = -(Inv_32 Q_2. + D_3 Q_3.).
+// pbar() orders the four waves, tg_wait() holds the first Tg write until the previous Tg has
+// been consumed; qcnt hands Q_2. from wave 2 to wave 3 (qtarget: arrivals so far).
+template <int D, class Bar, class Wait>
+__device__ __forceinline__ void ut_blocks(const _Float16* Kn1, const halfx8* ka, const float* sGl, const float* sBeta,
+                                          const float* sBG, _Float16* XB, _Float16* TgAT, _Float16* TgGT,
+                                          _Float16* TgGlT, bool pt, int pw, int ln, Bar&& pbar, Wait&& tg_wait,
+                                          int* qcnt, int qtarget) {
+    constexpr int KS = D / 32, RK = D + 8;
+    const int g = ln >> 4, cl = ln & 15;
+    auto slot = [&](int i) { return XB + i * kXT; };
+    // ---- gram: diagonal block (pw, pw) and the transposed blocks (a, pw), a < pw
+    // (each 32-wide step as two 16x16x16 products over its two 4-element halves per lane)
+    auto mma32 = [](halfx8 x, halfx8 y, floatx4 c) {
+        c = __builtin_amdgcn_mfma_f32_16x16x16f16(halfx4{x[0], x[1], x[2], x[3]}, halfx4{y[0], y[1], y[2], y[3]}, c, 0,
+                                                 0, 0);
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(halfx4{x[4], x[5], x[6], x[7]}, halfx4{y[4], y[5], y[6], y[7]}, c,
+                                                    0, 0, 0);
+    };
+    floatx4 gd = zero4();
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int i0 = 32 * ti + 8 * q + 4 * hf;
-            const float4 g4 = *reinterpret_cast<const float4*>(sGl + i0);
-            const float4 b4 = *reinterpret_cast<const float4*>(sBeta + i0);
-            const float gi[4] = {g4.x, g4.y, g4.z, g4.w};
-            const float bi[4] = {b4.x, b4.y, b4.z, b4.w};
-            float v[4];
+    for (int ks = 0; ks < KS; ++ks) gd = mma32(ka[ks], ka[ks], gd);
+    floatx4 gt[3];
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
-                v[u] = (i0 + u > j) ? bi[u] * __builtin_amdgcn_exp2f(gi[u] - Gj) * acc[4 * q + u] : 0.f;
-            halfx4 vh, vl;
-            split4(v, vh, vl);
-            st4h(LTh + j * RT + i0, vh);
-            st4h(LTl + j * RT + i0, vl);
-            if (ti == tj && ((i0 >> 4) == (j >> 4))) {
-                // L_bb[i][m] with m = j: column j of the diagonal block
-                float* ld = Ld + (i0 >> 4) * (16 * 20) + (j & 15);
+    for (int a = 0; a < 3; ++a) {
+        gt[a] = zero4();
+        if (a < pw) {
 #pragma unroll
-                for (int u = 0; u < 4; ++u) ld[((i0 + u) & 15) * 20] = v[u];
-            }
+            for (int ks = 0; ks < KS; ++ks) gt[a] = mma32(ld8(Kn1 + (16 * a + cl) * RK + 32 * ks + 8 * g), ka[ks], gt[a]);
         }
     }
-    pbar(ln);
-
-    // ---- solve, halves q = 0, 1 (one wave each): rows of the 16x16
-    //      diagonal inverses, then Inv' = D' - D' N D'
-    if (pw < 2) {
-        const int q = pw;
-        {   // lanes 0..31: row cr of the diagonal inverse D_bb, bb = 2q + (ln >> 4)
-            const int bb = 2 * q + ((ln >> 4) & 1), cr = ln & 15, o = 16 * (bb & 1);
-            if (ln < 32) {
-                float y[16];
+    // ---- gate factors: L_{pw,a}^T (rows of block a, columns of block pw), N = -L_{pw,pw}, N^T
+    const int tc = 16 * pw + cl;
+    const float Gc = sGl[tc], Bc = sBeta[tc];
+    floatx4 LT[3];
 #pragma unroll
-                for (int m = 0; m < 16; ++m) y[m] = (m == cr) ? 1.f : 0.f;
-                const float* Lb = Ld + bb * (16 * 20);
-                // rows of L_bb, loaded three steps ahead of their use
-                float4 rw[16][4];
+    for (int a = 0; a < 3; ++a) {
+        const float4 gr = *reinterpret_cast<const float4*>(sGl + 16 * a + 4 * g);
+        const float grs[4] = {gr.x, gr.y, gr.z, gr.w};
 #pragma unroll
-                for (int i = 15; i >= 13; --i)
+        for (int u = 0; u < 4; ++u) LT[a][u] = Bc * __builtin_amdgcn_exp2f(Gc - grs[u]) * gt[a][u];
+    }
+    floatx4 n, nt;
+    {
+        const float4 gw = *reinterpret_cast<const float4*>(sGl + 16 * pw + 4 * g);
+        const float4 bw = *reinterpret_cast<const float4*>(sBeta + 16 * pw + 4 * g);
+        const float gws[4] = {gw.x, gw.y, gw.z, gw.w}, bws[4] = {bw.x, bw.y, bw.z, bw.w};
 #pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4)
-                        if (4 * q4 < i) rw[i][q4] = reinterpret_cast<const float4*>(Lb + i * 20)[q4];
-#pragma unroll
-                for (int i = 15; i >= 1; --i) {
-                    if (i - 3 >= 1) {
-#pragma unroll
-                        for (int q4 = 0; q4 < 4; ++q4)
-                            if (4 * q4 < i - 3)
-                                rw[i - 3][q4] = reinterpret_cast<const float4*>(Lb + (i - 3) * 20)[q4];
-                    }
-                    const float yi = y[i];
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        if (4 * q4 >= i) break;
-                        const float l4[4] = {rw[i][q4].x, rw[i][q4].y, rw[i][q4].z, rw[i][q4].w};
-#pragma unroll
-                        for (int u = 0; u < 4; ++u)
-                            if (4 * q4 + u < i) y[4 * q4 + u] -= yi * l4[u];
-                    }
-                }
-                // y = row cr of D_bb: D' and Inv' rows (hi/lo), Tg rows
-                const int rloc = o + cr;
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    halfx4 vh, vl;
-                    split4(y + 4 * q4, vh, vl);
-                    st4h(DVh + (32 * q + rloc) * RV + o + 4 * q4, vh);
-                    st4h(DVl + (32 * q + rloc) * RV + o + 4 * q4, vl);
-                    st4h(IVh + (32 * q + rloc) * RV + o + 4 * q4, vh);
-                    st4h(IVl + (32 * q + rloc) * RV + o + 4 * q4, vl);
-                    const int t0 = 16 * bb + 4 * q4;
-                    halfx4 ta, tg, tl;
-                    tg4(y + 4 * q4, sBeta, sBG, t0, ta, tg, tl);
-                    out(16 * bb + cr, t0, ta, tg, tl);
-                }
-            }
+        for (int u = 0; u < 4; ++u) {
+            const int r = 4 * g + u;
+            n[u] = r > cl ? -bws[u] * __builtin_amdgcn_exp2f(gws[u] - Gc) * gd[u] : 0.f;
+            nt[u] = cl > r ? -Bc * __builtin_amdgcn_exp2f(Gc - gws[u]) * gd[u] : 0.f;
         }
-        // Q = N^T D'^T: only contraction k = 16..31 and rows r < 16 of N^T are nonzero
-        HL fa, fb;
-        if (lq < 16) {
-            fa.hi = ld8(LTh + (32 * q + lq) * RT + 32 * q + 16 + 8 * hf);
-            fa.lo = ld8(LTl + (32 * q + lq) * RT + 32 * q + 16 + 8 * hf);
+    }
+    // ---- diagonal block inverse D_pw (and its transpose)
+    floatx4 Dm, Dt;
+    inv16(n, nt, ln, Dm, Dt);
+    st_cm(slot(pw), Dm, ln);
+    tg_wait();
+    st_tg(TgAT, TgGT, TgGlT, pt, Dm, pw, pw, ln, sBeta, sBG);
+    pbar(ln);
+    // ---- the halves' off-diagonal blocks, and the D-terms of Q
+    const HL4 DT = split4v(Dt);
+    floatx4 q0 = zero4(), q1 = zero4();
+    if (pw == 1 || pw == 3) {
+        const int a = pw - 1;
+        const floatx4 pr = mm16(split4v(LT[a]), ld_b(slot(a), ln), zero4());   // L_{pw,a} D_a
+        const floatx4 iv = -mm16(DT, split4v(pr), zero4());                    // -D_pw L_{pw,a} D_a
+        st_cm(slot(pw == 1 ? 4 : 5), iv, ln);
+        st_tg(TgAT, TgGT, TgGlT, pt, iv, pw, a, ln, sBeta, sBG);
+    }
+    if (pw >= 2) {
+        q1 = mm16(split4v(LT[1]), ld_b(slot(1), ln), zero4());   // L_{pw,1} D_1
+        q0 = mm16(split4v(LT[0]), ld_b(slot(0), ln), zero4());   // L_{pw,0} D_0
+    }
+    pbar(ln);
+    // ---- lower-left quarter
+    if (pw >= 2) {
+        q0 = mm16(split4v(LT[1]), ld_b(slot(4), ln), q0);        // + L_{pw,1} Inv_10
+        if (pw == 2) {
+            st_cm(slot(6), q0, ln);
+            st_cm(slot(7), q1, ln);
+            count_arrival(qcnt, ln);
+            st_tg(TgAT, TgGT, TgGlT, pt, -mm16(DT, split4v(q0), zero4()), 2, 0, ln, sBeta, sBG);
+            st_tg(TgAT, TgGT, TgGlT, pt, -mm16(DT, split4v(q1), zero4()), 2, 1, ln, sBeta, sBG);
         } else {
-#pragma unroll
-            for (int u = 0; u < 8; ++u) fa.hi[u] = fa.lo[u] = (_Float16)0.f;
-        }
-        fb.hi = ld8(DVh + (32 * q + lq) * RV + 16 + 8 * hf);
-        fb.lo = ld8(DVl + (32 * q + lq) * RV + 16 + 8 * hf);
-        const floatx16 Qt = mma3(fa, fb, zero16());
-        // R^T = D'^T Q: Q has rows k < 16 only, i.e. contraction step 0 in
-        // accumulator order
-        HL da;
-        da.hi = colfrag_acc(DVh + 32 * q * RV, RV, 0, 0, 0, ln);
-        da.lo = colfrag_acc(DVl + 32 * q * RV, RV, 0, 0, 0, ln);
-        const floatx16 Rt = mma3(da, split_acc(Qt, 0), zero16());
-        // lane column m holds R[m][t], t = acc_row(h, j); nonzero for m >= 16, t < 16
-        if (lq >= 16) {
-            const int m = 32 * q + lq;
-#pragma unroll
-            for (int q4 = 0; q4 < 2; ++q4) {
-                const int tl = 8 * q4 + 4 * hf;   // rows acc_row(h, 4 q4 + 0..3)
-                float v[4] = {-Rt[4 * q4], -Rt[4 * q4 + 1], -Rt[4 * q4 + 2], -Rt[4 * q4 + 3]};
-                halfx4 vh, vl;
-                split4(v, vh, vl);
-                st4h(IVh + m * RV + tl, vh);
-                st4h(IVl + m * RV + tl, vl);
-                const int t0 = 32 * q + tl;
-                halfx4 ta, tg, tgl;
-                tg4(v, sBeta, sBG, t0, ta, tg, tgl);
-                out(m, t0, ta, tg, tgl);
-            }
-        }
-    }
-    pbar(ln);
-
-    // ---- solve, lower-left 32x32 block: -Inv'_1 L'_10 Inv'_0, computed as
-    //      its transpose Inv'_0^T (L'_10^T Inv'_1^T)
-    if (pw == 0) {
-        floatx16 Q2 = zero16();
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            HL fa, fb;
-            fa.hi = ld8(LTh + lq * RT + 32 + 16 * kk + 8 * hf);
-            fa.lo = ld8(LTl + lq * RT + 32 + 16 * kk + 8 * hf);
-            fb.hi = ld8(IVh + (32 + lq) * RV + 16 * kk + 8 * hf);
-            fb.lo = ld8(IVl + (32 + lq) * RV + 16 * kk + 8 * hf);
-            Q2 = mma3(fa, fb, Q2);
-        }
-        floatx16 R2 = zero16();
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-            HL da;
-            da.hi = colfrag_acc(IVh, RV, 0, 0, st, ln);
-            da.lo = colfrag_acc(IVl, RV, 0, 0, st, ln);
-            R2 = mma3(da, split_acc(Q2, st), R2);
-        }
-        const int m = 32 + lq;
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            const int t0 = 8 * q4 + 4 * hf;
-            const float v[4] = {-R2[4 * q4], -R2[4 * q4 + 1], -R2[4 * q4 + 2], -R2[4 * q4 + 3]};
-            halfx4 ta, tg, tl;
-            tg4(v, sBeta, sBG, t0, ta, tg, tl);
-            out(m, t0, ta, tg, tl);
+            floatx4 r0 = mm16(DT, split4v(q0), zero4()), r1 = mm16(DT, split4v(q1), zero4());
+            wait_count(qcnt, qtarget);
+            const HL4 A32 = ld_a(slot(5), ln);
+            r0 = mm16(A32, ld_b(slot(6), ln), r0);
+            r1 = mm16(A32, ld_b(slot(7), ln), r1);
+            st_tg(TgAT, TgGT, TgGlT, pt, -r0, 3, 0, ln, sBeta, sBG);
+            st_tg(TgAT, TgGT, TgGlT, pt, -r1, 3, 1, ln, sBeta, sBG);
         }
     }
 }
@@ -410,9 +431,7 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
     constexpr int NC = (WITH_T ? 2 : 1) * NB;   // carry waves
     constexpr int NP = 4;                       // preparation waves
     constexpr int NT = (NC + NP) * 64;
-    constexpr int RK = LY::RK, RT = LY::RT, RV = LY::RV;
-    constexpr int G8 = D / 8;
-    constexpr int NLD = 64 * G8 / (NP * 64);    // 8-element groups per prep thread per tensor
+    constexpr int RK = LY::RK, RT = LY::RT;
 
     __shared__ __align__(16) unsigned char smem[LY::total];
     int* sCnt = reinterpret_cast<int*>(smem + LY::Misc);
@@ -447,6 +466,7 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
             const int len = a.seg_len[seg];
             const int nc = (len + 63) / 64;
             const long long chain_off = (long long)b * a.h_v + h;
+            if (tid == 0) sCnt[1] = sCnt[2] = sCnt[3] = 0;
             __syncthreads();
 
             if constexpr (R != 2) {
@@ -464,8 +484,6 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
 #pragma unroll
                     for (int j = 0; j < 16; ++j)
                         X[xb][j] = (TR && 32 * xb + 8 * (j >> 2) + (j & 3) == diag) ? 1.f : 0.f;
-                floatx16 Un[2];
-                Un[0] = Un[1] = zero16();
                 int ew = 0;
                 for (int c = -1; c < nc; ++c) {
                     // opaque zeros: per-lane LDS offsets are recomputed every chunk instead of
@@ -477,13 +495,27 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                     const int ln = lane + lzv, hf = ln >> 5, lq = ln & 31;
                     const int p = c & 1, pn = (c + 1) & 1;
                     if (c >= 0) {
-                        const E* Wf = reinterpret_cast<const E*>(sm + LY::Wf + p * LY::sz_Wf);
+                        const E* Wf = reinterpret_cast<const E*>(sm + LY::Wf);
                         const E* Kn = reinterpret_cast<const E*>(sm + LY::Kn + p * LY::sz_K);
                         const float* Sc = reinterpret_cast<const float*>(sm + LY::Sc + p * LY::sz_Sc);
                         floatx16 Vn[2];
+                        Vn[0] = Vn[1] = zero16();
+                        if (!TR) {
+                            // U = Tg V for this wave's columns, both token halves per V fragment
+                            const E* TgA = reinterpret_cast<const E*>(sm + LY::TgA);
+                            const E* Vc = reinterpret_cast<const E*>(sm + LY::Vn + p * LY::sz_K);
+#pragma unroll
+                            for (int kk = 0; kk < 4; ++kk) {
+                                const halfx8 fb = colfrag_nat(Vc, RK, 0, col0, kk, ln);
+#pragma unroll
+                                for (int mt = 0; mt < 2; ++mt)
+                                    Vn[mt] = OpF16::mma(colfrag_nat(TgA, RT, 0, 32 * mt, kk, ln), fb, Vn[mt]);
+                            }
+                            // Tg(c) consumed: the preparation of chunk c+1 may overwrite it
+                            count_arrival(sCnt + 2, ln);
+                        }
 #pragma unroll
                         for (int mt = 0; mt < 2; ++mt) {
-                            Vn[mt] = TR ? zero16() : Un[mt];
 #pragma unroll
                             for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
@@ -544,13 +576,15 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                         }
                     }
                     __syncthreads();  // preparation of chunk c+1 is complete
+                    // From here the preparation waves go on to chunk c+2.  Its staging
+                    // buffers are the other halves of the double buffers; its Tg waits for
+                    // the formation counter below.  W' has one buffer: every read of W'(c)
+                    // happened before the barrier above.
                     if (c + 1 < nc) {
                         const E* Kn1 = reinterpret_cast<const E*>(sm + LY::Kn + pn * LY::sz_K);
-                        const E* TgA = reinterpret_cast<const E*>(sm + LY::TgA);
                         const E* TgG = reinterpret_cast<const E*>(sm + LY::TgG);
                         const E* TgGl = reinterpret_cast<const E*>(sm + LY::TgGl);
-                        const E* Vn1 = reinterpret_cast<const E*>(sm + LY::Vn);
-                        E* Wf1 = reinterpret_cast<E*>(sm + LY::Wf + pn * LY::sz_Wf);
+                        E* Wf1 = reinterpret_cast<E*>(sm + LY::Wf);
                         // -W'^T tiles (d rows, token columns): their accumulators are the operand
                         // fragments of W' X in the carry, stored in that order
                         if (TR || !WITH_T) {
@@ -561,9 +595,9 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
 #pragma unroll
                                 for (int kk = 0; kk < 4; ++kk) {
                                     const halfx8 fa = colfrag_nat(Kn1, RK, 0, 32 * dt, kk, ln);
-                                    const halfx8 fb = ld8(TgG + (32 * mt + lq) * RT + 16 * kk + 8 * hf);
+                                    const halfx8 fb = colfrag_nat(TgG, RT, 0, 32 * mt, kk, ln);
                                     if (PT) {
-                                        const halfx8 fl = ld8(TgGl + (32 * mt + lq) * RT + 16 * kk + 8 * hf);
+                                        const halfx8 fl = colfrag_nat(TgGl, RT, 0, 32 * mt, kk, ln);
                                         acc = OpF16::mma(fa, fl, acc);
                                     }
                                     acc = OpF16::mma(fa, fb, acc);
@@ -577,19 +611,11 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                                 }
                             }
                         }
-                        if (!TR) {
-                            // both token halves per V fragment: one fragment live at a time
-                            Un[0] = Un[1] = zero16();
-#pragma unroll
-                            for (int kk = 0; kk < 4; ++kk) {
-                                const halfx8 fb = colfrag_nat(Vn1, RK, 0, col0, kk, ln);
-#pragma unroll
-                                for (int mt = 0; mt < 2; ++mt)
-                                    Un[mt] = OpF16::mma(ld8(TgA + (32 * mt + lq) * RT + 16 * kk + 8 * hf), fb, Un[mt]);
-                            }
-                        }
+                        // W'(c+1) formed (its Tg reads done): the forming waves count it, all
+                        // carry waves wait for the whole of W'(c+1)
+                        if (TR || !WITH_T) count_arrival(sCnt + 1, ln);
+                        wait_count(sCnt + 1, NB * (c + 2));
                     }
-                    __syncthreads();  // W'(c+1) written; staging buffers free
                 }
                 // epilogue: align the T waves' exponents, write T_hat / T_exp / S
                 if (TR && lane == 0) sEw[wave] = ew;
@@ -616,9 +642,10 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                 }
             } else {
                 // ======================== preparation waves ========================
+                // Wave pw owns token block pw (rows 16 pw .. 16 pw + 15) of every chunk.
                 const int pw = wave - NC;
-                const int ptid = tid - NC * 64;
-                Raw8<IN_BF16> pk[NLD], pv[NLD];
+                constexpr int KS = D / 32;  // 32-wide contraction steps over d
+                Raw8<IN_BF16> pk[KS], pv[KS];
                 float pla = 0.f, pbt = 0.f;
                 // uniform 64-bit bases per task and chunk, 32-bit per-lane byte offsets
                 constexpr int ESZ = IN_BF16 ? 2 : 4;
@@ -630,21 +657,22 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                 const float* la0 = a.log_alpha + row0 * a.h_v + h;
                 const float* bt0 = a.beta + row0 * a.h_v + h;
                 const unsigned kstride = (unsigned)a.h_k * (D * ESZ), vstride = (unsigned)a.h_v * (D * ESZ);
-                auto prefetch = [&](int cc, int ln, int pt) {
+                // lane (row 16 pw + (ln & 15), d = 32 ks + 8 (ln >> 4) .. + 7): the A / B operand
+                // layout of the 16x16x32 gram products
+                auto prefetch = [&](int cc, int ln) {
                     const int valid = min(64, len - 64 * cc);
                     const unsigned char* kc = kb0 + (long long)(64 * cc) * kstride;
                     const unsigned char* vc = vb0 + (long long)(64 * cc) * vstride;
-                    const int t0 = pt / G8;
-                    const unsigned d0b = 8 * ESZ * (pt % G8);
+                    const int t = 16 * pw + (ln & 15);
+                    const unsigned d0b = 8 * ESZ * (ln >> 4);
 #pragma unroll
-                    for (int r = 0; r < NLD; ++r) {
-                        const int t = t0 + (NP * 64 / G8) * r;
+                    for (int ks = 0; ks < KS; ++ks) {
                         if (t < valid) {
-                            pk[r].loadp(kc + (t * kstride + d0b));
-                            pv[r].loadp(vc + (t * vstride + d0b));
+                            pk[ks].loadp(kc + (t * kstride + d0b + 32 * ESZ * ks));
+                            pv[ks].loadp(vc + (t * vstride + d0b + 32 * ESZ * ks));
                         } else {
-                            pk[r].zero();
-                            pv[r].zero();
+                            pk[ks].zero();
+                            pv[ks].zero();
                         }
                     }
                     if (pw == 0) {
@@ -661,56 +689,55 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                 // the preparation waves are the critical path of every chunk: let their few
                 // instructions issue ahead of the carry waves' (matrix-core bound) stream
                 __builtin_amdgcn_s_setprio(2);
-                if (nc > 0) prefetch(0, lane, ptid);
+                if (nc > 0) prefetch(0, lane);
                 for (int c = -1; c < nc; ++c) {
                     int lz = 0, lzv = 0;
                     asm volatile("" : "+s"(lz));
                     asm volatile("" : "+v"(lzv));
                     unsigned char* sm = smem + lz;
-                    const int ln = lane + lzv, hf = ln >> 5, lq = ln & 31, pt = ptid + lzv;
+                    const int ln = lane + lzv, g = ln >> 4, cl = ln & 15;
                     const int pn = (c + 1) & 1;
                     if (c + 1 < nc) {
                         E* Kn1 = reinterpret_cast<E*>(sm + LY::Kn + pn * LY::sz_K);
-                        E* Vn = reinterpret_cast<E*>(sm + LY::Vn);
+                        E* Vn = reinterpret_cast<E*>(sm + LY::Vn + pn * LY::sz_K);
                         float* Scn = reinterpret_cast<float*>(sm + LY::Sc + pn * LY::sz_Sc);
-                        float* Ld = reinterpret_cast<float*>(sm + LY::Ld);
-                        E* LTh = reinterpret_cast<E*>(sm + LY::LTh);
-                        E* LTl = reinterpret_cast<E*>(sm + LY::LTl);
-                        E* DVh = reinterpret_cast<E*>(sm + LY::DVh);
-                        E* DVl = reinterpret_cast<E*>(sm + LY::DVl);
-                        E* IVh = reinterpret_cast<E*>(sm + LY::IVh);
-                        E* IVl = reinterpret_cast<E*>(sm + LY::IVl);
-                        E* TgA = reinterpret_cast<E*>(sm + LY::TgA);
-                        E* TgG = reinterpret_cast<E*>(sm + LY::TgG);
-                        E* TgGl = reinterpret_cast<E*>(sm + LY::TgGl);
+                        E* XB = reinterpret_cast<E*>(sm + LY::XB);
+                        E* TgAT = reinterpret_cast<E*>(sm + LY::TgA);
+                        E* TgGT = reinterpret_cast<E*>(sm + LY::TgG);
+                        E* TgGlT = reinterpret_cast<E*>(sm + LY::TgGl);
                         float* sGl = reinterpret_cast<float*>(sm + LY::Gv);
                         float* sBeta = sGl + 64;
                         float* sBG = sGl + 128;
 
-                        // ---- stage chunk c+1: K and V rows, gate prefix
-                        const int st0 = (unsigned)pt / G8, sd0 = 8 * ((unsigned)pt % G8);
+                        // ---- stage block pw of chunk c+1 (K, V as f16); K stays as the gram operand
+                        const int trow = 16 * pw + cl;
+                        float ksc = 1.f;
+                        if (a.qk_l2norm) {
+                            float ss = 0.f;
 #pragma unroll
-                        for (int r = 0; r < NLD; ++r) {
-                            const int t = st0 + (NP * 64 / G8) * r, d0 = sd0;
-                            float x[8];
-                            pk[r].get(x);
-                            if (a.qk_l2norm) {
-                                float ss = 0.f;
+                            for (int ks = 0; ks < KS; ++ks) {
+                                float x[8];
+                                pk[ks].get(x);
 #pragma unroll
                                 for (int u = 0; u < 8; ++u) ss += x[u] * x[u];
-#pragma unroll
-                                for (int o = 1; o < G8; o <<= 1) ss += __shfl_xor(ss, o, 64);
-                                const float sc = ss > 0.f ? 1.f / sqrtf(ss) : 0.f;
-#pragma unroll
-                                for (int u = 0; u < 8; ++u) x[u] *= sc;
                             }
-                            const u32x4 hk8 = {pk_f16(x[0], x[1]), pk_f16(x[2], x[3]), pk_f16(x[4], x[5]),
-                                               pk_f16(x[6], x[7])};
-                            pv[r].get(x);
+                            ss += __shfl_xor(ss, 16, 64);
+                            ss += __shfl_xor(ss, 32, 64);
+                            ksc = ss > 0.f ? 1.f / sqrtf(ss) : 0.f;
+                        }
+                        halfx8 ka[KS];
+#pragma unroll
+                        for (int ks = 0; ks < KS; ++ks) {
+                            float x[8];
+                            pk[ks].get(x);
+                            const u32x4 hk8 = {pk_f16(x[0] * ksc, x[1] * ksc), pk_f16(x[2] * ksc, x[3] * ksc),
+                                               pk_f16(x[4] * ksc, x[5] * ksc), pk_f16(x[6] * ksc, x[7] * ksc)};
+                            ka[ks] = __builtin_bit_cast(halfx8, hk8);
+                            pv[ks].get(x);
                             const u32x4 hv8 = {pk_f16(x[0], x[1]), pk_f16(x[2], x[3]), pk_f16(x[4], x[5]),
                                                pk_f16(x[6], x[7])};
-                            *reinterpret_cast<u32x4*>(Kn1 + t * RK + d0) = hk8;
-                            *reinterpret_cast<u32x4*>(Vn + t * RK + d0) = hv8;
+                            *reinterpret_cast<u32x4*>(Kn1 + trow * RK + 32 * ks + 8 * g) = hk8;
+                            *reinterpret_cast<u32x4*>(Vn + trow * RK + 32 * ks + 8 * g) = hv8;
                         }
                         if (pw == 0) {
                             const float G = wave_scan_dpp(pla);
@@ -722,18 +749,20 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                             Scn[ln] = fexp(Glast - G);
                             if (ln == 0) Scn[64] = fexp(Glast);
                         }
-                        if (c + 2 < nc) prefetch(c + 2, ln, pt);
+                        if (c + 2 < nc) prefetch(c + 2, ln);
                         pbar(ln);
 
-                        ut_solve<D, PT>(Kn1, sGl, sBeta, sBG, Ld, LTh, LTl, DVh, DVl, IVh, IVl, pw, ln, pbar,
-                                        [&](int row, int t0, halfx4 ta, halfx4 tg, halfx4 tl) {
-                                            st4h(TgA + row * RT + t0, ta);
-                                            st4h(TgG + row * RT + t0, tg);
-                                            if (PT) st4h(TgGl + row * RT + t0, tl);
-                                        });
+                        ut_blocks<D>(Kn1, ka, sGl, sBeta, sBG, XB, TgAT, TgGT, TgGlT, PT, pw, ln,
+                                     pbar,
+                                     [&] {
+                                         // Tg(c+1) overwrites Tg(c): wait until the carry waves
+                                         // formed W'(c) and U(c)
+                                         wait_count(sCnt + 1, NB * (c + 1));
+                                         wait_count(sCnt + 2, NB * (c + 1));
+                                     },
+                                     sCnt + 3, c + 2);
                     }
                     __syncthreads();  // chunk c+1 prepared
-                    __syncthreads();  // W'(c+1) written by the carry waves
                 }
                 __syncthreads();  // epilogue exponent exchange
             }
