@@ -296,27 +296,22 @@ __device__ __forceinline__ void st_tg(_Float16* TgAT, _Float16* TgGT, _Float16* 
 }
 
 // (I - N)^-1 = (I + N)(I + N^2)(I + N^4)(I + N^8) for a strictly lower 16x16 N (N^16 = 0).
-// The factors are polynomials in N and commute.  In: N and N^T; out: the inverse and its
-// transpose, both in accumulator layout.
-__device__ __forceinline__ void inv16(floatx4 n, floatx4 nt, int lane, floatx4& r, floatx4& rt) {
+// The factors are polynomials in N and commute, so each step multiplies by a power of N
+// from the left, with that power's transpose as the A operand.  In: N and N^T in
+// accumulator layout; returns the inverse in accumulator layout.
+__device__ __forceinline__ floatx4 inv16(floatx4 n, floatx4 nt, int lane) {
     floatx4 id;
 #pragma unroll
     for (int i = 0; i < 4; ++i) id[i] = (4 * (lane >> 4) + i == (lane & 15)) ? 1.f : 0.f;
     const HL4 N = split4v(n), NT = split4v(nt);
-    const floatx4 p = mm16(NT, N, zero4()), pt = mm16(N, NT, zero4());        // N^2, (N^T)^2
-    const HL4 P = split4v(p), PT = split4v(pt);
-    r = mm16(NT, P, id + n + p);                                              // (I + N)(I + N^2)
-    rt = mm16(P, NT, id + nt + pt);
-    const floatx4 p4 = mm16(PT, P, zero4()), p4t = mm16(P, PT, zero4());      // N^4, (N^T)^4
+    const floatx4 p2 = mm16(NT, N, zero4()), p2t = mm16(N, NT, zero4());      // N^2, (N^T)^2
+    const HL4 P2 = split4v(p2), P2T = split4v(p2t);
+    floatx4 r = mm16(NT, P2, id + n + p2);                                    // (I + N)(I + N^2)
+    const floatx4 p4 = mm16(P2T, P2, zero4()), p4t = mm16(P2, P2T, zero4());  // N^4, (N^T)^4
     const HL4 P4 = split4v(p4), P4T = split4v(p4t);
-    HL4 R = split4v(r), RT = split4v(rt);
-    r = mm16(RT, P4, r);                                                      // ... (I + N^4)
-    rt = mm16(P4, RT, rt);
-    const HL4 P8 = split4v(mm16(P4T, P4, zero4()));                           // N^8
-    R = split4v(r);
-    RT = split4v(rt);
-    r = mm16(RT, P8, r);                                                      // ... (I + N^8)
-    rt = mm16(P8, RT, rt);
+    r = mm16(P4T, split4v(r), r);                                             // (I + N^4) ...
+    const HL4 P8T = split4v(mm16(P4, P4T, zero4()));                          // (N^T)^8
+    return mm16(P8T, split4v(r), r);                                          // (I + N^8) ...
 }
 
 // Chunk-local UT transform, wave pw of four owning token block pw: from the staged K rows
@@ -338,13 +333,7 @@ __device__ __forceinline__ void ut_blocks(const _Float16* Kn1, const halfx8* ka,
     const int g = ln >> 4, cl = ln & 15;
     auto slot = [&](int i) { return XB + i * kXT; };
     // ---- gram: diagonal block (pw, pw) and the transposed blocks (a, pw), a < pw
-    // (each 32-wide step as two 16x16x16 products over its two 4-element halves per lane)
-    auto mma32 = [](halfx8 x, halfx8 y, floatx4 c) {
-        c = __builtin_amdgcn_mfma_f32_16x16x16f16(halfx4{x[0], x[1], x[2], x[3]}, halfx4{y[0], y[1], y[2], y[3]}, c, 0,
-                                                 0, 0);
-        return __builtin_amdgcn_mfma_f32_16x16x16f16(halfx4{x[4], x[5], x[6], x[7]}, halfx4{y[4], y[5], y[6], y[7]}, c,
-                                                    0, 0, 0);
-    };
+    auto mma32 = [](halfx8 x, halfx8 y, floatx4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(x, y, c, 0, 0, 0); };
     floatx4 gd = zero4();
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) gd = mma32(ka[ks], ka[ks], gd);
@@ -380,15 +369,15 @@ __device__ __forceinline__ void ut_blocks(const _Float16* Kn1, const halfx8* ka,
             nt[u] = cl > r ? -Bc * __builtin_amdgcn_exp2f(Gc - gws[u]) * gd[u] : 0.f;
         }
     }
-    // ---- diagonal block inverse D_pw (and its transpose)
-    floatx4 Dm, Dt;
-    inv16(n, nt, ln, Dm, Dt);
+    // ---- diagonal block inverse D_pw
+    const floatx4 Dm = inv16(n, nt, ln);
     st_cm(slot(pw), Dm, ln);
     tg_wait();
     st_tg(TgAT, TgGT, TgGlT, pt, Dm, pw, pw, ln, sBeta, sBG);
     pbar(ln);
-    // ---- the halves' off-diagonal blocks, and the D-terms of Q
-    const HL4 DT = split4v(Dt);
+    // ---- the halves' off-diagonal blocks, and the D-terms of Q (D_pw as an A operand
+    //      comes back through the transposing read of its exchange tile)
+    const HL4 DT = ld_a(slot(pw), ln);
     floatx4 q0 = zero4(), q1 = zero4();
     if (pw == 1 || pw == 3) {
         const int a = pw - 1;
@@ -642,10 +631,14 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                 }
             } else {
                 // ======================== preparation waves ========================
-                // Wave pw owns token block pw (rows 16 pw .. 16 pw + 15) of every chunk.
+                // Wave pw owns token block pw (rows 16 pw .. 16 pw + 15) of every chunk and stages
+                // its K rows.  With 16-bit inputs waves 0 and 1, which carry the least of the
+                // solve, stage V (blocks pw and pw + 2) once the gram is under way; with fp32
+                // inputs (twice the registers in flight) every wave stages its own V block first.
                 const int pw = wave - NC;
                 constexpr int KS = D / 32;  // 32-wide contraction steps over d
-                Raw8<IN_BF16> pk[KS], pv[KS];
+                constexpr bool VSPLIT = IN_BF16;
+                Raw8<IN_BF16> pk[KS], pv[(VSPLIT ? 2 : 1) * KS];
                 float pla = 0.f, pbt = 0.f;
                 // uniform 64-bit bases per task and chunk, 32-bit per-lane byte offsets
                 constexpr int ESZ = IN_BF16 ? 2 : 4;
@@ -667,12 +660,22 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                     const unsigned d0b = 8 * ESZ * (ln >> 4);
 #pragma unroll
                     for (int ks = 0; ks < KS; ++ks) {
-                        if (t < valid) {
+                        if (t < valid)
                             pk[ks].loadp(kc + (t * kstride + d0b + 32 * ESZ * ks));
-                            pv[ks].loadp(vc + (t * vstride + d0b + 32 * ESZ * ks));
-                        } else {
+                        else
                             pk[ks].zero();
-                            pv[ks].zero();
+                    }
+                    if (!VSPLIT || pw < 2) {
+#pragma unroll
+                        for (int hb = 0; hb < (VSPLIT ? 2 : 1); ++hb) {
+                            const int tv = t + 32 * hb;
+#pragma unroll
+                            for (int ks = 0; ks < KS; ++ks) {
+                                if (tv < valid)
+                                    pv[hb * KS + ks].loadp(vc + (tv * vstride + d0b + 32 * ESZ * ks));
+                                else
+                                    pv[hb * KS + ks].zero();
+                            }
                         }
                     }
                     if (pw == 0) {
@@ -733,11 +736,12 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                             const u32x4 hk8 = {pk_f16(x[0] * ksc, x[1] * ksc), pk_f16(x[2] * ksc, x[3] * ksc),
                                                pk_f16(x[4] * ksc, x[5] * ksc), pk_f16(x[6] * ksc, x[7] * ksc)};
                             ka[ks] = __builtin_bit_cast(halfx8, hk8);
-                            pv[ks].get(x);
-                            const u32x4 hv8 = {pk_f16(x[0], x[1]), pk_f16(x[2], x[3]), pk_f16(x[4], x[5]),
-                                               pk_f16(x[6], x[7])};
                             *reinterpret_cast<u32x4*>(Kn1 + trow * RK + 32 * ks + 8 * g) = hk8;
-                            *reinterpret_cast<u32x4*>(Vn + trow * RK + 32 * ks + 8 * g) = hv8;
+                            if (!VSPLIT) {
+                                pv[ks].get(x);
+                                *reinterpret_cast<u32x4*>(Vn + trow * RK + 32 * ks + 8 * g) =
+                                    u32x4{pk_f16(x[0], x[1]), pk_f16(x[2], x[3]), pk_f16(x[4], x[5]), pk_f16(x[6], x[7])};
+                            }
                         }
                         if (pw == 0) {
                             const float G = wave_scan_dpp(pla);
@@ -748,6 +752,19 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                             sBG[ln] = pbt * __builtin_amdgcn_exp2f(Gl);
                             Scn[ln] = fexp(Glast - G);
                             if (ln == 0) Scn[64] = fexp(Glast);
+                        }
+                        // V rows of blocks pw and pw + 2, held until the K stage and the gram
+                        // have gone ahead; the next prefetch waits for them to be consumed
+                        halfx8 vh[2 * KS];
+                        if (VSPLIT && pw < 2) {
+#pragma unroll
+                            for (int i = 0; i < 2 * KS; ++i) {
+                                float x[8];
+                                pv[i].get(x);
+                                vh[i] = __builtin_bit_cast(
+                                    halfx8, u32x4{pk_f16(x[0], x[1]), pk_f16(x[2], x[3]), pk_f16(x[4], x[5]),
+                                                  pk_f16(x[6], x[7])});
+                            }
                         }
                         if (c + 2 < nc) prefetch(c + 2, ln);
                         pbar(ln);
@@ -761,6 +778,14 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                                          wait_count(sCnt + 2, NB * (c + 1));
                                      },
                                      sCnt + 3, c + 2);
+                        if (VSPLIT && pw < 2) {
+#pragma unroll
+                            for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+                                for (int ks = 0; ks < KS; ++ks)
+                                    *reinterpret_cast<halfx8*>(Vn + (trow + 32 * hb) * RK + 32 * ks + 8 * g) =
+                                        vh[hb * KS + ks];
+                        }
                     }
                     __syncthreads();  // chunk c+1 prepared
                 }
