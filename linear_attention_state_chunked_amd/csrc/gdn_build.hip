@@ -203,8 +203,8 @@ struct GLayout {
     static constexpr int Wf = Kn + 2 * sz_K;           // -W'^T operand fragments
     static constexpr int Sc = Wf + sz_Wf;              // Gamma/gamma_i, Gamma (fp32, x2)
     static constexpr int Vn = Sc + 2 * sz_Sc;          // V rows (x2)
-    static constexpr int XB = Vn + 2 * sz_K;           // eight 16x16 exchange slots (hi, lo)
-    static constexpr int TgA = XB + 8 * kXT * 2;       // Tg, token-column-major
+    static constexpr int XB = Vn + 2 * sz_K;           // ten 16x16 exchange slots (hi, lo)
+    static constexpr int TgA = XB + 10 * kXT * 2;      // Tg, token-column-major
     static constexpr int TgG = TgA + sz_T64;           // Tg diag(gamma)
     static constexpr int TgGl = TgG + sz_T64;          // its low part (precise-T plan)
     static constexpr int Gv = TgGl + sz_T64;           // G log2 e, beta, beta gamma (fp32)
@@ -282,11 +282,11 @@ __device__ __forceinline__ HL4 ld_a(const _Float16* t, int lane) {
 }
 
 // Block (b, a) of Tg = (I + L)^-1 diag(beta) and of Tg diag(gamma) (hi, lo) from block (b, a)
-// of (I + L)^-1 in accumulator layout, into the token-column-major Tg tiles (row stride 72).
+// of (I + L)^-1 in accumulator layout, into the token-column-major Tg tiles (row stride 72);
+// bc, bgc: beta and beta gamma of this lane's column token 16 a + (lane & 15).
 __device__ __forceinline__ void st_tg(_Float16* TgAT, _Float16* TgGT, _Float16* TgGlT, bool pt, floatx4 v, int b,
-                                      int a, int lane, const float* sBeta, const float* sBG) {
+                                      int a, int lane, float bc, float bgc) {
     const int tc = 16 * a + (lane & 15);
-    const float bc = sBeta[tc], bgc = sBG[tc];
     const int o = tc * (64 + 8) + 16 * b + 4 * (lane >> 4);
     st4h(TgAT + o, __builtin_bit_cast(halfx4, u32x2{pk_f16(v[0] * bc, v[1] * bc), pk_f16(v[2] * bc, v[3] * bc)}));
     const floatx4 gv = v * bgc;
@@ -315,50 +315,77 @@ __device__ __forceinline__ floatx4 inv16(floatx4 n, floatx4 nt, int lane) {
 }
 
 // Chunk-local UT transform, wave pw of four owning token block pw: from the staged K rows
-// (f16, row stride D + 8; the wave's own block also in registers as the gram operand) and
-// the gate vectors (G log2 e, beta, beta gamma), L = strictly-lower(beta_i e^{G_i - G_j}
-// K K^T) and Tg = (I + L)^-1 diag(beta), written as its ten lower 16x16 blocks.
-//   D_b = (I + L_bb)^-1 (each wave its own), then the halves Inv_10 = -D_1 L_10 D_0 and
-//   Inv_32 = -D_3 L_32 D_2, then the lower-left quarter -Inv1 (L'_10 Inv0) with
-//   Q_b0 = L_b0 D_0 + L_b1 Inv_10, Q_b1 = L_b1 D_1 (b = 2, 3), block row 2 = -D_2 Q_2.,
-//   block row 3 = -(Inv_32 Q_2. + D_3 Q_3.).
-// pbar() orders the four waves, tg_wait() holds the first Tg write until the previous Tg has
-// been consumed; qcnt hands Q_2. from wave 2 to wave 3 (qtarget: arrivals so far).
+// (f16, row stride D + 8; the wave's own block also in registers) and the gate vectors
+// (G log2 e, beta, beta gamma), L = strictly-lower(beta_i e^{G_i - G_j} K K^T) and
+// Tg = (I + L)^-1 diag(beta), written as its ten lower 16x16 blocks.  With D_b = (I + L_bb)^-1
+// and Inv the blocks of (I + L)^-1:
+//   Inv_10 = -D_1 L_10 D_0,  Inv_32 = -D_3 L_32 D_2                     (the two halves)
+//   Q_b0 = L_b0 D_0 + L_b1 Inv_10,  Q_b1 = L_b1 D_1                     (b = 2, 3)
+//   Inv_2a = -D_2 Q_2a,  Inv_3a = -(Inv_32 Q_2a + D_3 Q_3a)             (lower-left quarter)
+// Work per wave: 0: D_0, Q_3. (gram blocks of row 3 against blocks 0, 1); 1: D_1, Inv_10;
+// 2: D_2, Q_2., Inv_2.; 3: D_3, Inv_32, Inv_3. .  pbar() orders the four waves, tg_wait() holds
+// the first Tg write until the previous Tg has been consumed; q2cnt / q3cnt hand Q_2. (wave 2)
+// and Q_3. (wave 0) to wave 3 (qtarget: arrivals so far in the task).
 template <int D, class Bar, class Wait>
 __device__ __forceinline__ void ut_blocks(const _Float16* Kn1, const halfx8* ka, const float* sGl, const float* sBeta,
                                           const float* sBG, _Float16* XB, _Float16* TgAT, _Float16* TgGT,
                                           _Float16* TgGlT, bool pt, int pw, int ln, Bar&& pbar, Wait&& tg_wait,
-                                          int* qcnt, int qtarget) {
+                                          int* q2cnt, int* q3cnt, int qtarget) {
     constexpr int KS = D / 32, RK = D + 8;
     const int g = ln >> 4, cl = ln & 15;
     auto slot = [&](int i) { return XB + i * kXT; };
-    // ---- gram: diagonal block (pw, pw) and the transposed blocks (a, pw), a < pw
+    auto krow = [&](int blk, int ks) { return ld8(Kn1 + (16 * blk + cl) * RK + 32 * ks + 8 * g); };
     auto mma32 = [](halfx8 x, halfx8 y, floatx4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(x, y, c, 0, 0, 0); };
+    // beta and beta gamma of this lane's column token in each block
+    float bcol[4], bgcol[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        bcol[a] = sBeta[16 * a + cl];
+        bgcol[a] = sBG[16 * a + cl];
+    }
+    // ---- gram: diagonal block (pw, pw); transposed blocks (a, c) = K_a K_c^T, c the column block:
+    //      (a, pw) for a < pw on waves 1..3 except (0, 3), (1, 3), which wave 0 forms
     floatx4 gd = zero4();
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) gd = mma32(ka[ks], ka[ks], gd);
-    floatx4 gt[3];
+    floatx4 gt[2];
+    int ga[2] = {0, 0}, gc = pw;   // row blocks of gt[0..1] and their common column block
+    if (pw == 0) {
+        ga[0] = 0; ga[1] = 1; gc = 3;
+        gt[0] = gt[1] = zero4();
 #pragma unroll
-    for (int a = 0; a < 3; ++a) {
-        gt[a] = zero4();
-        if (a < pw) {
+        for (int ks = 0; ks < KS; ++ks) {
+            const halfx8 k3 = krow(3, ks);
+            gt[0] = mma32(ka[ks], k3, gt[0]);
+            gt[1] = mma32(krow(1, ks), k3, gt[1]);
+        }
+    } else {
+        ga[0] = pw == 3 ? 2 : 0; ga[1] = 1;
+        gt[0] = gt[1] = zero4();
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) gt[a] = mma32(ld8(Kn1 + (16 * a + cl) * RK + 32 * ks + 8 * g), ka[ks], gt[a]);
+        for (int ks = 0; ks < KS; ++ks) {
+            gt[0] = mma32(krow(ga[0], ks), ka[ks], gt[0]);
+            if (pw == 2) gt[1] = mma32(krow(1, ks), ka[ks], gt[1]);
         }
     }
-    // ---- gate factors: L_{pw,a}^T (rows of block a, columns of block pw), N = -L_{pw,pw}, N^T
-    const int tc = 16 * pw + cl;
-    const float Gc = sGl[tc], Bc = sBeta[tc];
-    floatx4 LT[3];
+    // ---- gate factors: LT[i] = L_{gc, ga[i]}^T (rows of block ga[i], columns of block gc);
+    //      N = -L_{pw,pw} and N^T
+    floatx4 LT[2];
+    {
+        const int tc = 16 * gc + cl;
+        const float Gc = sGl[tc], Bc = sBeta[tc];
 #pragma unroll
-    for (int a = 0; a < 3; ++a) {
-        const float4 gr = *reinterpret_cast<const float4*>(sGl + 16 * a + 4 * g);
-        const float grs[4] = {gr.x, gr.y, gr.z, gr.w};
+        for (int i = 0; i < 2; ++i) {
+            const float4 gr = *reinterpret_cast<const float4*>(sGl + 16 * ga[i] + 4 * g);
+            const float grs[4] = {gr.x, gr.y, gr.z, gr.w};
 #pragma unroll
-        for (int u = 0; u < 4; ++u) LT[a][u] = Bc * __builtin_amdgcn_exp2f(Gc - grs[u]) * gt[a][u];
+            for (int u = 0; u < 4; ++u) LT[i][u] = Bc * __builtin_amdgcn_exp2f(Gc - grs[u]) * gt[i][u];
+        }
     }
     floatx4 n, nt;
     {
+        const int tc = 16 * pw + cl;
+        const float Gc = sGl[tc], Bc = sBeta[tc];
         const float4 gw = *reinterpret_cast<const float4*>(sGl + 16 * pw + 4 * g);
         const float4 bw = *reinterpret_cast<const float4*>(sBeta + 16 * pw + 4 * g);
         const float gws[4] = {gw.x, gw.y, gw.z, gw.w}, bws[4] = {bw.x, bw.y, bw.z, bw.w};
@@ -372,43 +399,43 @@ __device__ __forceinline__ void ut_blocks(const _Float16* Kn1, const halfx8* ka,
     // ---- diagonal block inverse D_pw
     const floatx4 Dm = inv16(n, nt, ln);
     st_cm(slot(pw), Dm, ln);
+    floatx4 q0 = zero4(), q1 = zero4();
     tg_wait();
-    st_tg(TgAT, TgGT, TgGlT, pt, Dm, pw, pw, ln, sBeta, sBG);
+    st_tg(TgAT, TgGT, TgGlT, pt, Dm, pw, pw, ln, bcol[pw], bgcol[pw]);
     pbar(ln);
-    // ---- the halves' off-diagonal blocks, and the D-terms of Q (D_pw as an A operand
+    // ---- the halves' off-diagonal blocks and the D_1 / D_0 terms of Q (D_pw as an A operand
     //      comes back through the transposing read of its exchange tile)
     const HL4 DT = ld_a(slot(pw), ln);
-    floatx4 q0 = zero4(), q1 = zero4();
     if (pw == 1 || pw == 3) {
         const int a = pw - 1;
-        const floatx4 pr = mm16(split4v(LT[a]), ld_b(slot(a), ln), zero4());   // L_{pw,a} D_a
-        const floatx4 iv = -mm16(DT, split4v(pr), zero4());                    // -D_pw L_{pw,a} D_a
+        const floatx4 pr = mm16(split4v(LT[0]), ld_b(slot(a), ln), zero4());  // L_{pw,a} D_a
+        const floatx4 iv = -mm16(DT, split4v(pr), zero4());                   // -D_pw L_{pw,a} D_a
         st_cm(slot(pw == 1 ? 4 : 5), iv, ln);
-        st_tg(TgAT, TgGT, TgGlT, pt, iv, pw, a, ln, sBeta, sBG);
-    }
-    if (pw >= 2) {
-        q1 = mm16(split4v(LT[1]), ld_b(slot(1), ln), zero4());   // L_{pw,1} D_1
-        q0 = mm16(split4v(LT[0]), ld_b(slot(0), ln), zero4());   // L_{pw,0} D_0
+        st_tg(TgAT, TgGT, TgGlT, pt, iv, pw, a, ln, bcol[a], bgcol[a]);
+    } else {
+        q1 = mm16(split4v(LT[1]), ld_b(slot(1), ln), zero4());   // L_{b,1} D_1
+        q0 = mm16(split4v(LT[0]), ld_b(slot(0), ln), zero4());   // L_{b,0} D_0
     }
     pbar(ln);
     // ---- lower-left quarter
-    if (pw >= 2) {
-        q0 = mm16(split4v(LT[1]), ld_b(slot(4), ln), q0);        // + L_{pw,1} Inv_10
+    if (pw == 0 || pw == 2) {
+        q0 = mm16(split4v(LT[1]), ld_b(slot(4), ln), q0);                   // + L_{b,1} Inv_10
+        st_cm(slot(pw == 2 ? 6 : 8), q0, ln);
+        st_cm(slot(pw == 2 ? 7 : 9), q1, ln);
+        count_arrival(pw == 2 ? q2cnt : q3cnt, ln);
         if (pw == 2) {
-            st_cm(slot(6), q0, ln);
-            st_cm(slot(7), q1, ln);
-            count_arrival(qcnt, ln);
-            st_tg(TgAT, TgGT, TgGlT, pt, -mm16(DT, split4v(q0), zero4()), 2, 0, ln, sBeta, sBG);
-            st_tg(TgAT, TgGT, TgGlT, pt, -mm16(DT, split4v(q1), zero4()), 2, 1, ln, sBeta, sBG);
-        } else {
-            floatx4 r0 = mm16(DT, split4v(q0), zero4()), r1 = mm16(DT, split4v(q1), zero4());
-            wait_count(qcnt, qtarget);
-            const HL4 A32 = ld_a(slot(5), ln);
-            r0 = mm16(A32, ld_b(slot(6), ln), r0);
-            r1 = mm16(A32, ld_b(slot(7), ln), r1);
-            st_tg(TgAT, TgGT, TgGlT, pt, -r0, 3, 0, ln, sBeta, sBG);
-            st_tg(TgAT, TgGT, TgGlT, pt, -r1, 3, 1, ln, sBeta, sBG);
+            st_tg(TgAT, TgGT, TgGlT, pt, -mm16(DT, split4v(q0), zero4()), 2, 0, ln, bcol[0], bgcol[0]);
+            st_tg(TgAT, TgGT, TgGlT, pt, -mm16(DT, split4v(q1), zero4()), 2, 1, ln, bcol[1], bgcol[1]);
         }
+    } else if (pw == 3) {
+        const HL4 A32 = ld_a(slot(5), ln);
+        wait_count(q2cnt, qtarget);
+        floatx4 r0 = mm16(A32, ld_b(slot(6), ln), zero4()), r1 = mm16(A32, ld_b(slot(7), ln), zero4());
+        wait_count(q3cnt, qtarget);
+        r0 = mm16(DT, ld_b(slot(8), ln), r0);
+        r1 = mm16(DT, ld_b(slot(9), ln), r1);
+        st_tg(TgAT, TgGT, TgGlT, pt, -r0, 3, 0, ln, bcol[0], bgcol[0]);
+        st_tg(TgAT, TgGT, TgGlT, pt, -r1, 3, 1, ln, bcol[1], bgcol[1]);
     }
 }
 
@@ -424,7 +451,7 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
 
     __shared__ __align__(16) unsigned char smem[LY::total];
     int* sCnt = reinterpret_cast<int*>(smem + LY::Misc);
-    int* sEw = sCnt + 4;
+    int* sEw = sCnt + 8;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -455,7 +482,7 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
             const int len = a.seg_len[seg];
             const int nc = (len + 63) / 64;
             const long long chain_off = (long long)b * a.h_v + h;
-            if (tid == 0) sCnt[1] = sCnt[2] = sCnt[3] = 0;
+            if (tid == 0) sCnt[1] = sCnt[2] = sCnt[3] = sCnt[4] = 0;
             __syncthreads();
 
             if constexpr (R != 2) {
@@ -632,9 +659,9 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
             } else {
                 // ======================== preparation waves ========================
                 // Wave pw owns token block pw (rows 16 pw .. 16 pw + 15) of every chunk and stages
-                // its K rows.  With 16-bit inputs waves 0 and 1, which carry the least of the
-                // solve, stage V (blocks pw and pw + 2) once the gram is under way; with fp32
-                // inputs (twice the registers in flight) every wave stages its own V block first.
+                // its K rows.  With 16-bit inputs waves 0 and 1, which finish the solve first,
+                // stage V (blocks pw and pw + 2) after it; with fp32 inputs (twice the registers
+                // in flight) every wave stages its own V block with its K rows.
                 const int pw = wave - NC;
                 constexpr int KS = D / 32;  // 32-wide contraction steps over d
                 constexpr bool VSPLIT = IN_BF16;
@@ -652,10 +679,9 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                 const unsigned kstride = (unsigned)a.h_k * (D * ESZ), vstride = (unsigned)a.h_v * (D * ESZ);
                 // lane (row 16 pw + (ln & 15), d = 32 ks + 8 (ln >> 4) .. + 7): the A / B operand
                 // layout of the 16x16x32 gram products
-                auto prefetch = [&](int cc, int ln) {
+                auto prefetch_k = [&](int cc, int ln) {
                     const int valid = min(64, len - 64 * cc);
                     const unsigned char* kc = kb0 + (long long)(64 * cc) * kstride;
-                    const unsigned char* vc = vb0 + (long long)(64 * cc) * vstride;
                     const int t = 16 * pw + (ln & 15);
                     const unsigned d0b = 8 * ESZ * (ln >> 4);
 #pragma unroll
@@ -665,6 +691,19 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                         else
                             pk[ks].zero();
                     }
+                };
+                auto prefetch_g = [&](int cc, int ln) {
+                    const int valid = min(64, len - 64 * cc);
+                    const bool ok = ln < valid;
+                    const unsigned go = (unsigned)ln * a.h_v;
+                    pla = ok ? (la0 + (long long)(64 * cc) * a.h_v)[go] : 0.f;
+                    pbt = ok ? (bt0 + (long long)(64 * cc) * a.h_v)[go] : 0.f;
+                };
+                auto prefetch_v = [&](int cc, int ln) {
+                    const int valid = min(64, len - 64 * cc);
+                    const unsigned char* vc = vb0 + (long long)(64 * cc) * vstride;
+                    const int t = 16 * pw + (ln & 15);
+                    const unsigned d0b = 8 * ESZ * (ln >> 4);
                     if (!VSPLIT || pw < 2) {
 #pragma unroll
                         for (int hb = 0; hb < (VSPLIT ? 2 : 1); ++hb) {
@@ -678,12 +717,6 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                             }
                         }
                     }
-                    if (pw == 0) {
-                        const bool ok = ln < valid;
-                        const unsigned go = (unsigned)ln * a.h_v;
-                        pla = ok ? (la0 + (long long)(64 * cc) * a.h_v)[go] : 0.f;
-                        pbt = ok ? (bt0 + (long long)(64 * cc) * a.h_v)[go] : 0.f;
-                    }
                 };
                 auto pbar = [&](int ln) {
                     pb_target += NP;
@@ -692,7 +725,11 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                 // the preparation waves are the critical path of every chunk: let their few
                 // instructions issue ahead of the carry waves' (matrix-core bound) stream
                 __builtin_amdgcn_s_setprio(2);
-                if (nc > 0) prefetch(0, lane);
+                if (nc > 0) {
+                    prefetch_k(0, lane);
+                    prefetch_v(0, lane);
+                    if (pw == 0) prefetch_g(0, lane);
+                }
                 for (int c = -1; c < nc; ++c) {
                     int lz = 0, lzv = 0;
                     asm volatile("" : "+s"(lz));
@@ -755,18 +792,11 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                         }
                         // V rows of blocks pw and pw + 2, held until the K stage and the gram
                         // have gone ahead; the next prefetch waits for them to be consumed
-                        halfx8 vh[2 * KS];
-                        if (VSPLIT && pw < 2) {
-#pragma unroll
-                            for (int i = 0; i < 2 * KS; ++i) {
-                                float x[8];
-                                pv[i].get(x);
-                                vh[i] = __builtin_bit_cast(
-                                    halfx8, u32x4{pk_f16(x[0], x[1]), pk_f16(x[2], x[3]), pk_f16(x[4], x[5]),
-                                                  pk_f16(x[6], x[7])});
-                            }
+                        if (c + 2 < nc) {
+                            prefetch_k(c + 2, ln);
+                            if (!VSPLIT) prefetch_v(c + 2, ln);
+                            if (pw == 0) prefetch_g(c + 2, ln);
                         }
-                        if (c + 2 < nc) prefetch(c + 2, ln);
                         pbar(ln);
 
                         ut_blocks<D>(Kn1, ka, sGl, sBeta, sBG, XB, TgAT, TgGT, TgGlT, PT, pw, ln,
@@ -777,14 +807,19 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                                          wait_count(sCnt + 1, NB * (c + 1));
                                          wait_count(sCnt + 2, NB * (c + 1));
                                      },
-                                     sCnt + 3, c + 2);
+                                     sCnt + 3, sCnt + 4, c + 2);
                         if (VSPLIT && pw < 2) {
 #pragma unroll
                             for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-                                for (int ks = 0; ks < KS; ++ks)
-                                    *reinterpret_cast<halfx8*>(Vn + (trow + 32 * hb) * RK + 32 * ks + 8 * g) =
-                                        vh[hb * KS + ks];
+                                for (int ks = 0; ks < KS; ++ks) {
+                                    float x[8];
+                                    pv[hb * KS + ks].get(x);
+                                    *reinterpret_cast<u32x4*>(Vn + (trow + 32 * hb) * RK + 32 * ks + 8 * g) =
+                                        u32x4{pk_f16(x[0], x[1]), pk_f16(x[2], x[3]), pk_f16(x[4], x[5]),
+                                              pk_f16(x[6], x[7])};
+                                }
+                            if (c + 2 < nc) prefetch_v(c + 2, ln);
                         }
                     }
                     __syncthreads();  // chunk c+1 prepared
