@@ -199,16 +199,16 @@ struct GLayout {
     static constexpr int sz_Wf = 2 * NB * 2 * 64 * 8 * 2;
     static constexpr int sz_Sc = 80 * 4;
     static constexpr int sz_T64 = 64 * RT * 2;
-    static constexpr int Kn = 0;                       // K rows (x2)
-    static constexpr int Wf = Kn + 2 * sz_K;           // -W'^T operand fragments
-    static constexpr int Sc = Wf + sz_Wf;              // Gamma/gamma_i, Gamma (fp32, x2)
-    static constexpr int Vn = Sc + 2 * sz_Sc;          // V rows (x2)
+    static constexpr int Kn = 0;                       // K rows (x3: carry, formation / solve, staging)
+    static constexpr int Wf = Kn + 3 * sz_K;           // -W'^T operand fragments
+    static constexpr int Sc = Wf + sz_Wf;              // Gamma/gamma_i, Gamma (fp32, x3)
+    static constexpr int Vn = Sc + 3 * sz_Sc;          // V rows (x2)
     static constexpr int XB = Vn + 2 * sz_K;           // ten 16x16 exchange slots (hi, lo)
     static constexpr int TgA = XB + 10 * kXT * 2;      // Tg, token-column-major
     static constexpr int TgG = TgA + sz_T64;           // Tg diag(gamma)
     static constexpr int TgGl = TgG + sz_T64;          // its low part (precise-T plan)
-    static constexpr int Gv = TgGl + sz_T64;           // G log2 e, beta, beta gamma (fp32)
-    static constexpr int Misc = Gv + 3 * 64 * 4;       // counter, exponents
+    static constexpr int Gv = TgGl + sz_T64;           // G log2 e, beta, beta gamma (fp32, x2)
+    static constexpr int Misc = Gv + 2 * 3 * 64 * 4;   // counters, exponents
     static constexpr int total = Misc + 32 * 4;
     // regions that must start at zero and are only partly written
     static constexpr int zero_begin = TgA, zero_end = Gv;
@@ -315,7 +315,7 @@ __device__ __forceinline__ floatx4 inv16(floatx4 n, floatx4 nt, int lane) {
 }
 
 // Chunk-local UT transform, wave pw of four owning token block pw: from the staged K rows
-// (f16, row stride D + 8; the wave's own block also in registers) and the gate vectors
+// (f16, row stride D + 8) and the gate vectors
 // (G log2 e, beta, beta gamma), L = strictly-lower(beta_i e^{G_i - G_j} K K^T) and
 // Tg = (I + L)^-1 diag(beta), written as its ten lower 16x16 blocks.  With D_b = (I + L_bb)^-1
 // and Inv the blocks of (I + L)^-1:
@@ -323,14 +323,15 @@ __device__ __forceinline__ floatx4 inv16(floatx4 n, floatx4 nt, int lane) {
 //   Q_b0 = L_b0 D_0 + L_b1 Inv_10,  Q_b1 = L_b1 D_1                     (b = 2, 3)
 //   Inv_2a = -D_2 Q_2a,  Inv_3a = -(Inv_32 Q_2a + D_3 Q_3a)             (lower-left quarter)
 // Work per wave: 0: D_0, Q_3. (gram blocks of row 3 against blocks 0, 1); 1: D_1, Inv_10;
-// 2: D_2, Q_2., Inv_2.; 3: D_3, Inv_32, Inv_3. .  pbar() orders the four waves, tg_wait() holds
+// 2: D_2, Q_2., Inv_2.; 3: D_3, Inv_32, Inv_3. .  side() runs while the gram products are in
+// flight.  pbar() orders the four waves, tg_wait() holds
 // the first Tg write until the previous Tg has been consumed; q2cnt / q3cnt hand Q_2. (wave 2)
 // and Q_3. (wave 0) to wave 3 (qtarget: arrivals so far in the task).
-template <int D, class Bar, class Wait>
-__device__ __forceinline__ void ut_blocks(const _Float16* Kn1, const halfx8* ka, const float* sGl, const float* sBeta,
+template <int D, class Bar, class Wait, class Side>
+__device__ __forceinline__ void ut_blocks(const _Float16* Kn1, const float* sGl, const float* sBeta,
                                           const float* sBG, _Float16* XB, _Float16* TgAT, _Float16* TgGT,
                                           _Float16* TgGlT, bool pt, int pw, int ln, Bar&& pbar, Wait&& tg_wait,
-                                          int* q2cnt, int* q3cnt, int qtarget) {
+                                          int* q2cnt, int* q3cnt, int qtarget, Side&& side) {
     constexpr int KS = D / 32, RK = D + 8;
     const int g = ln >> 4, cl = ln & 15;
     auto slot = [&](int i) { return XB + i * kXT; };
@@ -345,6 +346,9 @@ __device__ __forceinline__ void ut_blocks(const _Float16* Kn1, const halfx8* ka,
     }
     // ---- gram: diagonal block (pw, pw); transposed blocks (a, c) = K_a K_c^T, c the column block:
     //      (a, pw) for a < pw on waves 1..3 except (0, 3), (1, 3), which wave 0 forms
+    halfx8 ka[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) ka[ks] = krow(pw, ks);
     floatx4 gd = zero4();
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) gd = mma32(ka[ks], ka[ks], gd);
@@ -368,6 +372,8 @@ __device__ __forceinline__ void ut_blocks(const _Float16* Kn1, const halfx8* ka,
             if (pw == 2) gt[1] = mma32(krow(1, ks), ka[ks], gt[1]);
         }
     }
+    // independent work (staging of a later chunk) while the gram products are in flight
+    side();
     // ---- gate factors: LT[i] = L_{gc, ga[i]}^T (rows of block ga[i], columns of block gc);
     //      N = -L_{pw,pw} and N^T
     floatx4 LT[2];
@@ -509,11 +515,11 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                     asm volatile("" : "+v"(lzv));
                     unsigned char* sm = smem + lz;
                     const int ln = lane + lzv, hf = ln >> 5, lq = ln & 31;
-                    const int p = c & 1, pn = (c + 1) & 1;
+                    const int p = c & 1, p3 = (c + 3) % 3, pn3 = (c + 4) % 3;
                     if (c >= 0) {
                         const E* Wf = reinterpret_cast<const E*>(sm + LY::Wf);
-                        const E* Kn = reinterpret_cast<const E*>(sm + LY::Kn + p * LY::sz_K);
-                        const float* Sc = reinterpret_cast<const float*>(sm + LY::Sc + p * LY::sz_Sc);
+                        const E* Kn = reinterpret_cast<const E*>(sm + LY::Kn + p3 * LY::sz_K);
+                        const float* Sc = reinterpret_cast<const float*>(sm + LY::Sc + p3 * LY::sz_Sc);
                         floatx16 Vn[2];
                         Vn[0] = Vn[1] = zero16();
                         if (!TR) {
@@ -597,7 +603,7 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                     // the formation counter below.  W' has one buffer: every read of W'(c)
                     // happened before the barrier above.
                     if (c + 1 < nc) {
-                        const E* Kn1 = reinterpret_cast<const E*>(sm + LY::Kn + pn * LY::sz_K);
+                        const E* Kn1 = reinterpret_cast<const E*>(sm + LY::Kn + pn3 * LY::sz_K);
                         const E* TgG = reinterpret_cast<const E*>(sm + LY::TgG);
                         const E* TgGl = reinterpret_cast<const E*>(sm + LY::TgGl);
                         E* Wf1 = reinterpret_cast<E*>(sm + LY::Wf);
@@ -658,14 +664,18 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                 }
             } else {
                 // ======================== preparation waves ========================
-                // Wave pw owns token block pw (rows 16 pw .. 16 pw + 15) of every chunk and stages
-                // its K rows.  With 16-bit inputs waves 0 and 1, which finish the solve first,
-                // stage V (blocks pw and pw + 2) after it; with fp32 inputs (twice the registers
-                // in flight) every wave stages its own V block with its K rows.
+                // Wave pw owns token block pw (rows 16 pw .. 16 pw + 15) of every chunk in the
+                // solve.  While the gram products of chunk c+1 are in flight, each wave stages the
+                // K rows of its block of chunk c+2 and wave 0 its gate vectors; V rows of chunk c+1
+                // are staged after the solve, by waves 0 and 1 (blocks pw, pw + 2) with 16-bit
+                // inputs, by every wave for its own block with fp32 inputs (twice the registers).
                 const int pw = wave - NC;
                 constexpr int KS = D / 32;  // 32-wide contraction steps over d
                 constexpr bool VSPLIT = IN_BF16;
-                Raw8<IN_BF16> pk[KS], pv[(VSPLIT ? 2 : 1) * KS];
+                constexpr int NVB = VSPLIT ? 2 : 1;
+                const bool vstager = !VSPLIT || pw < 2;
+                auto vblk = [&](int i) { return VSPLIT ? pw + 2 * i : pw; };
+                Raw8<IN_BF16> pk[KS], pv[NVB * KS];
                 float pla = 0.f, pbt = 0.f;
                 // uniform 64-bit bases per task and chunk, 32-bit per-lane byte offsets
                 constexpr int ESZ = IN_BF16 ? 2 : 4;
@@ -677,45 +687,84 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                 const float* la0 = a.log_alpha + row0 * a.h_v + h;
                 const float* bt0 = a.beta + row0 * a.h_v + h;
                 const unsigned kstride = (unsigned)a.h_k * (D * ESZ), vstride = (unsigned)a.h_v * (D * ESZ);
-                // lane (row 16 pw + (ln & 15), d = 32 ks + 8 (ln >> 4) .. + 7): the A / B operand
-                // layout of the 16x16x32 gram products
-                auto prefetch_k = [&](int cc, int ln) {
-                    const int valid = min(64, len - 64 * cc);
-                    const unsigned char* kc = kb0 + (long long)(64 * cc) * kstride;
-                    const int t = 16 * pw + (ln & 15);
+                // lane (row 16 blk + (ln & 15), d = 32 ks + 8 (ln >> 4) .. + 7)
+                auto load_rows = [&](Raw8<IN_BF16>* dst, const unsigned char* base, unsigned stride, int blk, int valid,
+                                     int ln) {
+                    const int t = 16 * blk + (ln & 15);
                     const unsigned d0b = 8 * ESZ * (ln >> 4);
 #pragma unroll
                     for (int ks = 0; ks < KS; ++ks) {
                         if (t < valid)
-                            pk[ks].loadp(kc + (t * kstride + d0b + 32 * ESZ * ks));
+                            dst[ks].loadp(base + (t * stride + d0b + 32 * ESZ * ks));
                         else
-                            pk[ks].zero();
+                            dst[ks].zero();
                     }
                 };
-                auto prefetch_g = [&](int cc, int ln) {
+                auto store_rows = [&](const Raw8<IN_BF16>* src, E* dst, int blk, float sc, int ln) {
+                    E* row = dst + (16 * blk + (ln & 15)) * RK + 8 * (ln >> 4);
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) {
+                        float x[8];
+                        src[ks].get(x);
+                        *reinterpret_cast<u32x4*>(row + 32 * ks) =
+                            u32x4{pk_f16(x[0] * sc, x[1] * sc), pk_f16(x[2] * sc, x[3] * sc),
+                                  pk_f16(x[4] * sc, x[5] * sc), pk_f16(x[6] * sc, x[7] * sc)};
+                    }
+                };
+                // K rows of block pw and (wave 0) the gates of chunk cc
+                auto prefetch_kg = [&](int cc, int ln) {
                     const int valid = min(64, len - 64 * cc);
-                    const bool ok = ln < valid;
-                    const unsigned go = (unsigned)ln * a.h_v;
-                    pla = ok ? (la0 + (long long)(64 * cc) * a.h_v)[go] : 0.f;
-                    pbt = ok ? (bt0 + (long long)(64 * cc) * a.h_v)[go] : 0.f;
+                    load_rows(pk, kb0 + (long long)(64 * cc) * kstride, kstride, pw, valid, ln);
+                    if (pw == 0) {
+                        const bool ok = ln < valid;
+                        const unsigned go = (unsigned)ln * a.h_v;
+                        pla = ok ? (la0 + (long long)(64 * cc) * a.h_v)[go] : 0.f;
+                        pbt = ok ? (bt0 + (long long)(64 * cc) * a.h_v)[go] : 0.f;
+                    }
                 };
                 auto prefetch_v = [&](int cc, int ln) {
                     const int valid = min(64, len - 64 * cc);
-                    const unsigned char* vc = vb0 + (long long)(64 * cc) * vstride;
-                    const int t = 16 * pw + (ln & 15);
-                    const unsigned d0b = 8 * ESZ * (ln >> 4);
-                    if (!VSPLIT || pw < 2) {
+                    if (vstager) {
 #pragma unroll
-                        for (int hb = 0; hb < (VSPLIT ? 2 : 1); ++hb) {
-                            const int tv = t + 32 * hb;
+                        for (int i = 0; i < NVB; ++i)
+                            load_rows(pv + i * KS, vb0 + (long long)(64 * cc) * vstride, vstride, vblk(i), valid, ln);
+                    }
+                };
+                auto stage_kg = [&](int cc, unsigned char* sm, int ln) {
+                    float sc = 1.f;
+                    if (a.qk_l2norm) {
+                        float ss = 0.f;
 #pragma unroll
-                            for (int ks = 0; ks < KS; ++ks) {
-                                if (tv < valid)
-                                    pv[hb * KS + ks].loadp(vc + (tv * vstride + d0b + 32 * ESZ * ks));
-                                else
-                                    pv[hb * KS + ks].zero();
-                            }
+                        for (int ks = 0; ks < KS; ++ks) {
+                            float x[8];
+                            pk[ks].get(x);
+#pragma unroll
+                            for (int u = 0; u < 8; ++u) ss += x[u] * x[u];
                         }
+                        ss += __shfl_xor(ss, 16, 64);
+                        ss += __shfl_xor(ss, 32, 64);
+                        sc = ss > 0.f ? 1.f / sqrtf(ss) : 0.f;
+                    }
+                    store_rows(pk, reinterpret_cast<E*>(sm + LY::Kn + (cc % 3) * LY::sz_K), pw, sc, ln);
+                    if (pw == 0) {
+                        float* sGl = reinterpret_cast<float*>(sm + LY::Gv + (cc & 1) * (3 * 64 * 4));
+                        float* Scc = reinterpret_cast<float*>(sm + LY::Sc + (cc % 3) * LY::sz_Sc);
+                        const float G = wave_scan_dpp(pla);
+                        const float Glast = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(G), 63));
+                        const float Gl = G * 1.4426950408889634f;
+                        sGl[ln] = Gl;
+                        sGl[64 + ln] = pbt;
+                        sGl[128 + ln] = pbt * __builtin_amdgcn_exp2f(Gl);
+                        Scc[ln] = fexp(Glast - G);
+                        if (ln == 0) Scc[64] = fexp(Glast);
+                    }
+                };
+                auto stage_v = [&](int cc, unsigned char* sm, int ln) {
+                    if (vstager) {
+#pragma unroll
+                        for (int i = 0; i < NVB; ++i)
+                            store_rows(pv + i * KS, reinterpret_cast<E*>(sm + LY::Vn + (cc & 1) * LY::sz_K), vblk(i),
+                                       1.f, ln);
                     }
                 };
                 auto pbar = [&](int ln) {
@@ -726,101 +775,44 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                 // instructions issue ahead of the carry waves' (matrix-core bound) stream
                 __builtin_amdgcn_s_setprio(2);
                 if (nc > 0) {
-                    prefetch_k(0, lane);
+                    prefetch_kg(0, lane);
                     prefetch_v(0, lane);
-                    if (pw == 0) prefetch_g(0, lane);
+                    stage_kg(0, smem, lane);
+                    if (nc > 1) prefetch_kg(1, lane);
+                    pbar(lane);
                 }
                 for (int c = -1; c < nc; ++c) {
                     int lz = 0, lzv = 0;
                     asm volatile("" : "+s"(lz));
                     asm volatile("" : "+v"(lzv));
                     unsigned char* sm = smem + lz;
-                    const int ln = lane + lzv, g = ln >> 4, cl = ln & 15;
-                    const int pn = (c + 1) & 1;
+                    const int ln = lane + lzv;
                     if (c + 1 < nc) {
-                        E* Kn1 = reinterpret_cast<E*>(sm + LY::Kn + pn * LY::sz_K);
-                        E* Vn = reinterpret_cast<E*>(sm + LY::Vn + pn * LY::sz_K);
-                        float* Scn = reinterpret_cast<float*>(sm + LY::Sc + pn * LY::sz_Sc);
+                        const E* Kn1 = reinterpret_cast<const E*>(sm + LY::Kn + ((c + 1) % 3) * LY::sz_K);
                         E* XB = reinterpret_cast<E*>(sm + LY::XB);
                         E* TgAT = reinterpret_cast<E*>(sm + LY::TgA);
                         E* TgGT = reinterpret_cast<E*>(sm + LY::TgG);
                         E* TgGlT = reinterpret_cast<E*>(sm + LY::TgGl);
-                        float* sGl = reinterpret_cast<float*>(sm + LY::Gv);
-                        float* sBeta = sGl + 64;
-                        float* sBG = sGl + 128;
-
-                        // ---- stage block pw of chunk c+1 (K, V as f16); K stays as the gram operand
-                        const int trow = 16 * pw + cl;
-                        float ksc = 1.f;
-                        if (a.qk_l2norm) {
-                            float ss = 0.f;
-#pragma unroll
-                            for (int ks = 0; ks < KS; ++ks) {
-                                float x[8];
-                                pk[ks].get(x);
-#pragma unroll
-                                for (int u = 0; u < 8; ++u) ss += x[u] * x[u];
-                            }
-                            ss += __shfl_xor(ss, 16, 64);
-                            ss += __shfl_xor(ss, 32, 64);
-                            ksc = ss > 0.f ? 1.f / sqrtf(ss) : 0.f;
-                        }
-                        halfx8 ka[KS];
-#pragma unroll
-                        for (int ks = 0; ks < KS; ++ks) {
-                            float x[8];
-                            pk[ks].get(x);
-                            const u32x4 hk8 = {pk_f16(x[0] * ksc, x[1] * ksc), pk_f16(x[2] * ksc, x[3] * ksc),
-                                               pk_f16(x[4] * ksc, x[5] * ksc), pk_f16(x[6] * ksc, x[7] * ksc)};
-                            ka[ks] = __builtin_bit_cast(halfx8, hk8);
-                            *reinterpret_cast<u32x4*>(Kn1 + trow * RK + 32 * ks + 8 * g) = hk8;
-                            if (!VSPLIT) {
-                                pv[ks].get(x);
-                                *reinterpret_cast<u32x4*>(Vn + trow * RK + 32 * ks + 8 * g) =
-                                    u32x4{pk_f16(x[0], x[1]), pk_f16(x[2], x[3]), pk_f16(x[4], x[5]), pk_f16(x[6], x[7])};
-                            }
-                        }
-                        if (pw == 0) {
-                            const float G = wave_scan_dpp(pla);
-                            const float Glast = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(G), 63));
-                            const float Gl = G * 1.4426950408889634f;
-                            sGl[ln] = Gl;
-                            sBeta[ln] = pbt;
-                            sBG[ln] = pbt * __builtin_amdgcn_exp2f(Gl);
-                            Scn[ln] = fexp(Glast - G);
-                            if (ln == 0) Scn[64] = fexp(Glast);
-                        }
-                        // V rows of blocks pw and pw + 2, held until the K stage and the gram
-                        // have gone ahead; the next prefetch waits for them to be consumed
-                        if (c + 2 < nc) {
-                            prefetch_k(c + 2, ln);
-                            if (!VSPLIT) prefetch_v(c + 2, ln);
-                            if (pw == 0) prefetch_g(c + 2, ln);
-                        }
-                        pbar(ln);
-
-                        ut_blocks<D>(Kn1, ka, sGl, sBeta, sBG, XB, TgAT, TgGT, TgGlT, PT, pw, ln,
-                                     pbar,
+                        const float* sGl = reinterpret_cast<const float*>(sm + LY::Gv + ((c + 1) & 1) * (3 * 64 * 4));
+                        // solve chunk c+1 (K and gates staged before the last workgroup barrier);
+                        // meanwhile stage K and gates of chunk c+2 (buffers last read before it)
+                        ut_blocks<D>(Kn1, sGl, sGl + 64, sGl + 128, XB, TgAT, TgGT, TgGlT, PT, pw, ln, pbar,
                                      [&] {
                                          // Tg(c+1) overwrites Tg(c): wait until the carry waves
                                          // formed W'(c) and U(c)
                                          wait_count(sCnt + 1, NB * (c + 1));
                                          wait_count(sCnt + 2, NB * (c + 1));
                                      },
-                                     sCnt + 3, sCnt + 4, c + 2);
-                        if (VSPLIT && pw < 2) {
-#pragma unroll
-                            for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-                                for (int ks = 0; ks < KS; ++ks) {
-                                    float x[8];
-                                    pv[hb * KS + ks].get(x);
-                                    *reinterpret_cast<u32x4*>(Vn + (trow + 32 * hb) * RK + 32 * ks + 8 * g) =
-                                        u32x4{pk_f16(x[0], x[1]), pk_f16(x[2], x[3]), pk_f16(x[4], x[5]),
-                                              pk_f16(x[6], x[7])};
-                                }
-                            if (c + 2 < nc) prefetch_v(c + 2, ln);
-                        }
+                                     sCnt + 3, sCnt + 4, c + 2,
+                                     [&] {
+                                         if (c + 2 < nc) {
+                                             stage_kg(c + 2, sm, ln);
+                                             if (c + 3 < nc) prefetch_kg(c + 3, ln);
+                                         }
+                                     });
+                        // V of chunk c+1 (its buffer was last read by U(c-1), a period ago)
+                        stage_v(c + 1, sm, ln);
+                        if (c + 2 < nc) prefetch_v(c + 2, ln);
                     }
                     __syncthreads();  // chunk c+1 prepared
                 }
