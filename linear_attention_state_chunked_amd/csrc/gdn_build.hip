@@ -11,24 +11,27 @@
 //
 // Warp specialisation.  Carry waves own 32 columns of X each (T columns, then S
 // columns), keep them in matrix-core accumulators for the whole segment and run the
-// carry of chunk c; four preparation waves meanwhile stage chunk c+1, form its gram and
-// solve it.  After the one workgroup barrier per chunk the carry waves turn the solve
-// into W' (stored as ready-made operand fragments) and U (kept in registers) for chunk
-// c+1 while the preparation waves already stage chunk c+2 (K, V and gate buffers are
-// doubled).  Bounded LDS counters order the rest: the preparation waves' own stages,
-// the carry waves' W' hand-off, and the reuse of the Tg buffer.
+// carry of chunk c; four preparation waves meanwhile solve chunk c+1 (gram, UT
+// transform) and stage chunk c+2 (K and gates under the gram products, V after the
+// solve).  After the one workgroup barrier per chunk the carry waves turn the solve
+// into W' (stored as ready-made operand fragments) and U (formed at the start of the
+// next carry) while the preparation waves go on with chunk c+2; K and the gamma
+// vectors are triple-buffered, V and the gate vectors doubled.  Bounded LDS counters
+// order the rest: the preparation waves' own stages, the carry waves' W' hand-off,
+// the reuse of the Tg buffer and two hand-offs inside the solve.
 //
-// Layout rules.  Every matrix in LDS is a natural row-major f16 tile written with
-// 8- or 16-byte stores.  Row fragments are plain 16-byte reads; column fragments
-// (contraction over tokens, e.g. K^T or V) come from the gfx950 transposing read
-// ds_read_b64_tr_b16, which hands each lane of a 16-lane group one column of a 4x16
-// block.  Products whose result must be stored are computed transposed, so that each
-// lane's accumulator column is a run of a row of the result.
+// Layout rules.  Every K / V tile in LDS is a natural row-major f16 tile written with
+// 16-byte stores.  Row fragments are plain 16-byte reads; column fragments (contraction
+// over tokens, e.g. K^T or V) come from the gfx950 transposing read ds_read_b64_tr_b16,
+// which hands each lane of a 16-lane group one column of a 4x16 block.  Products whose
+// result must be stored are computed transposed, so that each lane's accumulator column
+// is a run of a row of the result.  Tg is stored token-column-major for the same reason.
 //
-// The 64x64 unit lower-triangular solve: 16x16 diagonal inverses by substitution in
-// fp32, then Inv = D - D N D merges (D block diagonal, N strictly block lower) for the
-// two 32x32 halves and for the whole, on the matrix cores with hi/lo-split f16
-// operands (about 22-bit operands, fp32 accumulation).
+// The 64x64 unit lower-triangular solve works on 16x16 blocks, one token block per
+// preparation wave: the diagonal inverses as the product (I+N)(I+N^2)(I+N^4)(I+N^8),
+// then two merge levels; all products on the matrix cores with hi/lo-split f16
+// operands (about 22-bit operands, fp32 accumulation).  Only small 16x16 tiles pass
+// between the waves.
 #include <type_traits>
 
 #include "device_common.hpp"
