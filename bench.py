@@ -394,20 +394,24 @@ def main():
         path.step()
     torch.cuda.synchronize()
 
-    # timed region: exactly K steps
+    # timed region: exactly K steps; HIP events on the launch stream bracket every build
+    # and compose launch inside it (recording them costs no device time)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        path.step()
+    for e in evs:
+        e[0].record(path.stream)
+        path.build()
+        e[1].record(path.stream)
+        path.compose()
+        e[2].record(path.stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall / args.steps * 1e3
     value = path.N * args.steps / wall
 
-    # per-call device time of the dominant kernel (build) and of the compose, HIP events
-    # on the launch stream
-    reps = max(5, args.steps)
-    t_build = float(np.median(time_events(path.build, reps, path.stream)))
-    t_comp = float(np.median(time_events(path.compose, reps, path.stream)))
+    # average per-launch device time of the dominant kernel (build) and of the compose
+    t_build = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e-3
+    t_comp = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e-3
     n_chunks = sum((int(cu[i + 1] - cu[i]) + 63) // 64 for i in range(len(cu) - 1))
     flops = build_flops_per_chunk() * n_chunks * path.h_v
     achieved = flops / t_build

@@ -539,21 +539,29 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                             // Tg(c) consumed: the preparation of chunk c+1 may overwrite it
                             count_arrival(sCnt + 2, ln);
                         }
+                        // -W' X: each X fragment (converted once) feeds both token halves
 #pragma unroll
-                        for (int mt = 0; mt < 2; ++mt) {
+                        for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
-                            for (int kb = 0; kb < NB; ++kb)
+                            for (int st = 0; st < 2; ++st) {
+                                if (PT && TR) {
+                                    const HL xb = split_acc(X[kb], st);
 #pragma unroll
-                                for (int st = 0; st < 2; ++st) {
-                                    const halfx8 fa = ld8(Wf + (((mt * NB + kb) * 2 + st) * 64 + ln) * 8);
-                                    if (PT && TR) {
-                                        const HL xb = split_acc(X[kb], st);
+                                    for (int mt = 0; mt < 2; ++mt) {
+                                        const halfx8 fa = ld8(Wf + (((mt * NB + kb) * 2 + st) * 64 + ln) * 8);
                                         Vn[mt] = OpF16::mma(fa, xb.lo, Vn[mt]);
                                         Vn[mt] = OpF16::mma(fa, xb.hi, Vn[mt]);
-                                    } else {
-                                        Vn[mt] = OpF16::mma(fa, OpF16::from_acc(X[kb], st), Vn[mt]);
                                     }
+                                } else {
+                                    const halfx8 xf = OpF16::from_acc(X[kb], st);
+#pragma unroll
+                                    for (int mt = 0; mt < 2; ++mt)
+                                        Vn[mt] = OpF16::mma(ld8(Wf + (((mt * NB + kb) * 2 + st) * 64 + ln) * 8), xf, Vn[mt]);
                                 }
+                                __builtin_amdgcn_sched_barrier(0);
+                            }
+#pragma unroll
+                        for (int mt = 0; mt < 2; ++mt) {
                             const float4* s4 = reinterpret_cast<const float4*>(Sc + 32 * mt + 4 * hf);
 #pragma unroll
                             for (int q = 0; q < 4; ++q) {
@@ -563,7 +571,6 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                                 Vn[mt][4 * q + 2] *= sv.z;
                                 Vn[mt][4 * q + 3] *= sv.w;
                             }
-                            __builtin_amdgcn_sched_barrier(0);
                         }
                         const float Gamma = Sc[64];
 #pragma unroll
