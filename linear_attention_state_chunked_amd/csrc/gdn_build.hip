@@ -422,29 +422,28 @@ __device__ __forceinline__ void ut_blocks(const _Float16* Kn1, const float* sGl,
         st_cm(slot(pw == 1 ? 4 : 5), iv, ln);
         st_tg(TgAT, TgGT, TgGlT, pt, iv, pw, a, ln, bcol[a], bgcol[a]);
     } else {
-        q1 = mm16(split4v(LT[1]), ld_b(slot(1), ln), zero4());   // L_{b,1} D_1
+        q1 = mm16(split4v(LT[1]), ld_b(slot(1), ln), zero4());   // Q_b1 = L_{b,1} D_1
+        st_cm(slot(pw == 2 ? 7 : 9), q1, ln);
         q0 = mm16(split4v(LT[0]), ld_b(slot(0), ln), zero4());   // L_{b,0} D_0
     }
     pbar(ln);
-    // ---- lower-left quarter
+    // ---- lower-left quarter: the Q_.1 terms are ready, the Q_.0 terms need Inv_10
     if (pw == 0 || pw == 2) {
-        q0 = mm16(split4v(LT[1]), ld_b(slot(4), ln), q0);                   // + L_{b,1} Inv_10
+        q0 = mm16(split4v(LT[1]), ld_b(slot(4), ln), q0);        // Q_b0 = ... + L_{b,1} Inv_10
         st_cm(slot(pw == 2 ? 6 : 8), q0, ln);
-        st_cm(slot(pw == 2 ? 7 : 9), q1, ln);
         count_arrival(pw == 2 ? q2cnt : q3cnt, ln);
         if (pw == 2) {
-            st_tg(TgAT, TgGT, TgGlT, pt, -mm16(DT, split4v(q0), zero4()), 2, 0, ln, bcol[0], bgcol[0]);
             st_tg(TgAT, TgGT, TgGlT, pt, -mm16(DT, split4v(q1), zero4()), 2, 1, ln, bcol[1], bgcol[1]);
+            st_tg(TgAT, TgGT, TgGlT, pt, -mm16(DT, split4v(q0), zero4()), 2, 0, ln, bcol[0], bgcol[0]);
         }
     } else if (pw == 3) {
         const HL4 A32 = ld_a(slot(5), ln);
-        wait_count(q2cnt, qtarget);
-        floatx4 r0 = mm16(A32, ld_b(slot(6), ln), zero4()), r1 = mm16(A32, ld_b(slot(7), ln), zero4());
-        wait_count(q3cnt, qtarget);
-        r0 = mm16(DT, ld_b(slot(8), ln), r0);
-        r1 = mm16(DT, ld_b(slot(9), ln), r1);
-        st_tg(TgAT, TgGT, TgGlT, pt, -r0, 3, 0, ln, bcol[0], bgcol[0]);
+        const floatx4 r1 = mm16(A32, ld_b(slot(7), ln), mm16(DT, ld_b(slot(9), ln), zero4()));
         st_tg(TgAT, TgGT, TgGlT, pt, -r1, 3, 1, ln, bcol[1], bgcol[1]);
+        wait_count(q2cnt, qtarget);
+        wait_count(q3cnt, qtarget);
+        const floatx4 r0 = mm16(A32, ld_b(slot(6), ln), mm16(DT, ld_b(slot(8), ln), zero4()));
+        st_tg(TgAT, TgGT, TgGlT, pt, -r0, 3, 0, ln, bcol[0], bgcol[0]);
     }
 }
 
@@ -676,7 +675,7 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                 // ======================== preparation waves ========================
                 // Wave pw owns token block pw (rows 16 pw .. 16 pw + 15) of every chunk in the
                 // solve.  While the gram products of chunk c+1 are in flight, each wave stages the
-                // K rows of its block of chunk c+2 and wave 0 its gate vectors; V rows of chunk c+1
+                // K rows of its block of chunk c+2 and wave 1 its gate vectors; V rows of chunk c+1
                 // are staged after the solve, by waves 0 and 1 (blocks pw, pw + 2) with 16-bit
                 // inputs, by every wave for its own block with fp32 inputs (twice the registers).
                 const int pw = wave - NC;
@@ -721,11 +720,12 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                                   pk_f16(x[4] * sc, x[5] * sc), pk_f16(x[6] * sc, x[7] * sc)};
                     }
                 };
-                // K rows of block pw and (wave 0) the gates of chunk cc
+                // K rows of block pw and (wave 1, which has the least gram work) the gates of chunk cc
+                constexpr int GW = 1;
                 auto prefetch_kg = [&](int cc, int ln) {
                     const int valid = min(64, len - 64 * cc);
                     load_rows(pk, kb0 + (long long)(64 * cc) * kstride, kstride, pw, valid, ln);
-                    if (pw == 0) {
+                    if (pw == GW) {
                         const bool ok = ln < valid;
                         const unsigned go = (unsigned)ln * a.h_v;
                         pla = ok ? (la0 + (long long)(64 * cc) * a.h_v)[go] : 0.f;
@@ -756,7 +756,7 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                         sc = ss > 0.f ? 1.f / sqrtf(ss) : 0.f;
                     }
                     store_rows(pk, reinterpret_cast<E*>(sm + LY::Kn + (cc % 3) * LY::sz_K), pw, sc, ln);
-                    if (pw == 0) {
+                    if (pw == GW) {
                         float* sGl = reinterpret_cast<float*>(sm + LY::Gv + (cc & 1) * (3 * 64 * 4));
                         float* Scc = reinterpret_cast<float*>(sm + LY::Sc + (cc % 3) * LY::sz_Sc);
                         const float G = wave_scan_dpp(pla);
