@@ -14,8 +14,8 @@
 // carry of chunk c; four preparation waves meanwhile solve chunk c+1 (gram, UT
 // transform) and stage chunk c+2 (K and gates under the gram products, V after the
 // solve).  After the one workgroup barrier per chunk the carry waves turn the solve
-// into W' (stored as ready-made operand fragments) and U (formed at the start of the
-// next carry) while the preparation waves go on with chunk c+2; K and the gamma
+// into W' (T waves; stored as ready-made operand fragments) and U (S waves; kept in
+// their accumulators for the next carry) while the preparation waves go on with chunk c+2; K and the gamma
 // vectors are triple-buffered, V and the gate vectors doubled.  Bounded LDS counters
 // order the rest: the preparation waves' own stages, the carry waves' W' hand-off,
 // the reuse of the Tg buffer and two hand-offs inside the solve.
@@ -196,7 +196,10 @@ constexpr int kXT = 2 * 16 * kXS;   // one exchange slot (f16 elements): hi tile
 template <int D>
 struct GLayout {
     static constexpr int NB = D / 32;
-    static constexpr int RK = D + 8;                   // K, V rows
+    // K, V rows.  A transposing column read takes 4 rows x 64 bytes per half-wave; a row
+    // stride of 16 (mod 64) dwords puts those rows in disjoint bank quarters (D + 8 gave
+    // two-way conflicts); the 16-row fragment reads of the gram cost the same either way.
+    static constexpr int RK = D + 32;
     static constexpr int RT = 64 + 8;                  // 64-wide rows of the Tg tiles
     static constexpr int sz_K = 64 * RK * 2;
     static constexpr int sz_Wf = 2 * NB * 2 * 64 * 8 * 2;
@@ -318,7 +321,7 @@ __device__ __forceinline__ floatx4 inv16(floatx4 n, floatx4 nt, int lane) {
 }
 
 // Chunk-local UT transform, wave pw of four owning token block pw: from the staged K rows
-// (f16, row stride D + 8) and the gate vectors
+// (f16, row stride D + 32) and the gate vectors
 // (G log2 e, beta, beta gamma), L = strictly-lower(beta_i e^{G_i - G_j} K K^T) and
 // Tg = (I + L)^-1 diag(beta), written as its ten lower 16x16 blocks.  With D_b = (I + L_bb)^-1
 // and Inv the blocks of (I + L)^-1:
@@ -335,7 +338,7 @@ __device__ __forceinline__ void ut_blocks(const _Float16* Kn1, const float* sGl,
                                           const float* sBG, _Float16* XB, _Float16* TgAT, _Float16* TgGT,
                                           _Float16* TgGlT, bool pt, int pw, int ln, Bar&& pbar, Wait&& tg_wait,
                                           int* q2cnt, int* q3cnt, int qtarget, Side&& side) {
-    constexpr int KS = D / 32, RK = D + 8;
+    constexpr int KS = D / 32, RK = GLayout<D>::RK;
     const int g = ln >> 4, cl = ln & 15;
     auto slot = [&](int i) { return XB + i * kXT; };
     auto krow = [&](int blk, int ks) { return ld8(Kn1 + (16 * blk + cl) * RK + 32 * ks + 8 * g); };
@@ -509,6 +512,10 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                     for (int j = 0; j < 16; ++j)
                         X[xb][j] = (TR && 32 * xb + 8 * (j >> 2) + (j & 3) == diag) ? 1.f : 0.f;
                 int ew = 0;
+                // S waves enter chunk c holding U(c) = Tg(c) V(c) in Vn (formed after the previous
+                // workgroup barrier); the T waves start from zero
+                floatx16 Vn[2];
+                Vn[0] = Vn[1] = zero16();
                 for (int c = -1; c < nc; ++c) {
                     // opaque zeros: per-lane LDS offsets are recomputed every chunk instead of
                     // being hoisted out of the loop into long-lived registers
@@ -522,22 +529,7 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                         const E* Wf = reinterpret_cast<const E*>(sm + LY::Wf);
                         const E* Kn = reinterpret_cast<const E*>(sm + LY::Kn + p3 * LY::sz_K);
                         const float* Sc = reinterpret_cast<const float*>(sm + LY::Sc + p3 * LY::sz_Sc);
-                        floatx16 Vn[2];
-                        Vn[0] = Vn[1] = zero16();
-                        if (!TR) {
-                            // U = Tg V for this wave's columns, both token halves per V fragment
-                            const E* TgA = reinterpret_cast<const E*>(sm + LY::TgA);
-                            const E* Vc = reinterpret_cast<const E*>(sm + LY::Vn + p * LY::sz_K);
-#pragma unroll
-                            for (int kk = 0; kk < 4; ++kk) {
-                                const halfx8 fb = colfrag_nat(Vc, RK, 0, col0, kk, ln);
-#pragma unroll
-                                for (int mt = 0; mt < 2; ++mt)
-                                    Vn[mt] = OpF16::mma(colfrag_nat(TgA, RT, 0, 32 * mt, kk, ln), fb, Vn[mt]);
-                            }
-                            // Tg(c) consumed: the preparation of chunk c+1 may overwrite it
-                            count_arrival(sCnt + 2, ln);
-                        }
+                        if (TR) Vn[0] = Vn[1] = zero16();
                         // -W' X: each X fragment (converted once) feeds both token halves
 #pragma unroll
                         for (int kb = 0; kb < NB; ++kb)
@@ -642,9 +634,25 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                                 }
                             }
                         }
-                        // W'(c+1) formed (its Tg reads done): the forming waves count it, all
-                        // carry waves wait for the whole of W'(c+1)
+                        // W'(c+1) formed (its Tg reads done): the forming waves count it
                         if (TR || !WITH_T) count_arrival(sCnt + 1, ln);
+                        if (!TR) {
+                            // U(c+1) = Tg V for this wave's columns, both token halves per V fragment,
+                            // formed beside W'(c+1) and carried into the next chunk in Vn
+                            const E* TgA = reinterpret_cast<const E*>(sm + LY::TgA);
+                            const E* Vc = reinterpret_cast<const E*>(sm + LY::Vn + (p ^ 1) * LY::sz_K);
+                            Vn[0] = Vn[1] = zero16();
+#pragma unroll
+                            for (int kk = 0; kk < 4; ++kk) {
+                                const halfx8 fb = colfrag_nat(Vc, RK, 0, col0, kk, ln);
+#pragma unroll
+                                for (int mt = 0; mt < 2; ++mt)
+                                    Vn[mt] = OpF16::mma(colfrag_nat(TgA, RT, 0, 32 * mt, kk, ln), fb, Vn[mt]);
+                            }
+                            // Tg(c+1) consumed: the preparation of chunk c+2 may overwrite it
+                            count_arrival(sCnt + 2, ln);
+                        }
+                        // every carry wave waits for the whole of W'(c+1)
                         wait_count(sCnt + 1, NB * (c + 2));
                     }
                 }
