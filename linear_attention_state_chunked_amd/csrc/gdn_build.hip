@@ -12,8 +12,8 @@
 // Warp specialisation.  Carry waves own 32 columns of X each (T columns, then S
 // columns), keep them in matrix-core accumulators for the whole segment and run the
 // carry of chunk c; four preparation waves meanwhile solve chunk c+1 (gram, UT
-// transform) and stage chunk c+2 (K and gates under the gram products, V after the
-// solve).  After the one workgroup barrier per chunk the carry waves turn the solve
+// transform) and stage K and gates of chunk c+2 under the gram products; the S waves
+// stage V of chunk c+1 at the end of their carry (16-bit inputs).  After the one workgroup barrier per chunk the carry waves turn the solve
 // into W' (T waves; stored as ready-made operand fragments) and U (S waves; kept in
 // their accumulators for the next carry) while the preparation waves go on with chunk c+2; K and the gamma
 // vectors are triple-buffered, V and the gate vectors doubled.  Bounded LDS counters
@@ -196,10 +196,12 @@ constexpr int kXT = 2 * 16 * kXS;   // one exchange slot (f16 elements): hi tile
 template <int D>
 struct GLayout {
     static constexpr int NB = D / 32;
-    // K, V rows.  A transposing column read takes 4 rows x 64 bytes per half-wave; a row
-    // stride of 16 (mod 64) dwords puts those rows in disjoint bank quarters (D + 8 gave
-    // two-way conflicts); the 16-row fragment reads of the gram cost the same either way.
-    static constexpr int RK = D + 32;
+    // K, V rows.  gfx950's LDS serves 32 lanes per pass from 128 four-byte banks (fitted
+    // to probe timings of these access patterns).  A transposing column read puts 4 rows x
+    // 16 dwords in one pass, the 16-byte row-fragment reads and stores of the gram and the
+    // staging 16 rows x 2 x 4 dwords; a row stride of 72 dwords (D = 128) or 56 (D = 64)
+    // keeps both conflict-free (D + 8 gave two-way conflicts on the column reads).
+    static constexpr int RK = D == 128 ? D + 16 : D + 48;
     static constexpr int RT = 64 + 8;                  // 64-wide rows of the Tg tiles
     static constexpr int sz_K = 64 * RK * 2;
     static constexpr int sz_Wf = 2 * NB * 2 * 64 * 8 * 2;
@@ -321,7 +323,7 @@ __device__ __forceinline__ floatx4 inv16(floatx4 n, floatx4 nt, int lane) {
 }
 
 // Chunk-local UT transform, wave pw of four owning token block pw: from the staged K rows
-// (f16, row stride D + 32) and the gate vectors
+// (f16, row stride GLayout<D>::RK) and the gate vectors
 // (G log2 e, beta, beta gamma), L = strictly-lower(beta_i e^{G_i - G_j} K K^T) and
 // Tg = (I + L)^-1 diag(beta), written as its ten lower 16x16 blocks.  With D_b = (I + L_bb)^-1
 // and Inv the blocks of (I + L)^-1:
@@ -457,6 +459,7 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
     constexpr int NB = D / 32;
     constexpr int NC = (WITH_T ? 2 : 1) * NB;   // carry waves
     constexpr int NP = 4;                       // preparation waves
+    constexpr bool CV = IN_BF16;                // V rows staged by the S carry waves
     constexpr int NT = (NC + NP) * 64;
     constexpr int RK = LY::RK, RT = LY::RT;
 
@@ -516,6 +519,42 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                 // workgroup barrier); the T waves start from zero
                 floatx16 Vn[2];
                 Vn[0] = Vn[1] = zero16();
+                // With 16-bit inputs the S waves stage the V rows, one chunk ahead of U: S wave sw
+                // owns rows RPW sw .. RPW sw + RPW - 1, four 16-byte pieces per lane (a row's
+                // pieces on consecutive lanes), loaded a chunk before they are stored.
+                constexpr int RPW = 64 / NB, CPR = D / 8;
+                constexpr int ESZ = IN_BF16 ? 2 : 4;
+                Raw8<IN_BF16> cv[4];
+                const int sw = (WITH_T && !TR) ? wave - NB : wave;
+                const unsigned vstride = (unsigned)a.h_v * (D * ESZ);
+                const unsigned char* vb0 =
+                    reinterpret_cast<const unsigned char*>(a.v) + (((long long)b * N + start) * a.h_v + h) * (D * ESZ);
+                auto cv_prefetch = [&](int cc, int ln) {
+                    const int valid = min(64, len - 64 * cc);
+                    const unsigned char* base = vb0 + (long long)(64 * cc) * vstride;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int t = RPW * sw + (64 * q + ln) / CPR, ch = (64 * q + ln) % CPR;
+                        if (t < valid)
+                            cv[q].loadp(base + (t * vstride + ch * 8 * ESZ));
+                        else
+                            cv[q].zero();
+                    }
+                };
+                auto cv_stage = [&](int cc, unsigned char* sm, int ln) {
+                    E* dst = reinterpret_cast<E*>(sm + LY::Vn + (cc & 1) * LY::sz_K);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int t = RPW * sw + (64 * q + ln) / CPR, ch = (64 * q + ln) % CPR;
+                        float x[8];
+                        cv[q].get(x);
+                        *reinterpret_cast<u32x4*>(dst + t * RK + 8 * ch) =
+                            u32x4{pk_f16(x[0], x[1]), pk_f16(x[2], x[3]), pk_f16(x[4], x[5]), pk_f16(x[6], x[7])};
+                    }
+                };
+                if constexpr (CV && !TR) {
+                    if (nc > 0) cv_prefetch(0, lane);
+                }
                 for (int c = -1; c < nc; ++c) {
                     // opaque zeros: per-lane LDS offsets are recomputed every chunk instead of
                     // being hoisted out of the loop into long-lived registers
@@ -530,57 +569,100 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                         const E* Kn = reinterpret_cast<const E*>(sm + LY::Kn + p3 * LY::sz_K);
                         const float* Sc = reinterpret_cast<const float*>(sm + LY::Sc + p3 * LY::sz_Sc);
                         if (TR) Vn[0] = Vn[1] = zero16();
-                        // -W' X: each X fragment (converted once) feeds both token halves
+                        // Vn rows scaled by Gamma / gamma_i; X <- Gamma X before its update
+                        auto scale_vn = [&] {
 #pragma unroll
-                        for (int kb = 0; kb < NB; ++kb)
+                            for (int mt = 0; mt < 2; ++mt) {
+                                const float4* s4 = reinterpret_cast<const float4*>(Sc + 32 * mt + 4 * hf);
 #pragma unroll
-                            for (int st = 0; st < 2; ++st) {
-                                if (PT && TR) {
+                                for (int q = 0; q < 4; ++q) {
+                                    const float4 sv = s4[2 * q];   // rows 8q + 4h + 0..3
+                                    Vn[mt][4 * q + 0] *= sv.x;
+                                    Vn[mt][4 * q + 1] *= sv.y;
+                                    Vn[mt][4 * q + 2] *= sv.z;
+                                    Vn[mt][4 * q + 3] *= sv.w;
+                                }
+                            }
+                        };
+                        const float Gamma = Sc[64];
+                        auto wfrag = [&](int mt, int kb, int st) {
+                            return ld8(Wf + (((mt * NB + kb) * 2 + st) * 64 + ln) * 8);
+                        };
+                        if constexpr (PT && TR) {
+                            // hi/lo X and Vn operands (the precise-T plan): plain loops, which
+                            // keep this variant within its registers
+#pragma unroll
+                            for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+                                for (int st = 0; st < 2; ++st) {
                                     const HL xb = split_acc(X[kb], st);
 #pragma unroll
                                     for (int mt = 0; mt < 2; ++mt) {
-                                        const halfx8 fa = ld8(Wf + (((mt * NB + kb) * 2 + st) * 64 + ln) * 8);
+                                        const halfx8 fa = wfrag(mt, kb, st);
                                         Vn[mt] = OpF16::mma(fa, xb.lo, Vn[mt]);
                                         Vn[mt] = OpF16::mma(fa, xb.hi, Vn[mt]);
                                     }
-                                } else {
-                                    const halfx8 xf = OpF16::from_acc(X[kb], st);
-#pragma unroll
-                                    for (int mt = 0; mt < 2; ++mt)
-                                        Vn[mt] = OpF16::mma(ld8(Wf + (((mt * NB + kb) * 2 + st) * 64 + ln) * 8), xf, Vn[mt]);
+                                    __builtin_amdgcn_sched_barrier(0);
                                 }
-                                __builtin_amdgcn_sched_barrier(0);
-                            }
+                            scale_vn();
 #pragma unroll
-                        for (int mt = 0; mt < 2; ++mt) {
-                            const float4* s4 = reinterpret_cast<const float4*>(Sc + 32 * mt + 4 * hf);
+                            for (int xb = 0; xb < NB; ++xb) {
 #pragma unroll
-                            for (int q = 0; q < 4; ++q) {
-                                const float4 sv = s4[2 * q];   // rows 8q + 4h + 0..3
-                                Vn[mt][4 * q + 0] *= sv.x;
-                                Vn[mt][4 * q + 1] *= sv.y;
-                                Vn[mt][4 * q + 2] *= sv.z;
-                                Vn[mt][4 * q + 3] *= sv.w;
-                            }
-                        }
-                        const float Gamma = Sc[64];
+                                for (int j = 0; j < 16; ++j) X[xb][j] *= Gamma;
 #pragma unroll
-                        for (int xb = 0; xb < NB; ++xb) {
+                                for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                            for (int j = 0; j < 16; ++j) X[xb][j] *= Gamma;
-#pragma unroll
-                            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                                for (int st = 0; st < 2; ++st) {
-                                    const halfx8 fa = colfrag_acc(Kn, RK, 32 * mt, 32 * xb, st, ln);
-                                    if (PT && TR) {
+                                    for (int st = 0; st < 2; ++st) {
+                                        const halfx8 fa = colfrag_acc(Kn, RK, 32 * mt, 32 * xb, st, ln);
                                         const HL vb = split_acc(Vn[mt], st);
                                         X[xb] = OpF16::mma(fa, vb.lo, X[xb]);
                                         X[xb] = OpF16::mma(fa, vb.hi, X[xb]);
-                                    } else {
-                                        X[xb] = OpF16::mma(fa, OpF16::from_acc(Vn[mt], st), X[xb]);
                                     }
+                            }
+                        } else {
+                            // -W' X in steps (kb, st), each X fragment converted once for both
+                            // token halves; the W' fragments are read two steps ahead (a ring of
+                            // three) so that LDS latency hides behind earlier products
+                            constexpr int NSW = 2 * NB;
+                            halfx8 fw[3][2];
+                            auto wload = [&](int i, halfx8 (&dst)[2]) {
+#pragma unroll
+                                for (int mt = 0; mt < 2; ++mt) dst[mt] = wfrag(mt, i >> 1, i & 1);
+                            };
+                            wload(0, fw[0]);
+                            wload(1, fw[1]);
+#pragma unroll
+                            for (int i = 0; i < NSW; ++i) {
+                                if (i + 2 < NSW) wload(i + 2, fw[(i + 2) % 3]);
+                                const halfx8 xf = OpF16::from_acc(X[i >> 1], i & 1);
+#pragma unroll
+                                for (int mt = 0; mt < 2; ++mt) Vn[mt] = OpF16::mma(fw[i % 3][mt], xf, Vn[mt]);
+                                __builtin_amdgcn_sched_barrier(0);
+                            }
+                            scale_vn();
+                            // X <- Gamma X + K^T Vn in steps (mt, st, xb): consecutive products on
+                            // different X blocks, each Vn operand converted once for its NB steps,
+                            // the K column fragments read two steps ahead
+                            constexpr int NSX = 4 * NB;
+                            auto kload = [&](int i) {
+                                const int ms = i / NB;
+                                return colfrag_acc(Kn, RK, 32 * (ms >> 1), 32 * (i % NB), ms & 1, ln);
+                            };
+                            halfx8 fk[3], vb;
+                            fk[0] = kload(0);
+                            fk[1] = kload(1);
+#pragma unroll
+                            for (int i = 0; i < NSX; ++i) {
+                                if (i + 2 < NSX) fk[(i + 2) % 3] = kload(i + 2);
+                                const int xb = i % NB, ms = i / NB;
+                                if (ms == 0) {
+#pragma unroll
+                                    for (int j = 0; j < 16; ++j) X[xb][j] *= Gamma;
                                 }
+                                if (xb == 0) vb = OpF16::from_acc(Vn[ms >> 1], ms & 1);
+                                X[xb] = OpF16::mma(fk[i % 3], vb, X[xb]);
+                                __builtin_amdgcn_sched_barrier(0);
+                            }
                         }
                         if (TR) {
                             float m = 0.f;
@@ -597,6 +679,12 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                                 ew += e;
                             }
                         }
+                    }
+                    if constexpr (CV && !TR) {
+                        // V of chunk c+1 for U(c+1) after the barrier (its buffer held V(c-1),
+                        // consumed after the barrier before last), then the loads of chunk c+2
+                        if (c + 1 < nc) cv_stage(c + 1, sm, ln);
+                        if (c + 2 < nc) cv_prefetch(c + 2, ln);
                     }
                     __syncthreads();  // preparation of chunk c+1 is complete
                     // From here the preparation waves go on to chunk c+2.  Its staging
@@ -683,16 +771,12 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                 // ======================== preparation waves ========================
                 // Wave pw owns token block pw (rows 16 pw .. 16 pw + 15) of every chunk in the
                 // solve.  While the gram products of chunk c+1 are in flight, each wave stages the
-                // K rows of its block of chunk c+2 and wave 1 its gate vectors; V rows of chunk c+1
-                // are staged after the solve, by waves 0 and 1 (blocks pw, pw + 2) with 16-bit
-                // inputs, by every wave for its own block with fp32 inputs (twice the registers).
+                // K rows of its block of chunk c+2 and wave 1 its gate vectors.  With fp32 inputs
+                // each wave also stages the V rows of its block of chunk c+1 after the solve (with
+                // 16-bit inputs the S carry waves do that).
                 const int pw = wave - NC;
                 constexpr int KS = D / 32;  // 32-wide contraction steps over d
-                constexpr bool VSPLIT = IN_BF16;
-                constexpr int NVB = VSPLIT ? 2 : 1;
-                const bool vstager = !VSPLIT || pw < 2;
-                auto vblk = [&](int i) { return VSPLIT ? pw + 2 * i : pw; };
-                Raw8<IN_BF16> pk[KS], pv[NVB * KS];
+                Raw8<IN_BF16> pk[KS], pv[KS];
                 float pla = 0.f, pbt = 0.f;
                 // uniform 64-bit bases per task and chunk, 32-bit per-lane byte offsets
                 constexpr int ESZ = IN_BF16 ? 2 : 4;
@@ -742,11 +826,7 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                 };
                 auto prefetch_v = [&](int cc, int ln) {
                     const int valid = min(64, len - 64 * cc);
-                    if (vstager) {
-#pragma unroll
-                        for (int i = 0; i < NVB; ++i)
-                            load_rows(pv + i * KS, vb0 + (long long)(64 * cc) * vstride, vstride, vblk(i), valid, ln);
-                    }
+                    load_rows(pv, vb0 + (long long)(64 * cc) * vstride, vstride, pw, valid, ln);
                 };
                 auto stage_kg = [&](int cc, unsigned char* sm, int ln) {
                     float sc = 1.f;
@@ -778,12 +858,7 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                     }
                 };
                 auto stage_v = [&](int cc, unsigned char* sm, int ln) {
-                    if (vstager) {
-#pragma unroll
-                        for (int i = 0; i < NVB; ++i)
-                            store_rows(pv + i * KS, reinterpret_cast<E*>(sm + LY::Vn + (cc & 1) * LY::sz_K), vblk(i),
-                                       1.f, ln);
-                    }
+                    store_rows(pv, reinterpret_cast<E*>(sm + LY::Vn + (cc & 1) * LY::sz_K), pw, 1.f, ln);
                 };
                 auto pbar = [&](int ln) {
                     pb_target += NP;
@@ -794,7 +869,7 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                 __builtin_amdgcn_s_setprio(2);
                 if (nc > 0) {
                     prefetch_kg(0, lane);
-                    prefetch_v(0, lane);
+                    if constexpr (!CV) prefetch_v(0, lane);
                     stage_kg(0, smem, lane);
                     if (nc > 1) prefetch_kg(1, lane);
                     pbar(lane);
@@ -829,8 +904,10 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                                          }
                                      });
                         // V of chunk c+1 (its buffer was last read by U(c-1), a period ago)
-                        stage_v(c + 1, sm, ln);
-                        if (c + 2 < nc) prefetch_v(c + 2, ln);
+                        if constexpr (!CV) {
+                            stage_v(c + 1, sm, ln);
+                            if (c + 2 < nc) prefetch_v(c + 2, ln);
+                        }
                     }
                     __syncthreads();  // chunk c+1 prepared
                 }
