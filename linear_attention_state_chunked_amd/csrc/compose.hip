@@ -48,14 +48,14 @@ __device__ __forceinline__ halfx8 t_frag(const _Float16* base) {
 
 // Dense kind.  One workgroup per (chain, element block, role); role 0 composes S,
 // role 1 (launched only when the composed transition is wanted) composes T.  D/32
-// compute waves each keep 32 columns of the running S (or T) in accumulators; D/32
-// loader waves hold the next element's (T_i, S_i) in registers, loaded from HBM
-// while the current element is multiplied, and write them into LDS (T_i as hi/lo
-// f16, S_i as fp32, row-major) between two workgroup barriers.
+// compute waves each keep 32 columns of the running S (or T) in accumulators; D/16
+// loader waves hold the next element's (T_i, and for role 0 S_i) in registers, loaded
+// from HBM while the current element is multiplied, and write them into LDS (T_i as
+// hi/lo f16, S_i as fp32, row-major) between two workgroup barriers.
 template <int D>
-__global__ __launch_bounds__(D * 4) void fold_dense_kernel(FoldArgs a) {
-    constexpr int NB = D / 32;                        // compute waves = loader waves
-    constexpr int NLT = NB * 64;                      // loader threads
+__global__ __launch_bounds__(D * 6) void fold_dense_kernel(FoldArgs a) {
+    constexpr int NB = D / 32;                        // compute waves
+    constexpr int NLT = 2 * NB * 64;                  // loader threads
     constexpr int RS = D + 8;                         // staged row stride (halves)
     constexpr int TPL = D * D / (4 * NLT);            // float4 of T_i per loader thread
     static_assert(TPL * 4 * NLT == D * D, "staging split");
@@ -88,10 +88,11 @@ __global__ __launch_bounds__(D * 4) void fold_dense_kernel(FoldArgs a) {
             const f4* src = reinterpret_cast<const f4*>(a.T_hat + so * DD);
 #pragma unroll
             for (int r = 0; r < TPL; ++r) tr[r] = src[lt + NLT * r];
-            // (the transition role stages a second copy of T_i, from cache, in place of S_i)
-            const f4* srs = reinterpret_cast<const f4*>((t_role ? a.T_hat : a.S) + so * DD);
+            if (!t_role) {  // the transition role needs no S_i
+                const f4* srs = reinterpret_cast<const f4*>(a.S + so * DD);
 #pragma unroll
-            for (int r = 0; r < TPL; ++r) ts[r] = srs[lt + NLT * r];
+                for (int r = 0; r < TPL; ++r) ts[r] = srs[lt + NLT * r];
+            }
             ei = a.T_exp[so];
         };
         auto stage = [&]() __attribute__((always_inline)) {
@@ -109,7 +110,7 @@ __global__ __launch_bounds__(D * 4) void fold_dense_kernel(FoldArgs a) {
                 }
                 *reinterpret_cast<half4*>(&sT[0][row * RS + col]) = h;
                 *reinterpret_cast<half4*>(&sT[1][row * RS + col]) = l;
-                *reinterpret_cast<f4*>(&sS[row * RSS + col]) = ts[r];
+                if (!t_role) *reinterpret_cast<f4*>(&sS[row * RSS + col]) = ts[r];
             }
             if (lt == 0) sE = ei;
         };
@@ -311,8 +312,8 @@ hipError_t launch_fold(const FoldArgs& a, int d, int with_T, hipStream_t s) {
     if (a.kind == 0 && !a.naive) {
         // role 1 (the composed transition) only when its outputs are wanted
         const dim3 g3(a.n_chain, a.n_block, (with_T && a.out_T) ? 2 : 1);
-        if (d == 128) hipLaunchKernelGGL((fold_dense_kernel<128>), g3, dim3(512), 0, s, a);
-        else if (d == 64) hipLaunchKernelGGL((fold_dense_kernel<64>), g3, dim3(256), 0, s, a);
+        if (d == 128) hipLaunchKernelGGL((fold_dense_kernel<128>), g3, dim3(768), 0, s, a);
+        else if (d == 64) hipLaunchKernelGGL((fold_dense_kernel<64>), g3, dim3(384), 0, s, a);
         else return hipErrorInvalidValue;
     } else {
         // naive addition of any kind, and the diagonal / scalar kinds

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -148,10 +149,15 @@ bool build_prec_f32(const hypic_build_desc* d) {
            (d->precision == HYPIC_PREC_AUTO && d->in_dtype == HYPIC_F32 && d->d_k == 64);
 }
 
+// compute units of the current device, queried once per device
 int device_cu_count() {
+    static std::atomic<int> cached[64];
     int dev = 0, n = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
+    const bool cacheable = dev >= 0 && dev < 64;
+    if (cacheable && (n = cached[dev].load(std::memory_order_relaxed)) > 0) return n;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (cacheable && n > 0) cached[dev].store(n, std::memory_order_relaxed);
     return n;
 }
 
@@ -315,24 +321,26 @@ namespace {
 // FOLD runs one workgroup per chain (two with the composed T) for n steps; SCAN's block
 // reduce runs two per (chain, block) for B steps, the scan of the aggregates one (two)
 // per chain for n/B steps, and the optional re-fold one per (chain, block) for B steps.
-int64_t dense_rounds(int64_t wgs) {
-    int cus = device_cu_count();
-    if (cus <= 0) cus = 256;
-    return (wgs + cus - 1) / cus;
+// `cus` is the device's compute unit count, looked up once per call by the caller.
+int planner_cus() {
+    const int n = device_cu_count();
+    return n > 0 ? n : 256;
 }
 
-int64_t dense_fold_cost(const hypic_compose_desc* d) {
-    return dense_rounds((int64_t)d->n_chain * (d->T_total ? 2 : 1)) * d->n_elem;
+int64_t dense_rounds(int64_t wgs, int cus) { return (wgs + cus - 1) / cus; }
+
+int64_t dense_fold_cost(const hypic_compose_desc* d, int cus) {
+    return dense_rounds((int64_t)d->n_chain * (d->T_total ? 2 : 1), cus) * d->n_elem;
 }
 
-int64_t dense_scan_cost(const hypic_compose_desc* d, int64_t b) {
+int64_t dense_scan_cost(const hypic_compose_desc* d, int64_t b, int cus) {
     const int64_t C = d->n_chain, nb = (d->n_elem + b - 1) / b;
-    int64_t cost = dense_rounds(2 * C * nb) * b + dense_rounds(C * (d->T_total ? 2 : 1)) * nb;
-    if (d->S_prefix) cost += dense_rounds(C * nb) * b;
+    int64_t cost = dense_rounds(2 * C * nb, cus) * b + dense_rounds(C * (d->T_total ? 2 : 1), cus) * nb;
+    if (d->S_prefix) cost += dense_rounds(C * nb, cus) * b;
     return cost;
 }
 
-int scan_block_size(const hypic_compose_desc* d) {
+int scan_block_size(const hypic_compose_desc* d, int cus) {
     if (d->scan_block > 0) return d->scan_block;
     const int64_t n = d->n_elem;
     if (d->kind != HYPIC_DENSE_DELTA) {
@@ -341,9 +349,9 @@ int scan_block_size(const hypic_compose_desc* d) {
         return std::max(b, 2);
     }
     int best = 2;
-    int64_t best_cost = dense_scan_cost(d, 2);
+    int64_t best_cost = dense_scan_cost(d, 2, cus);
     for (int64_t b = 3; b <= n; ++b) {
-        const int64_t c = dense_scan_cost(d, b);
+        const int64_t c = dense_scan_cost(d, b, cus);
         if (c < best_cost) {
             best_cost = c;
             best = (int)b;
@@ -352,11 +360,12 @@ int scan_block_size(const hypic_compose_desc* d) {
     return best;
 }
 
-hypic_compose_mode resolve_mode(const hypic_compose_desc* d) {
+hypic_compose_mode resolve_mode(const hypic_compose_desc* d, int cus) {
     if (d->mode != HYPIC_COMPOSE_AUTO) return d->mode;
     if (d->kind == HYPIC_DENSE_DELTA)
-        return (d->n_elem >= 4 && dense_scan_cost(d, scan_block_size(d)) < dense_fold_cost(d)) ? HYPIC_COMPOSE_SCAN
-                                                                                                  : HYPIC_COMPOSE_FOLD;
+        return (d->n_elem >= 4 && dense_scan_cost(d, scan_block_size(d, cus), cus) < dense_fold_cost(d, cus))
+                   ? HYPIC_COMPOSE_SCAN
+                   : HYPIC_COMPOSE_FOLD;
     // few chains cannot fill the GPU with one block per chain: use the blocked scan
     return (d->n_elem >= 16 && (int64_t)d->n_chain * 4 < 1024) ? HYPIC_COMPOSE_SCAN : HYPIC_COMPOSE_FOLD;
 }
@@ -394,7 +403,7 @@ hypic_status validate_compose(const hypic_compose_desc* d) {
                     d->n_elem);
     if (!d->S_final) return fail(HYPIC_ERR_INVALID_ARGUMENT, "compose: S_final is NULL");
     if (d->n_elem > 0 && !d->S) return fail(HYPIC_ERR_INVALID_ARGUMENT, "compose: S is NULL");
-    const hypic_compose_mode m = resolve_mode(d);
+    const hypic_compose_mode m = resolve_mode(d, planner_cus());
     if (m != HYPIC_COMPOSE_NAIVE_ADD && d->n_elem > 0 && (!d->T_hat || !d->T_exp))
         return fail(HYPIC_ERR_INVALID_ARGUMENT, "compose: T_hat and T_exp are required");
     if ((d->T_total == nullptr) != (d->T_total_exp == nullptr))
@@ -413,15 +422,17 @@ hypic_status validate_compose(const hypic_compose_desc* d) {
 
 size_t hypic_compose_workspace_bytes(const hypic_compose_desc* d) {
     if (!d || d->n_elem <= 0 || d->n_chain <= 0) return 0;
-    if (resolve_mode(d) != HYPIC_COMPOSE_SCAN) return 0;
-    const int B = scan_block_size(d);
+    const int cus = planner_cus();
+    if (resolve_mode(d, cus) != HYPIC_COMPOSE_SCAN) return 0;
+    const int B = scan_block_size(d, cus);
     return scan_layout(d, (d->n_elem + B - 1) / B).bytes;
 }
 
 hypic_status hypic_compose(const hypic_compose_desc* d, hypic_stream_t stream) {
     hypic_status st = validate_compose(d);
     if (st != HYPIC_OK) return st;
-    const hypic_compose_mode m = resolve_mode(d);
+    const int cus = planner_cus();
+    const hypic_compose_mode m = resolve_mode(d, cus);
     const int kind = d->kind == HYPIC_DENSE_DELTA ? 0 : (d->kind == HYPIC_DIAG ? 1 : 2);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const int D = d->d_k;
@@ -429,7 +440,7 @@ hypic_status hypic_compose(const hypic_compose_desc* d, hypic_stream_t stream) {
     int nblk = 1, B = d->n_elem;
     ScanLayout L;
     if (m == HYPIC_COMPOSE_SCAN && d->n_elem > 0) {
-        B = scan_block_size(d);
+        B = scan_block_size(d, cus);
         nblk = (d->n_elem + B - 1) / B;
         L = scan_layout(d, nblk);
         if (!d->workspace || d->workspace_bytes < L.bytes)
