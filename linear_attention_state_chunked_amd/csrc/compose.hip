@@ -170,22 +170,27 @@ __global__ __launch_bounds__(D * 6) void fold_dense_kernel(FoldArgs a) {
         floatx16 acc[NB];
 #pragma unroll
         for (int ob = 0; ob < NB; ++ob) acc[ob] = zero16();
+        // steps (kb, st, ob); the T_i fragments (hi, lo) of a step are read LA steps ahead
+        // (a ring of LA + 1) so that LDS latency hides behind the products of earlier steps
+        constexpr int NSTEP = NB * 2 * NB, LA = 1, NR = LA + 1;
+        auto tload = [&](int i, halfx8& ah, halfx8& al) {
+            const int ob = i % NB, ks = i / NB;  // ks = 2 kb + st
+            const int off = (32 * ob + l32) * RS + 16 * ks + 4 * half;
+            ah = t_frag(Th + off);
+            al = t_frag(Tl + off);
+        };
+        halfx8 fh[NR], fl[NR], bh, bl;
 #pragma unroll
-        for (int kb = 0; kb < NB; ++kb) {
+        for (int i = 0; i < LA; ++i) tload(i, fh[i], fl[i]);
 #pragma unroll
-            for (int st = 0; st < 2; ++st) {
-                halfx8 bh, bl;
-                split_hilo(X[kb], st, sc, bh, bl);
-#pragma unroll
-                for (int ob = 0; ob < NB; ++ob) {
-                    const int off = (32 * ob + l32) * RS + 32 * kb + 16 * st + 4 * half;
-                    const halfx8 ah = t_frag(Th + off);
-                    const halfx8 al = t_frag(Tl + off);
-                    acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, bh, acc[ob], 0, 0, 0);
-                    acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bl, acc[ob], 0, 0, 0);
-                    acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bh, acc[ob], 0, 0, 0);
-                }
-            }
+        for (int i = 0; i < NSTEP; ++i) {
+            if (i + LA < NSTEP) tload(i + LA, fh[(i + LA) % NR], fl[(i + LA) % NR]);
+            const int ob = i % NB, ks = i / NB;
+            if (ob == 0) split_hilo(X[ks >> 1], ks & 1, sc, bh, bl);
+            acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fl[i % NR], bh, acc[ob], 0, 0, 0);
+            acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fh[i % NR], bl, acc[ob], 0, 0, 0);
+            acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fh[i % NR], bh, acc[ob], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
         if (t_role) {
             // X = T_i (X 2^-sx): exponent += sx + e_i, then renormalise
