@@ -108,10 +108,24 @@ __device__ __forceinline__ void load8(const void* base, long long idx, bool bf16
 // ---------------------------------------------------------------------------------------
 // wave reductions (64 lanes)
 
+// Maximum over the 64 lanes with no LDS traffic: DPP lane permutations reduce each row of
+// 16 lanes (quad_perm [1,0,3,2], quad_perm [2,3,0,1], half-row mirror, row mirror), then
+// the four row maxima are read out with readlane.  A shuffle-based reduction issues six
+// ds_bpermute round trips, which queue behind the matrix-core kernels' fragment reads.
+template <int CTRL>
+__device__ __forceinline__ float dpp_perm(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
+    v = fmaxf(v, dpp_perm<0xb1>(v));    // quad_perm [1,0,3,2]
+    v = fmaxf(v, dpp_perm<0x4e>(v));    // quad_perm [2,3,0,1]
+    v = fmaxf(v, dpp_perm<0x141>(v));   // row_half_mirror
+    v = fmaxf(v, dpp_perm<0x140>(v));   // row_mirror
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {

@@ -12,13 +12,14 @@
 // Warp specialisation.  Carry waves own 32 columns of X each (T columns, then S
 // columns), keep them in matrix-core accumulators for the whole segment and run the
 // carry of chunk c; four preparation waves meanwhile solve chunk c+1 (gram, UT
-// transform) and stage K and gates of chunk c+2 under the gram products; the S waves
-// stage V of chunk c+1 at the end of their carry (16-bit inputs).  After the one workgroup barrier per chunk the carry waves turn the solve
-// into W' (T waves; stored as ready-made operand fragments) and U (S waves; kept in
-// their accumulators for the next carry) while the preparation waves go on with chunk c+2; K and the gamma
-// vectors are triple-buffered, V and the gate vectors doubled.  Bounded LDS counters
-// order the rest: the preparation waves' own stages, the carry waves' W' hand-off,
-// the reuse of the Tg buffer and two hand-offs inside the solve.
+// transform) and stage K and gates of chunk c+2 under the gram products.  After the one
+// workgroup barrier per chunk the carry waves turn the solve into W' (T waves; stored as
+// ready-made operand fragments) and U (S waves; kept in their accumulators for the next
+// carry) while the preparation waves go on with chunk c+2; with 16-bit inputs the S waves
+// then stage V of chunk c+2 while the T waves finish W'.  K and the gamma vectors are
+// triple-buffered, V and the gate vectors doubled.  Bounded LDS counters order the rest:
+// the preparation waves' own stages, the carry waves' W' hand-off, the reuse of the Tg
+// buffers (one arrival per carry wave and chunk) and two hand-offs inside the solve.
 //
 // Layout rules.  Every K / V tile in LDS is a natural row-major f16 tile written with
 // 16-byte stores.  Row fragments are plain 16-byte reads; column fragments (contraction
@@ -681,10 +682,12 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                         }
                     }
                     if constexpr (CV && !TR) {
-                        // V of chunk c+1 for U(c+1) after the barrier (its buffer held V(c-1),
-                        // consumed after the barrier before last), then the loads of chunk c+2
-                        if (c + 1 < nc) cv_stage(c + 1, sm, ln);
-                        if (c + 2 < nc) cv_prefetch(c + 2, ln);
+                        // V of chunk 0 for U(0) after the first barrier; later chunks are
+                        // staged after each U formation, off the barrier's critical path
+                        if (c < 0 && nc > 0) {
+                            cv_stage(0, sm, ln);
+                            if (nc > 1) cv_prefetch(1, ln);
+                        }
                     }
                     __syncthreads();  // preparation of chunk c+1 is complete
                     // From here the preparation waves go on to chunk c+2.  Its staging
@@ -722,8 +725,11 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                                 }
                             }
                         }
-                        // W'(c+1) formed (its Tg reads done): the forming waves count it
+                        // W'(c+1) formed (its Tg reads done): the forming waves count it on the
+                        // W' hand-off counter and, with T, on the Tg-reuse counter
                         if (TR || !WITH_T) count_arrival(sCnt + 1, ln);
+                        if (WITH_T && TR && ln == 0)
+                            __hip_atomic_fetch_add(sCnt + 2, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
                         if (!TR) {
                             // U(c+1) = Tg V for this wave's columns, both token halves per V fragment,
                             // formed beside W'(c+1) and carried into the next chunk in Vn
@@ -739,6 +745,14 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                             }
                             // Tg(c+1) consumed: the preparation of chunk c+2 may overwrite it
                             count_arrival(sCnt + 2, ln);
+                            if constexpr (CV) {
+                                // V of chunk c+2 into the buffer that held V(c) (read by U(c),
+                                // formed before the previous barrier), then the loads of c+3
+                                if (c + 2 < nc) {
+                                    cv_stage(c + 2, sm, ln);
+                                    if (c + 3 < nc) cv_prefetch(c + 3, ln);
+                                }
+                            }
                         }
                         // every carry wave waits for the whole of W'(c+1)
                         wait_count(sCnt + 1, NB * (c + 2));
@@ -893,8 +907,7 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                                      [&] {
                                          // Tg(c+1) overwrites Tg(c): wait until the carry waves
                                          // formed W'(c) and U(c)
-                                         wait_count(sCnt + 1, NB * (c + 1));
-                                         wait_count(sCnt + 2, NB * (c + 1));
+                                         wait_count(sCnt + 2, NC * (c + 1));
                                      },
                                      sCnt + 3, sCnt + 4, c + 2,
                                      [&] {
