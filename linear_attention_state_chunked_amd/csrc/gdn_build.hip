@@ -16,7 +16,7 @@
 // workgroup barrier per chunk the carry waves turn the solve into W' (T waves; stored as
 // ready-made operand fragments) and U (S waves; kept in their accumulators for the next
 // carry) while the preparation waves go on with chunk c+2; with 16-bit inputs the S waves
-// then stage V of chunk c+2 while the T waves finish W'.  K and the gamma vectors are
+// (or, in the fast plan, the T waves before the barrier) stage V.  K and the gamma vectors are
 // triple-buffered, V and the gate vectors doubled.  Bounded LDS counters order the rest:
 // the preparation waves' own stages, the carry waves' W' hand-off, the reuse of the Tg
 // buffers (one arrival per carry wave and chunk) and two hand-offs inside the solve.
@@ -460,7 +460,9 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
     constexpr int NB = D / 32;
     constexpr int NC = (WITH_T ? 2 : 1) * NB;   // carry waves
     constexpr int NP = 4;                       // preparation waves
-    constexpr bool CV = IN_BF16;                // V rows staged by the S carry waves
+    constexpr bool CV = IN_BF16;                // V rows staged by carry waves (else by the preparation waves)
+    constexpr bool VT = CV && WITH_T && !PT;    // ... by the T waves, in their idle tail before the barrier
+    constexpr bool VS = CV && !VT;              // ... by the S waves, after forming U
     constexpr int NT = (NC + NP) * 64;
     constexpr int RK = LY::RK, RT = LY::RT;
 
@@ -520,9 +522,10 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                 // workgroup barrier); the T waves start from zero
                 floatx16 Vn[2];
                 Vn[0] = Vn[1] = zero16();
-                // With 16-bit inputs the S waves stage the V rows, one chunk ahead of U: S wave sw
-                // owns rows RPW sw .. RPW sw + RPW - 1, four 16-byte pieces per lane (a row's
-                // pieces on consecutive lanes), loaded a chunk before they are stored.
+                // With 16-bit inputs the carry waves of one kind (T in the fast plan, else S) stage
+                // the V rows: wave sw of that kind owns rows RPW sw .. RPW sw + RPW - 1, four
+                // 16-byte pieces per lane (a row's pieces on consecutive lanes), loaded a chunk
+                // before they are stored.
                 constexpr int RPW = 64 / NB, CPR = D / 8;
                 constexpr int ESZ = IN_BF16 ? 2 : 4;
                 Raw8<IN_BF16> cv[4];
@@ -553,7 +556,7 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                             u32x4{pk_f16(x[0], x[1]), pk_f16(x[2], x[3]), pk_f16(x[4], x[5]), pk_f16(x[6], x[7])};
                     }
                 };
-                if constexpr (CV && !TR) {
+                if constexpr ((VS && !TR) || (VT && TR)) {
                     if (nc > 0) cv_prefetch(0, lane);
                 }
                 for (int c = -1; c < nc; ++c) {
@@ -681,13 +684,20 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                             }
                         }
                     }
-                    if constexpr (CV && !TR) {
+                    if constexpr (VS && !TR) {
                         // V of chunk 0 for U(0) after the first barrier; later chunks are
                         // staged after each U formation, off the barrier's critical path
                         if (c < 0 && nc > 0) {
                             cv_stage(0, sm, ln);
                             if (nc > 1) cv_prefetch(1, ln);
                         }
+                    }
+                    if constexpr (VT && TR) {
+                        // V of chunk c+1 for U(c+1) after the barrier (its buffer held V(c-1),
+                        // read by U(c-1) before the barrier before last), then the loads of
+                        // chunk c+2; the T waves reach the barrier early, the S waves late
+                        if (c + 1 < nc) cv_stage(c + 1, sm, ln);
+                        if (c + 2 < nc) cv_prefetch(c + 2, ln);
                     }
                     __syncthreads();  // preparation of chunk c+1 is complete
                     // From here the preparation waves go on to chunk c+2.  Its staging
@@ -745,7 +755,7 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                             }
                             // Tg(c+1) consumed: the preparation of chunk c+2 may overwrite it
                             count_arrival(sCnt + 2, ln);
-                            if constexpr (CV) {
+                            if constexpr (VS) {
                                 // V of chunk c+2 into the buffer that held V(c) (read by U(c),
                                 // formed before the previous barrier), then the loads of c+3
                                 if (c + 2 < nc) {
