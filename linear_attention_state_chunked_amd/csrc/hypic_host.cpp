@@ -600,7 +600,8 @@ hypic_status hypic_seam_advance(const hypic_seam_desc* d, hypic_stream_t stream)
     const int64_t dense = (int64_t)d->n_batch * d->h_v * d->d_k * d->d_v;
     const bool f32 = d->precision == HYPIC_PREC_F32 ||
                      (d->precision == HYPIC_PREC_AUTO && d->in_dtype == HYPIC_F32 && d->d_k == 64);
-    if (*std::max_element(len.begin(), len.end()) <= hypic::kSeamShort && d->d_k == d->d_v) {
+    const int w_max = *std::max_element(len.begin(), len.end());
+    if (w_max <= hypic::kSeamShort && d->d_k == d->d_v) {
         // short seams: closed rank-w form, fp32 arithmetic, every output in one launch
         hypic::SeamArgs q{};
         q.n_batch = d->n_batch;
@@ -626,7 +627,7 @@ hypic_status hypic_seam_advance(const hypic_seam_desc* d, hypic_stream_t stream)
         q.T_hat = d->T_hat;
         q.T_exp = d->T_exp;
         q.S_seam = d->S_seam;
-        e = hypic::launch_seam(q, d->d_k, s);
+        e = hypic::launch_seam(q, d->d_k, w_max, s);
         if (e != hipSuccess) return device_fail("seam: short-seam launch", e);
         return ok();
     }

@@ -135,7 +135,8 @@ hipError_t launch_fold(const FoldArgs& a, int d, int with_T, hipStream_t s);
 hipError_t launch_conv(const ConvArgs& a, long long total_tokens, hipStream_t s);
 // seams of at most kSeamShort tokens
 constexpr int kSeamShort = 16;
-hipError_t launch_seam(const SeamArgs& a, int d, hipStream_t s);
+// w_max: the longest seam (<= kSeamShort); seams of at most 8 tokens use a lighter instance
+hipError_t launch_seam(const SeamArgs& a, int d, int w_max, hipStream_t s);
 
 // resident workgroups per CU for the dense engine (for persistent grids)
 int dense_engine_max_lds(int d, int prec_f32, int with_q);

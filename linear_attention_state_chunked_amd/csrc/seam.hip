@@ -20,8 +20,10 @@
 
 namespace hypic {
 
+// W <= 8: at most 128 VGPRs (four waves per SIMD) and about 37 KB of LDS, so several
+// workgroups share a compute unit and hide each other's latency-bound w x w steps.
 template <int D, int W, bool IN_BF16>
-__global__ __launch_bounds__(4 * D) void seam_kernel(SeamArgs a) {
+__global__ __launch_bounds__(4 * D, W <= 8 ? 4 : 1) void seam_kernel(SeamArgs a) {
     constexpr int NT = 4 * D;
     constexpr int TPC = 4;               // threads per column
     constexpr int RPT = D / TPC;         // rows per thread
@@ -338,17 +340,18 @@ __global__ __launch_bounds__(4 * D) void seam_kernel(SeamArgs a) {
     }
 }
 
-template <int D>
-static hipError_t launch_seam_d(const SeamArgs& a, hipStream_t s) {
+template <int D, int W>
+static hipError_t launch_seam_w(const SeamArgs& a, hipStream_t s) {
     const dim3 grid(a.n_tasks);
-    if (a.in_bf16) hipLaunchKernelGGL((seam_kernel<D, kSeamShort, true>), grid, dim3(4 * D), 0, s, a);
-    else hipLaunchKernelGGL((seam_kernel<D, kSeamShort, false>), grid, dim3(4 * D), 0, s, a);
+    if (a.in_bf16) hipLaunchKernelGGL((seam_kernel<D, W, true>), grid, dim3(4 * D), 0, s, a);
+    else hipLaunchKernelGGL((seam_kernel<D, W, false>), grid, dim3(4 * D), 0, s, a);
     return hipGetLastError();
 }
 
-hipError_t launch_seam(const SeamArgs& a, int d, hipStream_t s) {
-    if (d == 128) return launch_seam_d<128>(a, s);
-    if (d == 64) return launch_seam_d<64>(a, s);
+hipError_t launch_seam(const SeamArgs& a, int d, int w_max, hipStream_t s) {
+    if (w_max > kSeamShort) return hipErrorInvalidValue;
+    if (d == 128) return w_max <= 8 ? launch_seam_w<128, 8>(a, s) : launch_seam_w<128, kSeamShort>(a, s);
+    if (d == 64) return w_max <= 8 ? launch_seam_w<64, 8>(a, s) : launch_seam_w<64, kSeamShort>(a, s);
     return hipErrorInvalidValue;
 }
 

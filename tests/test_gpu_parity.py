@@ -232,11 +232,12 @@ def test_diag_scalar_build_compose_and_naive(gpu, name, kind):
 # seam advance
 
 
-SEAM_WIDTHS = {"short": [1, 8, 16, 0, 5, 12, 3],          # all <= 16: closed rank-w kernel
+SEAM_WIDTHS = {"tiny": [1, 8, 0, 5, 8, 3, 2],              # all <= 8: closed rank-w kernel, 8-token instance
+               "short": [1, 8, 16, 0, 5, 12, 3],          # all <= 16: closed rank-w kernel
                "long": [1, 8, 8, 33, 64, 0, 70]}          # some > 16: chunked engine
 
 
-@pytest.mark.parametrize("widths", ["short", "long"])
+@pytest.mark.parametrize("widths", ["tiny", "short", "long"])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_seam_advance(gpu, dtype, widths):
     wl = WORKLOADS["gdn64k_bf16" if dtype == "bf16" else "tiny_gdn_f32"]
