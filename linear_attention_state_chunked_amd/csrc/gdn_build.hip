@@ -223,13 +223,14 @@ struct GLayout {
     static constexpr int zero_begin = TgA, zero_end = Gv;
 };
 
-// bounded LDS-counter barrier among a subset of waves (one arrival per wave)
+// bounded LDS-counter barrier among a subset of waves (one arrival per wave); the polls do
+// not sleep: a poll is one broadcast LDS read, and a sleep would add its wake-up delay to
+// every hand-off on the critical path
 __device__ __forceinline__ void prep_barrier(int* cnt, int target, int lane) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     if (lane == 0) __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     int spins = 0;
     while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target) {
-        __builtin_amdgcn_s_sleep(1);
         if (++spins > (1 << 22)) break;  // never hang: a broken invariant gives wrong data, not a hang
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
@@ -245,7 +246,6 @@ __device__ __forceinline__ void count_arrival(int* cnt, int lane) {
 __device__ __forceinline__ void wait_count(int* cnt, int target) {
     int spins = 0;
     while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target) {
-        __builtin_amdgcn_s_sleep(1);
         if (++spins > (1 << 22)) break;  // never hang: a broken invariant gives wrong data, not a hang
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
