@@ -324,26 +324,29 @@ __device__ __forceinline__ floatx4 inv16(floatx4 n, floatx4 nt, int lane) {
 }
 
 // Chunk-local UT transform, wave pw of four owning token block pw: from the staged K rows
-// (f16, row stride GLayout<D>::RK) and the gate vectors
-// (G log2 e, beta, beta gamma), L = strictly-lower(beta_i e^{G_i - G_j} K K^T) and
-// Tg = (I + L)^-1 diag(beta), written as its ten lower 16x16 blocks.  With D_b = (I + L_bb)^-1
-// and Inv the blocks of (I + L)^-1:
-//   Inv_10 = -D_1 L_10 D_0,  Inv_32 = -D_3 L_32 D_2                     (the two halves)
+// (f16, row stride GLayout<D>::RK) and the gate vectors (G log2 e, beta, beta gamma),
+// L = strictly-lower(beta_i e^{G_i - G_j} K K^T) and Tg = (I + L)^-1 diag(beta), written as
+// its ten lower 16x16 blocks.  With D_b = (I + L_bb)^-1 and Inv the blocks of (I + L)^-1:
+//   Inv_10 = -D_1 L_10 D_0,  Inv_32 = -D_3 L_32 D_2
 //   Q_b0 = L_b0 D_0 + L_b1 Inv_10,  Q_b1 = L_b1 D_1                     (b = 2, 3)
-//   Inv_2a = -D_2 Q_2a,  Inv_3a = -(Inv_32 Q_2a + D_3 Q_3a)             (lower-left quarter)
-// Work per wave: 0: D_0, Q_3. (gram blocks of row 3 against blocks 0, 1); 1: D_1, Inv_10;
-// 2: D_2, Q_2., Inv_2.; 3: D_3, Inv_32, Inv_3. .  side() runs while the gram products are in
-// flight.  pbar() orders the four waves, tg_wait() holds
-// the first Tg write until the previous Tg has been consumed; q2cnt / q3cnt hand Q_2. (wave 2)
-// and Q_3. (wave 0) to wave 3 (qtarget: arrivals so far in the task).
+//   Inv_2a = -D_2 Q_2a,  Inv_3a = -(Inv_32 Q_2a + D_3 Q_3a)
+// Phase 1, all four waves in parallel: the diagonal gram block (pw, pw) and D_pw; waves 0..2
+// also form two off-diagonal blocks of L each (0: L_30, L_31; 1: L_10, L_32; 2: L_20, L_21).
+// Every D_b and L_ba goes to an exchange slot; side() runs while the gram products are in
+// flight, tg_wait() holds the first Tg write until the previous Tg has been consumed.  One
+// barrier (pbar) among the four waves, then phase 2 without further hand-offs: wave 1 forms
+// Inv_10, wave 2 block row 2 and wave 3 block row 3, each recomputing the small shared
+// factors it needs (Inv_10, Q_2a) instead of waiting for another wave's.
 template <int D, class Bar, class Wait, class Side>
 __device__ __forceinline__ void ut_blocks(const _Float16* Kn1, const float* sGl, const float* sBeta,
                                           const float* sBG, _Float16* XB, _Float16* TgAT, _Float16* TgGT,
                                           _Float16* TgGlT, bool pt, int pw, int ln, Bar&& pbar, Wait&& tg_wait,
-                                          int* q2cnt, int* q3cnt, int qtarget, Side&& side) {
+                                          Side&& side) {
     constexpr int KS = D / 32, RK = GLayout<D>::RK;
     const int g = ln >> 4, cl = ln & 15;
     auto slot = [&](int i) { return XB + i * kXT; };
+    // exchange slots: D_b in slot b; L_10, L_20, L_21, L_30, L_31, L_32 in slots 4..9
+    auto lslot = [](int rb, int cb) { return rb == 1 ? 4 : rb == 2 ? 5 + cb : rb == 3 ? (cb < 2 ? 7 + cb : 9) : -1; };
     auto krow = [&](int blk, int ks) { return ld8(Kn1 + (16 * blk + cl) * RK + 32 * ks + 8 * g); };
     auto mma32 = [](halfx8 x, halfx8 y, floatx4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(x, y, c, 0, 0, 0); };
     // beta and beta gamma of this lane's column token in each block
@@ -353,48 +356,42 @@ __device__ __forceinline__ void ut_blocks(const _Float16* Kn1, const float* sGl,
         bcol[a] = sBeta[16 * a + cl];
         bgcol[a] = sBG[16 * a + cl];
     }
-    // ---- gram: diagonal block (pw, pw); transposed blocks (a, c) = K_a K_c^T, c the column block:
-    //      (a, pw) for a < pw on waves 1..3 except (0, 3), (1, 3), which wave 0 forms
+    // ---- gram: diagonal block (pw, pw); off-diagonal blocks G_{rb[i], cb[i]} = K_rb K_cb^T
+    //      in accumulator layout (rows: tokens of the later block rb, columns: block cb)
     halfx8 ka[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) ka[ks] = krow(pw, ks);
     floatx4 gd = zero4();
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) gd = mma32(ka[ks], ka[ks], gd);
-    floatx4 gt[2];
-    int ga[2] = {0, 0}, gc = pw;   // row blocks of gt[0..1] and their common column block
-    if (pw == 0) {
-        ga[0] = 0; ga[1] = 1; gc = 3;
-        gt[0] = gt[1] = zero4();
+    const bool has_off = pw < 3;
+    int rb[2] = {3, 3}, cb[2] = {0, 1};
+    if (pw == 1) { rb[0] = 1; cb[0] = 0; rb[1] = 3; cb[1] = 2; }
+    if (pw == 2) { rb[0] = 2; cb[0] = 0; rb[1] = 2; cb[1] = 1; }
+    floatx4 gt[2] = {zero4(), zero4()};
+    if (has_off) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const halfx8 k3 = krow(3, ks);
-            gt[0] = mma32(ka[ks], k3, gt[0]);
-            gt[1] = mma32(krow(1, ks), k3, gt[1]);
-        }
-    } else {
-        ga[0] = pw == 3 ? 2 : 0; ga[1] = 1;
-        gt[0] = gt[1] = zero4();
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            gt[0] = mma32(krow(ga[0], ks), ka[ks], gt[0]);
-            if (pw == 2) gt[1] = mma32(krow(1, ks), ka[ks], gt[1]);
+            const halfx8 k0r = krow(rb[0], ks), k1r = krow(rb[1], ks);
+            gt[0] = mma32(k0r, krow(cb[0], ks), gt[0]);
+            gt[1] = mma32(k1r, krow(cb[1], ks), gt[1]);
         }
     }
     // independent work (staging of a later chunk) while the gram products are in flight
     side();
-    // ---- gate factors: LT[i] = L_{gc, ga[i]}^T (rows of block ga[i], columns of block gc);
-    //      N = -L_{pw,pw} and N^T
-    floatx4 LT[2];
-    {
-        const int tc = 16 * gc + cl;
-        const float Gc = sGl[tc], Bc = sBeta[tc];
+    // ---- gate factors: L_{rb, cb}[r][c] = beta_r e^{G_r - G_c} G[r][c] (r later than c);
+    //      N = -L_{pw,pw} and N^T for the diagonal block
+    if (has_off) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const float4 gr = *reinterpret_cast<const float4*>(sGl + 16 * ga[i] + 4 * g);
-            const float grs[4] = {gr.x, gr.y, gr.z, gr.w};
+            const float Gc = sGl[16 * cb[i] + cl];
+            const float4 gr = *reinterpret_cast<const float4*>(sGl + 16 * rb[i] + 4 * g);
+            const float4 br = *reinterpret_cast<const float4*>(sBeta + 16 * rb[i] + 4 * g);
+            const float grs[4] = {gr.x, gr.y, gr.z, gr.w}, brs[4] = {br.x, br.y, br.z, br.w};
+            floatx4 l;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) LT[i][u] = Bc * __builtin_amdgcn_exp2f(Gc - grs[u]) * gt[i][u];
+            for (int u = 0; u < 4; ++u) l[u] = brs[u] * __builtin_amdgcn_exp2f(grs[u] - Gc) * gt[i][u];
+            st_cm(slot(lslot(rb[i], cb[i])), l, ln);
         }
     }
     floatx4 n, nt;
@@ -414,43 +411,44 @@ __device__ __forceinline__ void ut_blocks(const _Float16* Kn1, const float* sGl,
     // ---- diagonal block inverse D_pw
     const floatx4 Dm = inv16(n, nt, ln);
     st_cm(slot(pw), Dm, ln);
-    floatx4 q0 = zero4(), q1 = zero4();
     tg_wait();
     st_tg(TgAT, TgGT, TgGlT, pt, Dm, pw, pw, ln, bcol[pw], bgcol[pw]);
     pbar(ln);
-    // ---- the halves' off-diagonal blocks and the D_1 / D_0 terms of Q (D_pw as an A operand
-    //      comes back through the transposing read of its exchange tile)
-    const HL4 DT = ld_a(slot(pw), ln);
-    if (pw == 1 || pw == 3) {
-        const int a = pw - 1;
-        const floatx4 pr = mm16(split4v(LT[0]), ld_b(slot(a), ln), zero4());  // L_{pw,a} D_a
-        const floatx4 iv = -mm16(DT, split4v(pr), zero4());                   // -D_pw L_{pw,a} D_a
-        st_cm(slot(pw == 1 ? 4 : 5), iv, ln);
-        st_tg(TgAT, TgGT, TgGlT, pt, iv, pw, a, ln, bcol[a], bgcol[a]);
-    } else {
-        q1 = mm16(split4v(LT[1]), ld_b(slot(1), ln), zero4());   // Q_b1 = L_{b,1} D_1
-        st_cm(slot(pw == 2 ? 7 : 9), q1, ln);
-        q0 = mm16(split4v(LT[0]), ld_b(slot(0), ln), zero4());   // L_{b,0} D_0
+    // ---- phase 2.  A transposing read (ld_a) of a slot gives that tile as an A operand, a
+    //      plain read (ld_b) as a B operand; an accumulator tile is a B operand as it is.
+    if (pw == 0) return;
+    const HL4 D0b = ld_b(slot(0), ln), D1a = ld_a(slot(1), ln), L10a = ld_a(slot(4), ln);
+    // Inv_10 = -D_1 (L_10 D_0)
+    const floatx4 inv10 = -mm16(D1a, split4v(mm16(L10a, D0b, zero4())), zero4());
+    if (pw == 1) {
+        st_tg(TgAT, TgGT, TgGlT, pt, inv10, 1, 0, ln, bcol[0], bgcol[0]);
+        return;
     }
-    pbar(ln);
-    // ---- lower-left quarter: the Q_.1 terms are ready, the Q_.0 terms need Inv_10
-    if (pw == 0 || pw == 2) {
-        q0 = mm16(split4v(LT[1]), ld_b(slot(4), ln), q0);        // Q_b0 = ... + L_{b,1} Inv_10
-        st_cm(slot(pw == 2 ? 6 : 8), q0, ln);
-        count_arrival(pw == 2 ? q2cnt : q3cnt, ln);
-        if (pw == 2) {
-            st_tg(TgAT, TgGT, TgGlT, pt, -mm16(DT, split4v(q1), zero4()), 2, 1, ln, bcol[1], bgcol[1]);
-            st_tg(TgAT, TgGT, TgGlT, pt, -mm16(DT, split4v(q0), zero4()), 2, 0, ln, bcol[0], bgcol[0]);
-        }
-    } else if (pw == 3) {
-        const HL4 A32 = ld_a(slot(5), ln);
-        const floatx4 r1 = mm16(A32, ld_b(slot(7), ln), mm16(DT, ld_b(slot(9), ln), zero4()));
-        st_tg(TgAT, TgGT, TgGlT, pt, -r1, 3, 1, ln, bcol[1], bgcol[1]);
-        wait_count(q2cnt, qtarget);
-        wait_count(q3cnt, qtarget);
-        const floatx4 r0 = mm16(A32, ld_b(slot(6), ln), mm16(DT, ld_b(slot(8), ln), zero4()));
-        st_tg(TgAT, TgGT, TgGlT, pt, -r0, 3, 0, ln, bcol[0], bgcol[0]);
+    // Q_b0 = L_b0 D_0 + L_b1 Inv_10 and Q_b1 = L_b1 D_1 for b = 2 (and b = 3 on wave 3)
+    const HL4 D1b = ld_b(slot(1), ln), L20a = ld_a(slot(5), ln), L21a = ld_a(slot(6), ln);
+    const HL4 I10 = split4v(inv10);
+    const floatx4 q21 = mm16(L21a, D1b, zero4());
+    const floatx4 q20 = mm16(L21a, I10, mm16(L20a, D0b, zero4()));
+    if (pw == 2) {
+        const HL4 D2a = ld_a(slot(2), ln);
+        st_tg(TgAT, TgGT, TgGlT, pt, -mm16(D2a, split4v(q21), zero4()), 2, 1, ln, bcol[1], bgcol[1]);
+        st_tg(TgAT, TgGT, TgGlT, pt, -mm16(D2a, split4v(q20), zero4()), 2, 0, ln, bcol[0], bgcol[0]);
+        return;
     }
+    // wave 3: Inv_32 = -D_3 (L_32 D_2), then Inv_3a = -(Inv_32 Q_2a + D_3 Q_3a)
+    const HL4 D2b = ld_b(slot(2), ln), D3a = ld_a(slot(3), ln), L30a = ld_a(slot(7), ln),
+              L31a = ld_a(slot(8), ln), L32a = ld_a(slot(9), ln);
+    const floatx4 q31 = mm16(L31a, D1b, zero4());
+    const floatx4 q30 = mm16(L31a, I10, mm16(L30a, D0b, zero4()));
+    const floatx4 inv32 = -mm16(D3a, split4v(mm16(L32a, D2b, zero4())), zero4());
+    st_tg(TgAT, TgGT, TgGlT, pt, inv32, 3, 2, ln, bcol[2], bgcol[2]);
+    // Inv_32 as an A operand: through slot 9 (L_32, read above by this wave only)
+    st_cm(slot(9), inv32, ln);
+    const HL4 I32a = ld_a(slot(9), ln);
+    const floatx4 r1 = mm16(I32a, split4v(q21), mm16(D3a, split4v(q31), zero4()));
+    st_tg(TgAT, TgGT, TgGlT, pt, -r1, 3, 1, ln, bcol[1], bgcol[1]);
+    const floatx4 r0 = mm16(I32a, split4v(q20), mm16(D3a, split4v(q30), zero4()));
+    st_tg(TgAT, TgGT, TgGlT, pt, -r0, 3, 0, ln, bcol[0], bgcol[0]);
 }
 
 template <int D, bool WITH_T, bool IN_BF16, bool PERSIST, bool PT>
@@ -463,6 +461,7 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
     constexpr bool CV = IN_BF16;                // V rows staged by carry waves (else by the preparation waves)
     constexpr bool VT = CV && WITH_T && !PT;    // ... by the T waves, in their idle tail before the barrier
     constexpr bool VS = CV && !VT;              // ... by the S waves, after forming U
+    constexpr bool RL = VT;                     // T columns renormalised after the barrier (else before)
     constexpr int NT = (NC + NP) * 64;
     constexpr int RK = LY::RK, RT = LY::RT;
 
@@ -518,6 +517,25 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                     for (int j = 0; j < 16; ++j)
                         X[xb][j] = (TR && 32 * xb + 8 * (j >> 2) + (j & 3) == diag) ? 1.f : 0.f;
                 int ew = 0;
+                // T columns: rescale by an exact power of two so that max |X_T| lies in [0.5, 1)
+                // (f16 operands never underflow).  Branch-free; in the fast 16-bit plan it runs
+                // after the barrier under the latency of the W' formation's fragment reads (X is
+                // private to the wave), elsewhere at the end of the carry (registers)
+                auto renorm = [&] {
+                    float m = 0.f;
+#pragma unroll
+                    for (int xb = 0; xb < NB; ++xb)
+#pragma unroll
+                        for (int j = 0; j < 16; j += 2) m = fmaxf(m, fmaxf(fabsf(X[xb][j]), fabsf(X[xb][j + 1])));
+                    const int e = exp2_of(wave_max(m));
+                    if (RL || e != 0) {
+#pragma unroll
+                        for (int xb = 0; xb < NB; ++xb)
+#pragma unroll
+                            for (int j = 0; j < 16; ++j) X[xb][j] = ldexpf(X[xb][j], -e);
+                        ew += e;
+                    }
+                };
                 // S waves enter chunk c holding U(c) = Tg(c) V(c) in Vn (formed after the previous
                 // workgroup barrier); the T waves start from zero
                 floatx16 Vn[2];
@@ -668,21 +686,7 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                                 __builtin_amdgcn_sched_barrier(0);
                             }
                         }
-                        if (TR) {
-                            float m = 0.f;
-#pragma unroll
-                            for (int xb = 0; xb < NB; ++xb)
-#pragma unroll
-                                for (int j = 0; j < 16; j += 2) m = fmaxf(m, fmaxf(fabsf(X[xb][j]), fabsf(X[xb][j + 1])));
-                            const int e = exp2_of(wave_max(m));
-                            if (e != 0) {
-#pragma unroll
-                                for (int xb = 0; xb < NB; ++xb)
-#pragma unroll
-                                    for (int j = 0; j < 16; ++j) X[xb][j] = ldexpf(X[xb][j], -e);
-                                ew += e;
-                            }
-                        }
+                        if (!RL && TR) renorm();
                     }
                     if constexpr (VS && !TR) {
                         // V of chunk 0 for U(0) after the first barrier; later chunks are
@@ -694,10 +698,10 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                     }
                     if constexpr (VT && TR) {
                         // V of chunk c+1 for U(c+1) after the barrier (its buffer held V(c-1),
-                        // read by U(c-1) before the barrier before last), then the loads of
-                        // chunk c+2; the T waves reach the barrier early, the S waves late
+                        // read by U(c-1) before the barrier before last); the T waves reach the
+                        // barrier early, the S waves late.  The loads of chunk c+2 are issued
+                        // after the W' formation below.
                         if (c + 1 < nc) cv_stage(c + 1, sm, ln);
-                        if (c + 2 < nc) cv_prefetch(c + 2, ln);
                     }
                     __syncthreads();  // preparation of chunk c+1 is complete
                     // From here the preparation waves go on to chunk c+2.  Its staging
@@ -713,25 +717,44 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                         // fragments of W' X in the carry, stored in that order
                         if (TR || !WITH_T) {
                             const int dt = wave;
-#pragma unroll
-                            for (int mt = 0; mt < 2; ++mt) {
-                                floatx16 acc = zero16();
-#pragma unroll
-                                for (int kk = 0; kk < 4; ++kk) {
-                                    const halfx8 fa = colfrag_nat(Kn1, RK, 0, 32 * dt, kk, ln);
-                                    const halfx8 fb = colfrag_nat(TgG, RT, 0, 32 * mt, kk, ln);
-                                    if (PT) {
-                                        const halfx8 fl = colfrag_nat(TgGl, RT, 0, 32 * mt, kk, ln);
-                                        acc = OpF16::mma(fa, fl, acc);
-                                    }
-                                    acc = OpF16::mma(fa, fb, acc);
-                                }
+                            auto store_w = [&](int mt, const floatx16& acc) {
 #pragma unroll
                                 for (int st = 0; st < 2; ++st) {
                                     halfx8 w;
 #pragma unroll
                                     for (int i = 0; i < 8; ++i) w[i] = (_Float16)(-acc[8 * st + i]);
                                     *reinterpret_cast<halfx8*>(Wf1 + (((mt * NB + dt) * 2 + st) * 64 + ln) * 8) = w;
+                                }
+                            };
+                            if constexpr (PT) {
+#pragma unroll
+                                for (int mt = 0; mt < 2; ++mt) {
+                                    floatx16 acc = zero16();
+#pragma unroll
+                                    for (int kk = 0; kk < 4; ++kk) {
+                                        const halfx8 fa = colfrag_nat(Kn1, RK, 0, 32 * dt, kk, ln);
+                                        acc = OpF16::mma(fa, colfrag_nat(TgGl, RT, 0, 32 * mt, kk, ln), acc);
+                                        acc = OpF16::mma(fa, colfrag_nat(TgG, RT, 0, 32 * mt, kk, ln), acc);
+                                    }
+                                    store_w(mt, acc);
+                                }
+                            } else {
+                                // all fragments in flight first; the renormalisation of the previous
+                                // chunk's T columns runs under their latency
+                                halfx8 fa[4], fb[4];
+#pragma unroll
+                                for (int kk = 0; kk < 4; ++kk) {
+                                    fa[kk] = colfrag_nat(Kn1, RK, 0, 32 * dt, kk, ln);
+                                    fb[kk] = colfrag_nat(TgG, RT, 0, 0, kk, ln);
+                                }
+                                if (RL && TR && c >= 0) renorm();
+#pragma unroll
+                                for (int mt = 0; mt < 2; ++mt) {
+                                    floatx16 acc = zero16();
+#pragma unroll
+                                    for (int kk = 0; kk < 4; ++kk)
+                                        acc = OpF16::mma(fa[kk], mt == 0 ? fb[kk] : colfrag_nat(TgG, RT, 0, 32, kk, ln), acc);
+                                    store_w(mt, acc);
                                 }
                             }
                         }
@@ -740,6 +763,9 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                         if (TR || !WITH_T) count_arrival(sCnt + 1, ln);
                         if (WITH_T && TR && ln == 0)
                             __hip_atomic_fetch_add(sCnt + 2, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                        if constexpr (VT && TR) {
+                            if (c + 2 < nc) cv_prefetch(c + 2, ln);
+                        }
                         if (!TR) {
                             // U(c+1) = Tg V for this wave's columns, both token halves per V fragment,
                             // formed beside W'(c+1) and carried into the next chunk in Vn
@@ -766,6 +792,8 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                         }
                         // every carry wave waits for the whole of W'(c+1)
                         wait_count(sCnt + 1, NB * (c + 2));
+                    } else if (RL && TR && c >= 0) {
+                        renorm();   // last chunk
                     }
                 }
                 // epilogue: align the T waves' exponents, write T_hat / T_exp / S
@@ -919,7 +947,6 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                                          // formed W'(c) and U(c)
                                          wait_count(sCnt + 2, NC * (c + 1));
                                      },
-                                     sCnt + 3, sCnt + 4, c + 2,
                                      [&] {
                                          if (c + 2 < nc) {
                                              stage_kg(c + 2, sm, ln);
