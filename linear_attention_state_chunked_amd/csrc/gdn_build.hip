@@ -459,9 +459,9 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
     constexpr int NC = (WITH_T ? 2 : 1) * NB;   // carry waves
     constexpr int NP = 4;                       // preparation waves
     constexpr bool CV = IN_BF16;                // V rows staged by carry waves (else by the preparation waves)
-    constexpr bool VT = CV && WITH_T && !PT;    // ... by the T waves, in their idle tail before the barrier
-    constexpr bool VS = CV && !VT;              // ... by the S waves, after forming U
-    constexpr bool RL = VT;                     // T columns renormalised after the barrier (else before)
+    constexpr bool VS = CV;                     // ... by the S waves, after forming U
+    constexpr bool VT = CV && WITH_T && !PT;    // ... and, in the fast plan, half of them by the T waves
+                                                //     in their idle tail before the barrier
     constexpr int NT = (NC + NP) * 64;
     constexpr int RK = LY::RK, RT = LY::RT;
 
@@ -518,17 +518,19 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                         X[xb][j] = (TR && 32 * xb + 8 * (j >> 2) + (j & 3) == diag) ? 1.f : 0.f;
                 int ew = 0;
                 // T columns: rescale by an exact power of two so that max |X_T| lies in [0.5, 1)
-                // (f16 operands never underflow).  Branch-free; in the fast 16-bit plan it runs
-                // after the barrier under the latency of the W' formation's fragment reads (X is
-                // private to the wave), elsewhere at the end of the carry (registers)
+                // (f16 operands never underflow).  The NaN-propagating maximum maps to gfx950's
+                // three-input maximum with |.| source modifiers (fmaxf would first canonicalise
+                // every input: twice the instructions)
                 auto renorm = [&] {
                     float m = 0.f;
 #pragma unroll
                     for (int xb = 0; xb < NB; ++xb)
 #pragma unroll
-                        for (int j = 0; j < 16; j += 2) m = fmaxf(m, fmaxf(fabsf(X[xb][j]), fabsf(X[xb][j + 1])));
+                        for (int j = 0; j < 16; j += 2)
+                            m = __builtin_elementwise_maximum(
+                                m, __builtin_elementwise_maximum(__builtin_fabsf(X[xb][j]), __builtin_fabsf(X[xb][j + 1])));
                     const int e = exp2_of(wave_max(m));
-                    if (RL || e != 0) {
+                    if (e != 0) {
 #pragma unroll
                         for (int xb = 0; xb < NB; ++xb)
 #pragma unroll
@@ -540,14 +542,14 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                 // workgroup barrier); the T waves start from zero
                 floatx16 Vn[2];
                 Vn[0] = Vn[1] = zero16();
-                // With 16-bit inputs the carry waves of one kind (T in the fast plan, else S) stage
-                // the V rows: wave sw of that kind owns rows RPW sw .. RPW sw + RPW - 1, four
-                // 16-byte pieces per lane (a row's pieces on consecutive lanes), loaded a chunk
-                // before they are stored.
-                constexpr int RPW = 64 / NB, CPR = D / 8;
+                // With 16-bit inputs the S waves (and in the fast plan also the T waves) stage the
+                // V rows: staging wave sw of NVW owns rows RPW sw .. RPW sw + RPW - 1, NQ 16-byte
+                // pieces per lane (a row's pieces on consecutive lanes), loaded well before they
+                // are stored.
+                constexpr int NVW = VT ? 2 * NB : NB, RPW = 64 / NVW, CPR = D / 8, NQ = RPW * CPR / 64;
                 constexpr int ESZ = IN_BF16 ? 2 : 4;
-                Raw8<IN_BF16> cv[4];
-                const int sw = (WITH_T && !TR) ? wave - NB : wave;
+                Raw8<IN_BF16> cv[NQ];
+                const int sw = (VT || !(WITH_T && !TR)) ? wave : wave - NB;
                 const unsigned vstride = (unsigned)a.h_v * (D * ESZ);
                 const unsigned char* vb0 =
                     reinterpret_cast<const unsigned char*>(a.v) + (((long long)b * N + start) * a.h_v + h) * (D * ESZ);
@@ -555,7 +557,7 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                     const int valid = min(64, len - 64 * cc);
                     const unsigned char* base = vb0 + (long long)(64 * cc) * vstride;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
+                    for (int q = 0; q < NQ; ++q) {
                         const int t = RPW * sw + (64 * q + ln) / CPR, ch = (64 * q + ln) % CPR;
                         if (t < valid)
                             cv[q].loadp(base + (t * vstride + ch * 8 * ESZ));
@@ -566,7 +568,7 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                 auto cv_stage = [&](int cc, unsigned char* sm, int ln) {
                     E* dst = reinterpret_cast<E*>(sm + LY::Vn + (cc & 1) * LY::sz_K);
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
+                    for (int q = 0; q < NQ; ++q) {
                         const int t = RPW * sw + (64 * q + ln) / CPR, ch = (64 * q + ln) % CPR;
                         float x[8];
                         cv[q].get(x);
@@ -686,7 +688,7 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                                 __builtin_amdgcn_sched_barrier(0);
                             }
                         }
-                        if (!RL && TR) renorm();
+                        if (TR) renorm();
                     }
                     if constexpr (VS && !TR) {
                         // V of chunk 0 for U(0) after the first barrier; later chunks are
@@ -739,15 +741,13 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                                     store_w(mt, acc);
                                 }
                             } else {
-                                // all fragments in flight first; the renormalisation of the previous
-                                // chunk's T columns runs under their latency
+                                // the fragments of the first half in flight before the products
                                 halfx8 fa[4], fb[4];
 #pragma unroll
                                 for (int kk = 0; kk < 4; ++kk) {
                                     fa[kk] = colfrag_nat(Kn1, RK, 0, 32 * dt, kk, ln);
                                     fb[kk] = colfrag_nat(TgG, RT, 0, 0, kk, ln);
                                 }
-                                if (RL && TR && c >= 0) renorm();
 #pragma unroll
                                 for (int mt = 0; mt < 2; ++mt) {
                                     floatx16 acc = zero16();
@@ -792,8 +792,6 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                         }
                         // every carry wave waits for the whole of W'(c+1)
                         wait_count(sCnt + 1, NB * (c + 2));
-                    } else if (RL && TR && c >= 0) {
-                        renorm();   // last chunk
                     }
                 }
                 // epilogue: align the T waves' exponents, write T_hat / T_exp / S
