@@ -212,8 +212,8 @@ struct GLayout {
     static constexpr int Wf = Kn + 3 * sz_K;           // -W'^T operand fragments
     static constexpr int Sc = Wf + sz_Wf;              // Gamma/gamma_i, Gamma (fp32, x3)
     static constexpr int Vn = Sc + 3 * sz_Sc;          // V rows (x2)
-    static constexpr int XB = Vn + 2 * sz_K;           // ten 16x16 exchange slots (hi, lo)
-    static constexpr int TgA = XB + 10 * kXT * 2;      // Tg, token-column-major
+    static constexpr int XB = Vn + 2 * sz_K;           // twelve 16x16 exchange slots (hi, lo)
+    static constexpr int TgA = XB + 12 * kXT * 2;      // Tg, token-column-major
     static constexpr int TgG = TgA + sz_T64;           // Tg diag(gamma)
     static constexpr int TgGl = TgG + sz_T64;          // its low part (precise-T plan)
     static constexpr int Gv = TgGl + sz_T64;           // G log2 e, beta, beta gamma (fp32, x2)
@@ -330,13 +330,13 @@ __device__ __forceinline__ floatx4 inv16(floatx4 n, floatx4 nt, int lane) {
 //   Inv_10 = -D_1 L_10 D_0,  Inv_32 = -D_3 L_32 D_2
 //   Q_b0 = L_b0 D_0 + L_b1 Inv_10,  Q_b1 = L_b1 D_1                     (b = 2, 3)
 //   Inv_2a = -D_2 Q_2a,  Inv_3a = -(Inv_32 Q_2a + D_3 Q_3a)
-// Phase 1, all four waves in parallel: the diagonal gram block (pw, pw) and D_pw; waves 0..2
-// also form two off-diagonal blocks of L each (0: L_30, L_31; 1: L_10, L_32; 2: L_20, L_21).
-// Every D_b and L_ba goes to an exchange slot; side() runs while the gram products are in
-// flight, tg_wait() holds the first Tg write until the previous Tg has been consumed.  One
-// barrier (pbar) among the four waves, then phase 2 without further hand-offs: wave 1 forms
-// Inv_10, wave 2 block row 2 and wave 3 block row 3, each recomputing the small shared
-// factors it needs (Inv_10, Q_2a) instead of waiting for another wave's.
+// Phase 1, all four waves in parallel: the diagonal gram block (pw, pw) and D_pw, and the
+// off-diagonal blocks of L (0: L_30, L_31; 1: L_10; 2: L_20, L_21; 3: L_32).  Every D_b and
+// L_ba goes to an exchange slot; side() runs while the gram products are in flight, tg_wait()
+// holds the first Tg write until the previous Tg has been consumed.  One barrier (pbar) among
+// the four waves, then phase 2 without further hand-offs: wave 1 forms Inv_10, wave 2 block
+// row 2, wave 0 Inv_32 and Inv_31, wave 3 Inv_30; each recomputes the small shared factors
+// it needs (Inv_10, Inv_32, Q) instead of waiting for another wave's.
 template <int D, class Bar, class Wait, class Side>
 __device__ __forceinline__ void ut_blocks(const _Float16* Kn1, const float* sGl, const float* sBeta,
                                           const float* sBG, _Float16* XB, _Float16* TgAT, _Float16* TgGT,
@@ -345,7 +345,8 @@ __device__ __forceinline__ void ut_blocks(const _Float16* Kn1, const float* sGl,
     constexpr int KS = D / 32, RK = GLayout<D>::RK;
     const int g = ln >> 4, cl = ln & 15;
     auto slot = [&](int i) { return XB + i * kXT; };
-    // exchange slots: D_b in slot b; L_10, L_20, L_21, L_30, L_31, L_32 in slots 4..9
+    // exchange slots: D_b in slot b; L_10, L_20, L_21, L_30, L_31, L_32 in slots 4..9; slots 10
+    // and 11 are private to waves 0 and 3 (Inv_32 turned into an A operand)
     auto lslot = [](int rb, int cb) { return rb == 1 ? 4 : rb == 2 ? 5 + cb : rb == 3 ? (cb < 2 ? 7 + cb : 9) : -1; };
     auto krow = [&](int blk, int ks) { return ld8(Kn1 + (16 * blk + cl) * RK + 32 * ks + 8 * g); };
     auto mma32 = [](halfx8 x, halfx8 y, floatx4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(x, y, c, 0, 0, 0); };
@@ -364,26 +365,24 @@ __device__ __forceinline__ void ut_blocks(const _Float16* Kn1, const float* sGl,
     floatx4 gd = zero4();
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) gd = mma32(ka[ks], ka[ks], gd);
-    const bool has_off = pw < 3;
+    const int n_off = (pw == 0 || pw == 2) ? 2 : 1;
     int rb[2] = {3, 3}, cb[2] = {0, 1};
-    if (pw == 1) { rb[0] = 1; cb[0] = 0; rb[1] = 3; cb[1] = 2; }
+    if (pw == 1) { rb[0] = 1; cb[0] = 0; }
     if (pw == 2) { rb[0] = 2; cb[0] = 0; rb[1] = 2; cb[1] = 1; }
+    if (pw == 3) { rb[0] = 3; cb[0] = 2; }
     floatx4 gt[2] = {zero4(), zero4()};
-    if (has_off) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const halfx8 k0r = krow(rb[0], ks), k1r = krow(rb[1], ks);
-            gt[0] = mma32(k0r, krow(cb[0], ks), gt[0]);
-            gt[1] = mma32(k1r, krow(cb[1], ks), gt[1]);
-        }
+    for (int ks = 0; ks < KS; ++ks) {
+        gt[0] = mma32(krow(rb[0], ks), krow(cb[0], ks), gt[0]);
+        if (n_off > 1) gt[1] = mma32(krow(rb[1], ks), krow(cb[1], ks), gt[1]);
     }
     // independent work (staging of a later chunk) while the gram products are in flight
     side();
     // ---- gate factors: L_{rb, cb}[r][c] = beta_r e^{G_r - G_c} G[r][c] (r later than c);
     //      N = -L_{pw,pw} and N^T for the diagonal block
-    if (has_off) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < 2; ++i) {
+        if (i < n_off) {
             const float Gc = sGl[16 * cb[i] + cl];
             const float4 gr = *reinterpret_cast<const float4*>(sGl + 16 * rb[i] + 4 * g);
             const float4 br = *reinterpret_cast<const float4*>(sBeta + 16 * rb[i] + 4 * g);
@@ -416,7 +415,18 @@ __device__ __forceinline__ void ut_blocks(const _Float16* Kn1, const float* sGl,
     pbar(ln);
     // ---- phase 2.  A transposing read (ld_a) of a slot gives that tile as an A operand, a
     //      plain read (ld_b) as a B operand; an accumulator tile is a B operand as it is.
-    if (pw == 0) return;
+    if (pw == 0) {
+        // Inv_32 and Inv_31 = -(Inv_32 Q_21 + D_3 Q_31)
+        const HL4 D1b = ld_b(slot(1), ln), D2b = ld_b(slot(2), ln), D3a = ld_a(slot(3), ln);
+        const HL4 L21a = ld_a(slot(6), ln), L31a = ld_a(slot(8), ln), L32a = ld_a(slot(9), ln);
+        const floatx4 inv32 = -mm16(D3a, split4v(mm16(L32a, D2b, zero4())), zero4());
+        st_cm(slot(10), inv32, ln);
+        st_tg(TgAT, TgGT, TgGlT, pt, inv32, 3, 2, ln, bcol[2], bgcol[2]);
+        const floatx4 q21 = mm16(L21a, D1b, zero4()), q31 = mm16(L31a, D1b, zero4());
+        const floatx4 r1 = mm16(ld_a(slot(10), ln), split4v(q21), mm16(D3a, split4v(q31), zero4()));
+        st_tg(TgAT, TgGT, TgGlT, pt, -r1, 3, 1, ln, bcol[1], bgcol[1]);
+        return;
+    }
     const HL4 D0b = ld_b(slot(0), ln), D1a = ld_a(slot(1), ln), L10a = ld_a(slot(4), ln);
     // Inv_10 = -D_1 (L_10 D_0)
     const floatx4 inv10 = -mm16(D1a, split4v(mm16(L10a, D0b, zero4())), zero4());
@@ -424,30 +434,24 @@ __device__ __forceinline__ void ut_blocks(const _Float16* Kn1, const float* sGl,
         st_tg(TgAT, TgGT, TgGlT, pt, inv10, 1, 0, ln, bcol[0], bgcol[0]);
         return;
     }
-    // Q_b0 = L_b0 D_0 + L_b1 Inv_10 and Q_b1 = L_b1 D_1 for b = 2 (and b = 3 on wave 3)
-    const HL4 D1b = ld_b(slot(1), ln), L20a = ld_a(slot(5), ln), L21a = ld_a(slot(6), ln);
+    const HL4 L20a = ld_a(slot(5), ln), L21a = ld_a(slot(6), ln);
     const HL4 I10 = split4v(inv10);
-    const floatx4 q21 = mm16(L21a, D1b, zero4());
+    // Q_20 = L_20 D_0 + L_21 Inv_10
     const floatx4 q20 = mm16(L21a, I10, mm16(L20a, D0b, zero4()));
     if (pw == 2) {
-        const HL4 D2a = ld_a(slot(2), ln);
+        const HL4 D1b = ld_b(slot(1), ln), D2a = ld_a(slot(2), ln);
+        const floatx4 q21 = mm16(L21a, D1b, zero4());
         st_tg(TgAT, TgGT, TgGlT, pt, -mm16(D2a, split4v(q21), zero4()), 2, 1, ln, bcol[1], bgcol[1]);
         st_tg(TgAT, TgGT, TgGlT, pt, -mm16(D2a, split4v(q20), zero4()), 2, 0, ln, bcol[0], bgcol[0]);
         return;
     }
-    // wave 3: Inv_32 = -D_3 (L_32 D_2), then Inv_3a = -(Inv_32 Q_2a + D_3 Q_3a)
+    // wave 3: Inv_30 = -(Inv_32 Q_20 + D_3 Q_30), Q_30 = L_30 D_0 + L_31 Inv_10
     const HL4 D2b = ld_b(slot(2), ln), D3a = ld_a(slot(3), ln), L30a = ld_a(slot(7), ln),
               L31a = ld_a(slot(8), ln), L32a = ld_a(slot(9), ln);
-    const floatx4 q31 = mm16(L31a, D1b, zero4());
-    const floatx4 q30 = mm16(L31a, I10, mm16(L30a, D0b, zero4()));
     const floatx4 inv32 = -mm16(D3a, split4v(mm16(L32a, D2b, zero4())), zero4());
-    st_tg(TgAT, TgGT, TgGlT, pt, inv32, 3, 2, ln, bcol[2], bgcol[2]);
-    // Inv_32 as an A operand: through slot 9 (L_32, read above by this wave only)
-    st_cm(slot(9), inv32, ln);
-    const HL4 I32a = ld_a(slot(9), ln);
-    const floatx4 r1 = mm16(I32a, split4v(q21), mm16(D3a, split4v(q31), zero4()));
-    st_tg(TgAT, TgGT, TgGlT, pt, -r1, 3, 1, ln, bcol[1], bgcol[1]);
-    const floatx4 r0 = mm16(I32a, split4v(q20), mm16(D3a, split4v(q30), zero4()));
+    st_cm(slot(11), inv32, ln);
+    const floatx4 q30 = mm16(L31a, I10, mm16(L30a, D0b, zero4()));
+    const floatx4 r0 = mm16(ld_a(slot(11), ln), split4v(q20), mm16(D3a, split4v(q30), zero4()));
     st_tg(TgAT, TgGT, TgGlT, pt, -r0, 3, 0, ln, bcol[0], bgcol[0]);
 }
 
