@@ -920,7 +920,7 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                 };
                 // the preparation waves are the critical path of every chunk: let their few
                 // instructions issue ahead of the carry waves' (matrix-core bound) stream
-                __builtin_amdgcn_s_setprio(2);
+                __builtin_amdgcn_s_setprio(3);
                 if (nc > 0) {
                     prefetch_kg(0, lane);
                     if constexpr (!CV) prefetch_v(0, lane);
