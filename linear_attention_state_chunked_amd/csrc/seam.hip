@@ -29,9 +29,9 @@ __global__ __launch_bounds__(4 * D, W <= 8 ? 4 : 1) void seam_kernel(SeamArgs a)
     constexpr int RPT = D / TPC;         // rows per thread
     constexpr int G8 = D / 8;            // 8-element groups per row
     static_assert(W * G8 <= NT, "one 8-element group per thread per tensor");
-    __shared__ float sK[W][D + 1];       // +1: the w x w dot products read rows at a stride
-    __shared__ float sV[W][D];
-    __shared__ float sQ[W][D + 1];
+    __shared__ __align__(16) float sK[W][D + 4];   // rows 16-byte aligned: 4-float LDS reads
+    __shared__ __align__(16) float sV[W][D];
+    __shared__ __align__(16) float sQ[W][D + 4];
     __shared__ float sL[W][W + 1];       // L, later M
     __shared__ float sMq[W][W + 1];
     __shared__ float sTg[W][W + 1];
@@ -121,20 +121,43 @@ __global__ __launch_bounds__(4 * D, W <= 8 ? 4 : 1) void seam_kernel(SeamArgs a)
     __syncthreads();
     const float Gamma = w > 0 ? sGam[w - 1] : 1.f;
 
-    // ---- w x w: L (strictly lower) and Mq (lower with diagonal)
-    for (int p = tid; p < W * W; p += NT) {
-        const int r = p / W, c = p % W;
-        float dk = 0.f, dq = 0.f;
-        if (r < w && c <= r) {
-#pragma unroll 8
-            for (int i = 0; i < D; ++i) {
-                dk += sK[r][i] * sK[c][i];
-                dq += sQ[r][i] * sK[c][i];
+    // ---- w x w: L (strictly lower) and Mq (lower with diagonal).  Every thread takes part:
+    //      each dot product of length D is split over SUBS adjacent lanes (D / SUBS elements
+    //      each, 4-float LDS reads) and summed with DPP lane permutations.
+    {
+        constexpr int SUBS = NT / 64;        // 8 (D = 128), 4 (D = 64)
+        constexpr int EPS = D / SUBS;        // 16
+        static_assert((W * W) % 64 == 0 && (SUBS == 4 || SUBS == 8), "pair tiling");
+        const int sub = tid % SUBS;
+        for (int p0 = 0; p0 < W * W; p0 += 64) {
+            const int p = p0 + tid / SUBS;
+            const int r = p / W, c = p % W;
+            const bool on = r < w && c <= r;
+            float dk = 0.f, dq = 0.f;
+            if (on) {
+#pragma unroll
+                for (int e = 0; e < EPS; e += 4) {
+                    const float4 kr = *reinterpret_cast<const float4*>(&sK[r][sub * EPS + e]);
+                    const float4 kc = *reinterpret_cast<const float4*>(&sK[c][sub * EPS + e]);
+                    const float4 qr = *reinterpret_cast<const float4*>(&sQ[r][sub * EPS + e]);
+                    dk += kr.x * kc.x + kr.y * kc.y + kr.z * kc.z + kr.w * kc.w;
+                    dq += qr.x * kc.x + qr.y * kc.y + qr.z * kc.z + qr.w * kc.w;
+                }
+            }
+            dk += dpp_perm<0xb1>(dk);            // quad_perm [1,0,3,2]
+            dq += dpp_perm<0xb1>(dq);
+            dk += dpp_perm<0x4e>(dk);            // quad_perm [2,3,0,1]
+            dq += dpp_perm<0x4e>(dq);
+            if constexpr (SUBS == 8) {
+                dk += dpp_perm<0x141>(dk);       // row_half_mirror: the other quad of the 8
+                dq += dpp_perm<0x141>(dq);
+            }
+            if (sub == 0) {
+                const float g = on ? expf(sG[r] - sG[c]) : 0.f;
+                sL[r][c] = (c < r) ? sBeta[r] * g * dk : 0.f;
+                sMq[r][c] = g * dq;
             }
         }
-        const float g = (r < w && c <= r) ? expf(sG[r] - sG[c]) : 0.f;
-        sL[r][c] = (c < r) ? sBeta[r] * g * dk : 0.f;
-        sMq[r][c] = g * dq;
     }
     __syncthreads();
     // ---- Tg = (I + L)^-1 diag(beta): column c by forward substitution (one lane each)
