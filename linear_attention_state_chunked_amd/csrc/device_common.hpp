@@ -128,6 +128,35 @@ __device__ __forceinline__ float wave_max(float v) {
     return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
+// Inclusive prefix sum over the 64 lanes with DPP row shifts and row broadcasts (no
+// LDS round trips): rows of 16 lanes first, then carried across rows.
+template <int CTRL, int ROW_MASK, int BANK_MASK>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, BANK_MASK, false));
+}
+__device__ __forceinline__ float wave_scan_dpp(float v) {
+    float r = v + dpp_mov<0x111, 0xf, 0xf>(v);   // row_shr:1
+    r += dpp_mov<0x112, 0xf, 0xf>(v);            // row_shr:2
+    r += dpp_mov<0x113, 0xf, 0xf>(v);            // row_shr:3
+    r += dpp_mov<0x114, 0xf, 0xe>(r);            // row_shr:4, lanes 4..15 of each row
+    r += dpp_mov<0x118, 0xf, 0xc>(r);            // row_shr:8, lanes 8..15 of each row
+    r += dpp_mov<0x142, 0xa, 0xf>(r);            // row_bcast:15 into rows 1 and 3
+    r += dpp_mov<0x143, 0xc, 0xf>(r);            // row_bcast:31 into rows 2 and 3
+    return r;
+}
+
+// Sum over aligned groups of G adjacent lanes (G = 4, 8 or 16, within one DPP row); every lane
+// of a group gets its group's sum.  All 64 lanes must be active.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+    static_assert(G == 4 || G == 8 || G == 16, "group of 4, 8 or 16 lanes");
+    v += dpp_perm<0xb1>(v);                        // quad_perm [1,0,3,2]
+    v += dpp_perm<0x4e>(v);                        // quad_perm [2,3,0,1]
+    if constexpr (G >= 8) v += dpp_perm<0x141>(v);  // row_half_mirror
+    if constexpr (G >= 16) v += dpp_perm<0x140>(v); // row_mirror
+    return v;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);

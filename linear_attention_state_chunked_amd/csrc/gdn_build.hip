@@ -74,23 +74,6 @@ __device__ __forceinline__ halfx8 colfrag_nat(const _Float16* M, int rs, int rb,
     return cat8(tr4(M, rs, r0, c0, lane), tr4(M, rs, r0 + 4, c0, lane));
 }
 
-// Inclusive prefix sum over the 64 lanes with DPP row shifts and row broadcasts (no
-// LDS round trips): rows of 16 lanes first, then carried across rows.
-template <int CTRL, int ROW_MASK, int BANK_MASK>
-__device__ __forceinline__ float dpp_mov(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, BANK_MASK, false));
-}
-__device__ __forceinline__ float wave_scan_dpp(float v) {
-    float r = v + dpp_mov<0x111, 0xf, 0xf>(v);   // row_shr:1
-    r += dpp_mov<0x112, 0xf, 0xf>(v);            // row_shr:2
-    r += dpp_mov<0x113, 0xf, 0xf>(v);            // row_shr:3
-    r += dpp_mov<0x114, 0xf, 0xe>(r);            // row_shr:4, lanes 4..15 of each row
-    r += dpp_mov<0x118, 0xf, 0xc>(r);            // row_shr:8, lanes 8..15 of each row
-    r += dpp_mov<0x142, 0xa, 0xf>(r);            // row_bcast:15 into rows 1 and 3
-    r += dpp_mov<0x143, 0xc, 0xf>(r);            // row_bcast:31 into rows 2 and 3
-    return r;
-}
-
 // e^x through the hardware base-2 exponential (arguments here are small and <= 0)
 __device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 

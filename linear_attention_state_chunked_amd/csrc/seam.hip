@@ -83,11 +83,9 @@ __global__ __launch_bounds__(4 * D, W <= 8 ? 4 : 1) void seam_kernel(SeamArgs a)
                     sk += xk[u] * xk[u];
                     sq += xq[u] * xq[u];
                 }
-#pragma unroll
-                for (int o = 1; o < G8; o <<= 1) {
-                    sk += __shfl_xor(sk, o, 64);
-                    sq += __shfl_xor(sq, o, 64);
-                }
+                // a token row's G8 pieces sit on G8 adjacent lanes: DPP sums, no LDS round trip
+                sk = group_sum<G8>(sk);
+                sq = group_sum<G8>(sq);
                 const float ck = sk > 0.f ? 1.f / sqrtf(sk) : 0.f;
                 const float cq = sq > 0.f ? 1.f / sqrtf(sq) : 0.f;
 #pragma unroll
@@ -108,8 +106,8 @@ __global__ __launch_bounds__(4 * D, W <= 8 ? 4 : 1) void seam_kernel(SeamArgs a)
             const long long gi = ((long long)b * a.n_tokens + tok0 + lane) * a.h_v + h;
             const float la = ok ? a.log_alpha[gi] : 0.f;
             const float bt = ok ? a.beta[gi] : 0.f;
-            const float G = wave_inclusive_scan(la, lane);
-            const float Gl = __shfl(G, w > 0 ? w - 1 : 0, 64);
+            const float G = wave_scan_dpp(la);
+            const float Gl = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(G), w > 0 ? w - 1 : 0));
             if (lane < W) {
                 sG[lane] = G;
                 sGam[lane] = expf(G);
