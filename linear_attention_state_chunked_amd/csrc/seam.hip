@@ -58,6 +58,9 @@ __global__ __launch_bounds__(4 * D, W <= 8 ? 4 : 1) void seam_kernel(SeamArgs a)
     const long long DD = (long long)D * D;
     const bool want_o = a.o != nullptr;
     const bool want_in = a.S_in != nullptr && (want_o || a.S_out != nullptr);
+    // thread (column j, part) owns rows [i0, i0 + RPT) of column j of every d x d block
+    const int j = tid % D, part = tid / D, i0 = part * RPT;
+    float sin_run[RPT];
 
     // ---- seam tokens: k, v (and q) rows, optionally L2-normalised; gates
     {
@@ -118,6 +121,13 @@ __global__ __launch_bounds__(4 * D, W <= 8 ? 4 : 1) void seam_kernel(SeamArgs a)
     }
     __syncthreads();
     const float Gamma = w > 0 ? sGam[w - 1] : 1.f;
+    // this thread's run of S_in, loaded before the w x w steps so that its HBM latency hides
+    // behind them (after the token loads, whose registers are free by now)
+    if (want_in) {
+        const float* Sin = a.S_in + s * a.in_stride + chain * DD + j;
+#pragma unroll
+        for (int ii = 0; ii < RPT; ++ii) sin_run[ii] = Sin[(long long)(i0 + ii) * D];
+    }
 
     // ---- w x w: L (strictly lower) and Mq (lower with diagonal).  Every thread takes part:
     //      each dot product of length D is split over SUBS adjacent lanes (D / SUBS elements
@@ -182,7 +192,6 @@ __global__ __launch_bounds__(4 * D, W <= 8 ? 4 : 1) void seam_kernel(SeamArgs a)
 
     // ---- w x d factors, thread (column j, part) computes rows [RW*part, RW*part + RW):
     //      U = Tg V, RT = M K  (RS = diag(Gamma/gamma) U is formed where it is used)
-    const int j = tid % D, part = tid / D, i0 = part * RPT;
     constexpr int RW = W / TPC;
 #pragma unroll
     for (int rr = 0; rr < RW; ++rr) {
@@ -245,10 +254,7 @@ __global__ __launch_bounds__(4 * D, W <= 8 ? 4 : 1) void seam_kernel(SeamArgs a)
     }
 
     if (want_in) {
-        const float* Sin = a.S_in + s * a.in_stride + chain * DD + j;
-        float sv[RPT];
-#pragma unroll
-        for (int ii = 0; ii < RPT; ++ii) sv[ii] = Sin[(long long)(i0 + ii) * D];
+        float (&sv)[RPT] = sin_run;
         // P = K S_in[:, j] and QS = Q S_in[:, j]: partial sums over this thread's rows in
         // four LDS slots (one per part), summed in a fixed order (bitwise reproducible)
         auto slot = [&](int q) -> float (*)[D] { return q == 0 ? sP : q == 1 ? sQS : q == 2 ? sY : sZ; };
