@@ -214,7 +214,7 @@ __device__ __forceinline__ void prep_barrier(int* cnt, int target, int lane) {
     if (lane == 0) __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     int spins = 0;
     while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target) {
-        if (++spins > (1 << 22)) break;  // never hang: a broken invariant gives wrong data, not a hang
+        if (++spins > (1 << 18)) break;  // never hang: a broken invariant gives wrong data, not a hang
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
@@ -229,7 +229,7 @@ __device__ __forceinline__ void count_arrival(int* cnt, int lane) {
 __device__ __forceinline__ void wait_count(int* cnt, int target) {
     int spins = 0;
     while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target) {
-        if (++spins > (1 << 22)) break;  // never hang: a broken invariant gives wrong data, not a hang
+        if (++spins > (1 << 18)) break;  // never hang: a broken invariant gives wrong data, not a hang
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
@@ -438,7 +438,7 @@ __device__ __forceinline__ void ut_blocks(const _Float16* Kn1, const float* sGl,
     st_tg(TgAT, TgGT, TgGlT, pt, -r0, 3, 0, ln, bcol[0], bgcol[0]);
 }
 
-template <int D, bool WITH_T, bool IN_BF16, bool PERSIST, bool PT>
+template <int D, bool WITH_T, bool IN_BF16, bool PERSIST, bool PT, bool STREAM>
 __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_build_kernel(EngineArgs a) {
     using LY = GLayout<D>;
     using E = _Float16;
@@ -473,18 +473,28 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
     // own instead of through one merged control-flow graph.
     auto run = [&](auto role) {
         constexpr int R = decltype(role)::value;  // 0: T carry, 1: S carry, 2: preparation
-        for (int it = blockIdx.x; it < a.n_tasks; it += PERSIST ? (int)gridDim.x : a.n_tasks) {
-            const int task = a.order ? a.order[it] : it;
+        // STREAM: one pass runs all of this workgroup's tasks (it, it + G, it + 2G, ...; equal
+        // segments) as one stream of chunks, so the preparation of a task's first chunk overlaps
+        // the last carry of the previous one; c then counts chunks over the whole stream
+        for (int it = blockIdx.x; it < a.n_tasks; it += (PERSIST && !STREAM) ? (int)gridDim.x : a.n_tasks) {
+            const int task = (!STREAM && a.order) ? a.order[it] : it;
             const int per_seg = a.n_batch * a.h_v;
             const int seg = task / per_seg;
             const int rem = task - seg * per_seg;
             const int b = rem / a.h_v;
             const int h = rem - b * a.h_v;
             const int hk = (h * a.h_k) / a.h_v;
-            const long long start = a.seg_start[seg];
-            const int len = a.seg_len[seg];
-            const int nc = (len + 63) / 64;
+            const long long start = STREAM ? a.stream_start0 + seg * a.stream_stride : a.seg_start[seg];
+            const int len = STREAM ? a.stream_len : a.seg_len[seg];
+            const int ncT = (len + 63) / 64;                 // chunks per task
+            const int ntw = STREAM ? (a.n_tasks - it + (int)gridDim.x - 1) / (int)gridDim.x : 1;
+            const int nc = ncT * ntw;                        // chunks in this pass
             const long long chain_off = (long long)b * a.h_v + h;
+            // task k of this pass is task it + k G: the same batch row and head, segment
+            // seg + k dseg (the grid is a multiple of the heads per segment), so its token rows
+            // start k dseg stream_stride rows further on
+            const int dseg = STREAM ? (int)gridDim.x / per_seg : 0;
+            auto rows_of = [&](int k) { return (long long)(k * dseg) * a.stream_stride; };
             if (tid == 0) sCnt[1] = sCnt[2] = sCnt[3] = sCnt[4] = 0;
             __syncthreads();
 
@@ -498,11 +508,19 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                 asm volatile("" : "+v"(tz));
                 const int diag = col0 + (lane & 31) + tz - 4 * (lane >> 5);
                 floatx16 X[NB];
+                auto reset_x = [&] {
+                    // a fresh opaque zero per call: the identity pattern is not loop-invariant
+                    // to the compiler, so it is not kept in 64 registers across the chunk loop
+                    int rz = 0;
+                    asm volatile("" : "+v"(rz));
+                    const int dg = diag + rz;
 #pragma unroll
-                for (int xb = 0; xb < NB; ++xb)
+                    for (int xb = 0; xb < NB; ++xb)
 #pragma unroll
-                    for (int j = 0; j < 16; ++j)
-                        X[xb][j] = (TR && 32 * xb + 8 * (j >> 2) + (j & 3) == diag) ? 1.f : 0.f;
+                        for (int j = 0; j < 16; ++j)
+                            X[xb][j] = (TR && 32 * xb + 8 * (j >> 2) + (j & 3) == dg) ? 1.f : 0.f;
+                };
+                reset_x();
                 int ew = 0;
                 // T columns: rescale by an exact power of two so that max |X_T| lies in [0.5, 1)
                 // (f16 operands never underflow).  The NaN-propagating maximum maps to gfx950's
@@ -541,8 +559,14 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                 const unsigned char* vb0 =
                     reinterpret_cast<const unsigned char*>(a.v) + (((long long)b * N + start) * a.h_v + h) * (D * ESZ);
                 auto cv_prefetch = [&](int cc, int ln) {
+                    const unsigned char* vb = vb0;
+                    if constexpr (STREAM) {
+                        const int k = cc / ncT;
+                        cc -= k * ncT;
+                        vb += rows_of(k) * vstride;
+                    }
                     const int valid = min(64, len - 64 * cc);
-                    const unsigned char* base = vb0 + (long long)(64 * cc) * vstride;
+                    const unsigned char* base = vb + (long long)(64 * cc) * vstride;
 #pragma unroll
                     for (int q = 0; q < NQ; ++q) {
                         const int t = RPW * sw + (64 * q + ln) / CPR, ch = (64 * q + ln) % CPR;
@@ -561,6 +585,30 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                         cv[q].get(x);
                         *reinterpret_cast<u32x4*>(dst + t * RK + 8 * ch) =
                             u32x4{pk_f16(x[0], x[1]), pk_f16(x[2], x[3]), pk_f16(x[4], x[5]), pk_f16(x[6], x[7])};
+                    }
+                };
+                // write a finished chain: the T waves align their slices to the largest of the
+                // exponents in ex (one per T wave)
+                auto write_out = [&](int segw, long long chw, const int* ex) {
+                    const int half = lane >> 5, l32 = lane & 31;
+                    if (TR) {
+                        int emax = ex[0];
+#pragma unroll
+                        for (int w = 1; w < NB; ++w) emax = max(emax, ex[w]);
+                        float* dst = a.T_hat + ((long long)segw * a.n_batch * a.h_v + chw) * D * D + col0 +
+                                     (4 * half) * D + l32;
+#pragma unroll
+                        for (int xb = 0; xb < NB; ++xb)
+#pragma unroll
+                            for (int j = 0; j < 16; ++j)
+                                dst[(32 * xb + 8 * (j >> 2) + (j & 3)) * D] = ldexpf(X[xb][j], ew - emax);
+                        if (wave == 0 && lane == 0) a.T_exp[(long long)segw * a.n_batch * a.h_v + chw] = emax;
+                    } else {
+                        float* dst = a.S_out + segw * a.out_stride + chw * D * D + col0 + (4 * half) * D + l32;
+#pragma unroll
+                        for (int xb = 0; xb < NB; ++xb)
+#pragma unroll
+                            for (int j = 0; j < 16; ++j) dst[(32 * xb + 8 * (j >> 2) + (j & 3)) * D] = X[xb][j];
                     }
                 };
                 if constexpr ((VS && !TR) || (VT && TR)) {
@@ -692,7 +740,16 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                         // after the W' formation below.
                         if (c + 1 < nc) cv_stage(c + 1, sm, ln);
                     }
+                    // STREAM: the last chunk of a task ends here; exponent slots alternate by task
+                    const bool task_end = STREAM && c >= 0 && (c + 1) % ncT == 0;
+                    if (task_end && TR && lane == 0) sEw[4 * ((c / ncT) & 1) + wave] = ew;
                     __syncthreads();  // preparation of chunk c+1 is complete
+                    if (task_end) {
+                        const int k = c / ncT;
+                        write_out(seg + k * dseg, chain_off, sEw + 4 * (k & 1));
+                        reset_x();
+                        ew = 0;
+                    }
                     // From here the preparation waves go on to chunk c+2.  Its staging
                     // buffers are the other halves of the double buffers; its Tg waits for
                     // the formation counter below.  W' has one buffer: every read of W'(c)
@@ -782,27 +839,10 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                     }
                 }
                 // epilogue: align the T waves' exponents, write T_hat / T_exp / S
-                if (TR && lane == 0) sEw[wave] = ew;
-                __syncthreads();
-                const int half = lane >> 5, l32 = lane & 31;
-                if (TR) {
-                    int emax = sEw[0];
-#pragma unroll
-                    for (int w = 1; w < NB; ++w) emax = max(emax, sEw[w]);
-                    float* dst = a.T_hat + ((long long)seg * a.n_batch * a.h_v + chain_off) * D * D + col0 +
-                                 (4 * half) * D + l32;
-#pragma unroll
-                    for (int xb = 0; xb < NB; ++xb)
-#pragma unroll
-                        for (int j = 0; j < 16; ++j)
-                            dst[(32 * xb + 8 * (j >> 2) + (j & 3)) * D] = ldexpf(X[xb][j], ew - emax);
-                    if (wave == 0 && lane == 0) a.T_exp[(long long)seg * a.n_batch * a.h_v + chain_off] = emax;
-                } else {
-                    float* dst = a.S_out + seg * a.out_stride + chain_off * D * D + col0 + (4 * half) * D + l32;
-#pragma unroll
-                    for (int xb = 0; xb < NB; ++xb)
-#pragma unroll
-                        for (int j = 0; j < 16; ++j) dst[(32 * xb + 8 * (j >> 2) + (j & 3)) * D] = X[xb][j];
+                if constexpr (!STREAM) {
+                    if (TR && lane == 0) sEw[wave] = ew;
+                    __syncthreads();
+                    write_out(seg, chain_off, sEw);
                 }
             } else {
                 // ======================== preparation waves ========================
@@ -852,13 +892,23 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                 // K rows of block pw and (wave 1, which has the least gram work) the gates of chunk cc
                 constexpr int GW = 1;
                 auto prefetch_kg = [&](int cc, int ln) {
+                    const unsigned char* kb = kb0;
+                    const float *la = la0, *bt = bt0;
+                    if constexpr (STREAM) {
+                        const int k = cc / ncT;
+                        cc -= k * ncT;
+                        const long long dr = rows_of(k);
+                        kb += dr * kstride;
+                        la += dr * a.h_v;
+                        bt += dr * a.h_v;
+                    }
                     const int valid = min(64, len - 64 * cc);
-                    load_rows(pk, kb0 + (long long)(64 * cc) * kstride, kstride, pw, valid, ln);
+                    load_rows(pk, kb + (long long)(64 * cc) * kstride, kstride, pw, valid, ln);
                     if (pw == GW) {
                         const bool ok = ln < valid;
                         const unsigned go = (unsigned)ln * a.h_v;
-                        pla = ok ? (la0 + (long long)(64 * cc) * a.h_v)[go] : 0.f;
-                        pbt = ok ? (bt0 + (long long)(64 * cc) * a.h_v)[go] : 0.f;
+                        pla = ok ? (la + (long long)(64 * cc) * a.h_v)[go] : 0.f;
+                        pbt = ok ? (bt + (long long)(64 * cc) * a.h_v)[go] : 0.f;
                     }
                 };
                 auto prefetch_v = [&](int cc, int ln) {
@@ -946,7 +996,7 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                     }
                     __syncthreads();  // chunk c+1 prepared
                 }
-                __syncthreads();  // epilogue exponent exchange
+                if constexpr (!STREAM) __syncthreads();  // epilogue exponent exchange
             }
         }
     };
@@ -961,10 +1011,15 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
 template <int D, bool WITH_T, bool IN_BF16, bool PT>
 static hipError_t launch_v(const EngineArgs& a, int grid, hipStream_t s) {
     constexpr int nt = ((WITH_T ? 2 : 1) * D / 32 + 4) * 64;
-    if (a.persistent)
-        hipLaunchKernelGGL((gdn_build_kernel<D, WITH_T, IN_BF16, true, PT>), dim3(grid), dim3(nt), 0, s, a);
-    else
-        hipLaunchKernelGGL((gdn_build_kernel<D, WITH_T, IN_BF16, false, PT>), dim3(grid), dim3(nt), 0, s, a);
+    if (a.stream) {
+        // one stream of chunks per persistent workgroup (equal segments, 16-bit inputs)
+        if constexpr (!IN_BF16) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((gdn_build_kernel<D, WITH_T, IN_BF16, true, PT, IN_BF16>), dim3(grid), dim3(nt), 0, s, a);
+    } else if (a.persistent) {
+        hipLaunchKernelGGL((gdn_build_kernel<D, WITH_T, IN_BF16, true, PT, false>), dim3(grid), dim3(nt), 0, s, a);
+    } else {
+        hipLaunchKernelGGL((gdn_build_kernel<D, WITH_T, IN_BF16, false, PT, false>), dim3(grid), dim3(nt), 0, s, a);
+    }
     return hipGetLastError();
 }
 

@@ -277,11 +277,35 @@ hypic_status hypic_segment_build(const hypic_build_desc* d, hypic_stream_t strea
         // T columns switch to hi/lo operands so long segments stay well inside 2e-3
         a.precise_T = *std::max_element(len.begin(), len.end()) > kPreciseTTokens ? 1 : 0;
         int grid = (int)n_tasks;
-        if (d->schedule == HYPIC_SCHED_RR) {
+        // Equal, evenly spaced segments of at least two chunks with 16-bit inputs: every schedule
+        // gives the same task order (LPT sorts equal lengths stably), so one persistent workgroup
+        // per compute unit streams the chunks of its tasks and overlaps each task's start-up with
+        // the previous task's last chunk
+        bool uniform = d->in_dtype == HYPIC_BF16 && !build_prec_f32(d) && len[0] > 64;
+        const int64_t stride = d->n_seg > 1 ? start[1] - start[0] : 0;
+        for (int32_t i = 0; uniform && i < d->n_seg; ++i)
+            uniform = len[i] == len[0] && start[i] == start[0] + i * stride;
+        if (uniform || d->schedule == HYPIC_SCHED_RR) {
             const int cus = device_cu_count();
             if (cus <= 0) return fail(HYPIC_ERR_DEVICE, "build: cannot query the device's compute units");
             a.persistent = 1;
             grid = (int)std::min<int64_t>(n_tasks, cus);
+        }
+        // the stream needs the grid to be a multiple of the heads per segment (a workgroup's
+        // tasks then share batch row and head) and at least four chunks per task
+        if (uniform && (len[0] <= 192 || grid % (d->n_batch * d->h_v) != 0)) {
+            uniform = false;
+            if (d->schedule != HYPIC_SCHED_RR) {
+                a.persistent = 0;
+                grid = (int)n_tasks;
+            }
+        }
+        if (uniform) {
+            a.stream = 1;
+            a.order = nullptr;
+            a.stream_start0 = start[0];
+            a.stream_stride = stride;
+            a.stream_len = len[0];
         }
         e = hypic::launch_gdn_build(a, d->d_k, build_prec_f32(d) ? 1 : 0, grid, s);
         if (e != hipSuccess) return device_fail("build: dense build launch", e);

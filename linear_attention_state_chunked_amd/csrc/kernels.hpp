@@ -37,6 +37,12 @@ struct EngineArgs {
     int* T_exp;
     void* o;
     int precise_T;               // T columns with hi/lo operands (long segments)
+    // stream mode (persistent grid, equal segments, 16-bit inputs): segment s covers tokens
+    // [stream_start0 + s * stream_stride, ... + stream_len); each workgroup streams the chunks
+    // of its tasks it, it + grid, ... (natural order)
+    int stream;
+    long long stream_start0, stream_stride;
+    int stream_len;
 };
 
 // kind: 0 diagonal (GLA, per-channel log_alpha), 1 scalar
