@@ -476,7 +476,12 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
         // STREAM: one pass runs all of this workgroup's tasks (it, it + G, it + 2G, ...; equal
         // segments) as one stream of chunks, so the preparation of a task's first chunk overlaps
         // the last carry of the previous one; c then counts chunks over the whole stream
-        for (int it = blockIdx.x; it < a.n_tasks; it += (PERSIST && !STREAM) ? (int)gridDim.x : a.n_tasks) {
+        for (int it0 = blockIdx.x; it0 < a.n_tasks; it0 += (PERSIST && !STREAM) ? (int)gridDim.x : a.n_tasks) {
+            // STREAM: workgroups w and w + 8 of each group of 16 run value heads 2p and 2p + 1; the
+            // dispatcher deals workgroups to the 8 XCDs in turn, so the two value heads of a key
+            // head (consecutive tasks) share an XCD and its L2, and the second reads of their K
+            // rows hit there
+            const int it = (STREAM && (gridDim.x & 15) == 0) ? (it0 & ~15) | (2 * (it0 & 7) + ((it0 >> 3) & 1)) : it0;
             const int task = (!STREAM && a.order) ? a.order[it] : it;
             const int per_seg = a.n_batch * a.h_v;
             const int seg = task / per_seg;
@@ -621,7 +626,7 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                     asm volatile("" : "+s"(lz));
                     asm volatile("" : "+v"(lzv));
                     unsigned char* sm = smem + lz;
-                    const int ln = lane + lzv, hf = ln >> 5, lq = ln & 31;
+                    const int ln = lane + lzv, hf = ln >> 5;
                     const int p = c & 1, p3 = (c + 3) % 3, pn3 = (c + 4) % 3;
                     if (c >= 0) {
                         const E* Wf = reinterpret_cast<const E*>(sm + LY::Wf);
