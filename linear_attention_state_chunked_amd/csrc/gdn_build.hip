@@ -477,11 +477,13 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
         // segments) as one stream of chunks, so the preparation of a task's first chunk overlaps
         // the last carry of the previous one; c then counts chunks over the whole stream
         for (int it0 = blockIdx.x; it0 < a.n_tasks; it0 += (PERSIST && !STREAM) ? (int)gridDim.x : a.n_tasks) {
-            // STREAM: workgroups w and w + 8 of each group of 16 run value heads 2p and 2p + 1; the
-            // dispatcher deals workgroups to the 8 XCDs in turn, so the two value heads of a key
-            // head (consecutive tasks) share an XCD and its L2, and the second reads of their K
-            // rows hit there
-            const int it = (STREAM && (gridDim.x & 15) == 0) ? (it0 & ~15) | (2 * (it0 & 7) + ((it0 >> 3) & 1)) : it0;
+            // Within every full group of 16 task positions, positions w and w + 8 run tasks 2p and
+            // 2p + 1 (p = w mod 8): the dispatcher deals workgroups to the 8 XCDs in turn, so the two
+            // value heads of a key head (consecutive tasks) share an XCD and its L2, and the second
+            // reads of their K rows hit there.  A bijection on the task positions (a partial last
+            // group keeps its order); in the stream each group must lie inside the grid.
+            const int pair_bound = STREAM ? (int)gridDim.x : a.n_tasks;
+            const int it = (it0 | 15) < pair_bound ? (it0 & ~15) | (2 * (it0 & 7) + ((it0 >> 3) & 1)) : it0;
             const int task = (!STREAM && a.order) ? a.order[it] : it;
             const int per_seg = a.n_batch * a.h_v;
             const int seg = task / per_seg;
