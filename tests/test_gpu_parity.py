@@ -192,29 +192,37 @@ def test_schedules_are_bitwise_identical(ragged_dense):
         assert torch.equal(o["T_exp"], outs[0]["T_exp"])
 
 
-def test_stream_build_matches_per_task_build(gpu):
+@pytest.mark.parametrize("variant", ["fast", "no_T_skip_head", "precise_T"])
+def test_stream_build_matches_per_task_build(gpu, variant):
     """Equal segments take the stream path (one persistent workgroup per compute unit running
     the chunks of its tasks back to back); the same segments built with one workgroup per task
     (a ragged last segment turns the stream off) must agree bit for bit, and a block from a
-    workgroup's second task must match the oracle."""
+    workgroup's second task must match the oracle.  Variants: the fast plan; the plain state
+    pass (no T) with a skipped head; segments over 2,048 tokens (hi/lo T operands)."""
     wl = WORKLOADS["gdn64k_bf16"]
-    h_v, seg = wl.h_v, 256
+    h_v = wl.h_v
+    seg = 2112 if variant == "precise_T" else 256
+    skip = 8 if variant == "no_T_skip_head" else 0
+    with_T = variant != "no_T_skip_head"
     lens_u = [seg] * 16                      # 512 tasks: two per workgroup on 256 compute units
     lens_r = [seg] * 15 + [seg - 1]
     dev, chains = _dense_inputs(wl, sum(lens_u), h_v)
-    uni = H.hypic_segment_build(dev["k"], dev["v"], dev["log_alpha"], cu_of(lens_u), beta=dev["beta"])
-    rag = H.hypic_segment_build(dev["k"], dev["v"], dev["log_alpha"], cu_of(lens_r), beta=dev["beta"])
+    kw = dict(beta=dev["beta"], with_T=with_T, skip_head=skip)
+    uni = H.hypic_segment_build(dev["k"], dev["v"], dev["log_alpha"], cu_of(lens_u), **kw)
+    rag = H.hypic_segment_build(dev["k"], dev["v"], dev["log_alpha"], cu_of(lens_r), **kw)
     torch.cuda.synchronize()
-    for key in ("S", "T_hat", "T_exp"):
+    for key in ("S", "T_hat", "T_exp") if with_T else ("S",):
         assert torch.equal(uni[key][:15], rag[key][:15]), key
     s, h = 12, 5
-    lo, hi = s * seg, (s + 1) * seg
+    lo, hi = s * seg + skip, (s + 1) * seg
     c = chains[h]
     r = O.dense_recurrence(c["k"][lo:hi], c["v"][lo:hi], c["log_alpha"][lo:hi], c["beta"][lo:hi])
     e_S = float(O.rel_err(uni["S"][s, 0, h].cpu().numpy(), r["S"]))
-    e_T = float(O.rel_err_T("dense", uni["T_hat"][s, 0, h].cpu().numpy(), int(uni["T_exp"][s, 0, h]),
-                            r["T_hat"], r["T_exp"]))
-    print(f"stream build, segment {s} head {h}: S {e_S:.2e}, T {e_T:.2e}")
+    e_T = 0.0
+    if with_T:
+        e_T = float(O.rel_err_T("dense", uni["T_hat"][s, 0, h].cpu().numpy(), int(uni["T_exp"][s, 0, h]),
+                                r["T_hat"], r["T_exp"]))
+    print(f"stream build ({variant}), segment {s} head {h}: S {e_S:.2e}, T {e_T:.2e}")
     assert e_S < TOL_BF16 and e_T < TOL_BF16
 
 
