@@ -11,7 +11,8 @@
 // Dense kind: each wave owns 32 columns of S (and, for the composed transition, of
 // T) in matrix-core accumulators and computes T_i X with f16 hi/lo operand splits
 // (three products, ~22-bit operand precision) after scaling its column block by an
-// exact power of two; T_i is staged row-major in LDS as hi/lo f16 by loader waves,
+// exact power of two (the column maximum uses the NaN-propagating three-input maximum
+// with |.| modifiers); T_i is staged row-major in LDS as hi/lo f16 by loader waves,
 // one element ahead.
 // Diagonal / scalar kinds: elementwise, one thread per state entry stripe.
 #include "device_common.hpp"
@@ -164,7 +165,7 @@ __global__ __launch_bounds__(D * 6) void fold_dense_kernel(FoldArgs a) {
 #pragma unroll
         for (int xb = 0; xb < NB; ++xb)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) m = fmaxf(m, fabsf(X[xb][j]));
+            for (int j = 0; j < 16; ++j) m = __builtin_elementwise_maximum(m, __builtin_fabsf(X[xb][j]));
         const int sx = exp2_of(wave_max(m));
         const float sc = ldexpf(1.f, -sx);
         floatx16 acc[NB];
@@ -198,7 +199,7 @@ __global__ __launch_bounds__(D * 6) void fold_dense_kernel(FoldArgs a) {
 #pragma unroll
             for (int xb = 0; xb < NB; ++xb)
 #pragma unroll
-                for (int j = 0; j < 16; ++j) mm = fmaxf(mm, fabsf(acc[xb][j]));
+                for (int j = 0; j < 16; ++j) mm = __builtin_elementwise_maximum(mm, __builtin_fabsf(acc[xb][j]));
             const int e = exp2_of(wave_max(mm));
             const float r = ldexpf(1.f, -e);
 #pragma unroll
