@@ -16,10 +16,16 @@
 // workgroup barrier per chunk the carry waves turn the solve into W' (T waves; stored as
 // ready-made operand fragments) and U (S waves; kept in their accumulators for the next
 // carry) while the preparation waves go on with chunk c+2; with 16-bit inputs the S waves
-// (or, in the fast plan, the T waves before the barrier) stage V.  K and the gamma vectors are
-// triple-buffered, V and the gate vectors doubled.  Bounded LDS counters order the rest:
-// the preparation waves' own stages, the carry waves' W' hand-off, the reuse of the Tg
-// buffers (one arrival per carry wave and chunk) and two hand-offs inside the solve.
+// (and, in the fast plan, the T waves before the barrier) stage V.  K and the gamma vectors
+// are triple-buffered, V and the gate vectors doubled.  Bounded LDS counters order the
+// rest: the preparation waves' own barrier, the carry waves' W' hand-off and the reuse of
+// the Tg buffers (one arrival per carry wave and chunk).
+//
+// Task mapping.  One workgroup per (segment, batch row, value head) task, the two value
+// heads of a key head on workgroups of the same XCD.  With equal segments the grid is one
+// persistent workgroup per compute unit and each runs its tasks as one stream of chunks
+// (the loop counter counts chunks over the stream), so a task's first chunk is prepared
+// under the previous task's last carry.
 //
 // Layout rules.  Every K / V tile in LDS is a natural row-major f16 tile written with
 // 16-byte stores.  Row fragments are plain 16-byte reads; column fragments (contraction
@@ -30,9 +36,10 @@
 //
 // The 64x64 unit lower-triangular solve works on 16x16 blocks, one token block per
 // preparation wave: the diagonal inverses as the product (I+N)(I+N^2)(I+N^4)(I+N^8),
-// then two merge levels; all products on the matrix cores with hi/lo-split f16
-// operands (about 22-bit operands, fp32 accumulation).  Only small 16x16 tiles pass
-// between the waves.
+// one exchange of the diagonal inverses and the blocks of L among the four waves, then
+// each wave forms its share of the off-diagonal blocks of (I + L)^-1 without further
+// hand-offs; all products on the matrix cores with hi/lo-split f16 operands (about
+// 22-bit operands, fp32 accumulation).  Only small 16x16 tiles pass between the waves.
 #include <type_traits>
 
 #include "device_common.hpp"
