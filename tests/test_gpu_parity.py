@@ -226,6 +226,35 @@ def test_stream_build_matches_per_task_build(gpu, variant):
     assert e_S < TOL_BF16 and e_T < TOL_BF16
 
 
+def test_stream_build_d64_bf16(gpu):
+    """The stream path at d = 64 with 16-bit inputs: one head, 512 equal segments of 256 tokens
+    (two tasks per workgroup), against the per-task build bit for bit and the oracle on the
+    rounded inputs."""
+    wl = WORKLOADS["tiny_gdn_f32"]
+    seg, n_seg = 256, 512
+    c = chain_inputs(wl, 0, 0, seg * n_seg)
+    bf = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16)
+    k16, v16 = bf(c["k"]), bf(c["v"])
+    dev = {"k": k16[None, :, None, :].cuda(), "v": v16[None, :, None, :].cuda(),
+           "log_alpha": dev_tensor(c["log_alpha"][None, :, None]), "beta": dev_tensor(c["beta"][None, :, None])}
+    lens_u = [seg] * n_seg
+    lens_r = [seg] * (n_seg - 1) + [seg - 1]
+    uni = H.hypic_segment_build(dev["k"], dev["v"], dev["log_alpha"], cu_of(lens_u), beta=dev["beta"])
+    rag = H.hypic_segment_build(dev["k"], dev["v"], dev["log_alpha"], cu_of(lens_r), beta=dev["beta"])
+    torch.cuda.synchronize()
+    for key in ("S", "T_hat", "T_exp"):
+        assert torch.equal(uni[key][:n_seg - 1], rag[key][:n_seg - 1]), key
+    s = 300
+    lo, hi = s * seg, (s + 1) * seg
+    kr, vr = k16.float().numpy(), v16.float().numpy()
+    r = O.dense_recurrence(kr[lo:hi], vr[lo:hi], c["log_alpha"][lo:hi], c["beta"][lo:hi])
+    e_S = float(O.rel_err(uni["S"][s, 0, 0].cpu().numpy(), r["S"]))
+    e_T = float(O.rel_err_T("dense", uni["T_hat"][s, 0, 0].cpu().numpy(), int(uni["T_exp"][s, 0, 0]),
+                            r["T_hat"], r["T_exp"]))
+    print(f"stream build d=64 bf16, segment {s}: S {e_S:.2e}, T {e_T:.2e}")
+    assert e_S < TOL_BF16 and e_T < TOL_BF16
+
+
 # ----------------------------------------------------------------------------------------
 # diagonal (GLA) and scalar (RetNet) decay families
 
