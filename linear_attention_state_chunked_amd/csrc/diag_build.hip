@@ -8,7 +8,11 @@
 // K~[t][c] = k_t[c] exp(G_n[c] - G_t[c]).  Chunks are visited from the end of the
 // segment backwards so the decay exponent is a running suffix sum; K~ and V are
 // staged in LDS (f16, contraction axis in accumulator order) and contracted on the
-// matrix cores, the d x d state staying in accumulators.
+// matrix cores, the d x d state staying in accumulators.  One workgroup runs a segment's
+// chunks in sequence, so its loads are issued two chunks ahead into alternating register
+// sets: every chunk then waits on no HBM round trip of its own.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -17,22 +21,27 @@ namespace hypic {
 template <int D, class Op>
 __global__ __launch_bounds__(512) void diag_build_kernel(DiagArgs a) {
     using E = typename Op::elem;
+    // 16-bit inputs feed the f16 matrix cores, 32-bit inputs the f32 ones
+    constexpr bool BF = std::is_same<Op, OpF16>::value;
+    using KRaw = typename std::conditional<BF, uint16_t, float>::type;
     constexpr int PAD = 16 / (int)sizeof(E);
     constexpr int RS = 64 + PAD;
     constexpr int NT = 512;
     constexpr int KS = Op::KS, KH = Op::KH;
     constexpr int TILES = (D / 32) * (D / 32);
-    constexpr int TPW = (TILES + 7) / 8;  // tiles per wave
-    constexpr int NP = NT / D;            // token parts per chunk
-    constexpr int TP = kChunk / NP;       // tokens per part
+    constexpr int TPW = (TILES + 7) / 8;      // tiles per wave
+    constexpr int NP = NT / D;                // token parts per chunk
+    constexpr int TP = kChunk / NP;           // tokens per part
+    constexpr int VPT = kChunk * (D / 8) / NT;  // 8-wide value groups per thread and chunk
+    constexpr int VW = BF ? 1 : 2;            // 16-byte words per value group
+    static_assert(VPT >= 1 && VPT * NT == kChunk * (D / 8), "value groups cover the chunk");
     __shared__ __align__(16) E sKd[D * RS];   // K~^T: [c][t]
     __shared__ __align__(16) E sVt[D * RS];   // V^T : [d][t]
-    __shared__ float sR[D];                   // running suffix sum per channel
+    __shared__ float sR[D];                   // suffix sum per channel over the whole segment
     __shared__ float sPart[NT];               // per-part decay sums
     __shared__ float sMax;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, l32 = lane & 31;
-    const bool in_bf16 = a.in_bf16 != 0;
     const long long N = a.n_tokens;
 
     const int task = a.order ? a.order[blockIdx.x] : blockIdx.x;
@@ -44,66 +53,84 @@ __global__ __launch_bounds__(512) void diag_build_kernel(DiagArgs a) {
     const long long start = a.seg_start[seg];
     const int len = a.seg_len[seg];
     const long long chain = (long long)seg * a.n_batch * a.h_v + (long long)b * a.h_v + h;
+    // thread (c, p): channel c of the decayed keys over token part p of a chunk
+    const int c = tid % D, p = tid / D;
 
     floatx16 acc[TPW];
 #pragma unroll
     for (int i = 0; i < TPW; ++i) acc[i] = zero16();
-    if (tid < D) sR[tid] = 0.f;
-    __syncthreads();
 
-    const int nchunk = (len + kChunk - 1) / kChunk;
-    for (int ci = nchunk - 1; ci >= 0; --ci) {
+    // One chunk's inputs as loaded, undecoded, so that the loads stay in flight until the
+    // chunk is consumed two chunks later.  Rows past the segment's end are clamped to its
+    // last token (in bounds) and zeroed at consumption.
+    struct Regs {
+        KRaw k[TP];
+        float la[TP];
+        uint4 v[VPT][VW];
+    };
+    auto load = [&](Regs& r, int ci) {
         const int c0 = ci * kChunk;
-        const int valid = min(kChunk, len - c0);
+        const int last = min(kChunk, len - c0) - 1;
         const long long tok0 = start + c0;
-        // decayed keys: thread (c, p) handles channel c over token part p of the chunk;
-        // part offsets (suffix sums of later parts) are exchanged through LDS.
-        {
-            const int c = tid % D, p = tid / D;
-            float kv[TP], la[TP];
-            float tot = 0.f;
 #pragma unroll
-            for (int u = 0; u < TP; ++u) {
-                const int t = p * TP + u;
-                kv[u] = 0.f;
-                la[u] = 0.f;
-                if (t < valid) {
-                    const long long row = (b * N + tok0 + t);
-                    const long long ki = (row * a.h_k + hk) * D + c;
-                    kv[u] = in_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(a.k)[ki])
-                                    : reinterpret_cast<const float*>(a.k)[ki];
-                    la[u] = a.scalar ? a.log_alpha[row * a.h_v + h] : a.log_alpha[(row * a.h_v + h) * D + c];
-                }
-                tot += la[u];
-            }
-            sPart[p * D + c] = tot;
-            __syncthreads();
-            float run = sR[c];
-            for (int q = p + 1; q < NP; ++q) run += sPart[q * D + c];
-#pragma unroll
-            for (int u = TP - 1; u >= 0; --u) {
-                sKd[c * RS + acc_pos(p * TP + u)] = Op::cvt(kv[u] * expf(run));
-                run += la[u];
-            }
-            __syncthreads();
-            if (p == 0) {
-                float r = sR[c];
-                for (int q = 0; q < NP; ++q) r += sPart[q * D + c];
-                sR[c] = r;
-            }
+        for (int u = 0; u < TP; ++u) {
+            const long long row = b * N + tok0 + min(p * TP + u, last);
+            r.k[u] = reinterpret_cast<const KRaw*>(a.k)[(row * a.h_k + hk) * D + c];
+            r.la[u] = a.scalar ? a.log_alpha[row * a.h_v + h] : a.log_alpha[(row * a.h_v + h) * D + c];
         }
+#pragma unroll
+        for (int g = 0; g < VPT; ++g) {
+            const int i = tid + g * NT;
+            const int t = i / (D / 8), d0 = 8 * (i % (D / 8));
+            const long long idx = ((b * N + tok0 + min(t, last)) * a.h_v + h) * D + d0;
+            const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const KRaw*>(a.v) + idx);
+#pragma unroll
+            for (int w = 0; w < VW; ++w) r.v[g][w] = src[w];
+        }
+    };
+    float rR = 0.f;  // running suffix sum of the channel's log decays (same in every part)
+    auto step = [&](Regs& r, int ci) {
+        const int valid = min(kChunk, len - ci * kChunk);
+        float kv[TP], la[TP];
+        float tot = 0.f;
+#pragma unroll
+        for (int u = 0; u < TP; ++u) {
+            const bool ok = p * TP + u < valid;
+            kv[u] = ok ? (BF ? bf16_to_f32(r.k[u]) : (float)r.k[u]) : 0.f;
+            la[u] = ok ? r.la[u] : 0.f;
+            tot += la[u];
+        }
+        sPart[p * D + c] = tot;
         // values, transposed
-        for (int i = tid; i < kChunk * (D / 8); i += NT) {
+#pragma unroll
+        for (int g = 0; g < VPT; ++g) {
+            const int i = tid + g * NT;
             const int t = i / (D / 8), d0 = 8 * (i % (D / 8));
             float x[8];
-            if (t < valid) load8(a.v, ((b * N + tok0 + t) * a.h_v + h) * D + d0, in_bf16, x);
-            else {
+            const uint32_t ws[8] = {r.v[g][0].x, r.v[g][0].y, r.v[g][0].z, r.v[g][0].w,
+                                    r.v[g][VW - 1].x, r.v[g][VW - 1].y, r.v[g][VW - 1].z, r.v[g][VW - 1].w};
 #pragma unroll
-                for (int u = 0; u < 8; ++u) x[u] = 0.f;
+            for (int u = 0; u < 8; ++u) {
+                const float f = BF ? (u & 1 ? __uint_as_float(ws[u >> 1] & 0xffff0000u) : __uint_as_float(ws[u >> 1] << 16))
+                                   : __uint_as_float(ws[u]);
+                x[u] = t < valid ? f : 0.f;
             }
 #pragma unroll
             for (int u = 0; u < 8; ++u) sVt[(d0 + u) * RS + acc_pos(t)] = Op::cvt(x[u]);
         }
+        __syncthreads();
+        // decayed keys: suffix sums of the later parts come through LDS
+        float run = rR;
+        for (int q = p + 1; q < NP; ++q) run += sPart[q * D + c];
+#pragma unroll
+        for (int u = TP - 1; u >= 0; --u) {
+            sKd[c * RS + acc_pos(p * TP + u)] = Op::cvt(kv[u] * expf(run));
+            run += la[u];
+        }
+        float rn = rR;
+        for (int q = 0; q < NP; ++q) rn += sPart[q * D + c];
+        rR = rn;
+        if (ci >= 2) load(r, ci - 2);
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
@@ -118,7 +145,19 @@ __global__ __launch_bounds__(512) void diag_build_kernel(DiagArgs a) {
             }
         }
         __syncthreads();
+    };
+
+    // Chunks are visited from the end of the segment backwards, two register sets in turn.
+    const int nchunk = (len + kChunk - 1) / kChunk;
+    Regs ra, rb;
+    if (nchunk > 0) load(ra, nchunk - 1);
+    if (nchunk > 1) load(rb, nchunk - 2);
+    for (int ci = nchunk - 1; ci >= 0; ci -= 2) {
+        step(ra, ci);
+        if (ci >= 1) step(rb, ci - 1);
     }
+    if (p == 0) sR[c] = rR;
+    __syncthreads();
 
     float* dS = a.S + chain * D * D;
 #pragma unroll
