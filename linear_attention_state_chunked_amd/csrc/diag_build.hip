@@ -68,29 +68,36 @@ __global__ __launch_bounds__(512) void diag_build_kernel(DiagArgs a) {
         float la[TP];
         uint4 v[VPT][VW];
     };
+    // per-token strides (elements) of keys, gates and values; 32-bit offsets within a chunk
+    const int ks = a.h_k * D, ls = a.scalar ? a.h_v : a.h_v * D, vs = a.h_v * D;
+    const int lc = a.scalar ? 0 : c;
     auto load = [&](Regs& r, int ci) {
         const int c0 = ci * kChunk;
         const int last = min(kChunk, len - c0) - 1;
-        const long long tok0 = start + c0;
+        const long long row0 = b * N + start + c0;  // first token row of the chunk (uniform)
+        const KRaw* kb = reinterpret_cast<const KRaw*>(a.k) + (row0 * a.h_k + hk) * D;
+        const float* lb = a.log_alpha + (a.scalar ? row0 * a.h_v + h : (row0 * a.h_v + h) * D);
+        const KRaw* vb = reinterpret_cast<const KRaw*>(a.v) + (row0 * a.h_v + h) * D;
 #pragma unroll
         for (int u = 0; u < TP; ++u) {
-            const long long row = b * N + tok0 + min(p * TP + u, last);
-            r.k[u] = reinterpret_cast<const KRaw*>(a.k)[(row * a.h_k + hk) * D + c];
-            r.la[u] = a.scalar ? a.log_alpha[row * a.h_v + h] : a.log_alpha[(row * a.h_v + h) * D + c];
+            const int t = min(p * TP + u, last);
+            r.k[u] = kb[t * ks + c];
+            r.la[u] = lb[t * ls + lc];
         }
 #pragma unroll
         for (int g = 0; g < VPT; ++g) {
             const int i = tid + g * NT;
             const int t = i / (D / 8), d0 = 8 * (i % (D / 8));
-            const long long idx = ((b * N + tok0 + min(t, last)) * a.h_v + h) * D + d0;
-            const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const KRaw*>(a.v) + idx);
+            const uint4* src = reinterpret_cast<const uint4*>(vb + min(t, last) * vs + d0);
 #pragma unroll
             for (int w = 0; w < VW; ++w) r.v[g][w] = src[w];
         }
     };
     float rR = 0.f;  // running suffix sum of the channel's log decays (same in every part)
+    // Chunk ci < 0 is an all-zero step (adds exact zeros).  Every step issues its loads, so
+    // the wait before a register set's use never covers the set loaded after it.
     auto step = [&](Regs& r, int ci) {
-        const int valid = min(kChunk, len - ci * kChunk);
+        const int valid = ci >= 0 ? min(kChunk, len - ci * kChunk) : 0;
         float kv[TP], la[TP];
         float tot = 0.f;
 #pragma unroll
@@ -124,13 +131,15 @@ __global__ __launch_bounds__(512) void diag_build_kernel(DiagArgs a) {
         for (int q = p + 1; q < NP; ++q) run += sPart[q * D + c];
 #pragma unroll
         for (int u = TP - 1; u >= 0; --u) {
-            sKd[c * RS + acc_pos(p * TP + u)] = Op::cvt(kv[u] * expf(run));
+            // f16 operands: the hardware exp2 (about 1 ulp of fp32) is far below their rounding
+            const float dec = BF ? __builtin_amdgcn_exp2f(run * 1.4426950408889634f) : expf(run);
+            sKd[c * RS + acc_pos(p * TP + u)] = Op::cvt(kv[u] * dec);
             run += la[u];
         }
         float rn = rR;
         for (int q = 0; q < NP; ++q) rn += sPart[q * D + c];
         rR = rn;
-        if (ci >= 2) load(r, ci - 2);
+        load(r, max(ci - 2, 0));
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
@@ -149,12 +158,17 @@ __global__ __launch_bounds__(512) void diag_build_kernel(DiagArgs a) {
 
     // Chunks are visited from the end of the segment backwards, two register sets in turn.
     const int nchunk = (len + kChunk - 1) / kChunk;
-    Regs ra, rb;
-    if (nchunk > 0) load(ra, nchunk - 1);
-    if (nchunk > 1) load(rb, nchunk - 2);
-    for (int ci = nchunk - 1; ci >= 0; ci -= 2) {
-        step(ra, ci);
-        if (ci >= 1) step(rb, ci - 1);
+    if (nchunk > 0) {
+        Regs ra, rb;
+        load(ra, nchunk - 1);
+        // keep the first set's loads ahead of the second's, as in the loop, so that waiting
+        // for one set never waits for the other
+        __builtin_amdgcn_sched_barrier(0);
+        load(rb, max(nchunk - 2, 0));
+        for (int ci = nchunk - 1; ci >= 0; ci -= 2) {
+            step(ra, ci);
+            step(rb, ci - 1);
+        }
     }
     if (p == 0) sR[c] = rR;
     __syncthreads();
