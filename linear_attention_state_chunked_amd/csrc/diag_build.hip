@@ -32,9 +32,13 @@ __global__ __launch_bounds__(512) void diag_build_kernel(DiagArgs a) {
     constexpr int TPW = (TILES + 7) / 8;      // tiles per wave
     constexpr int NP = NT / D;                // token parts per chunk
     constexpr int TP = kChunk / NP;           // tokens per part
-    constexpr int VPT = kChunk * (D / 8) / NT;  // 8-wide value groups per thread and chunk
-    constexpr int VW = BF ? 1 : 2;            // 16-byte words per value group
-    static_assert(VPT >= 1 && VPT * NT == kChunk * (D / 8), "value groups cover the chunk");
+    // values: thread (cg, tg) stages channels [CPT*cg, CPT*cg + CPT) of tokens [4*tg, 4*tg + 4)
+    constexpr int CPT = D / 32;
+    constexpr int VWORDS = CPT * (int)sizeof(KRaw) / 4;  // 32-bit words per token and thread
+    static_assert(32 * (kChunk / 4) == NT && (VWORDS == 1 || VWORDS == 2 || VWORDS == 4), "value staging map");
+    using VVec = typename std::conditional<VWORDS == 1, uint32_t,
+                 typename std::conditional<VWORDS == 2, uint2, uint4>::type>::type;
+    static_assert(TP % 4 == 0 && (RS * sizeof(E)) % 16 == 0, "packed key writes stay aligned");
     __shared__ __align__(16) E sKd[D * RS];   // K~^T: [c][t]
     __shared__ __align__(16) E sVt[D * RS];   // V^T : [d][t]
     __shared__ float sR[D];                   // suffix sum per channel over the whole segment
@@ -55,6 +59,7 @@ __global__ __launch_bounds__(512) void diag_build_kernel(DiagArgs a) {
     const long long chain = (long long)seg * a.n_batch * a.h_v + (long long)b * a.h_v + h;
     // thread (c, p): channel c of the decayed keys over token part p of a chunk
     const int c = tid % D, p = tid / D;
+    const int cg = tid % 32, tg = tid / 32;
 
     floatx16 acc[TPW];
 #pragma unroll
@@ -66,7 +71,7 @@ __global__ __launch_bounds__(512) void diag_build_kernel(DiagArgs a) {
     struct Regs {
         KRaw k[TP];
         float la[TP];
-        uint4 v[VPT][VW];
+        VVec v[4];
     };
     // per-token strides (elements) of keys, gates and values; 32-bit offsets within a chunk
     const int ks = a.h_k * D, ls = a.scalar ? a.h_v : a.h_v * D, vs = a.h_v * D;
@@ -85,13 +90,8 @@ __global__ __launch_bounds__(512) void diag_build_kernel(DiagArgs a) {
             r.la[u] = lb[t * ls + lc];
         }
 #pragma unroll
-        for (int g = 0; g < VPT; ++g) {
-            const int i = tid + g * NT;
-            const int t = i / (D / 8), d0 = 8 * (i % (D / 8));
-            const uint4* src = reinterpret_cast<const uint4*>(vb + min(t, last) * vs + d0);
-#pragma unroll
-            for (int w = 0; w < VW; ++w) r.v[g][w] = src[w];
-        }
+        for (int j = 0; j < 4; ++j)
+            r.v[j] = *reinterpret_cast<const VVec*>(vb + min(4 * tg + j, last) * vs + CPT * cg);
     };
     float rR = 0.f;  // running suffix sum of the channel's log decays (same in every part)
     // Chunk ci < 0 is an all-zero step (adds exact zeros).  Every step issues its loads, so
@@ -108,33 +108,47 @@ __global__ __launch_bounds__(512) void diag_build_kernel(DiagArgs a) {
             tot += la[u];
         }
         sPart[p * D + c] = tot;
-        // values, transposed
+        // values, transposed: each channel's four tokens are adjacent in the accumulator order
 #pragma unroll
-        for (int g = 0; g < VPT; ++g) {
-            const int i = tid + g * NT;
-            const int t = i / (D / 8), d0 = 8 * (i % (D / 8));
-            float x[8];
-            const uint32_t ws[8] = {r.v[g][0].x, r.v[g][0].y, r.v[g][0].z, r.v[g][0].w,
-                                    r.v[g][VW - 1].x, r.v[g][VW - 1].y, r.v[g][VW - 1].z, r.v[g][VW - 1].w};
+        for (int e = 0; e < CPT; ++e) {
+            E x[4];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const float f = BF ? (u & 1 ? __uint_as_float(ws[u >> 1] & 0xffff0000u) : __uint_as_float(ws[u >> 1] << 16))
-                                   : __uint_as_float(ws[u]);
-                x[u] = t < valid ? f : 0.f;
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t w = reinterpret_cast<const uint32_t*>(&r.v[j])[BF ? e >> 1 : e];
+                const float f = BF ? (e & 1 ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16))
+                                   : __uint_as_float(w);
+                x[j] = Op::cvt(4 * tg + j < valid ? f : 0.f);
             }
-#pragma unroll
-            for (int u = 0; u < 8; ++u) sVt[(d0 + u) * RS + acc_pos(t)] = Op::cvt(x[u]);
+            E* dst = sVt + (CPT * cg + e) * RS + acc_pos(4 * tg);
+            if constexpr (BF) {
+                *reinterpret_cast<halfx4*>(dst) = halfx4{x[0], x[1], x[2], x[3]};
+            } else {
+                *reinterpret_cast<float4*>(dst) = make_float4(x[0], x[1], x[2], x[3]);
+            }
         }
         __syncthreads();
         // decayed keys: suffix sums of the later parts come through LDS
         float run = rR;
         for (int q = p + 1; q < NP; ++q) run += sPart[q * D + c];
+        E kd[TP];
 #pragma unroll
         for (int u = TP - 1; u >= 0; --u) {
             // f16 operands: the hardware exp2 (about 1 ulp of fp32) is far below their rounding
             const float dec = BF ? __builtin_amdgcn_exp2f(run * 1.4426950408889634f) : expf(run);
-            sKd[c * RS + acc_pos(p * TP + u)] = Op::cvt(kv[u] * dec);
+            kd[u] = Op::cvt(kv[u] * dec);
             run += la[u];
+        }
+        // four consecutive tokens sit at four adjacent positions of the accumulator order
+        // (rows 8- or 16-byte aligned): one write each
+#pragma unroll
+        for (int m = 0; m < TP / 4; ++m) {
+            E* dst = sKd + c * RS + acc_pos(p * TP + 4 * m);
+            if constexpr (BF) {
+                halfx4 w = {kd[4 * m], kd[4 * m + 1], kd[4 * m + 2], kd[4 * m + 3]};
+                *reinterpret_cast<halfx4*>(dst) = w;
+            } else {
+                *reinterpret_cast<float4*>(dst) = make_float4(kd[4 * m], kd[4 * m + 1], kd[4 * m + 2], kd[4 * m + 3]);
+            }
         }
         float rn = rR;
         for (int q = 0; q < NP; ++q) rn += sPart[q * D + c];

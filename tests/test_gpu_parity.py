@@ -291,6 +291,34 @@ def test_diag_scalar_build_compose_and_naive(gpu, name, kind):
         assert naive_err > 10 * TOL_BF16   # decay makes naive addition structurally wrong
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("kind", ["scalar", "diag"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_diag_scalar_build_shapes(gpu, d, kind, dtype):
+    """Diagonal / scalar build at both head sizes with 32- and 16-bit inputs, on ragged segments:
+    empty, one token, a partial chunk, exactly one chunk, one token past it, and odd and even
+    chunk counts with ragged tails; against the oracle on the inputs as the kernel sees them."""
+    rng = np.random.default_rng(101 + d)
+    lens = [0, 1, 63, 64, 65, 200, 130, 256]
+    n, h = sum(lens), 2
+    k = rng.standard_normal((n, h, d))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((n, h, d))
+    if kind == "scalar":
+        la = np.log1p(-(2.0 ** -rng.uniform(3.0, 8.0, size=(n, h))))
+    else:
+        la = -np.logaddexp(0.0, -(2.0 + rng.standard_normal((n, h, d)))) / 16.0   # log sigmoid / 16
+    la = la.astype(np.float32).astype(np.float64)   # the gates as the kernel reads them
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    kt, vt = torch.from_numpy(k).to(tdt), torch.from_numpy(v).to(tdt)
+    out = H.hypic_segment_build(kt[None].cuda(), vt[None].cuda(), dev_tensor(la[None]), cu_of(lens), kind=kind)
+    torch.cuda.synchronize()
+    kr, vr = kt.double().numpy(), vt.double().numpy()
+    chains = [{"k": kr[:, i], "v": vr[:, i], "log_alpha": la[:, i]} for i in range(h)]
+    e_T, e_S = _check_build(out, chains, lens, kind, TOL_BF16 if dtype == "bf16" else TOL_F32)
+    print(f"{kind} d={d} {dtype}: T {e_T:.2e}, S {e_S:.2e}")
+
+
 # ----------------------------------------------------------------------------------------
 # seam advance
 
