@@ -238,59 +238,67 @@ __global__ __launch_bounds__(D * 6) void fold_dense_kernel(FoldArgs a) {
     }
 }
 
-// Diagonal (T a d_k vector) and scalar (T one value) kinds: elementwise.
+// Diagonal (T a d_k vector) and scalar (T one value) kinds: elementwise.  Entry (r, c) of the
+// state only ever meets T[r] (or the scalar T), so a chain's d x d state is split over NZ
+// workgroups of contiguous rows, each reading the T entries of its own rows directly (no LDS
+// exchange, no barrier on the state path).  The slice-0 workgroup also carries the running
+// product of the transitions, renormalised by its maximum after every element.
+template <int D>
+constexpr int fold_diag_slices() { return D * D / (256 * 4); }
+
 template <int D>
 __global__ __launch_bounds__(256) void fold_diag_kernel(FoldArgs a) {
     constexpr int NT = 256;
-    constexpr int PER = D * D / NT;
-    __shared__ float sT[D];
+    constexpr int PER = 4;                      // state entries per thread
+    constexpr int NZ = fold_diag_slices<D>();   // row slices per chain
+    constexpr int SL = D * D / NZ;              // entries per slice
+    static_assert(NZ * NT * PER == D * D && SL % D == 0, "slices of whole rows");
     __shared__ float sRed[4];
-    __shared__ int sEi;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int chain = blockIdx.x, blk = blockIdx.y;
+    const int chain = blockIdx.x, blk = blockIdx.y, z = blockIdx.z;
     const bool scalar = a.kind == 2;
+    const bool carry_T = a.out_T && z == 0;
     const int e0 = blk * a.per_block;
     const int e1 = min(a.n_elem, e0 + a.per_block);
     const long long DD = (long long)D * D;
     const int tlen = scalar ? 1 : D;
+    const int base = z * SL;
+    int trow[PER];  // T index of each entry's row
+#pragma unroll
+    for (int r = 0; r < PER; ++r) trow[r] = scalar ? 0 : (base + tid + NT * r) / D;
 
     float x[PER];
     if (a.init_S) {
-        const float* src = a.init_S + ((long long)blk * a.n_chain + chain) * DD;
+        const float* src = a.init_S + ((long long)blk * a.n_chain + chain) * DD + base;
 #pragma unroll
         for (int r = 0; r < PER; ++r) x[r] = src[tid + NT * r];
     } else {
 #pragma unroll
         for (int r = 0; r < PER; ++r) x[r] = 0.f;
     }
-    float tv = 1.f;  // thread tid < tlen owns T[tid]
+    float tv = 1.f;  // slice 0: thread tid < tlen owns T[tid]
     int te = 0;
     for (int el = e0; el < e1; ++el) {
         const int slot = a.slot ? a.slot[el] : el;
         const long long so = (long long)slot * a.n_chain + chain;
         if (a.prefix) {
-            float* dst = a.prefix + ((long long)el * a.n_chain + chain) * DD;
+            float* dst = a.prefix + ((long long)el * a.n_chain + chain) * DD + base;
 #pragma unroll
             for (int r = 0; r < PER; ++r) dst[tid + NT * r] = x[r];
         }
-        const float* Si = a.S + so * DD;
+        const float* Si = a.S + so * DD + base;
         if (a.naive) {
 #pragma unroll
             for (int r = 0; r < PER; ++r) x[r] += Si[tid + NT * r];
             continue;
         }
-        if (tid < tlen) sT[tid] = a.T_hat[so * tlen + tid];
-        if (tid == 0) sEi = a.T_exp[so];
-        __syncthreads();
-        const int ei = sEi;
+        const float* Ti = a.T_hat + so * tlen;
+        const int ei = a.T_exp[so];
 #pragma unroll
-        for (int r = 0; r < PER; ++r) {
-            const int row = (tid + NT * r) / D;
-            x[r] = ldexpf((scalar ? sT[0] : sT[row]) * x[r], ei) + Si[tid + NT * r];
-        }
-        if (a.out_T) {
+        for (int r = 0; r < PER; ++r) x[r] = ldexpf(Ti[trow[r]] * x[r], ei) + Si[tid + NT * r];
+        if (carry_T) {
             // running product of transitions, renormalised by the block max
-            if (tid < tlen) tv *= sT[tid];
+            if (tid < tlen) tv *= Ti[tid];
             float m = tid < tlen ? fabsf(tv) : 0.f;
             m = wave_max(m);
             if (lane == 0) sRed[wave] = m;
@@ -299,22 +307,21 @@ __global__ __launch_bounds__(256) void fold_diag_kernel(FoldArgs a) {
             const int e = exp2_of(mm);
             tv = ldexpf(tv, -e);
             te += ei + e;
+            __syncthreads();
         }
-        __syncthreads();
     }
     if (a.out_S) {
-        float* dst = a.out_S + ((long long)blk * a.n_chain + chain) * DD;
+        float* dst = a.out_S + ((long long)blk * a.n_chain + chain) * DD + base;
 #pragma unroll
         for (int r = 0; r < PER; ++r) dst[tid + NT * r] = x[r];
     }
-    if (a.out_T) {
+    if (carry_T) {
         if (tid < tlen) a.out_T[((long long)blk * a.n_chain + chain) * tlen + tid] = tv;
         if (tid == 0) a.out_e[(long long)blk * a.n_chain + chain] = te;
     }
 }
 
 hipError_t launch_fold(const FoldArgs& a, int d, int with_T, hipStream_t s) {
-    const dim3 grid(a.n_chain, a.n_block);
     if (a.kind == 0 && !a.naive) {
         // role 1 (the composed transition) only when its outputs are wanted
         const dim3 g3(a.n_chain, a.n_block, (with_T && a.out_T) ? 2 : 1);
@@ -323,8 +330,10 @@ hipError_t launch_fold(const FoldArgs& a, int d, int with_T, hipStream_t s) {
         else return hipErrorInvalidValue;
     } else {
         // naive addition of any kind, and the diagonal / scalar kinds
-        if (d == 128) hipLaunchKernelGGL((fold_diag_kernel<128>), grid, dim3(256), 0, s, a);
-        else if (d == 64) hipLaunchKernelGGL((fold_diag_kernel<64>), grid, dim3(256), 0, s, a);
+        if (d == 128)
+            hipLaunchKernelGGL((fold_diag_kernel<128>), dim3(a.n_chain, a.n_block, fold_diag_slices<128>()), dim3(256), 0, s, a);
+        else if (d == 64)
+            hipLaunchKernelGGL((fold_diag_kernel<64>), dim3(a.n_chain, a.n_block, fold_diag_slices<64>()), dim3(256), 0, s, a);
         else return hipErrorInvalidValue;
     }
     return hipGetLastError();

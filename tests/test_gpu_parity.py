@@ -133,6 +133,42 @@ def test_compose_random_elements(gpu, d):
             assert max(eS, eT, eP) < TOL_F32, (mode, blk, c, eS, eT, eP)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("kind", ["scalar", "diag"])
+def test_compose_random_elements_diag_scalar(gpu, d, kind):
+    """Diagonal / scalar compose of random elements with slots, an initial state, prefix states
+    and the composed transition, in every mode, and naive addition; against the oracle's fold."""
+    n_slot, n_chain, n_elem = 23, 3, 37
+    rng = np.random.default_rng([13, d, len(kind)])
+    tshape = (n_slot, n_chain, d) if kind == "diag" else (n_slot, n_chain)
+    T_hat = rng.uniform(0.5, 1.0, size=tshape).astype(np.float32)
+    T_exp = rng.integers(-3, 1, size=(n_slot, n_chain)).astype(np.int32)
+    S = rng.standard_normal((n_slot, n_chain, d, d)).astype(np.float32)
+    slot = rng.integers(0, n_slot, size=n_elem).astype(np.int32)
+    S0 = rng.standard_normal((n_chain, d, d)).astype(np.float32)
+    refs = []
+    for c in range(n_chain):
+        elems = [{"T_hat": T_hat[s, c], "T_exp": T_exp[s, c], "S": S[s, c]} for s in slot]
+        refs.append((O.compose_fold(kind, elems, S0=S0[c]), O.naive_add(elems, S0=S0[c])))
+    Td, ed, Sd = dev_tensor(T_hat), dev_tensor(T_exp, torch.int32), dev_tensor(S)
+    sd, S0d = dev_tensor(slot, torch.int32), dev_tensor(S0)
+    for mode, blk in (("fold", 0), ("scan", 0), ("scan", 5), ("auto", 0)):
+        r = H.hypic_compose(Td, ed, Sd, kind=kind, slot=sd, S0=S0d, mode=mode, want_T=True, want_prefix=True,
+                            scan_block=blk)
+        torch.cuda.synchronize()
+        for c in range(n_chain):
+            ref = refs[c][0]
+            eS = float(O.rel_err(r["S_final"][c].cpu().numpy(), ref["S_final"]))
+            eT = float(O.rel_err_T(kind, r["T_total"][c].cpu().numpy(), int(r["T_total_exp"][c]),
+                                   ref["T_hat"], ref["T_exp"]))
+            eP = float(np.max(O.rel_err(r["S_prefix"][:, c].cpu().numpy(), ref["S_prefix"])))
+            assert max(eS, eT, eP) < TOL_F32, (mode, blk, c, eS, eT, eP)
+    r = H.hypic_compose(None, None, Sd, kind=kind, slot=sd, S0=S0d, mode="naive_add")
+    torch.cuda.synchronize()
+    for c in range(n_chain):
+        assert float(O.rel_err(r["S_final"][c].cpu().numpy(), refs[c][1])) < TOL_F32
+
+
 # ----------------------------------------------------------------------------------------
 # bf16 dense build: ragged segments spanning several chunks, empty segments, GQA
 
