@@ -58,7 +58,9 @@ __global__ __launch_bounds__(512) void diag_build_kernel(DiagArgs a) {
     const int len = a.seg_len[seg];
     const long long chain = (long long)seg * a.n_batch * a.h_v + (long long)b * a.h_v + h;
     // thread (c, p): channel c of the decayed keys over token part p of a chunk
-    const int c = tid % D, p = tid / D;
+    // p is uniform over a wave (D >= 64): per-token offsets and bounds stay in scalar registers
+    const int c = tid % D, p = __builtin_amdgcn_readfirstlane(tid / D);
+    static_assert(D % kWave == 0, "token parts cover whole waves");
     const int cg = tid % 32, tg = tid / 32;
 
     floatx16 acc[TPW];
