@@ -300,6 +300,52 @@ def test_diag_closed_form():
     assert np.max(O.rel_err(r["S"], S)) < 1e-13
 
 
+@pytest.mark.parametrize("kind", ["diag", "scalar"])
+def test_diag_scalar_compose_equals_whole_chain(kind):
+    # Composition law (HYPIC news article, linear-layer paragraph) for the decaying families,
+    # with gates strong enough that every segment's T_hat carries an exponent <= -3: a sign or
+    # index slip in how apply_T / compose_T use the exponent changes S and T by powers of two.
+    rng = np.random.default_rng(31)
+    n, dk, dv = 240, 6, 4
+    k, v = rng.standard_normal((n, dk)), rng.standard_normal((n, dv))
+    if kind == "diag":
+        la = -0.08 - 0.1 * rng.random((n, dk))
+        rec = lambda lo, hi: O.diag_recurrence(k[lo:hi], v[lo:hi], la[lo:hi], renorm_every=7)
+    else:
+        la = np.log(0.9) * (1.0 + 0.5 * rng.random(n))
+        rec = lambda lo, hi: O.scalar_recurrence(k[lo:hi], v[lo:hi], la[lo:hi], renorm_every=7)
+    # G[t] = sum of log alpha over tokens 0..t-1, per channel (scalar: the same for all)
+    G = np.zeros((n + 1, dk))
+    G[1:] = np.cumsum(la if kind == "diag" else la[:, None] * np.ones(dk), axis=0)
+    S0 = rng.standard_normal((dk, dv))
+
+    def closed(hi):
+        """State after tokens [0, hi) from S0: e^{G_hi} S0 + sum_t e^{G_hi - G_{t+1}} k_t v_t^T."""
+        S = np.exp(G[hi])[:, None] * S0
+        for t in range(hi):
+            S = S + np.exp(G[hi] - G[t + 1])[:, None] * np.outer(k[t], v[t])
+        return S
+
+    cuts = [0, 37, 90, 130, 160, 240]
+    els = [_as_el(rec(lo, hi)) for lo, hi in zip(cuts[:-1], cuts[1:])]
+    assert all(int(e["T_exp"]) <= -3 for e in els)
+    f = O.compose_fold(kind, els, S0=S0)
+    assert np.max(O.rel_err(f["S_final"], closed(n))) < 1e-12
+    Tf = O.T_value(kind, f["T_hat"], f["T_exp"])
+    Tn = np.exp(G[n]) if kind == "diag" else np.exp(G[n, 0])
+    assert np.max(np.abs(Tf - Tn)) < 1e-12 * np.max(np.abs(Tn))
+    for i, lo in enumerate(cuts[:-1]):          # the state entering each element
+        assert np.max(O.rel_err(f["S_prefix"][i], closed(lo))) < 1e-12
+    # pairwise affine_compose in a tree gives the same element as the whole chain
+    ab = O.affine_compose(kind, els[0], els[1])
+    cde = O.affine_compose(kind, O.affine_compose(kind, els[2], els[3]), els[4])
+    tot = O.affine_compose(kind, ab, cde)
+    whole = rec(0, n)
+    assert np.max(O.rel_err(tot["S"], whole["S"])) < 1e-12
+    assert np.max(O.rel_err_T(kind, tot["T_hat"], tot["T_exp"], whole["T_hat"], whole["T_exp"])) < 1e-12
+    assert np.max(O.rel_err(O.apply_T(kind, tot["T_hat"], tot["T_exp"], S0) + tot["S"], closed(n))) < 1e-12
+
+
 def test_scalar_closed_form_and_diag_agreement():
     rng = np.random.default_rng(16)
     n, dk, dv, g = 70, 5, 3, 0.97
