@@ -33,9 +33,22 @@
  *     failure nothing is enqueued, the call returns a status != HYPIC_OK and
  *     hypic_last_error() (thread-local) describes the problem.  A launch
  *     failure returns HYPIC_ERR_DEVICE.  Device faults surface at the caller's
- *     next synchronisation.  Every call is asynchronous on `stream`
- *     (NULL = the null stream); host arrays may be freed when the call returns.
+ *     next synchronisation.  Every call enqueues its work on `stream` (NULL =
+ *     the null stream) and host arrays may be freed when the call returns.
+ *     The host segment table (cu_seqlens / cu_seam) of at most 160 segments
+ *     travels inside the kernel arguments: such a call copies nothing, needs no
+ *     workspace and returns without waiting for the device.  A larger table is
+ *     uploaded into the call's workspace by a copy from pageable host memory,
+ *     which blocks the calling thread until the runtime has staged it.
  *   - NaN/Inf inputs propagate; they are not checked.
+ *   - f16 operand range (the dense kind under HYPIC_PREC_F16, which AUTO picks
+ *     for bf16 inputs, and the diagonal/scalar build with bf16 inputs): v, S
+ *     and the chunk intermediates enter the matrix cores as f16, so |v| and |S|
+ *     must stay below 2^15 (the largest f16 is 65504) and values below 2^-14
+ *     lose relative precision (f16 subnormals; zero below 2^-25).  k is
+ *     expected L2-normalised (|k| <= 1).  T is renormalised by powers of two and
+ *     has no range limit.  S and o are linear in v, so a caller with v outside
+ *     this range scales v by a power of two and S and o back.
  *   - Supported shapes: d_k == d_v in {64, 128}; chunk == 64; conv width 4.
  *     Anything else returns HYPIC_ERR_UNSUPPORTED.
  *   - Outputs are bitwise reproducible run to run and independent of the
@@ -83,8 +96,13 @@ typedef enum {
     HYPIC_SCHED_RR = 2       /* persistent workgroups, task i -> slot i mod n_slots   */
 } hypic_schedule;
 
-/* Operand precision of the dense build's matrix-core products.  Accumulation
- * is always float32.  AUTO: F32 for float32 inputs, F16 for bf16 inputs. */
+/* Operand precision of the dense kind's matrix-core products (the segment build
+ * and seams longer than 16 tokens; shorter seams always run in float32 vector
+ * arithmetic).  Accumulation is always float32.
+ *   AUTO: F16 for bf16 inputs; F32 for float32 inputs at d = 64.  There is no
+ *         float32-operand plan at d = 128, so float32 inputs at d = 128 return
+ *         HYPIC_ERR_UNSUPPORTED under AUTO; ask for F16 explicitly to accept f16
+ *         operands (relative error about 1e-3 instead of about 1e-6). */
 typedef enum {
     HYPIC_PREC_AUTO = 0,
     HYPIC_PREC_F32 = 1, /* float32 operands (fp32 matrix cores), for fp32 inputs   */
@@ -127,9 +145,9 @@ typedef enum { HYPIC_ACT_NONE = 0, HYPIC_ACT_SILU = 1 } hypic_activation;
  *   S           float32 [n_seg, B, h_v, d_k, d_v]
  * Outputs are segment-major so that they serve directly as the element store
  * of hypic_compose (slot = segment, chain = b * h_v + h).
- * Requires a workspace of hypic_segment_build_workspace_bytes() bytes
- * (device memory, 256-byte aligned) that stays untouched until the call's
- * work on `stream` has finished.
+ * Workspace: hypic_segment_build_workspace_bytes() bytes of device memory,
+ * 256-byte aligned, untouched until the call's work on `stream` has finished;
+ * 0 (workspace may be NULL) for at most 160 segments.
  * ---------------------------------------------------------------------------------- */
 typedef struct {
     hypic_kind kind;
@@ -217,7 +235,8 @@ size_t hypic_compose_workspace_bytes(const hypic_compose_desc* desc);
  *
  * Seam s covers tokens [cu_seam[s], cu_seam[s+1]) of the packed seam axis
  * (any length; w <= 64 runs as a single chunk).  Needs
- * hypic_seam_advance_workspace_bytes() of device workspace (the seam table).
+ * hypic_seam_advance_workspace_bytes() of device workspace (0 for at most 160
+ * seams).
  * Layouts (B = n_batch, N = n_tokens = packed seam tokens):
  *   q, k        [B, N, h_k, d_k]  in_dtype;   v [B, N, h_v, d_v] in_dtype
  *   log_alpha, beta  float32 [B, N, h_v]
@@ -276,7 +295,7 @@ size_t hypic_seam_advance_workspace_bytes(const hypic_seam_desc* desc);
  *   y          [B, N, C] out_dtype
  *   state_out  [n_seg, B, W-1, C] in_dtype, or NULL
  * channels must be a multiple of 8.  Needs hypic_conv_warmup_workspace_bytes()
- * of device workspace (the segment table).
+ * of device workspace (0 for at most 160 segments).
  * ---------------------------------------------------------------------------------- */
 typedef struct {
     hypic_dtype in_dtype;
@@ -317,6 +336,34 @@ size_t hypic_conv_warmup_workspace_bytes(const hypic_conv_desc* desc);
 hypic_status hypic_plan_schedule(const int64_t* weights, int32_t n, int32_t groups,
                                  hypic_schedule schedule, int32_t* order, int32_t* assign,
                                  int64_t* makespan);
+
+/* ------------------------------------------------------------------------------------
+ * hypic_seam_widths -- the seam window width of each segment from the seam-width knob
+ * ([readme], "PIC modes": the knob is independent of the compose mode, default 8;
+ * [news], seam-window paragraph: the first w tokens of a reused segment are recomputed).
+ *
+ * Host-only integer arithmetic, no GPU use.  For each of the n segments of length
+ * seg_lens[i] (host int64, >= 0) writes w[i] (host int32):
+ *   sink == 0         -> 0 (the whole cached segment is reused, no seam);
+ *   0 < sink <= 1     -> ceil(sink * len), a fraction of the segment;
+ *   sink > 1          -> floor(sink), an absolute token count;
+ * always capped at len.  The widths feed cu_seam of hypic_seam_advance and skip_head
+ * of hypic_segment_build.  Returns HYPIC_ERR_INVALID_ARGUMENT for n < 0, NULL arrays
+ * with n > 0, a negative length, or a negative or non-finite sink.
+ * ---------------------------------------------------------------------------------- */
+#define HYPIC_SEAM_SINK_DEFAULT 8.0
+hypic_status hypic_seam_widths(const int64_t* seg_lens, int32_t n, double sink, int32_t* w);
+
+/* ------------------------------------------------------------------------------------
+ * hypic_device_status -- device-side invariant check.
+ *
+ * Synchronises the current device, then reads and clears its sticky status word.  The
+ * dense build's waves hand work to each other through bounded waits on LDS counters; a
+ * wait that runs out (a hand-off that never came) lets the kernel finish and sets the
+ * word.  Returns HYPIC_OK, or HYPIC_ERR_DEVICE (with a message) when any launch since
+ * the previous call set it: the outputs of those launches are unreliable.
+ * ---------------------------------------------------------------------------------- */
+hypic_status hypic_device_status(void);
 
 const char* hypic_last_error(void);
 int hypic_version(void);

@@ -9,8 +9,10 @@ and only marshal arguments, with torch providing device memory and streams.
 from .api import (  # noqa: F401
     hypic_compose,
     hypic_conv_warmup,
+    hypic_device_status,
     hypic_plan_schedule,
     hypic_seam_advance,
+    hypic_seam_widths,
     hypic_segment_build,
 )
 from ._abi import HypicError, LIB_PATH, lib  # noqa: F401

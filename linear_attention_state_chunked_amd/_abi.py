@@ -20,6 +20,8 @@ PREC = {"auto": 0, "f32": 1, "f16": 2}
 COMPOSE = {"auto": 0, "fold": 1, "scan": 2, "naive_add": 3}
 ACT = {"none": 0, "silu": 1}
 KIND = {"dense": DENSE, "diag": DIAG, "scalar": SCALAR}
+INLINE_SEGS = 160          # segment tables up to this size need no workspace
+SEAM_SINK_DEFAULT = 8.0
 
 _p = C.c_void_p
 _i32 = C.c_int32
@@ -78,6 +80,8 @@ EXPORTS = {
     "hypic_conv_warmup": ([C.POINTER(ConvDesc), _p], _enum),
     "hypic_conv_warmup_workspace_bytes": ([C.POINTER(ConvDesc)], C.c_size_t),
     "hypic_plan_schedule": ([_p, _i32, _i32, _enum, _p, _p, _p], _enum),
+    "hypic_seam_widths": ([_p, _i32, C.c_double, _p], _enum),
+    "hypic_device_status": ([], _enum),
     "hypic_last_error": ([], C.c_char_p),
     "hypic_version": ([], C.c_int),
 }

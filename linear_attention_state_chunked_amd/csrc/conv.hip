@@ -38,10 +38,10 @@ __global__ __launch_bounds__(256) void conv_kernel(ConvArgs a) {
     const int seg = blockIdx.y, b = blockIdx.z;
     const int tb = (int)(i / groups);
     const int c0 = 8 * (int)(i - (long long)tb * groups);
-    const int len = a.seg_len[seg];
+    const int len = seg_len(a.seg, seg);
     const int nblk = max((len + kConvT - 1) / kConvT, 1);   // block 0 also writes state_out
     if (tb >= nblk) return;
-    const long long start = a.seg_start[seg];
+    const long long start = seg_start(a.seg, seg);
     const bool in_bf16 = a.in_bf16 != 0;
     const long long C = a.channels;
     int srow = -1;

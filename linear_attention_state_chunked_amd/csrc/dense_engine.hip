@@ -92,15 +92,15 @@ __global__ __launch_bounds__(D * 4) void dense_engine_kernel(EngineArgs a) {
 
     // one task per workgroup, or a grid-stride loop over tasks (static round robin)
     for (int it = blockIdx.x; it < a.n_tasks; it += PERSIST ? (int)gridDim.x : a.n_tasks) {
-        const int task = a.order ? a.order[it] : it;
         const int per_seg = a.n_batch * a.h_v;
+        const int task = task_at(a.seg, it, per_seg);
         const int seg = task / per_seg;
         const int rem = task - seg * per_seg;
         const int b = rem / a.h_v;
         const int h = rem - b * a.h_v;
         const int hk = (h * a.h_k) / a.h_v;
-        const long long start = a.seg_start[seg];
-        const int len = a.seg_len[seg];
+        const long long start = seg_start(a.seg, seg);
+        const int len = seg_len(a.seg, seg);
         const long long chain_off = (long long)b * a.h_v + h;
 
         // ---- X = [I | S_in]

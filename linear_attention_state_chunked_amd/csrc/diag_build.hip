@@ -48,14 +48,14 @@ __global__ __launch_bounds__(512) void diag_build_kernel(DiagArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, l32 = lane & 31;
     const long long N = a.n_tokens;
 
-    const int task = a.order ? a.order[blockIdx.x] : blockIdx.x;
     const int per_seg = a.n_batch * a.h_v;
+    const int task = task_at(a.seg, blockIdx.x, per_seg);
     const int seg = task / per_seg;
     const int rem = task - seg * per_seg;
     const int b = rem / a.h_v, h = rem - (rem / a.h_v) * a.h_v;
     const int hk = (h * a.h_k) / a.h_v;
-    const long long start = a.seg_start[seg];
-    const int len = a.seg_len[seg];
+    const long long start = seg_start(a.seg, seg);
+    const int len = seg_len(a.seg, seg);
     const long long chain = (long long)seg * a.n_batch * a.h_v + (long long)b * a.h_v + h;
     // thread (c, p): channel c of the decayed keys over token part p of a chunk
     // p is uniform over a wave (D >= 64): per-token offsets and bounds stay in scalar registers

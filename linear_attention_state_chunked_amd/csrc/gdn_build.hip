@@ -213,6 +213,17 @@ struct GLayout {
     static constexpr int zero_begin = TgA, zero_end = Gv;
 };
 
+// Sticky status word of this device (see take_device_status).
+__device__ unsigned int g_device_status;
+
+// A bounded wait ran out: the hand-off it waited for never came.  The wave goes on, so the
+// kernel still ends, and the status word records that this launch's outputs are unreliable.
+__device__ __forceinline__ void wait_expired() {
+    __hip_atomic_fetch_or(&g_device_status, kStatusWaitExpired, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+constexpr int kSpinLimit = 1 << 18;
+
 // bounded LDS-counter barrier among a subset of waves (one arrival per wave); the polls do
 // not sleep: a poll is one broadcast LDS read, and a sleep would add its wake-up delay to
 // every hand-off on the critical path
@@ -221,7 +232,10 @@ __device__ __forceinline__ void prep_barrier(int* cnt, int target, int lane) {
     if (lane == 0) __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     int spins = 0;
     while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target) {
-        if (++spins > (1 << 18)) break;  // never hang: a broken invariant gives wrong data, not a hang
+        if (++spins > kSpinLimit) {
+            wait_expired();
+            break;
+        }
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
@@ -236,7 +250,10 @@ __device__ __forceinline__ void count_arrival(int* cnt, int lane) {
 __device__ __forceinline__ void wait_count(int* cnt, int target) {
     int spins = 0;
     while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target) {
-        if (++spins > (1 << 18)) break;  // never hang: a broken invariant gives wrong data, not a hang
+        if (++spins > kSpinLimit) {
+            wait_expired();
+            break;
+        }
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
@@ -491,15 +508,15 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
             // group keeps its order); in the stream each group must lie inside the grid.
             const int pair_bound = STREAM ? (int)gridDim.x : a.n_tasks;
             const int it = (it0 | 15) < pair_bound ? (it0 & ~15) | (2 * (it0 & 7) + ((it0 >> 3) & 1)) : it0;
-            const int task = (!STREAM && a.order) ? a.order[it] : it;
             const int per_seg = a.n_batch * a.h_v;
+            const int task = STREAM ? it : task_at(a.seg, it, per_seg);
             const int seg = task / per_seg;
             const int rem = task - seg * per_seg;
             const int b = rem / a.h_v;
             const int h = rem - b * a.h_v;
             const int hk = (h * a.h_k) / a.h_v;
-            const long long start = STREAM ? a.stream_start0 + seg * a.stream_stride : a.seg_start[seg];
-            const int len = STREAM ? a.stream_len : a.seg_len[seg];
+            const long long start = STREAM ? a.stream_start0 + seg * a.stream_stride : seg_start(a.seg, seg);
+            const int len = STREAM ? a.stream_len : seg_len(a.seg, seg);
             const int ncT = (len + 63) / 64;                 // chunks per task
             const int ntw = STREAM ? (a.n_tasks - it + (int)gridDim.x - 1) / (int)gridDim.x : 1;
             const int nc = ncT * ntw;                        // chunks in this pass
@@ -1041,6 +1058,15 @@ template <int D, bool IN_BF16>
 static hipError_t launch_t(const EngineArgs& a, int grid, hipStream_t s) {
     if (!a.T_hat) return launch_v<D, false, IN_BF16, false>(a, grid, s);
     return a.precise_T ? launch_v<D, true, IN_BF16, true>(a, grid, s) : launch_v<D, true, IN_BF16, false>(a, grid, s);
+}
+
+hipError_t take_device_status(unsigned* out) {
+    unsigned v = 0;
+    const unsigned z = 0;
+    hipError_t e = hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_device_status), sizeof v, 0, hipMemcpyDeviceToHost);
+    if (e == hipSuccess && v) e = hipMemcpyToSymbol(HIP_SYMBOL(g_device_status), &z, sizeof z, 0, hipMemcpyHostToDevice);
+    *out = v;
+    return e;
 }
 
 hipError_t launch_gdn_build(const EngineArgs& a, int d, int prec_f32, int grid, hipStream_t s) {

@@ -62,29 +62,61 @@ hypic_status check_offsets(const int64_t* cu, int32_t n, int64_t limit, const ch
     return HYPIC_OK;
 }
 
-// Segment table uploaded to the workspace: starts (int64), lengths (int32), task order.
-struct SegTable {
+// Segment table of a launch.  Up to hypic::kInlineSegs segments it travels inside the
+// kernel arguments: no copy, no workspace, and the call is asynchronous.  A larger table
+// (starts int64, lengths int32, segment order int32) is uploaded to the workspace.
+struct SegTableLayout {
     size_t off_start = 0, off_len = 0, off_order = 0, bytes = 0;
 };
 
-SegTable seg_table_layout(int32_t n_seg, int64_t n_order) {
-    SegTable t;
+SegTableLayout seg_table_layout(int32_t n_seg) {
+    SegTableLayout t;
+    if (n_seg <= hypic::kInlineSegs) return t;
     t.off_start = 0;
-    t.off_len = align_up(sizeof(int64_t) * std::max<int64_t>(n_seg, 1));
-    t.off_order = t.off_len + align_up(sizeof(int32_t) * std::max<int64_t>(n_seg, 1));
-    t.bytes = t.off_order + align_up(sizeof(int32_t) * std::max<int64_t>(n_order, 0));
+    t.off_len = align_up(sizeof(int64_t) * n_seg);
+    t.off_order = t.off_len + align_up(sizeof(int32_t) * n_seg);
+    t.bytes = t.off_order + align_up(sizeof(int32_t) * n_seg);
     return t;
 }
 
-// host image of the segment table, copied in one transfer
-hipError_t upload_seg_table(const SegTable& L, void* ws, const std::vector<int64_t>& start,
-                            const std::vector<int32_t>& len, const std::vector<int32_t>& order, hipStream_t s) {
+// Fill `t` for segments (start, len) processed in `order` (empty = natural order).  A table
+// too large for the kernel arguments goes to the workspace in one transfer from pageable
+// host memory: the runtime stages it before returning, so the host arrays may die afterwards.
+hipError_t fill_seg_table(hypic::SegTable& t, const SegTableLayout& L, void* ws, const std::vector<int64_t>& start,
+                          const std::vector<int32_t>& len, const std::vector<int32_t>& order, hipStream_t s) {
+    const int32_t n = (int32_t)start.size();
+    t.n = n;
+    t.has_order = order.empty() ? 0 : 1;
+    if (n <= hypic::kInlineSegs) {
+        t.inl = 1;
+        for (int32_t i = 0; i < n; ++i) {
+            t.start[i] = start[i];
+            t.len[i] = len[i];
+            t.order[i] = order.empty() ? i : order[i];
+        }
+        return hipSuccess;
+    }
+    t.inl = 0;
     std::vector<unsigned char> img(L.bytes, 0);
-    if (!start.empty()) memcpy(img.data() + L.off_start, start.data(), start.size() * sizeof(int64_t));
-    if (!len.empty()) memcpy(img.data() + L.off_len, len.data(), len.size() * sizeof(int32_t));
+    memcpy(img.data() + L.off_start, start.data(), start.size() * sizeof(int64_t));
+    memcpy(img.data() + L.off_len, len.data(), len.size() * sizeof(int32_t));
     if (!order.empty()) memcpy(img.data() + L.off_order, order.data(), order.size() * sizeof(int32_t));
-    // pageable source: the runtime stages it before returning, so img may die afterwards
+    unsigned char* w = static_cast<unsigned char*>(ws);
+    t.start_p = reinterpret_cast<const long long*>(w + L.off_start);
+    t.len_p = reinterpret_cast<const int*>(w + L.off_len);
+    t.order_p = reinterpret_cast<const int*>(w + L.off_order);
     return hipMemcpyAsync(ws, img.data(), L.bytes, hipMemcpyHostToDevice, s);
+}
+
+// The workspace a call needs for its segment table: present when L.bytes > 0, aligned.
+hypic_status check_workspace(const char* who, size_t need, void* ws, size_t have) {
+    if (need == 0) return HYPIC_OK;
+    if (!ws || have < need)
+        return fail(HYPIC_ERR_WORKSPACE_TOO_SMALL, "%s: workspace of %zu bytes needed, %zu given", who, need,
+                    ws ? have : (size_t)0);
+    if (reinterpret_cast<uintptr_t>(ws) % kAlign)
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "%s: workspace must be 256-byte aligned", who);
+    return HYPIC_OK;
 }
 
 bool supported_d(int d) { return d == 64 || d == 128; }
@@ -136,10 +168,12 @@ hypic_status validate_build(const hypic_build_desc* d) {
     if (d->precision < HYPIC_PREC_AUTO || d->precision > HYPIC_PREC_F16)
         return fail(HYPIC_ERR_INVALID_ARGUMENT, "build: unknown precision %d", (int)d->precision);
     if (d->kind == HYPIC_DENSE_DELTA) {
-        const bool f32 = d->precision == HYPIC_PREC_F32 ||
-                         (d->precision == HYPIC_PREC_AUTO && d->in_dtype == HYPIC_F32 && d->d_k == 64);
-        if (f32 && d->d_k != 64)
+        if (d->precision == HYPIC_PREC_F32 && d->d_k != 64)
             return fail(HYPIC_ERR_UNSUPPORTED, "build: the F32 operand plan supports d = 64 only");
+        if (d->precision == HYPIC_PREC_AUTO && d->in_dtype == HYPIC_F32 && d->d_k != 64)
+            return fail(HYPIC_ERR_UNSUPPORTED,
+                        "build: float32 inputs at d = %d have no float32-operand plan; request "
+                        "HYPIC_PREC_F16 explicitly to accept f16 operands (about 1e-3 relative error)", d->d_k);
     }
     return HYPIC_OK;
 }
@@ -161,16 +195,13 @@ int device_cu_count() {
     return n;
 }
 
-// LPT order of segments (longest first, ties by index), expanded to tasks.
-std::vector<int32_t> lpt_task_order(const std::vector<int32_t>& len, int32_t per_seg) {
+// LPT order of segments: longest first, ties by index.  The tasks of one segment (its
+// batch rows and heads) stay together; the kernels expand a segment position to its tasks.
+std::vector<int32_t> lpt_segment_order(const std::vector<int32_t>& len) {
     std::vector<int32_t> segs(len.size());
     std::iota(segs.begin(), segs.end(), 0);
     std::stable_sort(segs.begin(), segs.end(), [&](int32_t a, int32_t b) { return len[a] > len[b]; });
-    std::vector<int32_t> order;
-    order.reserve(segs.size() * per_seg);
-    for (int32_t s : segs)
-        for (int32_t j = 0; j < per_seg; ++j) order.push_back(s * per_seg + j);
-    return order;
+    return segs;
 }
 
 }  // namespace
@@ -179,6 +210,45 @@ std::vector<int32_t> lpt_task_order(const std::vector<int32_t>& len, int32_t per
 
 const char* hypic_last_error(void) { return g_err.c_str(); }
 int hypic_version(void) { return HYPIC_VERSION; }
+
+hypic_status hypic_device_status(void) {
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) return device_fail("device status: synchronize", e);
+    unsigned flags = 0;
+    e = hypic::take_device_status(&flags);
+    if (e != hipSuccess) return device_fail("device status: read", e);
+    if (flags & hypic::kStatusWaitExpired)
+        return fail(HYPIC_ERR_DEVICE,
+                    "device status: a bounded wait inside the dense build gave up (a hand-off between the "
+                    "waves of a workgroup never came); outputs since the last status call are unreliable");
+    if (flags) return fail(HYPIC_ERR_DEVICE, "device status: flags 0x%x", flags);
+    return ok();
+}
+
+hypic_status hypic_seam_widths(const int64_t* seg_lens, int32_t n, double sink, int32_t* w) {
+    if (n < 0) return fail(HYPIC_ERR_INVALID_ARGUMENT, "seam widths: n = %d < 0", n);
+    if (n > 0 && (!seg_lens || !w)) return fail(HYPIC_ERR_INVALID_ARGUMENT, "seam widths: NULL array");
+    if (!(sink >= 0.0) || sink > 1e18) return fail(HYPIC_ERR_INVALID_ARGUMENT, "seam widths: sink %g out of range", sink);
+    for (int32_t i = 0; i < n; ++i)
+        if (seg_lens[i] < 0) return fail(HYPIC_ERR_INVALID_ARGUMENT, "seam widths: segment %d has negative length", i);
+    for (int32_t i = 0; i < n; ++i) {
+        const int64_t len = seg_lens[i];
+        int64_t x;
+        if (sink == 0.0) {
+            x = 0;  // reuse the whole segment: no seam
+        } else if (sink <= 1.0) {
+            // a fraction of the segment: ceil(sink * len), computed exactly for the small
+            // lengths involved (len < 2^53)
+            const double f = sink * (double)len;
+            x = (int64_t)f;
+            if ((double)x < f) ++x;
+        } else {
+            x = (int64_t)sink;  // an absolute token count (the integer part)
+        }
+        w[i] = (int32_t)std::min<int64_t>(x, std::min<int64_t>(len, INT32_MAX));
+    }
+    return ok();
+}
 
 hypic_status hypic_plan_schedule(const int64_t* weights, int32_t n, int32_t groups, hypic_schedule schedule,
                                  int32_t* order, int32_t* assign, int64_t* makespan) {
@@ -219,8 +289,7 @@ hypic_status hypic_plan_schedule(const int64_t* weights, int32_t n, int32_t grou
 
 size_t hypic_segment_build_workspace_bytes(const hypic_build_desc* d) {
     if (!d || d->n_seg < 0) return 0;
-    const int64_t n_order = d->schedule == HYPIC_SCHED_LPT ? build_tasks(d) : 0;
-    return seg_table_layout(d->n_seg, n_order).bytes;
+    return seg_table_layout(d->n_seg).bytes;
 }
 
 hypic_status hypic_segment_build(const hypic_build_desc* d, hypic_stream_t stream) {
@@ -228,12 +297,9 @@ hypic_status hypic_segment_build(const hypic_build_desc* d, hypic_stream_t strea
     if (st != HYPIC_OK) return st;
     const int64_t n_tasks = build_tasks(d);
     if (n_tasks == 0) return ok();
-    const SegTable L = seg_table_layout(d->n_seg, d->schedule == HYPIC_SCHED_LPT ? n_tasks : 0);
-    if (!d->workspace || d->workspace_bytes < L.bytes)
-        return fail(HYPIC_ERR_WORKSPACE_TOO_SMALL, "build: workspace of %zu bytes needed, %zu given", L.bytes,
-                    d->workspace ? d->workspace_bytes : (size_t)0);
-    if (reinterpret_cast<uintptr_t>(d->workspace) % kAlign)
-        return fail(HYPIC_ERR_INVALID_ARGUMENT, "build: workspace must be 256-byte aligned");
+    const SegTableLayout L = seg_table_layout(d->n_seg);
+    st = check_workspace("build", L.bytes, d->workspace, d->workspace_bytes);
+    if (st != HYPIC_OK) return st;
 
     std::vector<int64_t> start(d->n_seg);
     std::vector<int32_t> len(d->n_seg);
@@ -242,14 +308,11 @@ hypic_status hypic_segment_build(const hypic_build_desc* d, hypic_stream_t strea
         len[i] = (int32_t)std::max<int64_t>(0, d->cu_seqlens[i + 1] - start[i]);
     }
     std::vector<int32_t> order;
-    if (d->schedule == HYPIC_SCHED_LPT) order = lpt_task_order(len, d->n_batch * d->h_v);
+    if (d->schedule == HYPIC_SCHED_LPT) order = lpt_segment_order(len);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    hipError_t e = upload_seg_table(L, d->workspace, start, len, order, s);
+    hypic::SegTable tab{};
+    hipError_t e = fill_seg_table(tab, L, d->workspace, start, len, order, s);
     if (e != hipSuccess) return device_fail("build: segment table upload", e);
-    unsigned char* ws = static_cast<unsigned char*>(d->workspace);
-    const long long* dstart = reinterpret_cast<const long long*>(ws + L.off_start);
-    const int* dlen = reinterpret_cast<const int*>(ws + L.off_len);
-    const int* dorder = order.empty() ? nullptr : reinterpret_cast<const int*>(ws + L.off_order);
 
     if (d->kind == HYPIC_DENSE_DELTA) {
         hypic::EngineArgs a{};
@@ -260,9 +323,7 @@ hypic_status hypic_segment_build(const hypic_build_desc* d, hypic_stream_t strea
         a.n_seg = d->n_seg;
         a.qk_l2norm = d->qk_l2norm;
         a.in_bf16 = d->in_dtype == HYPIC_BF16;
-        a.seg_start = dstart;
-        a.seg_len = dlen;
-        a.order = dorder;
+        a.seg = tab;
         a.n_tasks = (int)n_tasks;
         a.k = d->k;
         a.v = d->v;
@@ -302,7 +363,6 @@ hypic_status hypic_segment_build(const hypic_build_desc* d, hypic_stream_t strea
         }
         if (uniform) {
             a.stream = 1;
-            a.order = nullptr;
             a.stream_start0 = start[0];
             a.stream_stride = stride;
             a.stream_len = len[0];
@@ -318,9 +378,7 @@ hypic_status hypic_segment_build(const hypic_build_desc* d, hypic_stream_t strea
         a.n_seg = d->n_seg;
         a.scalar = d->kind == HYPIC_SCALAR;
         a.in_bf16 = d->in_dtype == HYPIC_BF16;
-        a.seg_start = dstart;
-        a.seg_len = dlen;
-        a.order = dorder;
+        a.seg = tab;
         a.n_tasks = (int)n_tasks;
         a.k = d->k;
         a.v = d->v;
@@ -587,9 +645,19 @@ hypic_status validate_seam(const hypic_seam_desc* d) {
                     (long long)d->state_stride, (long long)dense);
     if (d->precision < HYPIC_PREC_AUTO || d->precision > HYPIC_PREC_F16)
         return fail(HYPIC_ERR_INVALID_ARGUMENT, "seam: unknown precision");
-    const bool f32 = d->precision == HYPIC_PREC_F32 ||
-                     (d->precision == HYPIC_PREC_AUTO && d->in_dtype == HYPIC_F32 && d->d_k == 64);
-    if (f32 && d->d_k != 64) return fail(HYPIC_ERR_UNSUPPORTED, "seam: the F32 operand plan supports d = 64 only");
+    // seams of at most kSeamShort tokens run in float32 vector arithmetic at any d; longer
+    // ones run the chunk engine, whose float32-operand plan covers d = 64 only
+    int64_t w_max = 0;
+    for (int32_t i = 0; i < d->n_seam; ++i) w_max = std::max<int64_t>(w_max, d->cu_seam[i + 1] - d->cu_seam[i]);
+    if (w_max > hypic::kSeamShort && d->d_k != 64) {
+        if (d->precision == HYPIC_PREC_F32)
+            return fail(HYPIC_ERR_UNSUPPORTED, "seam: the F32 operand plan supports d = 64 only (seams > %d tokens)",
+                        hypic::kSeamShort);
+        if (d->precision == HYPIC_PREC_AUTO && d->in_dtype == HYPIC_F32)
+            return fail(HYPIC_ERR_UNSUPPORTED,
+                        "seam: float32 inputs at d = %d with seams longer than %d tokens have no float32-operand "
+                        "plan; request HYPIC_PREC_F16 explicitly to accept f16 operands", d->d_k, hypic::kSeamShort);
+    }
     return HYPIC_OK;
 }
 
@@ -597,7 +665,7 @@ hypic_status validate_seam(const hypic_seam_desc* d) {
 
 size_t hypic_seam_advance_workspace_bytes(const hypic_seam_desc* d) {
     if (!d || d->n_seam < 0) return 0;
-    return seg_table_layout(d->n_seam, 0).bytes;
+    return seg_table_layout(d->n_seam).bytes;
 }
 
 hypic_status hypic_seam_advance(const hypic_seam_desc* d, hypic_stream_t stream) {
@@ -605,12 +673,9 @@ hypic_status hypic_seam_advance(const hypic_seam_desc* d, hypic_stream_t stream)
     if (st != HYPIC_OK) return st;
     const int64_t n_tasks = (int64_t)d->n_seam * d->n_batch * d->h_v;
     if (n_tasks == 0) return ok();
-    const SegTable L = seg_table_layout(d->n_seam, 0);
-    if (!d->workspace || d->workspace_bytes < L.bytes)
-        return fail(HYPIC_ERR_WORKSPACE_TOO_SMALL, "seam: workspace of %zu bytes needed, %zu given", L.bytes,
-                    d->workspace ? d->workspace_bytes : (size_t)0);
-    if (reinterpret_cast<uintptr_t>(d->workspace) % kAlign)
-        return fail(HYPIC_ERR_INVALID_ARGUMENT, "seam: workspace must be 256-byte aligned");
+    const SegTableLayout L = seg_table_layout(d->n_seam);
+    st = check_workspace("seam", L.bytes, d->workspace, d->workspace_bytes);
+    if (st != HYPIC_OK) return st;
     std::vector<int64_t> start(d->n_seam);
     std::vector<int32_t> len(d->n_seam);
     for (int32_t i = 0; i < d->n_seam; ++i) {
@@ -618,9 +683,9 @@ hypic_status hypic_seam_advance(const hypic_seam_desc* d, hypic_stream_t stream)
         len[i] = (int32_t)(d->cu_seam[i + 1] - d->cu_seam[i]);
     }
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    hipError_t e = upload_seg_table(L, d->workspace, start, len, {}, s);
+    hypic::SegTable tab{};
+    hipError_t e = fill_seg_table(tab, L, d->workspace, start, len, {}, s);
     if (e != hipSuccess) return device_fail("seam: table upload", e);
-    unsigned char* ws = static_cast<unsigned char*>(d->workspace);
     const int64_t dense = (int64_t)d->n_batch * d->h_v * d->d_k * d->d_v;
     const bool f32 = d->precision == HYPIC_PREC_F32 ||
                      (d->precision == HYPIC_PREC_AUTO && d->in_dtype == HYPIC_F32 && d->d_k == 64);
@@ -635,8 +700,7 @@ hypic_status hypic_seam_advance(const hypic_seam_desc* d, hypic_stream_t stream)
         q.qk_l2norm = d->qk_l2norm;
         q.in_bf16 = d->in_dtype == HYPIC_BF16;
         q.out_bf16 = d->out_dtype == HYPIC_BF16;
-        q.seg_start = reinterpret_cast<const long long*>(ws + L.off_start);
-        q.seg_len = reinterpret_cast<const int*>(ws + L.off_len);
+        q.seg = tab;
         q.n_tasks = (int)n_tasks;
         q.q = d->q;
         q.k = d->k;
@@ -664,8 +728,7 @@ hypic_status hypic_seam_advance(const hypic_seam_desc* d, hypic_stream_t stream)
     a.qk_l2norm = d->qk_l2norm;
     a.in_bf16 = d->in_dtype == HYPIC_BF16;
     a.out_bf16 = d->out_dtype == HYPIC_BF16;
-    a.seg_start = reinterpret_cast<const long long*>(ws + L.off_start);
-    a.seg_len = reinterpret_cast<const int*>(ws + L.off_len);
+    a.seg = tab;
     a.n_tasks = (int)n_tasks;
     a.k = d->k;
     a.v = d->v;
@@ -731,19 +794,16 @@ hypic_status validate_conv(const hypic_conv_desc* d) {
 
 size_t hypic_conv_warmup_workspace_bytes(const hypic_conv_desc* d) {
     if (!d || d->n_seg < 0) return 0;
-    return seg_table_layout(d->n_seg, 0).bytes;
+    return seg_table_layout(d->n_seg).bytes;
 }
 
 hypic_status hypic_conv_warmup(const hypic_conv_desc* d, hypic_stream_t stream) {
     hypic_status st = validate_conv(d);
     if (st != HYPIC_OK) return st;
     if (d->n_seg == 0) return ok();
-    const SegTable L = seg_table_layout(d->n_seg, 0);
-    if (!d->workspace || d->workspace_bytes < L.bytes)
-        return fail(HYPIC_ERR_WORKSPACE_TOO_SMALL, "conv: workspace of %zu bytes needed, %zu given", L.bytes,
-                    d->workspace ? d->workspace_bytes : (size_t)0);
-    if (reinterpret_cast<uintptr_t>(d->workspace) % kAlign)
-        return fail(HYPIC_ERR_INVALID_ARGUMENT, "conv: workspace must be 256-byte aligned");
+    const SegTableLayout L = seg_table_layout(d->n_seg);
+    st = check_workspace("conv", L.bytes, d->workspace, d->workspace_bytes);
+    if (st != HYPIC_OK) return st;
     std::vector<int64_t> start(d->n_seg);
     std::vector<int32_t> len(d->n_seg);
     int64_t span = 3;
@@ -753,9 +813,9 @@ hypic_status hypic_conv_warmup(const hypic_conv_desc* d, hypic_stream_t stream) 
         span = std::max<int64_t>(span, len[i]);
     }
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    hipError_t e = upload_seg_table(L, d->workspace, start, len, {}, s);
+    hypic::SegTable tab{};
+    hipError_t e = fill_seg_table(tab, L, d->workspace, start, len, {}, s);
     if (e != hipSuccess) return device_fail("conv: table upload", e);
-    unsigned char* ws = static_cast<unsigned char*>(d->workspace);
     hypic::ConvArgs a{};
     a.n_batch = d->n_batch;
     a.n_tokens = d->n_tokens;
@@ -764,8 +824,7 @@ hypic_status hypic_conv_warmup(const hypic_conv_desc* d, hypic_stream_t stream) 
     a.in_bf16 = d->in_dtype == HYPIC_BF16;
     a.out_bf16 = d->out_dtype == HYPIC_BF16;
     a.silu = d->activation == HYPIC_ACT_SILU;
-    a.seg_start = reinterpret_cast<const long long*>(ws + L.off_start);
-    a.seg_len = reinterpret_cast<const int*>(ws + L.off_len);
+    a.seg = tab;
     a.x = d->x;
     a.state_in = d->state_in;
     a.n_state = d->n_state;

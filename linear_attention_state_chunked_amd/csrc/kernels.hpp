@@ -7,6 +7,39 @@
 
 namespace hypic {
 
+// Per-segment table of one launch: first covered token and covered length of every
+// segment and, when a processing order is given (LPT), the order of the segments.  Up to
+// kInlineSegs segments travel inside the kernel arguments, so nothing is copied before the
+// launch; a larger table lives in device memory (the call's workspace).
+constexpr int kInlineSegs = 160;
+struct SegTable {
+    int n;                      // segments
+    int inl;                    // 1: the arrays below hold the table, else the pointers
+    int has_order;              // 1: segments are processed in order[] (LPT), else natural
+    const long long* start_p;   // device [n]
+    const int* len_p;           // device [n]
+    const int* order_p;         // device [n]
+    long long start[kInlineSegs];
+    int len[kInlineSegs];
+    int order[kInlineSegs];
+};
+__device__ __forceinline__ long long seg_start(const SegTable& t, int s) { return t.inl ? t.start[s] : t.start_p[s]; }
+__device__ __forceinline__ int seg_len(const SegTable& t, int s) { return t.inl ? t.len[s] : t.len_p[s]; }
+// Task at position it of the processing order.  The per_seg tasks of one segment (its
+// batch rows and heads) are contiguous, and an order permutes whole segments.
+__device__ __forceinline__ int task_at(const SegTable& t, int it, int per_seg) {
+    if (!t.has_order) return it;
+    const int j = it / per_seg;
+    const int s = t.inl ? t.order[j] : t.order_p[j];
+    return s * per_seg + (it - j * per_seg);
+}
+
+// Sticky per-device status word: a bounded wait inside a kernel that gave up sets a bit
+// (an ordinary vector atomic), so a broken hand-off is reported instead of passing as
+// silently wrong data.  take_device_status() reads and clears it (synchronous).
+constexpr unsigned kStatusWaitExpired = 1u;
+hipError_t take_device_status(unsigned* out);
+
 // One dense (gated delta rule) chunk-engine launch.  Each task is one
 // (segment, batch, value head) chain; it runs the segment's tokens chunk by chunk
 // from X = [I | S_in] and emits T_hat/T_exp (if T_hat), the end state and, with q,
@@ -19,9 +52,6 @@ struct EngineArgs {
     int qk_l2norm;
     int in_bf16;
     int out_bf16;
-    const long long* seg_start;  // device [n_seg], first token of the segment's covered range
-    const int* seg_len;          // device [n_seg], covered tokens
-    const int* order;            // device [n_tasks] task order, or null (natural)
     int n_tasks;
     int persistent;              // 1: grid-stride over tasks (static round robin)
     const void* k;
@@ -43,6 +73,7 @@ struct EngineArgs {
     int stream;
     long long stream_start0, stream_stride;
     int stream_len;
+    SegTable seg;                // covered range [start, start + len) of every segment
 };
 
 // kind: 0 diagonal (GLA, per-channel log_alpha), 1 scalar
@@ -54,9 +85,6 @@ struct DiagArgs {
     int scalar;
     int in_bf16;
     int qk_l2norm;
-    const long long* seg_start;
-    const int* seg_len;
-    const int* order;
     int n_tasks;
     const void* k;
     const void* v;
@@ -64,6 +92,7 @@ struct DiagArgs {
     float* T_hat;
     int* T_exp;
     float* S;
+    SegTable seg;
 };
 
 // One fold launch: grid (chain, block).  Block `blk` folds elements
@@ -95,8 +124,6 @@ struct SeamArgs {
     int h_k, h_v;
     int qk_l2norm;
     int in_bf16, out_bf16;
-    const long long* seg_start;  // device [n_seam]
-    const int* seg_len;          // device [n_seam]
     int n_tasks;
     const void* q;
     const void* k;
@@ -111,6 +138,7 @@ struct SeamArgs {
     float* T_hat;
     int* T_exp;
     float* S_seam;
+    SegTable seg;                // seam s: tokens [start, start + len)
 };
 
 struct ConvArgs {
@@ -120,9 +148,6 @@ struct ConvArgs {
     int n_seg;
     int in_bf16, out_bf16;
     int silu;
-    const long long* seg_start;
-    const int* seg_len;
-    const int* seg_of_token_block;  // unused (reserved)
     const void* x;
     const void* state_in;
     int n_state;
@@ -131,6 +156,7 @@ struct ConvArgs {
     const float* bias;
     void* y;
     void* state_out;
+    SegTable seg;
 };
 
 hipError_t launch_dense_engine(const EngineArgs& a, int d, int prec_f32, int grid, hipStream_t s);

@@ -52,8 +52,8 @@ __global__ __launch_bounds__(4 * D, W <= 8 ? 4 : 1) void seam_kernel(SeamArgs a)
     const int b = rem / a.h_v;
     const int h = rem - b * a.h_v;
     const int hk = (h * a.h_k) / a.h_v;
-    const long long tok0 = a.seg_start[s];
-    const int w = a.seg_len[s];
+    const long long tok0 = seg_start(a.seg, s);
+    const int w = seg_len(a.seg, s);
     const long long chain = (long long)b * a.h_v + h;
     const long long DD = (long long)D * D;
     const bool want_o = a.o != nullptr;

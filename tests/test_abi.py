@@ -29,7 +29,7 @@ def L():
 def test_every_declared_symbol_is_exported(L):
     src = open(HEADER).read()
     declared = set(re.findall(r"^\s*(?:hypic_status|size_t|const char\*|int)\s+(hypic_\w+)\s*\(", src, re.M))
-    assert len(declared) == 11
+    assert len(declared) == 13
     assert declared == set(A.EXPORTS)
     out = subprocess.run(["nm", "-D", "--defined-only", A.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT (hypic_\w+)", out))
@@ -101,19 +101,31 @@ def test_build_offsets_and_workspace(L):
         d, _ = _build_desc(_cu=cu)
         assert L.hypic_segment_build(C.byref(d), None) == A.ERR_INVALID_ARGUMENT
         assert msg in L.hypic_last_error().decode()
+    # a table of at most INLINE_SEGS segments travels in the kernel arguments: no workspace
     d, cu = _build_desc()
+    assert L.hypic_segment_build_workspace_bytes(C.byref(d)) == 0
+    d, cu = _build_desc(schedule=A.SCHED["lpt"])
+    assert L.hypic_segment_build_workspace_bytes(C.byref(d)) == 0
+    # a larger one is uploaded into the workspace: starts, lengths and the segment order
+    n = A.INLINE_SEGS + 1
+    big = np.arange(0, 64 * (n + 1), 64, dtype=np.int64)
+    d, cu = _build_desc(_cu=big, n_tokens=int(big[-1]))
     need = L.hypic_segment_build_workspace_bytes(C.byref(d))
-    assert need > 0 and need % 256 == 0
-    d.workspace_bytes = 255          # below the segment table itself
+    assert need >= n * (8 + 4 + 4) and need % 256 == 0
+    d.workspace_bytes = need - 1
     assert L.hypic_segment_build(C.byref(d), None) == A.ERR_WORKSPACE_TOO_SMALL
     d.workspace = None
     d.workspace_bytes = need
     assert L.hypic_segment_build(C.byref(d), None) == A.ERR_WORKSPACE_TOO_SMALL
-    d, cu = _build_desc(schedule=A.SCHED["lpt"])
-    assert L.hypic_segment_build_workspace_bytes(C.byref(d)) >= need + 2 * 4   # task order included
-    # the F32 operand plan needs d = 64
+    d.workspace = 0x10010
+    assert L.hypic_segment_build(C.byref(d), None) == A.ERR_INVALID_ARGUMENT
+    assert "256-byte aligned" in L.hypic_last_error().decode()
+    # the F32 operand plan needs d = 64; AUTO does not hand float32 inputs at d = 128 to f16
     d, cu = _build_desc(precision=A.PREC["f32"])
     assert L.hypic_segment_build(C.byref(d), None) == A.ERR_UNSUPPORTED
+    d, cu = _build_desc(in_dtype=A.F32, precision=A.PREC["auto"])
+    assert L.hypic_segment_build(C.byref(d), None) == A.ERR_UNSUPPORTED
+    assert "HYPIC_PREC_F16" in L.hypic_last_error().decode()
     # diagonal kind: beta must be NULL, l2norm unsupported
     d, cu = _build_desc(kind=A.DIAG)
     assert L.hypic_segment_build(C.byref(d), None) == A.ERR_INVALID_ARGUMENT
@@ -163,12 +175,23 @@ def test_seam_and_conv_validation(L):
                 n_seam=2, cu_seam=cu.ctypes.data, qk_l2norm=0, q=0x1000, k=0x2000, v=0x3000, log_alpha=0x4000,
                 beta=0x5000, S_in=None, state_stride=0, o=0x6000, S_out=None, T_hat=None, T_exp=None, S_seam=None,
                 precision=0, workspace=None, workspace_bytes=0)
+    n = A.INLINE_SEGS + 1
+    big = np.arange(0, 8 * (n + 1), 8, dtype=np.int64)
+    long_seam = np.array([0, 8, 40], np.int64)
     for kw, status, msg in ((dict(q=None), A.ERR_INVALID_ARGUMENT, "without q"),
                             (dict(state_stride=10), A.ERR_INVALID_ARGUMENT, "state_stride"),
-                            (dict(), A.ERR_WORKSPACE_TOO_SMALL, "workspace")):
+                            (dict(n_seam=n, cu_seam=big.ctypes.data, n_tokens=int(big[-1])),
+                             A.ERR_WORKSPACE_TOO_SMALL, "workspace"),
+                            # float32 inputs, d = 128, a seam longer than 16 tokens: no float32 plan
+                            (dict(in_dtype=A.F32, cu_seam=long_seam.ctypes.data, n_tokens=40),
+                             A.ERR_UNSUPPORTED, "HYPIC_PREC_F16"),
+                            (dict(in_dtype=A.F32, precision=A.PREC["f32"], cu_seam=long_seam.ctypes.data,
+                                  n_tokens=40), A.ERR_UNSUPPORTED, "d = 64")):
         d = A.SeamDesc(**{**base, **kw})
         assert L.hypic_seam_advance(C.byref(d), None) == status, kw
         assert msg in L.hypic_last_error().decode()
+    d = A.SeamDesc(**base)
+    assert L.hypic_seam_advance_workspace_bytes(C.byref(d)) == 0
     cb = dict(in_dtype=A.BF16, out_dtype=A.BF16, n_batch=1, n_tokens=16, channels=64, width=4, n_seg=2,
               cu_seqlens=cu.ctypes.data, x=0x1000, state_in=None, n_state=0, state_index=None, weight=0x2000,
               bias=None, activation=0, y=0x3000, state_out=None, workspace=None, workspace_bytes=0)
@@ -176,10 +199,12 @@ def test_seam_and_conv_validation(L):
                             (dict(channels=12), A.ERR_UNSUPPORTED, "multiple of 8"),
                             (dict(state_in=0x4000, n_state=1), A.ERR_INVALID_ARGUMENT, "state_index"),
                             (dict(activation=5), A.ERR_INVALID_ARGUMENT, "activation"),
-                            (dict(), A.ERR_WORKSPACE_TOO_SMALL, "workspace")):
+                            (dict(n_seg=n, cu_seqlens=big.ctypes.data, n_tokens=int(big[-1])),
+                             A.ERR_WORKSPACE_TOO_SMALL, "workspace")):
         d = A.ConvDesc(**{**cb, **kw})
         assert L.hypic_conv_warmup(C.byref(d), None) == status, kw
         assert msg in L.hypic_last_error().decode()
+    assert L.hypic_conv_warmup_workspace_bytes(C.byref(A.ConvDesc(**cb))) == 0
 
 
 def test_plan_schedule_matches_oracle_exactly():
@@ -200,3 +225,105 @@ def test_plan_schedule_rejects(L):
     w = np.array([1, -2], np.int64)
     assert L.hypic_plan_schedule(w.ctypes.data, 2, 2, 1, None, None, None) == A.ERR_INVALID_ARGUMENT
     assert L.hypic_plan_schedule(w.ctypes.data, 2, 0, 1, None, None, None) == A.ERR_INVALID_ARGUMENT
+
+
+# ----------------------------------------------------------------------------------------
+# seam-width knob (HYPIC project README, "PIC modes": 0 reuses the whole segment, a value in
+# (0, 1] is a fraction of each segment, a value above 1 an absolute token count; default 8)
+
+
+def test_seam_widths_knob_cases():
+    from linear_attention_state_chunked_amd.api import hypic_seam_widths
+
+    lens = [0, 1, 5, 8, 9, 700, 4096]
+    assert hypic_seam_widths(lens).tolist() == [0, 1, 5, 8, 8, 8, 8]               # default 8
+    assert hypic_seam_widths(lens, 0).tolist() == [0] * 7                          # whole segment reused
+    assert hypic_seam_widths(lens, 1.0).tolist() == lens                           # the whole segment
+    assert hypic_seam_widths(lens, 0.5).tolist() == [0, 1, 3, 4, 5, 350, 2048]     # ceil(len / 2)
+    assert hypic_seam_widths(lens, 0.01).tolist() == [0, 1, 1, 1, 1, 7, 41]        # ceil(0.01 len)
+    assert hypic_seam_widths(lens, 16).tolist() == [0, 1, 5, 8, 9, 16, 16]         # absolute count
+    assert hypic_seam_widths(lens, 2.9).tolist() == [0, 1, 2, 2, 2, 2, 2]          # its integer part
+    assert hypic_seam_widths([], 8).tolist() == []
+    assert A.SEAM_SINK_DEFAULT == 8.0
+
+
+def test_seam_widths_rejects(L):
+    from linear_attention_state_chunked_amd.api import hypic_seam_widths
+
+    for lens, sink in (([3], -1.0), ([3], float("inf")), ([-1], 8.0)):
+        with pytest.raises(A.HypicError):
+            hypic_seam_widths(lens, sink)
+    with pytest.raises(ValueError):
+        hypic_seam_widths([3], float("nan"))
+    assert L.hypic_seam_widths(None, 2, 8.0, None) == A.ERR_INVALID_ARGUMENT
+
+
+# ----------------------------------------------------------------------------------------
+# the binding validates every tensor before calling the library (no GPU needed: the checks
+# run before the device check, and a host tensor is itself rejected)
+
+
+def _bt(*shape, dt=None):
+    import torch
+    return torch.zeros(shape, dtype=dt or torch.float32)
+
+
+@pytest.mark.parametrize("case", ["v_dtype", "v_shape", "la_dtype", "la_numel", "beta_dtype", "beta_diag",
+                                  "diag_la_last", "host"])
+def test_binding_rejects_bad_build_tensors(case):
+    import torch
+    from linear_attention_state_chunked_amd import api as H
+
+    B, N, hk, hv, d = 1, 64, 1, 2, 64
+    k, v = _bt(B, N, hk, d, dt=torch.bfloat16), _bt(B, N, hv, d, dt=torch.bfloat16)
+    la, beta = _bt(B, N, hv), _bt(B, N, hv)
+    kw = dict(kind="dense")
+    if case == "v_dtype":
+        v = v.float()
+    elif case == "v_shape":
+        v = _bt(B, N + 1, hv, d, dt=torch.bfloat16)
+    elif case == "la_dtype":
+        la = la.bfloat16()
+    elif case == "la_numel":
+        la = _bt(B, N, hv + 1)
+    elif case == "beta_dtype":
+        beta = beta.double()
+    elif case == "beta_diag":
+        kw = dict(kind="diag")
+        la = _bt(B, N, hv, d)
+    elif case == "diag_la_last":
+        kw = dict(kind="diag")
+        la, beta = _bt(B, N, hv * d, 1), None
+    with pytest.raises(ValueError):
+        H.hypic_segment_build(k, v, la, [0, N], beta, **kw)
+
+
+def test_binding_rejects_bad_compose_seam_conv_tensors():
+    import torch
+    from linear_attention_state_chunked_amd import api as H
+
+    n, c, d = 3, 2, 64
+    T, e, S = _bt(n, c, d, d), torch.zeros((n, c), dtype=torch.int32), _bt(n, c, d, d)
+    bad = [dict(T_hat=T.double()), dict(T_exp=e.long()), dict(T_hat=_bt(n, c, d)),
+           dict(S0=_bt(c, d, d + 1)), dict(slot=torch.zeros(n, dtype=torch.int64)), dict()]
+    for b in bad:
+        args = {"T_hat": T, "T_exp": e, "S": S, **b}
+        kw = {k: args.pop(k) for k in ("S0", "slot") if k in args}
+        with pytest.raises(ValueError):      # the last one: host tensors
+            H.hypic_compose(args["T_hat"], args["T_exp"], args["S"], **kw)
+    q = k = _bt(1, 16, 1, d)
+    v = _bt(1, 16, 2, d)
+    la = bt = _bt(1, 16, 2)
+    for kw in (dict(q=q.bfloat16()), dict(v=_bt(1, 16, 2, d + 1)), dict(log_alpha=la.bfloat16()),
+               dict(beta=_bt(1, 16, 3)), dict(S_in=_bt(1, 1, 2, d, d)), dict()):
+        a = {"q": q, "k": k, "v": v, "log_alpha": la, "beta": bt, **kw}
+        S_in = a.pop("S_in", None)
+        with pytest.raises(ValueError):
+            H.hypic_seam_advance(a["q"], a["k"], a["v"], a["log_alpha"], a["beta"], [0, 8, 16], S_in=S_in)
+    x = _bt(1, 16, 64, dt=torch.bfloat16)
+    for kw in (dict(weight=_bt(1, 64, 4).double()), dict(weight=_bt(1, 32, 4)), dict(bias=_bt(1, 63)),
+               dict(state_in=_bt(2, 1, 3, 64)), dict(state_index=torch.zeros(2, dtype=torch.int64)), dict()):
+        a = {"weight": _bt(1, 64, 4), **kw}
+        w = a.pop("weight")
+        with pytest.raises(ValueError):
+            H.hypic_conv_warmup(x, w, [0, 8, 16], **a)

@@ -93,6 +93,7 @@ def test_gdn64k_full_build_and_compose(gpu):
     c_auto = H.hypic_compose(E_T, E_e, E_S, mode="auto")
     c_fold = H.hypic_compose(E_T, E_e, E_S, mode="fold", want_T=True)
     torch.cuda.synchronize()
+    H.hypic_device_status()
     Th, Te, Sh = _host(E_T), _host(E_e), _host(E_S)
     Sa, Sf = _host(c_auto["S_final"]), _host(c_fold["S_final"])
     Tt, Tte = _host(c_fold["T_total"]), _host(c_fold["T_total_exp"])
@@ -157,6 +158,7 @@ def test_cold100k_full_schedules_scan_and_single_pass(gpu):
     num = torch.linalg.vector_norm((c["S_final"] - single).reshape(n_chain, -1).double(), dim=1)
     den = torch.linalg.vector_norm(single.reshape(n_chain, -1).double(), dim=1)
     e_all = float((num / den).max())
+    H.hypic_device_status()
     log(f"cold100k: composed vs single pass, max over {n_chain} chains {e_all:.2e}")
     assert e_all <= TOL
     idx = [layer * h_v + h for layer, h in chains]
