@@ -98,7 +98,10 @@ typedef enum {
 
 /* Operand precision of the dense kind's matrix-core products (the segment build
  * and seams longer than 16 tokens; shorter seams always run in float32 vector
- * arithmetic).  Accumulation is always float32.
+ * arithmetic).  Accumulation is always float32.  Per-segment relative errors,
+ * bf16 inputs, d = 128: F16 about 8e-4 (T) and 3e-4 (S) at 1,024 tokens, T growing
+ * like the square root of the chunk count; AUTO switches the T columns of segments
+ * longer than 2,048 tokens to hi/lo X and Vn operands (T about 1.1e-3 at 8k tokens).
  *   AUTO: F16 for bf16 inputs; F32 for float32 inputs at d = 64.  There is no
  *         float32-operand plan at d = 128, so float32 inputs at d = 128 return
  *         HYPIC_ERR_UNSUPPORTED under AUTO; ask for F16 explicitly to accept f16
@@ -106,7 +109,14 @@ typedef enum {
 typedef enum {
     HYPIC_PREC_AUTO = 0,
     HYPIC_PREC_F32 = 1, /* float32 operands (fp32 matrix cores), for fp32 inputs   */
-    HYPIC_PREC_F16 = 2  /* f16 operands, power-of-two renormalised T columns        */
+    HYPIC_PREC_F16 = 2, /* f16 operands, power-of-two renormalised T columns        */
+    /* Segment build only (a seam takes it as F16).  S as under F16; T from a separate
+     * transition-only pass with hi/lo-split f16 operands (about 22-bit) on every
+     * product that touches it.  Per-segment T error about 1e-5 instead of about
+     * 1e-3, so that the product of many cached transitions (hypic_compose's T_total)
+     * stays within 2e-3; costs a second pass over k.  Keys are still rounded to f16
+     * once, which is exact for bf16 keys of magnitude >= 2^-14. */
+    HYPIC_PREC_F16_PRECISE_T = 3
 } hypic_precision;
 
 typedef enum {

@@ -16,7 +16,7 @@ OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_DEVICE =
 F32, BF16 = 0, 1
 DENSE, DIAG, SCALAR = 0, 1, 2
 SCHED = {"natural": 0, "lpt": 1, "rr": 2}
-PREC = {"auto": 0, "f32": 1, "f16": 2}
+PREC = {"auto": 0, "f32": 1, "f16": 2, "f16_precise_t": 3}
 COMPOSE = {"auto": 0, "fold": 1, "scan": 2, "naive_add": 3}
 ACT = {"none": 0, "silu": 1}
 KIND = {"dense": DENSE, "diag": DIAG, "scalar": SCALAR}

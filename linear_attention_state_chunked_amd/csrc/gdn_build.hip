@@ -462,16 +462,29 @@ __device__ __forceinline__ void ut_blocks(const _Float16* Kn1, const float* sGl,
     st_tg(TgAT, TgGT, TgGlT, pt, -r0, 3, 0, ln, bcol[0], bgcol[0]);
 }
 
-template <int D, bool WITH_T, bool IN_BF16, bool PERSIST, bool PT, bool STREAM>
-__global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_build_kernel(EngineArgs a) {
+// Carry waves of a variant: D/32 per column kind present (T columns, S columns).
+template <int D, bool WITH_T, bool WITH_S>
+constexpr int gdn_carry_waves() {
+    return ((WITH_T ? 1 : 0) + (WITH_S ? 1 : 0)) * (D / 32);
+}
+
+// WITH_T / WITH_S: the T columns and the S columns of X are carried (at least one of them).
+// PT: hi/lo operands for the T columns.  Without S columns (the transition-only pass of the
+// precise plan) W' itself is kept as a hi/lo pair too, in the otherwise unused V buffers.
+template <int D, bool WITH_T, bool WITH_S, bool IN_BF16, bool PERSIST, bool PT, bool STREAM>
+__global__ __launch_bounds__((gdn_carry_waves<D, WITH_T, WITH_S>() + 4) * 64) void gdn_build_kernel(EngineArgs a) {
     using LY = GLayout<D>;
     using E = _Float16;
     constexpr int NB = D / 32;
-    constexpr int NC = (WITH_T ? 2 : 1) * NB;   // carry waves
+    constexpr int NC = gdn_carry_waves<D, WITH_T, WITH_S>();   // carry waves
+    static_assert(WITH_T || WITH_S, "a pass carries T columns, S columns or both");
+    static_assert(WITH_S || PT, "the transition-only pass is the precise plan's");
     constexpr int NP = 4;                       // preparation waves
-    constexpr bool CV = IN_BF16;                // V rows staged by carry waves (else by the preparation waves)
+    constexpr bool CV = IN_BF16 && WITH_S;      // V rows staged by carry waves
+    constexpr bool PV = !IN_BF16 && WITH_S;     // ... or by the preparation waves (fp32 inputs)
     constexpr bool VS = CV;                     // ... by the S waves, after forming U
     constexpr bool VT = CV && WITH_T && !PT;    // ... and, in the fast plan, half of them by the T waves
+    constexpr bool WLO = PT && !WITH_S;         // W' as hi/lo fragments (low half where V would be)
                                                 //     in their idle tail before the barrier
     constexpr int NT = (NC + NP) * 64;
     constexpr int RK = LY::RK, RT = LY::RT;
@@ -678,6 +691,10 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                         auto wfrag = [&](int mt, int kb, int st) {
                             return ld8(Wf + (((mt * NB + kb) * 2 + st) * 64 + ln) * 8);
                         };
+                        const E* Wl = reinterpret_cast<const E*>(sm + LY::Vn);
+                        auto wfrag_lo = [&](int mt, int kb, int st) {
+                            return ld8(Wl + (((mt * NB + kb) * 2 + st) * 64 + ln) * 8);
+                        };
                         if constexpr (PT && TR) {
                             // hi/lo X and Vn operands (the precise-T plan): plain loops, which
                             // keep this variant within its registers
@@ -689,6 +706,7 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
 #pragma unroll
                                     for (int mt = 0; mt < 2; ++mt) {
                                         const halfx8 fa = wfrag(mt, kb, st);
+                                        if constexpr (WLO) Vn[mt] = OpF16::mma(wfrag_lo(mt, kb, st), xb.hi, Vn[mt]);
                                         Vn[mt] = OpF16::mma(fa, xb.lo, Vn[mt]);
                                         Vn[mt] = OpF16::mma(fa, xb.hi, Vn[mt]);
                                     }
@@ -797,10 +815,20 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                             auto store_w = [&](int mt, const floatx16& acc) {
 #pragma unroll
                                 for (int st = 0; st < 2; ++st) {
-                                    halfx8 w;
+                                    const int o = (((mt * NB + dt) * 2 + st) * 64 + ln) * 8;
+                                    if constexpr (WLO) {
+                                        floatx16 neg;
 #pragma unroll
-                                    for (int i = 0; i < 8; ++i) w[i] = (_Float16)(-acc[8 * st + i]);
-                                    *reinterpret_cast<halfx8*>(Wf1 + (((mt * NB + dt) * 2 + st) * 64 + ln) * 8) = w;
+                                        for (int i = 0; i < 16; ++i) neg[i] = -acc[i];
+                                        const HL w = split_acc(neg, st);
+                                        *reinterpret_cast<halfx8*>(Wf1 + o) = w.hi;
+                                        *reinterpret_cast<halfx8*>(reinterpret_cast<E*>(sm + LY::Vn) + o) = w.lo;
+                                    } else {
+                                        halfx8 w;
+#pragma unroll
+                                        for (int i = 0; i < 8; ++i) w[i] = (_Float16)(-acc[8 * st + i]);
+                                        *reinterpret_cast<halfx8*>(Wf1 + o) = w;
+                                    }
                                 }
                             };
                             if constexpr (PT) {
@@ -987,7 +1015,7 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                 __builtin_amdgcn_s_setprio(3);
                 if (nc > 0) {
                     prefetch_kg(0, lane);
-                    if constexpr (!CV) prefetch_v(0, lane);
+                    if constexpr (PV) prefetch_v(0, lane);
                     stage_kg(0, smem, lane);
                     if (nc > 1) prefetch_kg(1, lane);
                     pbar(lane);
@@ -1020,7 +1048,7 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
                                          }
                                      });
                         // V of chunk c+1 (its buffer was last read by U(c-1), a period ago)
-                        if constexpr (!CV) {
+                        if constexpr (PV) {
                             stage_v(c + 1, sm, ln);
                             if (c + 2 < nc) prefetch_v(c + 2, ln);
                         }
@@ -1032,32 +1060,40 @@ __global__ __launch_bounds__(((WITH_T ? 2 : 1) * D / 32 + 4) * 64) void gdn_buil
         }
     };
     if (is_c) {
-        if (WITH_T && t_wave) run(std::integral_constant<int, 0>{});
-        else run(std::integral_constant<int, 1>{});
+        if constexpr (WITH_T) {
+            if (t_wave) run(std::integral_constant<int, 0>{});
+        }
+        if constexpr (WITH_S) {
+            if (!t_wave) run(std::integral_constant<int, 1>{});
+        }
     } else {
         run(std::integral_constant<int, 2>{});
     }
 }
 
-template <int D, bool WITH_T, bool IN_BF16, bool PT>
+template <int D, bool WITH_T, bool WITH_S, bool IN_BF16, bool PT>
 static hipError_t launch_v(const EngineArgs& a, int grid, hipStream_t s) {
-    constexpr int nt = ((WITH_T ? 2 : 1) * D / 32 + 4) * 64;
+    constexpr int nt = (gdn_carry_waves<D, WITH_T, WITH_S>() + 4) * 64;
     if (a.stream) {
         // one stream of chunks per persistent workgroup (equal segments, 16-bit inputs)
         if constexpr (!IN_BF16) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((gdn_build_kernel<D, WITH_T, IN_BF16, true, PT, IN_BF16>), dim3(grid), dim3(nt), 0, s, a);
+        hipLaunchKernelGGL((gdn_build_kernel<D, WITH_T, WITH_S, IN_BF16, true, PT, IN_BF16>), dim3(grid), dim3(nt), 0, s,
+                           a);
     } else if (a.persistent) {
-        hipLaunchKernelGGL((gdn_build_kernel<D, WITH_T, IN_BF16, true, PT, false>), dim3(grid), dim3(nt), 0, s, a);
+        hipLaunchKernelGGL((gdn_build_kernel<D, WITH_T, WITH_S, IN_BF16, true, PT, false>), dim3(grid), dim3(nt), 0, s, a);
     } else {
-        hipLaunchKernelGGL((gdn_build_kernel<D, WITH_T, IN_BF16, false, PT, false>), dim3(grid), dim3(nt), 0, s, a);
+        hipLaunchKernelGGL((gdn_build_kernel<D, WITH_T, WITH_S, IN_BF16, false, PT, false>), dim3(grid), dim3(nt), 0, s,
+                           a);
     }
     return hipGetLastError();
 }
 
 template <int D, bool IN_BF16>
 static hipError_t launch_t(const EngineArgs& a, int grid, hipStream_t s) {
-    if (!a.T_hat) return launch_v<D, false, IN_BF16, false>(a, grid, s);
-    return a.precise_T ? launch_v<D, true, IN_BF16, true>(a, grid, s) : launch_v<D, true, IN_BF16, false>(a, grid, s);
+    if (!a.T_hat) return launch_v<D, false, true, IN_BF16, false>(a, grid, s);             // state only
+    if (a.precise_T == 2) return launch_v<D, true, false, IN_BF16, true>(a, grid, s);       // transition only
+    if (a.precise_T == 1) return launch_v<D, true, true, IN_BF16, true>(a, grid, s);        // hi/lo X, Vn for T
+    return launch_v<D, true, true, IN_BF16, false>(a, grid, s);
 }
 
 hipError_t take_device_status(unsigned* out) {

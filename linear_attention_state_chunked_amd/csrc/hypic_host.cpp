@@ -165,8 +165,10 @@ hypic_status validate_build(const hypic_build_desc* d) {
         return fail(HYPIC_ERR_INVALID_ARGUMENT, "build: T_hat and T_exp must be both set or both NULL");
     if (d->schedule < HYPIC_SCHED_NATURAL || d->schedule > HYPIC_SCHED_RR)
         return fail(HYPIC_ERR_INVALID_ARGUMENT, "build: unknown schedule %d", (int)d->schedule);
-    if (d->precision < HYPIC_PREC_AUTO || d->precision > HYPIC_PREC_F16)
+    if (d->precision < HYPIC_PREC_AUTO || d->precision > HYPIC_PREC_F16_PRECISE_T)
         return fail(HYPIC_ERR_INVALID_ARGUMENT, "build: unknown precision %d", (int)d->precision);
+    if (d->precision == HYPIC_PREC_F16_PRECISE_T && d->kind != HYPIC_DENSE_DELTA)
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "build: F16_PRECISE_T applies to the dense kind only");
     if (d->kind == HYPIC_DENSE_DELTA) {
         if (d->precision == HYPIC_PREC_F32 && d->d_k != 64)
             return fail(HYPIC_ERR_UNSUPPORTED, "build: the F32 operand plan supports d = 64 only");
@@ -366,6 +368,17 @@ hypic_status hypic_segment_build(const hypic_build_desc* d, hypic_stream_t strea
             a.stream_start0 = start[0];
             a.stream_stride = stride;
             a.stream_len = len[0];
+        }
+        if (d->precision == HYPIC_PREC_F16_PRECISE_T && d->T_hat) {
+            // the precise plan: a transition-only pass with hi/lo operands, then the state pass
+            hypic::EngineArgs t = a;
+            t.precise_T = 2;
+            t.S_out = nullptr;
+            e = hypic::launch_gdn_build(t, d->d_k, 0, grid, s);
+            if (e != hipSuccess) return device_fail("build: transition pass launch", e);
+            a.T_hat = nullptr;
+            a.T_exp = nullptr;
+            a.precise_T = 0;
         }
         e = hypic::launch_gdn_build(a, d->d_k, build_prec_f32(d) ? 1 : 0, grid, s);
         if (e != hipSuccess) return device_fail("build: dense build launch", e);
@@ -643,7 +656,7 @@ hypic_status validate_seam(const hypic_seam_desc* d) {
     if (d->state_stride != 0 && d->state_stride < dense)
         return fail(HYPIC_ERR_INVALID_ARGUMENT, "seam: state_stride %lld overlaps seams (minimum %lld)",
                     (long long)d->state_stride, (long long)dense);
-    if (d->precision < HYPIC_PREC_AUTO || d->precision > HYPIC_PREC_F16)
+    if (d->precision < HYPIC_PREC_AUTO || d->precision > HYPIC_PREC_F16_PRECISE_T)
         return fail(HYPIC_ERR_INVALID_ARGUMENT, "seam: unknown precision");
     // seams of at most kSeamShort tokens run in float32 vector arithmetic at any d; longer
     // ones run the chunk engine, whose float32-operand plan covers d = 64 only

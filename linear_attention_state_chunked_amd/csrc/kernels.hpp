@@ -66,7 +66,8 @@ struct EngineArgs {
     float* T_hat;                // null: T columns skipped
     int* T_exp;
     void* o;
-    int precise_T;               // T columns with hi/lo operands (long segments)
+    int precise_T;               // 0: single f16 operands; 1: T columns with hi/lo X and Vn (with S);
+                                 // 2: transition-only pass, hi/lo Tg, W', X, Vn (no S columns)
     // stream mode (persistent grid, equal segments, 16-bit inputs): segment s covers tokens
     // [stream_start0 + s * stream_stride, ... + stream_len); each workgroup streams the chunks
     // of its tasks it, it + grid, ... (natural order)

@@ -9,7 +9,8 @@ Distributions (the same for the device and the CPU reference):
   * keys and queries: i.i.d. N(0,1) rows, scaled to unit L2 norm;
   * values: i.i.d. N(0,1);
   * write strength beta = sigmoid(N(0,1)), float32;
-  * gated-delta decay log(alpha) = -scale * softplus(N(0,1)), scale 0.05, float32;
+  * gated-delta decay log(alpha) = -scale * softplus(N(0,1)), scale 0.05 (0.005 for
+    the slow-decay workloads, 0 for the DeltaNet ones, alpha = 1), float32;
   * RetNet-style scalar decay gamma_h = 1 - 2**-(5 + 4h/15) for scalar head h;
   * GLA per-channel gates alpha = sigmoid(N(2,1)) ** (1/16), stored as log(alpha);
   * pre-convolution activations N(0,1), depthwise conv taps N(0,1)/2.
@@ -108,6 +109,17 @@ WORKLOADS = {
                             seam=8, conv_width=4, n_slots=128),
     # long cold request: 100k tokens in uneven segments, 30 layers x 32 heads
     "cold100k_bf16": Workload("cold100k_bf16", 4, 30, 16, 32, 128, "bf16", "dense"),
+    # composition checks where cross-segment terms stay large: slow decay (log alpha
+    # scale 0.005) and no decay at all (alpha = 1, DeltaNet), 32 v-heads on 16 k-heads,
+    # 16 x 1024 and 4 x 4096 tokens
+    "gdn_slow16x1k_bf16": Workload("gdn_slow16x1k_bf16", 5, 1, 16, 32, 128, "bf16", "dense",
+                                   alpha_scale=0.005, fixed_lens=(1024,) * 16),
+    "gdn_slow4x4k_bf16": Workload("gdn_slow4x4k_bf16", 6, 1, 16, 32, 128, "bf16", "dense",
+                                  alpha_scale=0.005, fixed_lens=(4096,) * 4),
+    "delta16x1k_bf16": Workload("delta16x1k_bf16", 7, 1, 16, 32, 128, "bf16", "dense",
+                                alpha_scale=0.0, fixed_lens=(1024,) * 16),
+    "delta4x4k_bf16": Workload("delta4x4k_bf16", 8, 1, 16, 32, 128, "bf16", "dense",
+                               alpha_scale=0.0, fixed_lens=(4096,) * 4),
 }
 
 

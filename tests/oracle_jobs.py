@@ -22,7 +22,8 @@ def _cu(lens):
 
 def dense_segments_job(args):
     """(workload, layer, head, segment ids or None = all, with_fold) ->
-    {'seg': {s: (T_hat, T_exp, S)}, 'S_final', 'T_hat', 'T_exp' (fold over all)}."""
+    {'seg': {s: (T_hat, T_exp, S)}, and with_fold (segments must be all):
+    'S_final', 'T_hat', 'T_exp', 'S_prefix' of the fold over all segments}."""
     name, layer, head, segs, with_fold = args
     wl = WORKLOADS[name]
     lens = segment_lengths(wl)
@@ -38,7 +39,7 @@ def dense_segments_job(args):
         elems.append(r)
     if with_fold:
         f = O.compose_fold("dense", elems)
-        out.update(S_final=f["S_final"], T_hat=f["T_hat"], T_exp=f["T_exp"])
+        out.update(S_final=f["S_final"], T_hat=f["T_hat"], T_exp=f["T_exp"], S_prefix=f["S_prefix"])
     return out
 
 

@@ -27,11 +27,8 @@ TOL = 2e-3
 DEV = "cuda:0"
 
 
-def tol_T_total(n_elem):
-    """Bound for a composed transition of n elements: each factor carries the
-    per-block bar, and to first order the relative error of a product is at most
-    the sum of its factors' relative errors."""
-    return TOL * n_elem
+# a precise-T plan transition per segment (hi/lo operands; about 100 x its emulated error)
+TOL_PRECISE_T = 2e-4
 
 
 def log(msg):
@@ -69,14 +66,13 @@ def _check_T_S(label, T_hat, T_exp, S, ref):
 
 
 def test_gdn64k_full_build_and_compose(gpu):
+    """Every (segment, head) block of the headline layer, the composed state of every head
+    (AUTO and FOLD), and the composed transition of every head from the precise-T plan."""
     wl = WORKLOADS["gdn64k_bf16"]
     lens = segment_lengths(wl)
     cu = cu_of(lens)
     n_seg, h_v, d = len(lens), wl.h_v, wl.d
-    final_heads = [5, 26]
-    seg_heads = {0: [0, 1, 31, 63], 13: [2, 40, 62], 22: [7, 33, 63], 31: [0, 17, 50, 62]}
-    jobs = [("gdn64k_bf16", 0, h, None, True) for h in final_heads]
-    jobs += [("gdn64k_bf16", 0, h, segs, False) for h, segs in seg_heads.items()]
+    jobs = [("gdn64k_bf16", 0, h, None, True) for h in range(h_v)]
     pool, res = start_pool(dense_segments_job, jobs)
     t0 = time.time()
     x = layer_inputs(wl, 0, with_q=False)
@@ -96,23 +92,38 @@ def test_gdn64k_full_build_and_compose(gpu):
     H.hypic_device_status()
     Th, Te, Sh = _host(E_T), _host(E_e), _host(E_S)
     Sa, Sf = _host(c_auto["S_final"]), _host(c_fold["S_final"])
-    Tt, Tte = _host(c_fold["T_total"]), _host(c_fold["T_total_exp"])
+    Tt_fast, Tte_fast = _host(c_fold["T_total"]), _host(c_fold["T_total_exp"])
+    del b, E_T, E_e, E_S, c_auto, c_fold
+    # the precise-T plan: the composed transition of 64 cached segments within the bar
+    p = H.hypic_segment_build(k, v, la, cu, beta, precision="f16_precise_t")
+    P = (p["T_hat"].reshape(n_seg, h_v, d, d), p["T_exp"].reshape(n_seg, h_v), p["S"].reshape(n_seg, h_v, d, d))
+    c_pre = H.hypic_compose(*P, mode="fold", want_T=True)
+    torch.cuda.synchronize()
+    H.hypic_device_status()
+    PTh, PTe, PSh = _host(P[0]), _host(P[1]), _host(P[2])
+    Tt, Tte = _host(c_pre["T_total"]), _host(c_pre["T_total_exp"])
+    del p, P, c_pre
     log("device done; waiting for the oracle")
     outs = _collect(pool, res)
-    worst = [0.0, 0.0, 0.0, 0.0]
-    for (name, layer, h, segs, fold), r in zip(jobs, outs):
+    worst = {"T": 0.0, "S": 0.0, "S_final": 0.0, "T_total": 0.0, "T_precise": 0.0, "T_total_fast": 0.0}
+    for h, r in enumerate(outs):
         for s, ref in r["seg"].items():
             eT, eS = _check_T_S(f"head {h} segment {s}", Th[s, h], Te[s, h], Sh[s, h], ref)
-            worst[0], worst[1] = max(worst[0], eT), max(worst[1], eS)
-        if fold:
-            for lab, Sx in (("auto", Sa), ("fold", Sf)):
-                e = float(O.rel_err(Sx[h], r["S_final"]))
-                assert e <= TOL, f"head {h} composed state ({lab}): {e:.3e}"
-                worst[2] = max(worst[2], e)
-            e = float(O.rel_err_T("dense", Tt[h], Tte[h], r["T_hat"], r["T_exp"]))
-            assert e <= tol_T_total(n_seg), f"head {h} composed T: {e:.3e}"
-            worst[3] = max(worst[3], e)
-    log(f"gdn64k: max T {worst[0]:.2e}, S {worst[1]:.2e}, S_final {worst[2]:.2e}, T_total {worst[3]:.2e}")
+            worst["T"], worst["S"] = max(worst["T"], eT), max(worst["S"], eS)
+            eP = float(O.rel_err_T("dense", PTh[s, h], PTe[s, h], ref[0], ref[1]))
+            ePS = float(O.rel_err(PSh[s, h], ref[2]))
+            assert eP <= TOL_PRECISE_T and ePS <= TOL, f"head {h} segment {s}: precise T {eP:.3e}, S {ePS:.3e}"
+            worst["T_precise"] = max(worst["T_precise"], eP)
+        for lab, Sx in (("auto", Sa), ("fold", Sf)):
+            e = float(O.rel_err(Sx[h], r["S_final"]))
+            assert e <= TOL, f"head {h} composed state ({lab}): {e:.3e}"
+            worst["S_final"] = max(worst["S_final"], e)
+        e = float(O.rel_err_T("dense", Tt[h], Tte[h], r["T_hat"], r["T_exp"]))
+        assert e <= TOL, f"head {h} composed T (precise plan): {e:.3e}"
+        worst["T_total"] = max(worst["T_total"], e)
+        worst["T_total_fast"] = max(worst["T_total_fast"], float(O.rel_err_T("dense", Tt_fast[h], Tte_fast[h],
+                                                                             r["T_hat"], r["T_exp"])))
+    log("gdn64k, all {} blocks: max ".format(n_seg * h_v) + ", ".join(f"{k_} {v_:.2e}" for k_, v_ in worst.items()))
 
 
 # ----------------------------------------------------------------------------------------
@@ -167,24 +178,39 @@ def test_cold100k_full_schedules_scan_and_single_pass(gpu):
     Sh = _host(E_S[:, idx])
     Sc = _host(c["S_final"][idx])
     Ss = _host(single[idx])
-    Tt, Tte = _host(c["T_total"][idx]), _host(c["T_total_exp"][idx])
-    del k, v, b, c, single
+    Tt_auto, Tte_auto = _host(c["T_total"][idx]), _host(c["T_total_exp"][idx])
+    del b, c, single, E_T, E_e, E_S
+    # the precise-T plan: composed transitions of the 20 cached segments within the bar
+    p = H.hypic_segment_build(k, v, la, cu, beta, schedule="lpt", precision="f16_precise_t")
+    P = (p["T_hat"].reshape(n_seg, n_chain, d, d), p["T_exp"].reshape(n_seg, n_chain),
+         p["S"].reshape(n_seg, n_chain, d, d))
+    cp = H.hypic_compose(*P, mode="scan", want_T=True)
+    torch.cuda.synchronize()
+    H.hypic_device_status()
+    PTh, PTe = _host(P[0][:, idx]), _host(P[1][:, idx])
+    Tt, Tte = _host(cp["T_total"][idx]), _host(cp["T_total_exp"][idx])
+    del k, v, p, P, cp
     log("device done; waiting for the oracle")
     outs = _collect(pool, res)
     worst = [0.0, 0.0, 0.0]
-    worst_T = 0.0
+    worst_T = worst_T_auto = worst_P = 0.0
     for j, ((layer, h), r) in enumerate(zip(chains, outs)):
         for s, ref in r["seg"].items():
             eT, eS = _check_T_S(f"layer {layer} head {h} segment {s}", Th[s, j], Te[s, j], Sh[s, j], ref)
             worst[0], worst[1] = max(worst[0], eT), max(worst[1], eS)
+            eP = float(O.rel_err_T("dense", PTh[s, j], PTe[s, j], ref[0], ref[1]))
+            assert eP <= TOL_PRECISE_T, f"layer {layer} head {h} segment {s}: precise T err {eP:.3e}"
+            worst_P = max(worst_P, eP)
         for lab, Sx in (("scan", Sc[j]), ("single pass", Ss[j])):
             e = float(O.rel_err(Sx, r["S_final"]))
             assert e <= TOL, f"layer {layer} head {h} final state ({lab}): {e:.3e}"
             worst[2] = max(worst[2], e)
         e = float(O.rel_err_T("dense", Tt[j], Tte[j], r["T_hat"], r["T_exp"]))
-        assert e <= tol_T_total(n_seg), f"layer {layer} head {h} composed T: {e:.3e}"
+        assert e <= TOL, f"layer {layer} head {h} composed T (precise plan): {e:.3e}"
         worst_T = max(worst_T, e)
-    log(f"cold100k: max T {worst[0]:.2e}, S {worst[1]:.2e}, final {worst[2]:.2e}, T_total {worst_T:.2e}")
+        worst_T_auto = max(worst_T_auto, float(O.rel_err_T("dense", Tt_auto[j], Tte_auto[j], r["T_hat"], r["T_exp"])))
+    log(f"cold100k: max T {worst[0]:.2e}, S {worst[1]:.2e}, final {worst[2]:.2e}; precise plan: segment T "
+        f"{worst_P:.2e}, T_total {worst_T:.2e} (AUTO plan's T_total {worst_T_auto:.2e})")
 
 
 # ----------------------------------------------------------------------------------------
@@ -244,7 +270,7 @@ def test_warm30_full_conv_seam_compose(gpu):
             y[nm] = r["y"]
             conv_state[nm][:, layer] = r["state_out"][:, 0]
         part = H.hypic_segment_build(y["k"].view(1, N, h_k, d), y["v"].view(1, N, h_v, d), la[layer:layer + 1],
-                                     cu, beta[layer:layer + 1], skip_head=w, qk_l2norm=True)
+                                     cu, beta[layer:layer + 1], skip_head=w, qk_l2norm=True, precision="f16")
         E_T[:n_slot].view(n_slot, L, h_v, d, d)[:, layer] = part["T_hat"][:, 0]
         E_e[:n_slot].view(n_slot, L, h_v)[:, layer] = part["T_exp"][:, 0]
         E_S[:n_slot].view(n_slot, L, h_v, d, d)[:, layer] = part["S"][:, 0]
