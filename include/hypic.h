@@ -235,6 +235,27 @@ hypic_status hypic_compose(const hypic_compose_desc* desc, hypic_stream_t stream
 size_t hypic_compose_workspace_bytes(const hypic_compose_desc* desc);
 
 /* ------------------------------------------------------------------------------------
+ * hypic_compose_noalloc -- hypic_compose for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.
+ *
+ * Same arguments, semantics and outputs as hypic_compose, except that
+ * desc->workspace / workspace_bytes are ignored: the scratch SCAN needs (block
+ * aggregates and block-entry states) lives in a fixed array of
+ * HYPIC_NOALLOC_SCRATCH_BYTES per device, which the library holds from the moment it
+ * is loaded on that device until the process ends.  A SCAN needing more (see
+ * hypic_compose_workspace_bytes) returns HYPIC_ERR_UNSUPPORTED; FOLD and NAIVE_ADD
+ * need none.  The call allocates nothing (no hipMalloc, no allocating library
+ * routine); its first call on a device looks up the array's device address.  Every
+ * call on one device shares that array and the array keeps the previous call's
+ * contents (SCAN writes all of it before reading it): calls that may overlap on one
+ * device -- different streams without ordering, or concurrent host threads on the
+ * same stream order -- race and give wrong results.
+ * ---------------------------------------------------------------------------------- */
+#define HYPIC_NOALLOC_SCRATCH_BYTES (32u << 20)
+hypic_status hypic_compose_noalloc(const hypic_compose_desc* desc, hypic_stream_t stream);
+
+/* ------------------------------------------------------------------------------------
  * hypic_seam_advance -- seam tokens through the running state (dense kind).
  *
  * [news], seam-window paragraph: the first w tokens of a reused segment are

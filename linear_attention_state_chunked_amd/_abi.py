@@ -22,6 +22,7 @@ ACT = {"none": 0, "silu": 1}
 KIND = {"dense": DENSE, "diag": DIAG, "scalar": SCALAR}
 INLINE_SEGS = 160          # segment tables up to this size need no workspace
 SEAM_SINK_DEFAULT = 8.0
+NOALLOC_SCRATCH_BYTES = 32 << 20   # fixed per-device scratch of hypic_compose_noalloc
 
 _p = C.c_void_p
 _i32 = C.c_int32
@@ -75,6 +76,7 @@ EXPORTS = {
     "hypic_segment_build_workspace_bytes": ([C.POINTER(BuildDesc)], C.c_size_t),
     "hypic_compose": ([C.POINTER(ComposeDesc), _p], _enum),
     "hypic_compose_workspace_bytes": ([C.POINTER(ComposeDesc)], C.c_size_t),
+    "hypic_compose_noalloc": ([C.POINTER(ComposeDesc), _p], _enum),
     "hypic_seam_advance": ([C.POINTER(SeamDesc), _p], _enum),
     "hypic_seam_advance_workspace_bytes": ([C.POINTER(SeamDesc)], C.c_size_t),
     "hypic_conv_warmup": ([C.POINTER(ConvDesc), _p], _enum),

@@ -158,8 +158,15 @@ def hypic_segment_build(k, v, log_alpha, cu_seqlens, beta=None, *, kind="dense",
     return {"T_hat": T_hat, "T_exp": T_exp, "S": S, "_workspace": ws}
 
 
+def hypic_compose_noalloc(T_hat, T_exp, S, **kw):
+    """hypic_compose through the allocation-free entry point: SCAN's scratch comes from
+    the library's fixed per-device array instead of a workspace (outputs are still
+    allocated here, by the caller's side).  Same arguments and results."""
+    return hypic_compose(T_hat, T_exp, S, _noalloc=True, **kw)
+
+
 def hypic_compose(T_hat, T_exp, S, *, kind="dense", slot=None, S0=None, mode="auto", want_prefix=False,
-                  want_T=False, scan_block=0, n_elem=None):
+                  want_T=False, scan_block=0, n_elem=None, _noalloc=False):
     """Compose cached elements in request order.
 
     Element store: S [n_slot, C, d, d] float32, T_hat [n_slot, C, ...] float32,
@@ -203,6 +210,9 @@ def hypic_compose(T_hat, T_exp, S, *, kind="dense", slot=None, S0=None, mode="au
                          S_final=_ptr(S_final), S_prefix=_ptr(S_prefix), T_total=_ptr(T_total),
                          T_total_exp=_ptr(T_total_exp), mode=A.COMPOSE[mode], scan_block=scan_block)
     L = A.lib()
+    if _noalloc:
+        A.check(L.hypic_compose_noalloc(C.byref(desc), _stream()))
+        return {"S_final": S_final, "S_prefix": S_prefix, "T_total": T_total, "T_total_exp": T_total_exp}
     nbytes = L.hypic_compose_workspace_bytes(C.byref(desc))
     ws = _workspace(nbytes, dev)
     desc.workspace, desc.workspace_bytes = ws.data_ptr(), ws.numel()

@@ -15,10 +15,38 @@
 // with |.| modifiers); T_i is staged row-major in LDS as hi/lo f16 by loader waves,
 // one element ahead.
 // Diagonal / scalar kinds: elementwise, one thread per state entry stripe.
+#include <mutex>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
 namespace hypic {
+
+// Scratch of the allocation-free compose entry point: one fixed array per device, held from
+// module load until the process ends.  Host code never passes `scratch` itself (on the host
+// the name only stands in for the symbol); it asks the runtime for the device address once
+// per device and hands that to the kernels.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void** ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* cached[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!cached[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        cached[dev] = p;
+    }
+    *ptr = cached[dev];
+    return hipSuccess;
+}
 
 __device__ __forceinline__ void split_hilo(const floatx16& x, int st, float scale, halfx8& hi, halfx8& lo) {
 #pragma unroll

@@ -523,7 +523,12 @@ size_t hypic_compose_workspace_bytes(const hypic_compose_desc* d) {
     return scan_layout(d, (d->n_elem + B - 1) / B).bytes;
 }
 
-hypic_status hypic_compose(const hypic_compose_desc* d, hypic_stream_t stream) {
+namespace {
+
+// The composition behind both compose entry points; `ws` / `ws_bytes` is the scratch the
+// SCAN mode uses (the caller's workspace, or the fixed per-device array).
+hypic_status compose_impl(const hypic_compose_desc* d, hypic_stream_t stream, void* ws_ptr, size_t ws_bytes,
+                          bool fixed_scratch) {
     hypic_status st = validate_compose(d);
     if (st != HYPIC_OK) return st;
     const int cus = planner_cus();
@@ -538,10 +543,20 @@ hypic_status hypic_compose(const hypic_compose_desc* d, hypic_stream_t stream) {
         B = scan_block_size(d, cus);
         nblk = (d->n_elem + B - 1) / B;
         L = scan_layout(d, nblk);
-        if (!d->workspace || d->workspace_bytes < L.bytes)
+        if (fixed_scratch) {
+            if (L.bytes > hypic::kNoAllocScratchBytes)
+                return fail(HYPIC_ERR_UNSUPPORTED,
+                            "compose_noalloc: this SCAN needs %zu bytes of scratch, the fixed per-device array "
+                            "holds %zu (use hypic_compose with a workspace, or FOLD)",
+                            L.bytes, hypic::kNoAllocScratchBytes);
+            hipError_t e = hypic::noalloc_scratch(&ws_ptr);
+            if (e != hipSuccess) return device_fail("compose_noalloc: scratch address", e);
+            ws_bytes = hypic::kNoAllocScratchBytes;
+        }
+        if (!ws_ptr || ws_bytes < L.bytes)
             return fail(HYPIC_ERR_WORKSPACE_TOO_SMALL, "compose: workspace of %zu bytes needed, %zu given", L.bytes,
-                        d->workspace ? d->workspace_bytes : (size_t)0);
-        if (reinterpret_cast<uintptr_t>(d->workspace) % kAlign)
+                        ws_ptr ? ws_bytes : (size_t)0);
+        if (reinterpret_cast<uintptr_t>(ws_ptr) % kAlign)
             return fail(HYPIC_ERR_INVALID_ARGUMENT, "compose: workspace must be 256-byte aligned");
     }
     hipError_t e;
@@ -566,7 +581,7 @@ hypic_status hypic_compose(const hypic_compose_desc* d, hypic_stream_t stream) {
         if (e != hipSuccess) return device_fail("compose: fold launch", e);
         return ok();
     }
-    unsigned char* ws = static_cast<unsigned char*>(d->workspace);
+    unsigned char* ws = static_cast<unsigned char*>(ws_ptr);
     float* aggT = reinterpret_cast<float*>(ws + L.aggT);
     int* aggE = reinterpret_cast<int*>(ws + L.aggE);
     float* aggS = reinterpret_cast<float*>(ws + L.aggS);
@@ -622,6 +637,18 @@ hypic_status hypic_compose(const hypic_compose_desc* d, hypic_stream_t stream) {
         if (e != hipSuccess) return device_fail("compose: scan re-fold launch", e);
     }
     return ok();
+}
+
+}  // namespace
+
+hypic_status hypic_compose(const hypic_compose_desc* d, hypic_stream_t stream) {
+    if (!d) return fail(HYPIC_ERR_INVALID_ARGUMENT, "compose: desc is NULL");
+    return compose_impl(d, stream, d->workspace, d->workspace_bytes, false);
+}
+
+hypic_status hypic_compose_noalloc(const hypic_compose_desc* d, hypic_stream_t stream) {
+    if (!d) return fail(HYPIC_ERR_INVALID_ARGUMENT, "compose_noalloc: desc is NULL");
+    return compose_impl(d, stream, nullptr, 0, true);
 }
 
 // ------------------------------------------------------------------------------------------
