@@ -169,7 +169,8 @@ typedef struct {
     int32_t n_seg;
     const int64_t* cu_seqlens;  /* host [n_seg + 1], cu[0] = 0, non-decreasing, cu[n_seg] <= N */
     int32_t skip_head;          /* >= 0 */
-    int32_t qk_l2norm;          /* 1: k is scaled to unit L2 norm per token and head on load */
+    int32_t qk_l2norm;          /* 1: k (and q, with outputs) scaled to unit L2 norm per token
+                                   and head on load */
     const void* k;
     const void* v;
     const float* log_alpha;
@@ -181,6 +182,15 @@ typedef struct {
     hypic_precision precision;
     void* workspace;
     size_t workspace_bytes;
+    /* Output-fused build (dense kind): with o != NULL every covered token t of a
+     * segment also gets o_t = S_t^T q_t, S_t the segment's zero-start state after
+     * token t -- the segment's own prefill outputs, with T and S(C|0) as side
+     * outputs.  q [B, N, h_k, d_k] in_dtype; o [B, N, h_v, d_v] out_dtype (tokens
+     * outside the covered ranges are not written).  Runs on the general chunk
+     * engine (one workgroup per (segment, chain)). */
+    const void* q;
+    void* o;
+    hypic_dtype out_dtype;
 } hypic_build_desc;
 
 hypic_status hypic_segment_build(const hypic_build_desc* desc, hypic_stream_t stream);

@@ -38,6 +38,7 @@ class BuildDesc(C.Structure):
         ("k", _p), ("v", _p), ("log_alpha", _p), ("beta", _p),
         ("T_hat", _p), ("T_exp", _p), ("S", _p),
         ("schedule", _enum), ("precision", _enum), ("workspace", _p), ("workspace_bytes", C.c_size_t),
+        ("q", _p), ("o", _p), ("out_dtype", _enum),
     ]
 
 

@@ -102,7 +102,7 @@ _FLOAT_IN = (torch.bfloat16, torch.float32)
 
 def hypic_segment_build(k, v, log_alpha, cu_seqlens, beta=None, *, kind="dense", with_T=True, skip_head=0,
                         qk_l2norm=False, schedule="natural", precision="auto", out=None, workspace_bytes=None,
-                        workspace=None):
+                        workspace=None, q=None, want_o=False, out_dtype=None):
     """Per-segment (T_hat, T_exp, S) for every (segment, batch, value head).
 
     k [B,N,h_k,d] (or [N,h_k,d]), v [B,N,h_v,d] of k's dtype; log_alpha float32
@@ -111,7 +111,9 @@ def hypic_segment_build(k, v, log_alpha, cu_seqlens, beta=None, *, kind="dense",
     [n_seg,B,h_v]) or None, T_exp [n_seg,B,h_v] int32 or None, and S
     [n_seg,B,h_v,d,d] float32.  `out` may hold preallocated "T_hat", "T_exp", "S"
     tensors of those shapes.  workspace_bytes overrides the queried workspace size;
-    workspace passes a caller-owned uint8 device tensor instead.
+    workspace passes a caller-owned uint8 device tensor instead.  With want_o (dense
+    kind, q [B,N,h_k,d] of k's dtype) the result also holds o [B,N,h_v,d] (out_dtype,
+    default k's): each covered token's output from the segment's zero-start state.
     """
     if kind not in A.KIND:
         raise ValueError(f"unknown kind {kind!r}")
@@ -129,8 +131,18 @@ def hypic_segment_build(k, v, log_alpha, cu_seqlens, beta=None, *, kind="dense",
         _check(beta, "beta", dtype=torch.float32, numel=B * N * h_v)
     elif beta is not None:
         raise ValueError("beta is used by the dense kind only")
+    if want_o:
+        if kd != A.DENSE:
+            raise ValueError("per-token outputs are implemented for the dense kind only")
+        q = _check(_as4(q, "q"), "q", dtype=k.dtype, shape=k.shape)
+    elif q is not None:
+        raise ValueError("q is given but want_o is False")
+    out_dtype = out_dtype or k.dtype
+    if out_dtype not in _FLOAT_IN:
+        raise ValueError(f"out_dtype must be bfloat16 or float32, got {out_dtype}")
     dev = _gpu_device(k, "k")
     _check(v, "v", device=dev)
+    _check(q, "q", device=dev, optional=True)
     la = _check(log_alpha.reshape(B, N, h_v, d) if kd == A.DIAG else log_alpha.reshape(B, N, h_v), "log_alpha",
                 device=dev)
     bt = _check(beta.reshape(B, N, h_v), "beta", device=dev) if beta is not None else None
@@ -142,11 +154,13 @@ def hypic_segment_build(k, v, log_alpha, cu_seqlens, beta=None, *, kind="dense",
         tshape = {A.DENSE: (n_seg, B, h_v, d, d), A.DIAG: (n_seg, B, h_v, d), A.SCALAR: (n_seg, B, h_v)}[kd]
         T_hat = _out(out, "T_hat", tshape, torch.float32, dev)
         T_exp = _out(out, "T_exp", (n_seg, B, h_v), torch.int32, dev)
+    o = _out(out, "o", (B, N, h_v, d), out_dtype, dev) if want_o else None
     desc = A.BuildDesc(kind=kd, in_dtype=_dtype(k), n_batch=B, n_tokens=N, h_k=h_k, h_v=h_v, d_k=d, d_v=v.shape[3],
                        chunk=64, n_seg=n_seg, cu_seqlens=cu.ctypes.data, skip_head=skip_head,
                        qk_l2norm=int(bool(qk_l2norm)), k=_ptr(k), v=_ptr(v), log_alpha=_ptr(la), beta=_ptr(bt),
                        T_hat=_ptr(T_hat), T_exp=_ptr(T_exp), S=_ptr(S), schedule=A.SCHED[schedule],
-                       precision=A.PREC[precision])
+                       precision=A.PREC[precision], q=_ptr(q), o=_ptr(o),
+                       out_dtype=A.BF16 if out_dtype == torch.bfloat16 else A.F32)
     L = A.lib()
     if workspace is not None:
         ws = _check(workspace, "workspace", dtype=torch.uint8, device=dev)
@@ -155,7 +169,7 @@ def hypic_segment_build(k, v, log_alpha, cu_seqlens, beta=None, *, kind="dense",
         ws = _workspace(nbytes, dev)
     desc.workspace, desc.workspace_bytes = ws.data_ptr(), ws.numel()
     A.check(L.hypic_segment_build(C.byref(desc), _stream()))
-    return {"T_hat": T_hat, "T_exp": T_exp, "S": S, "_workspace": ws}
+    return {"T_hat": T_hat, "T_exp": T_exp, "S": S, "o": o, "_workspace": ws}
 
 
 def hypic_compose_noalloc(T_hat, T_exp, S, **kw):

@@ -161,6 +161,16 @@ hypic_status validate_build(const hypic_build_desc* d) {
         return fail(HYPIC_ERR_INVALID_ARGUMENT, "build: beta must be NULL for the diagonal and scalar kinds");
     }
     if (d->n_seg > 0 && !d->S) return fail(HYPIC_ERR_INVALID_ARGUMENT, "build: S is NULL");
+    if (d->o) {
+        if (d->kind != HYPIC_DENSE_DELTA)
+            return fail(HYPIC_ERR_UNSUPPORTED, "build: per-token outputs are implemented for the dense kind only");
+        if (!d->q) return fail(HYPIC_ERR_INVALID_ARGUMENT, "build: o requested without q");
+        if (!aligned16(d->q)) return fail(HYPIC_ERR_INVALID_ARGUMENT, "build: q must be 16-byte aligned");
+        if (d->out_dtype != HYPIC_F32 && d->out_dtype != HYPIC_BF16)
+            return fail(HYPIC_ERR_INVALID_ARGUMENT, "build: unknown out_dtype %d", (int)d->out_dtype);
+        if (d->precision == HYPIC_PREC_F16_PRECISE_T)
+            return fail(HYPIC_ERR_UNSUPPORTED, "build: the output-fused build has no precise-T plan");
+    }
     if ((d->T_hat == nullptr) != (d->T_exp == nullptr))
         return fail(HYPIC_ERR_INVALID_ARGUMENT, "build: T_hat and T_exp must be both set or both NULL");
     if (d->schedule < HYPIC_SCHED_NATURAL || d->schedule > HYPIC_SCHED_RR)
@@ -316,7 +326,32 @@ hypic_status hypic_segment_build(const hypic_build_desc* d, hypic_stream_t strea
     hipError_t e = fill_seg_table(tab, L, d->workspace, start, len, order, s);
     if (e != hipSuccess) return device_fail("build: segment table upload", e);
 
-    if (d->kind == HYPIC_DENSE_DELTA) {
+    if (d->kind == HYPIC_DENSE_DELTA && d->o) {
+        // output-fused build: the general chunk engine from a zero state, with q
+        hypic::EngineArgs a{};
+        a.n_batch = d->n_batch;
+        a.n_tokens = d->n_tokens;
+        a.h_k = d->h_k;
+        a.h_v = d->h_v;
+        a.n_seg = d->n_seg;
+        a.qk_l2norm = d->qk_l2norm;
+        a.in_bf16 = d->in_dtype == HYPIC_BF16;
+        a.out_bf16 = d->out_dtype == HYPIC_BF16;
+        a.seg = tab;
+        a.n_tasks = (int)n_tasks;
+        a.k = d->k;
+        a.v = d->v;
+        a.q = d->q;
+        a.o = d->o;
+        a.log_alpha = d->log_alpha;
+        a.beta = d->beta;
+        a.S_out = d->S;
+        a.out_stride = (long long)d->n_batch * d->h_v * d->d_k * d->d_v;
+        a.T_hat = d->T_hat;
+        a.T_exp = d->T_exp;
+        e = hypic::launch_dense_engine(a, d->d_k, build_prec_f32(d) ? 1 : 0, (int)n_tasks, s);
+        if (e != hipSuccess) return device_fail("build: output-fused build launch", e);
+    } else if (d->kind == HYPIC_DENSE_DELTA) {
         hypic::EngineArgs a{};
         a.n_batch = d->n_batch;
         a.n_tokens = d->n_tokens;

@@ -206,6 +206,45 @@ def test_dense_bf16_skip_head_and_no_T(ragged_dense):
     assert torch.equal(plain["S"], out["S"])
 
 
+# ----------------------------------------------------------------------------------------
+# output-fused build: each covered token's output from the segment's zero-start state, with
+# T and S(C|0) as side outputs (the segment's own prefill forward)
+
+
+def _check_outputs(o, chains, lens, tol, skip=0, normalise=False):
+    """o [1, N, h, d] against the oracle's per-token outputs of each segment from zero."""
+    worst = 0.0
+    s0 = 0
+    for n in lens:
+        lo, hi = s0 + min(skip, n), s0 + n
+        for h, c in enumerate(chains):
+            k, q = (O.l2_normalise(c["k"]), O.l2_normalise(c["q"])) if normalise else (c["k"], c["q"])
+            if hi > lo:
+                r = O.dense_recurrence(k[lo:hi], c["v"][lo:hi], c["log_alpha"][lo:hi], c["beta"][lo:hi], q=q[lo:hi])
+                got = o[0, lo:hi, h].float().cpu().numpy()
+                e = float(O.rel_err(got, r["o"]))     # the segment's outputs as one block
+                assert e < tol, f"segment [{lo}, {hi}) head {h}: output err {e:.3e}"
+                worst = max(worst, e)
+        s0 += n
+    return worst
+
+
+@pytest.mark.parametrize("variant", ["bf16", "bf16_skip_l2norm_no_T", "f32_d64"])
+def test_output_fused_build(gpu, variant):
+    if variant == "f32_d64":
+        wl, lens, tol, h_v = WORKLOADS["tiny_gdn_f32"], [1, 63, 64, 65, 130, 0, 300], TOL_F32, 1
+    else:
+        wl, lens, tol, h_v = WORKLOADS["gdn64k_bf16"], RAGGED, TOL_BF16, 4
+    skip, l2, with_T = (8, True, False) if variant == "bf16_skip_l2norm_no_T" else (0, False, True)
+    dev, chains = _dense_inputs(wl, sum(lens), h_v, raw_keys=l2)
+    out = H.hypic_segment_build(dev["k"], dev["v"], dev["log_alpha"], cu_of(lens), beta=dev["beta"], q=dev["q"],
+                                want_o=True, out_dtype=torch.float32, skip_head=skip, qk_l2norm=l2, with_T=with_T)
+    torch.cuda.synchronize()
+    eo = _check_outputs(out["o"], chains, lens, tol, skip=skip, normalise=l2)
+    eT, eS = _check_build(out, chains, lens, "dense", tol, skip=skip, normalise=l2)
+    print(f"output-fused build {variant}: max o err {eo:.2e}, T err {eT:.2e}, S err {eS:.2e}")
+
+
 def test_dense_bf16_l2norm_on_load(gpu):
     wl = WORKLOADS["gdn64k_bf16"]
     lens = [100, 64, 37]
@@ -307,10 +346,8 @@ def test_diag_scalar_build_compose_and_naive(gpu, name, kind):
     la = dev_tensor(np.stack([c["log_alpha"] for c in chains], 1)[None])
     out = H.hypic_segment_build(k, v, la, cu_of(lens), kind=kind)
     torch.cuda.synchronize()
-    # per-segment parity on 4 heads spread over the decay range
-    sel = [0, 5, 10, 15]
-    sub = {"S": out["S"][:, :, sel], "T_hat": out["T_hat"][:, :, sel], "T_exp": out["T_exp"][:, :, sel]}
-    _check_build(sub, [chains[i] for i in sel], lens, kind, TOL_BF16)
+    # per-segment parity on every head
+    _check_build(out, chains, lens, kind, TOL_BF16)
     n_seg = len(lens)
     tshape = (n_seg, h, 128) if kind == "diag" else (n_seg, h)
     comp = H.hypic_compose(out["T_hat"].reshape(tshape), out["T_exp"].reshape(n_seg, h),
@@ -318,14 +355,15 @@ def test_diag_scalar_build_compose_and_naive(gpu, name, kind):
     naive = H.hypic_compose(None, None, out["S"].reshape(n_seg, h, 128, 128), kind=kind, mode="naive_add")
     torch.cuda.synchronize()
     fn = O.diag_recurrence if kind == "diag" else O.scalar_recurrence
-    for i in sel:
-        c = chains[i]
-        full = fn(c["k"], c["v"], c["log_alpha"])["S"]
-        err = float(O.rel_err(comp["S_final"][i].cpu().numpy(), full))
-        naive_err = float(O.rel_err(naive["S_final"][i].cpu().numpy(), full))
-        print(f"{name} head {i}: transition-compose err {err:.2e}, naive-addition err {naive_err:.3f}")
-        assert err < TOL_BF16
-        assert naive_err > 10 * TOL_BF16   # decay makes naive addition structurally wrong
+    # the whole prompt per head, all heads as one batch of independent chains
+    full = fn(np.stack([c["k"] for c in chains]), np.stack([c["v"] for c in chains]),
+              np.stack([c["log_alpha"] for c in chains]))["S"]
+    errs = O.rel_err(comp["S_final"].cpu().numpy(), full)
+    naive_errs = O.rel_err(naive["S_final"].cpu().numpy(), full)
+    for i in range(h):
+        print(f"{name} head {i}: transition-compose err {errs[i]:.2e}, naive-addition err {naive_errs[i]:.3f}")
+    assert float(np.max(errs)) < TOL_BF16
+    assert float(np.min(naive_errs)) > 10 * TOL_BF16   # decay makes naive addition structurally wrong
 
 
 @pytest.mark.parametrize("d", [64, 128])
