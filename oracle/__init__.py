@@ -19,7 +19,9 @@ the HYPIC pages and the published gated delta rule:
 * the seam window (HYPIC news article, seam-window paragraph; README, "PIC modes");
 * the depthwise causal convolution with carried state (conv-state warm-up,
   linear-layer paragraph);
-* LPT list scheduling (segment-parallelism paragraph; Graham 1969).
+* LPT list scheduling (segment-parallelism paragraph; Graham 1969);
+* RoPE state re-rotation of a cached element moved to a new offset (linear-layer
+  paragraph; README, "PIC modes", transition_rope).
 
 Parity pins for every function are in tests/test_oracle.py.
 """
@@ -38,6 +40,10 @@ from .reference import (  # noqa: F401
     opt_makespan_bruteforce,
     rel_err,
     rel_err_T,
+    rerotate,
+    rope_matrix,
+    rope_pairs,
+    rope_rotate,
     rr_schedule,
     scalar_recurrence,
     seam_advance,

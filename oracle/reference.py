@@ -292,6 +292,66 @@ def warm_chain_reference(xq, xk, xv, wq, wk, wv, beta, log_alpha, seg_lens, seam
 
 
 # ----------------------------------------------------------------------------------------
+# RoPE state re-rotation (HYPIC news article, linear-layer paragraph: the alignment patch
+# for variants that rotate q and k by absolute position; HYPIC project README, "PIC
+# modes": the transition_rope mode corrects the positions of segments reused elsewhere)
+
+
+def rope_pairs(d, rotary_dim, interleaved):
+    """Channel pairs (a, b) rotated together and the frequency index of each.
+
+    interleaved: pairs (2i, 2i+1); otherwise (i, i + rotary_dim/2), i < rotary_dim/2.
+    Channels >= rotary_dim are not rotated."""
+    h = rotary_dim // 2
+    if interleaved:
+        return [(2 * i, 2 * i + 1, i) for i in range(h)]
+    return [(i, i + h, i) for i in range(h)]
+
+
+def rope_matrix(d, delta, rotary_dim, base, interleaved):
+    """The d x d rotation R(delta): on each pair (a, b) with frequency
+    theta_i = base^(-2i / rotary_dim) it maps (x_a, x_b) to
+    (x_a cos(delta theta_i) - x_b sin(delta theta_i), x_a sin(delta theta_i) + x_b cos(delta theta_i));
+    identity on the other channels.  A key rotated at position p is R(p) k."""
+    R = np.eye(d)
+    for a, b, i in rope_pairs(d, rotary_dim, interleaved):
+        ang = float(delta) * float(base) ** (-2.0 * i / rotary_dim)
+        c, s_ = np.cos(ang), np.sin(ang)
+        R[a, a], R[a, b], R[b, a], R[b, b] = c, -s_, s_, c
+    return R
+
+
+def rope_rotate(x, positions, rotary_dim, base, interleaved):
+    """Rotate rows x[..., n, d] by R(positions[t]) each, channel pair by channel pair."""
+    x = np.array(_f64(x), copy=True)
+    pos = np.asarray(positions, np.float64)
+    out = x.copy()
+    for a, b, i in rope_pairs(x.shape[-1], rotary_dim, interleaved):
+        ang = pos * float(base) ** (-2.0 * i / rotary_dim)
+        c, s_ = np.cos(ang), np.sin(ang)
+        out[..., a] = x[..., a] * c - x[..., b] * s_
+        out[..., b] = x[..., a] * s_ + x[..., b] * c
+    return out
+
+
+def rerotate(kind, T_hat, T_exp, S, delta, rotary_dim, base, interleaved):
+    """A cached element whose keys were rotated at positions p + t, moved to p + delta + t.
+
+    Rotated keys R k give per-token transitions R A_t R^T and writes R k v^T, so the
+    segment's transition becomes R T R^T and its state R S (R = R(delta)).  A scalar
+    transition commutes with R and is unchanged.  Per-channel (diagonal) gates do not
+    commute with R unless tied on every rotated pair; that kind is not handled."""
+    if kind not in ("dense", "scalar"):
+        raise ValueError(f"re-rotation is defined here for the dense and scalar kinds, not {kind}")
+    d = np.shape(S)[-2]
+    R = rope_matrix(d, delta, rotary_dim, base, interleaved)
+    S2 = R @ _f64(S)
+    if kind == "dense":
+        return {"T_hat": R @ _f64(T_hat) @ R.T, "T_exp": np.asarray(T_exp), "S": S2}
+    return {"T_hat": _f64(T_hat), "T_exp": np.asarray(T_exp), "S": S2}
+
+
+# ----------------------------------------------------------------------------------------
 # schedules (integer)
 
 

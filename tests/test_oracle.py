@@ -487,3 +487,72 @@ def test_error_metric_conventions():
     Th = np.eye(3) * 0.5
     assert O.rel_err_T("dense", Th * 2, np.array(4), Th, np.array(5)) == 0
     assert abs(O.rel_err_T("dense", Th * 1.001, np.array(5), Th, np.array(5)) - 1e-3) < 1e-12
+
+
+# ----------------------------------------------------------------------------------------
+# RoPE state re-rotation (HYPIC news article, linear-layer paragraph; README, "PIC modes",
+# transition_rope): a segment cached with keys rotated at positions p + t and reused at
+# p + delta + t
+
+
+@pytest.mark.parametrize("interleaved", [False, True])
+@pytest.mark.parametrize("kind", ["dense", "scalar"])
+def test_rerotation_equals_recomputation_at_the_new_offset(kind, interleaved):
+    # pinned against recomputing the recurrence on keys rotated at the new positions
+    rng = np.random.default_rng(41)
+    n, d, rd, base, p0, delta = 50, 8, 6, 100.0, 1000, -377
+    k, v, la, b, _ = _rand_chain(rng, n, d, 3, unit=True)
+    pos = p0 + np.arange(n)
+    k0 = O.rope_rotate(k, pos, rd, base, interleaved)
+    k1 = O.rope_rotate(k, pos + delta, rd, base, interleaved)
+    if kind == "dense":
+        r0 = O.dense_recurrence(k0, v, la, b)
+        r1 = O.dense_recurrence(k1, v, la, b)
+    else:
+        r0 = O.scalar_recurrence(k0, v, la)
+        r1 = O.scalar_recurrence(k1, v, la)
+    m = O.rerotate(kind, r0["T_hat"], r0["T_exp"], r0["S"], delta, rd, base, interleaved)
+    assert np.max(O.rel_err(m["S"], r1["S"])) < 1e-12
+    assert np.max(O.rel_err_T(kind, m["T_hat"], m["T_exp"], r1["T_hat"], r1["T_exp"])) < 1e-12
+    # without the correction the cached state is wrong at the new offset
+    assert np.max(O.rel_err(r0["S"], r1["S"])) > 1e-2
+
+
+def test_rope_rotation_closed_form_and_group_laws():
+    # base 1, rotary_dim 4: every pair turns by exactly delta radians; a quarter turn maps
+    # (x_a, x_b) to (-x_b, x_a) on each pair and leaves channels 4, 5 alone
+    x = np.arange(1.0, 7.0)
+    for inter, pairs in ((True, [(0, 1), (2, 3)]), (False, [(0, 2), (1, 3)])):
+        y = O.rope_rotate(x[None], [np.pi / 2], 4, 1.0, inter)[0]
+        want = x.copy()
+        for a, b in pairs:
+            want[a], want[b] = -x[b], x[a]
+        assert np.allclose(y, want, atol=1e-15)
+    R = lambda t: O.rope_matrix(10, t, 8, 500.0, False)
+    assert np.allclose(R(0.0), np.eye(10))
+    assert np.allclose(R(3.0) @ R(-11.0), R(-8.0), atol=1e-14)             # R(a) R(b) = R(a + b)
+    assert np.allclose(R(7.5).T @ R(7.5), np.eye(10), atol=1e-14)          # orthogonal
+    # the matrix and the row rotation agree (both used by the re-rotation pin above)
+    rng = np.random.default_rng(43)
+    z = rng.standard_normal((5, 10))
+    assert np.allclose(O.rope_rotate(z, [12.0] * 5, 8, 500.0, True), z @ O.rope_matrix(10, 12.0, 8, 500.0, True).T)
+
+
+def test_rope_outputs_are_relative():
+    # rotating q and k by the same shift leaves every output o_t = S_t^T q_t unchanged: the
+    # re-rotated state is what the shifted queries read
+    rng = np.random.default_rng(44)
+    n, d, rd = 30, 8, 8
+    k, v, la, b, q = _rand_chain(rng, n, d, 4, unit=True)
+    a = O.dense_recurrence(O.rope_rotate(k, np.arange(n), rd, 50.0, False), v, la, b,
+                           q=O.rope_rotate(q, np.arange(n), rd, 50.0, False))
+    c = O.dense_recurrence(O.rope_rotate(k, np.arange(n) + 999, rd, 50.0, False), v, la, b,
+                           q=O.rope_rotate(q, np.arange(n) + 999, rd, 50.0, False))
+    assert np.max(np.abs(a["o"] - c["o"])) < 1e-12
+    m = O.rerotate("dense", a["T_hat"], a["T_exp"], a["S"], 999, rd, 50.0, False)
+    assert np.max(O.rel_err(m["S"], c["S"])) < 1e-12
+
+
+def test_rerotation_rejects_per_channel_gates():
+    with pytest.raises(ValueError):
+        O.rerotate("diag", np.ones(4), 0, np.zeros((4, 4)), 3, 4, 10.0, False)
