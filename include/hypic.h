@@ -364,6 +364,45 @@ hypic_status hypic_conv_warmup(const hypic_conv_desc* desc, hypic_stream_t strea
 size_t hypic_conv_warmup_workspace_bytes(const hypic_conv_desc* desc);
 
 /* ------------------------------------------------------------------------------------
+ * hypic_state_rerotate -- RoPE state re-rotation of cached elements reused at a new
+ * absolute offset.
+ *
+ * [news], linear-layer paragraph: variants that rotate q and k by absolute position
+ * (RoPE) need the cached state re-rotated; [readme], "PIC modes": transition_rope
+ * corrects the positions of segments reused somewhere else.  A segment cached with keys
+ * rotated at positions p + t and reused at p + delta + t has keys R k with
+ * R = R(delta): on each rotated channel pair (a, b) with frequency
+ * theta_i = rope_base^(-2i / rotary_dim), (x_a, x_b) -> (x_a cos - x_b sin,
+ * x_a sin + x_b cos) of the angle delta * theta_i; channels >= rotary_dim unchanged.
+ * Its per-token transitions become R A_t R^T and its writes R k v^T, so
+ *   S' = R S,   T' = R T R^T (DENSE; T_exp unchanged),   T' = T (SCALAR).
+ * Per-channel (DIAG) gates do not commute with R: HYPIC_ERR_UNSUPPORTED.
+ * Layouts (C = n_chain), float32, out may alias in (in-place update):
+ *   S_in, S_out          [n_elem, C, d_k, d_v]
+ *   T_hat_in, T_hat_out  [n_elem, C, d_k, d_k] (DENSE; NULL for SCALAR)
+ *   delta                host int64 [n_elem]: new offset minus the cached offset
+ * Pairs: interleaved = 1 pairs channels (2i, 2i+1); 0 pairs (i, i + rotary_dim/2).
+ * rotary_dim even, 2 <= rotary_dim <= d_k; rope_base > 0.  No workspace; the shifts
+ * travel in the kernel arguments (up to 160 elements per launch, more in batches).
+ * ---------------------------------------------------------------------------------- */
+typedef struct {
+    hypic_kind kind;
+    int32_t n_elem;
+    int32_t n_chain;
+    int32_t d_k, d_v;
+    int32_t rotary_dim;
+    int32_t interleaved;
+    double rope_base;
+    const int64_t* delta;
+    const float* T_hat_in;
+    float* T_hat_out;
+    const float* S_in;
+    float* S_out;
+} hypic_rerotate_desc;
+
+hypic_status hypic_state_rerotate(const hypic_rerotate_desc* desc, hypic_stream_t stream);
+
+/* ------------------------------------------------------------------------------------
  * hypic_plan_schedule -- host-only planner behind HYPIC_SCHED_* (no GPU use).
  *
  * Assigns n tasks of integer weight (chunks) to `groups` workers.  LPT: tasks in

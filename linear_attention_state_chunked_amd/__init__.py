@@ -15,5 +15,6 @@ from .api import (  # noqa: F401
     hypic_seam_advance,
     hypic_seam_widths,
     hypic_segment_build,
+    hypic_state_rerotate,
 )
 from ._abi import HypicError, LIB_PATH, lib  # noqa: F401

@@ -72,6 +72,14 @@ class ConvDesc(C.Structure):
     ]
 
 
+class RerotateDesc(C.Structure):
+    _fields_ = [
+        ("kind", _enum), ("n_elem", _i32), ("n_chain", _i32), ("d_k", _i32), ("d_v", _i32),
+        ("rotary_dim", _i32), ("interleaved", _i32), ("rope_base", C.c_double), ("delta", _p),
+        ("T_hat_in", _p), ("T_hat_out", _p), ("S_in", _p), ("S_out", _p),
+    ]
+
+
 EXPORTS = {
     "hypic_segment_build": ([C.POINTER(BuildDesc), _p], _enum),
     "hypic_segment_build_workspace_bytes": ([C.POINTER(BuildDesc)], C.c_size_t),
@@ -83,6 +91,7 @@ EXPORTS = {
     "hypic_conv_warmup": ([C.POINTER(ConvDesc), _p], _enum),
     "hypic_conv_warmup_workspace_bytes": ([C.POINTER(ConvDesc)], C.c_size_t),
     "hypic_plan_schedule": ([_p, _i32, _i32, _enum, _p, _p, _p], _enum),
+    "hypic_state_rerotate": ([C.POINTER(RerotateDesc), _p], _enum),
     "hypic_seam_widths": ([_p, _i32, C.c_double, _p], _enum),
     "hypic_device_status": ([], _enum),
     "hypic_last_error": ([], C.c_char_p),

@@ -351,6 +351,43 @@ def hypic_conv_warmup(x, weight, cu_seqlens, *, state_in=None, state_index=None,
     return {"y": y, "state_out": st_out, "_workspace": ws}
 
 
+def hypic_state_rerotate(T_hat, S, delta, *, kind="dense", rotary_dim=None, rope_base=10000.0, interleaved=False,
+                         inplace=False):
+    """RoPE re-rotation of cached elements moved by delta[i] positions.
+
+    S float32 [n_elem, C, d, d]; T_hat float32 [n_elem, C, d, d] (dense) or None
+    (scalar: the transition is unchanged); delta: host int64 [n_elem].  rotary_dim
+    defaults to d.  Returns {"T_hat", "S"}: new tensors, or the inputs updated in
+    place with inplace=True.
+    """
+    if kind not in A.KIND:
+        raise ValueError(f"unknown kind {kind!r}")
+    kd = A.KIND[kind]
+    if not isinstance(S, torch.Tensor) or S.dim() != 4:
+        raise ValueError("S must be a [n_elem, n_chain, d, d] tensor")
+    n_elem, n_chain, d = S.shape[0], S.shape[1], S.shape[2]
+    _check(S, "S", dtype=torch.float32, shape=(n_elem, n_chain, d, d))
+    if kd == A.DENSE:
+        _check(T_hat, "T_hat", dtype=torch.float32, shape=(n_elem, n_chain, d, d))
+    elif T_hat is not None and not isinstance(T_hat, torch.Tensor):
+        raise ValueError("T_hat must be a tensor or None")
+    dl = np.ascontiguousarray(np.asarray(delta, dtype=np.int64))
+    if dl.shape != (n_elem,):
+        raise ValueError(f"delta must hold {n_elem} shifts, got shape {dl.shape}")
+    dev = _gpu_device(S, "S")
+    if kd == A.DENSE:
+        _check(T_hat, "T_hat", device=dev)
+    S_out = S if inplace else torch.empty_like(S)
+    T_in = T_hat if kd == A.DENSE else None
+    T_out = (T_hat if inplace else torch.empty_like(T_hat)) if kd == A.DENSE else None
+    desc = A.RerotateDesc(kind=kd, n_elem=n_elem, n_chain=n_chain, d_k=d, d_v=S.shape[3],
+                          rotary_dim=d if rotary_dim is None else rotary_dim, interleaved=int(bool(interleaved)),
+                          rope_base=float(rope_base), delta=dl.ctypes.data if n_elem else None, T_hat_in=_ptr(T_in),
+                          T_hat_out=_ptr(T_out), S_in=_ptr(S), S_out=_ptr(S_out))
+    A.check(A.lib().hypic_state_rerotate(C.byref(desc), _stream()))
+    return {"T_hat": T_out if kd == A.DENSE else T_hat, "S": S_out}
+
+
 def hypic_plan_schedule(weights, groups: int, schedule: str = "lpt"):
     """Host-only LPT / round-robin assignment of integer task weights to groups.
 

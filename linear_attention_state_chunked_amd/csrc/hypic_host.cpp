@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
@@ -829,6 +830,56 @@ hypic_status hypic_seam_advance(const hypic_seam_desc* d, hypic_stream_t stream)
         r.out_stride = dense;
         e = hypic::launch_dense_engine(r, d->d_k, f32 ? 1 : 0, (int)n_tasks, s);
         if (e != hipSuccess) return device_fail("seam: zero-start engine launch", e);
+    }
+    return ok();
+}
+
+// ------------------------------------------------------------------------------------------
+// RoPE state re-rotation
+
+hypic_status hypic_state_rerotate(const hypic_rerotate_desc* d, hypic_stream_t stream) {
+    if (!d) return fail(HYPIC_ERR_INVALID_ARGUMENT, "rerotate: desc is NULL");
+    if (d->kind == HYPIC_DIAG)
+        return fail(HYPIC_ERR_UNSUPPORTED,
+                    "rerotate: per-channel gates do not commute with the RoPE rotation (only the dense and "
+                    "scalar kinds re-rotate exactly)");
+    if (d->kind != HYPIC_DENSE_DELTA && d->kind != HYPIC_SCALAR)
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "rerotate: unknown kind %d", (int)d->kind);
+    if (d->n_elem < 0 || d->n_chain < 1)
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "rerotate: bad n_elem=%d n_chain=%d", d->n_elem, d->n_chain);
+    if (d->d_k != d->d_v || !supported_d(d->d_k))
+        return fail(HYPIC_ERR_UNSUPPORTED, "rerotate: d_k=%d d_v=%d (supported: d_k == d_v in {64, 128})", d->d_k,
+                    d->d_v);
+    if (d->rotary_dim < 2 || d->rotary_dim > d->d_k || d->rotary_dim % 2)
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "rerotate: rotary_dim=%d must be even and in [2, d_k]", d->rotary_dim);
+    if (d->interleaved != 0 && d->interleaved != 1)
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "rerotate: interleaved must be 0 or 1");
+    if (!(d->rope_base > 0.0) || d->rope_base > 1e30)
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "rerotate: rope_base %g must be positive and finite", d->rope_base);
+    if ((int64_t)d->n_chain > INT32_MAX / 2) return fail(HYPIC_ERR_UNSUPPORTED, "rerotate: too many chains");
+    if (d->n_elem == 0) return ok();
+    if (!d->delta) return fail(HYPIC_ERR_INVALID_ARGUMENT, "rerotate: delta is NULL");
+    if (!d->S_in || !d->S_out) return fail(HYPIC_ERR_INVALID_ARGUMENT, "rerotate: S_in and S_out are required");
+    const bool dense = d->kind == HYPIC_DENSE_DELTA;
+    if (dense && (!d->T_hat_in || !d->T_hat_out))
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "rerotate: the dense kind needs T_hat_in and T_hat_out");
+    hypic::RotArgs r{};
+    r.n_chain = d->n_chain;
+    r.rotary_dim = d->rotary_dim;
+    r.interleaved = d->interleaved;
+    r.dense = dense ? 1 : 0;
+    r.log2_base = std::log2(d->rope_base);
+    r.T_in = dense ? d->T_hat_in : nullptr;
+    r.T_out = dense ? d->T_hat_out : nullptr;
+    r.S_in = d->S_in;
+    r.S_out = d->S_out;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    for (int32_t e0 = 0; e0 < d->n_elem; e0 += hypic::kRotInline) {
+        const int n = std::min<int32_t>(hypic::kRotInline, d->n_elem - e0);
+        r.elem0 = e0;
+        for (int i = 0; i < n; ++i) r.delta[i] = d->delta[e0 + i];
+        hipError_t e = hypic::launch_rerotate(r, d->d_k, n, s);
+        if (e != hipSuccess) return device_fail("rerotate: launch", e);
     }
     return ok();
 }

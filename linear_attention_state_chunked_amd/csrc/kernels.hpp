@@ -175,6 +175,25 @@ constexpr int kSeamShort = 16;
 // w_max: the longest seam (<= kSeamShort); seams of at most 8 tokens use a lighter instance
 hipError_t launch_seam(const SeamArgs& a, int d, int w_max, hipStream_t s);
 
+// RoPE state re-rotation of up to kRotInline elements per launch (the position shifts
+// travel in the kernel arguments): S_out = R S_in and, with dense, T_out = R T_in R^T,
+// R = R(delta[e]); elements elem0 + e of [n_elem, n_chain, d, d] arrays; may run in place.
+constexpr int kRotInline = 160;
+struct RotArgs {
+    int n_chain;
+    int rotary_dim;
+    int interleaved;   // 1: pairs (2i, 2i+1); 0: pairs (i, i + rotary_dim/2)
+    int dense;         // 1: rotate T too (rows and columns); 0: scalar T, untouched
+    int elem0;
+    double log2_base;
+    const float* T_in;
+    float* T_out;
+    const float* S_in;
+    float* S_out;
+    long long delta[kRotInline];
+};
+hipError_t launch_rerotate(const RotArgs& r, int d, int n_elem, hipStream_t s);
+
 // resident workgroups per CU for the dense engine (for persistent grids)
 int dense_engine_max_lds(int d, int prec_f32, int with_q);
 

@@ -29,7 +29,7 @@ def L():
 def test_every_declared_symbol_is_exported(L):
     src = open(HEADER).read()
     declared = set(re.findall(r"^\s*(?:hypic_status|size_t|const char\*|int)\s+(hypic_\w+)\s*\(", src, re.M))
-    assert len(declared) == 14
+    assert len(declared) == 15
     assert declared == set(A.EXPORTS)
     out = subprocess.run(["nm", "-D", "--defined-only", A.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT (hypic_\w+)", out))
@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported(L):
 def test_struct_layouts_match_the_header(tmp_path):
     lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "hypic.h"', "int main(void) {"]
     structs = {"hypic_build_desc": A.BuildDesc, "hypic_compose_desc": A.ComposeDesc,
-               "hypic_seam_desc": A.SeamDesc, "hypic_conv_desc": A.ConvDesc}
+               "hypic_seam_desc": A.SeamDesc, "hypic_conv_desc": A.ConvDesc, "hypic_rerotate_desc": A.RerotateDesc}
     for cname, cls in structs.items():
         lines.append(f'printf("{cname} %zu\\n", sizeof({cname}));')
         for f, _ in cls._fields_:
@@ -327,3 +327,24 @@ def test_binding_rejects_bad_compose_seam_conv_tensors():
         w = a.pop("weight")
         with pytest.raises(ValueError):
             H.hypic_conv_warmup(x, w, [0, 8, 16], **a)
+
+
+def test_rerotate_validation(L):
+    dl = np.array([3, -5], np.int64)
+    base = dict(kind=A.DENSE, n_elem=2, n_chain=3, d_k=64, d_v=64, rotary_dim=64, interleaved=0, rope_base=1e4,
+                delta=dl.ctypes.data, T_hat_in=0x1000, T_hat_out=0x1000, S_in=0x2000, S_out=0x2000)
+    for kw, status, msg in ((dict(kind=A.DIAG), A.ERR_UNSUPPORTED, "commute"),
+                            (dict(rotary_dim=63), A.ERR_INVALID_ARGUMENT, "even"),
+                            (dict(rotary_dim=66), A.ERR_INVALID_ARGUMENT, "rotary_dim"),
+                            (dict(rope_base=0.0), A.ERR_INVALID_ARGUMENT, "rope_base"),
+                            (dict(rope_base=float("nan")), A.ERR_INVALID_ARGUMENT, "rope_base"),
+                            (dict(interleaved=2), A.ERR_INVALID_ARGUMENT, "interleaved"),
+                            (dict(delta=None), A.ERR_INVALID_ARGUMENT, "delta"),
+                            (dict(T_hat_in=None), A.ERR_INVALID_ARGUMENT, "T_hat_in"),
+                            (dict(d_k=96, d_v=96), A.ERR_UNSUPPORTED, "d_k"),
+                            (dict(n_chain=0), A.ERR_INVALID_ARGUMENT, "n_chain")):
+        d = A.RerotateDesc(**{**base, **kw})
+        assert L.hypic_state_rerotate(C.byref(d), None) == status, kw
+        assert msg in L.hypic_last_error().decode(), kw
+    d = A.RerotateDesc(**{**base, "n_elem": 0})
+    assert L.hypic_state_rerotate(C.byref(d), None) == A.OK      # nothing to do, nothing enqueued

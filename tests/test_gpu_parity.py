@@ -489,3 +489,83 @@ def test_conv_warmup(gpu, act, out_dtype):
             assert O.rel_err(res["y"][0, lo:hi].float().cpu().numpy(), y) < tol, s
         # the carried state is a copy: bit-exact
         assert np.array_equal(res["state_out"][s, 0].float().cpu().numpy(), so.astype(np.float32)), s
+
+
+# ----------------------------------------------------------------------------------------
+# RoPE state re-rotation of cached elements moved to a new offset
+
+
+@pytest.mark.parametrize("d,rd,interleaved,kind,n_elem,inplace", [
+    (128, 128, False, "dense", 5, False),
+    (128, 96, True, "dense", 4, True),
+    (64, 32, False, "scalar", 6, False),
+    (64, 64, True, "dense", 170, False),      # more shifts than one launch carries
+])
+def test_rerotate_elements(gpu, d, rd, interleaved, kind, n_elem, inplace):
+    rng = np.random.default_rng(500 + d + rd + n_elem)
+    n_chain = 3 if n_elem < 100 else 2
+    T = rng.standard_normal((n_elem, n_chain, d, d)).astype(np.float32)
+    S = rng.standard_normal((n_elem, n_chain, d, d)).astype(np.float32)
+    delta = rng.integers(-200_000, 200_000, size=n_elem).astype(np.int64)
+    delta[0] = 0
+    Td, Sd = dev_tensor(T), dev_tensor(S)
+    r = H.hypic_state_rerotate(Td if kind == "dense" else None, Sd, delta, kind=kind, rotary_dim=rd,
+                               rope_base=10000.0, interleaved=interleaved, inplace=inplace)
+    torch.cuda.synchronize()
+    if inplace:
+        assert r["S"].data_ptr() == Sd.data_ptr()
+    Sg = r["S"].cpu().numpy()
+    Tg = r["T_hat"].cpu().numpy() if kind == "dense" else None
+    worst = 0.0
+    for e in range(n_elem):
+        for c in range(n_chain):
+            ref = O.rerotate(kind, T[e, c] if kind == "dense" else np.float64(1.0), 0, S[e, c], int(delta[e]), rd,
+                             10000.0, interleaved)
+            err = float(O.rel_err(Sg[e, c], ref["S"]))
+            if kind == "dense":
+                err = max(err, float(O.rel_err(Tg[e, c], ref["T_hat"])))
+            worst = max(worst, err)
+    print(f"rerotate d={d} rd={rd} interleaved={interleaved} {kind} x{n_elem}: max err {worst:.2e}")
+    assert worst < TOL_F32
+    assert np.array_equal(Sg[0], S[0])          # a zero shift is the identity, bit for bit
+
+
+def test_rerotate_end_to_end_at_new_offset(gpu):
+    """Cache two segments with keys rotated at their original offsets (fp32, d = 64, the F32
+    plan), re-rotate both to the offsets of a different request and compose them: the state
+    equals the recurrence over the keys rotated at the new positions."""
+    wl = WORKLOADS["tiny_gdn_f32"]
+    c = chain_inputs(wl, 0, 0, 512)
+    rd, base = 48, 5000.0
+    lens = [300, 212]
+    p_old = [7000, 123]            # where each segment was first prefilled
+    p_new = [40, 340]              # where the request places them (contiguous from 40)
+    ks, vs, las, bts = [], [], [], []
+    s0 = 0
+    for n, p in zip(lens, p_old):
+        ks.append(O.rope_rotate(c["k"][s0:s0 + n], p + np.arange(n), rd, base, False).astype(np.float32))
+        vs.append(c["v"][s0:s0 + n]); las.append(c["log_alpha"][s0:s0 + n]); bts.append(c["beta"][s0:s0 + n])
+        s0 += n
+    k = dev_tensor(np.concatenate(ks)[None, :, None])
+    v = dev_tensor(np.concatenate(vs)[None, :, None])
+    la = dev_tensor(np.concatenate(las)[None, :, None])
+    bt = dev_tensor(np.concatenate(bts)[None, :, None])
+    b = H.hypic_segment_build(k, v, la, cu_of(lens), bt)
+    delta = np.array([pn - po for pn, po in zip(p_new, p_old)], np.int64)
+    r = H.hypic_state_rerotate(b["T_hat"].reshape(2, 1, 64, 64), b["S"].reshape(2, 1, 64, 64), delta,
+                               rotary_dim=rd, rope_base=base)
+    comp = H.hypic_compose(r["T_hat"], b["T_exp"].reshape(2, 1), r["S"], mode="fold", want_T=True)
+    torch.cuda.synchronize()
+    k_new = np.concatenate([O.rope_rotate(c["k"][a:a + n], p + np.arange(n), rd, base, False)
+                            for a, n, p in ((0, lens[0], p_new[0]), (lens[0], lens[1], p_new[1]))])
+    full = O.dense_recurrence(k_new, c["v"][:512], c["log_alpha"][:512], c["beta"][:512])
+    eS = float(O.rel_err(comp["S_final"][0].cpu().numpy(), full["S"]))
+    eT = float(O.rel_err_T("dense", comp["T_total"][0].cpu().numpy(), int(comp["T_total_exp"][0]),
+                           full["T_hat"], full["T_exp"]))
+    # without the re-rotation the composed state is wrong at the new offsets
+    stale = H.hypic_compose(b["T_hat"].reshape(2, 1, 64, 64), b["T_exp"].reshape(2, 1), b["S"].reshape(2, 1, 64, 64),
+                            mode="fold")
+    e_stale = float(O.rel_err(stale["S_final"][0].cpu().numpy(), full["S"]))
+    print(f"rerotated compose at the new offsets: S {eS:.2e}, T {eT:.2e} (without re-rotation {e_stale:.2e})")
+    assert eS < TOL_F32 and eT < TOL_F32
+    assert e_stale > 100 * TOL_F32
