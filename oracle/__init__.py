@@ -12,7 +12,8 @@ the HYPIC pages and the published gated delta rule:
 * per-token transition A_t = alpha_t (I - beta_t k_t k_t^T) and write
   beta_t k_t v_t^T (gated delta rule, Yang, Kautz & Hatamizadeh, ICLR 2025);
   the diagonal (GLA) and scalar (RetNet/Mamba2) decay families named in the
-  HYPIC news article's linear-layer paragraph;
+  HYPIC news article's linear-layer paragraph, and the per-channel gated delta
+  rule A_t = diag(alpha_t)(I - beta_t k_t k_t^T) of the KDA family it also names;
 * the segment transition T_C (ordered product of the A_t) and zero-start end
   state S(C|0), composed by S(C1.C2) = T(C2) S(C1) + S(C2) (same paragraph);
 * naive addition S(C1) + S(C2), the straw-man the same paragraph rejects;
@@ -34,6 +35,7 @@ from .reference import (  # noqa: F401
     compose_T,
     dense_recurrence,
     diag_recurrence,
+    kda_recurrence,
     l2_normalise,
     lpt_schedule,
     naive_add,

@@ -110,6 +110,40 @@ def dense_recurrence(k, v, log_alpha, beta, S0=None, q=None, renorm_every=64):
     return {"T_hat": T, "T_exp": e, "S": S, "o": o}
 
 
+def kda_recurrence(k, v, log_alpha, beta, S0=None, q=None, renorm_every=64):
+    """Per-channel gated delta rule (KDA-style): A_t = diag(alpha_t) (I - beta_t k_t k_t^T),
+    S_t = A_t S_{t-1} + beta_t k_t v_t^T, the write not decayed at its own step.
+
+    k [..., n, d_k], v [..., n, d_v], log_alpha [..., n, d_k] (per channel), beta [..., n].
+    T is a dense d_k x d_k matrix, carried as (T_hat, T_exp) like the gated delta rule's,
+    so cached KDA segments compose with the dense composition law.  With q, o_t = S_t^T q_t.
+    """
+    k, v, la, b = _f64(k), _f64(v), _f64(log_alpha), _f64(beta)
+    batch = k.shape[:-2]
+    n, dk = k.shape[-2:]
+    dv = v.shape[-1]
+    S = np.zeros(batch + (dk, dv)) if S0 is None else np.array(_f64(S0), copy=True)
+    T = np.array(np.broadcast_to(np.eye(dk), batch + (dk, dk)), copy=True)
+    e = np.zeros(batch, np.int64)
+    o = np.zeros(batch + (n, dv)) if q is not None else None
+    qf = _f64(q) if q is not None else None
+    for t in range(n):
+        a = np.exp(la[..., t, :])[..., :, None]          # per-channel decay, rows
+        bt = b[..., t][..., None, None]
+        kt = k[..., t, :]
+        kcol = kt[..., :, None]
+        kS = kt[..., None, :] @ S
+        S = a * (S - bt * (kcol @ kS)) + bt * (kcol @ v[..., t, None, :])
+        kT = kt[..., None, :] @ T
+        T = a * (T - bt * (kcol @ kT))
+        if qf is not None:
+            o[..., t, :] = (qf[..., t, None, :] @ S)[..., 0, :]
+        if (t + 1) % renorm_every == 0:
+            T, e = _renorm(T, e, 2)
+    T, e = _renorm(T, e, 2)
+    return {"T_hat": T, "T_exp": e, "S": S, "o": o}
+
+
 def diag_recurrence(k, v, log_alpha, S0=None, q=None, renorm_every=64):
     """GLA per-channel decay: S_t = diag(alpha_t) S_{t-1} + k_t v_t^T.
 

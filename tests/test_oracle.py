@@ -556,3 +556,71 @@ def test_rope_outputs_are_relative():
 def test_rerotation_rejects_per_channel_gates():
     with pytest.raises(ValueError):
         O.rerotate("diag", np.ones(4), 0, np.zeros((4, 4)), 3, 4, 10.0, False)
+
+
+# ----------------------------------------------------------------------------------------
+# per-channel gated delta rule (KDA, named in the HYPIC news article's linear-layer paragraph):
+# A_t = diag(alpha_t) (I - beta_t k_t k_t^T)
+
+
+def _kda_brute(k, v, la, b, S0):
+    n, dk = k.shape
+    As = [np.diag(np.exp(la[t])) @ (np.eye(dk) - b[t] * np.outer(k[t], k[t])) for t in range(n)]
+    T = np.eye(dk)
+    for A in As:
+        T = A @ T
+    S = T @ S0
+    for t in range(n):
+        P = np.eye(dk)
+        for A in As[t + 1:]:
+            P = A @ P
+        S = S + P @ (b[t] * np.outer(k[t], v[t]))
+    return T, S
+
+
+@pytest.mark.parametrize("dk,dv,n", [(1, 1, 3), (3, 2, 5), (4, 4, 6)])
+def test_kda_brute_force(dk, dv, n):
+    rng = np.random.default_rng(60 + dk + n)
+    k, v, _, b, q = _rand_chain(rng, n, dk, dv)
+    la = -0.4 * rng.random((n, dk))
+    S0 = rng.standard_normal((dk, dv))
+    r = O.kda_recurrence(k, v, la, b, S0=S0, q=q, renorm_every=2)
+    T, S = _kda_brute(k, v, la, b, S0)
+    assert np.allclose(O.T_value("dense", r["T_hat"], r["T_exp"]), T, rtol=0, atol=1e-14)
+    assert np.allclose(r["S"], S, rtol=0, atol=1e-13)
+    for t in range(n):
+        _, St = _kda_brute(k[:t + 1], v[:t + 1], la[:t + 1], b[:t + 1], S0)
+        assert np.allclose(r["o"][t], St.T @ q[t], rtol=0, atol=1e-13)
+
+
+def test_kda_reductions():
+    rng = np.random.default_rng(62)
+    n, d = 90, 6
+    k, v, la, b, q = _rand_chain(rng, n, d, 4, unit=True)
+    # channel-uniform gates: the gated delta rule
+    ku = O.kda_recurrence(k, v, np.repeat(la[:, None], d, 1), b, q=q)
+    g = O.dense_recurrence(k, v, la, b, q=q)
+    assert np.max(O.rel_err(ku["S"], g["S"])) < 1e-13
+    assert np.max(O.rel_err_T("dense", ku["T_hat"], ku["T_exp"], g["T_hat"], g["T_exp"])) < 1e-13
+    assert np.max(np.abs(ku["o"] - g["o"])) < 1e-12
+    # no writes (beta = 0): pure per-channel decay, T = diag(e^{sum log alpha}), S = T S0
+    lad = -0.2 * rng.random((n, d))
+    S0 = rng.standard_normal((d, 4))
+    z = O.kda_recurrence(k, v, lad, np.zeros(n), S0=S0)
+    Tz = O.T_value("dense", z["T_hat"], z["T_exp"])
+    assert np.allclose(Tz, np.diag(np.exp(lad.sum(0))), rtol=1e-12, atol=0)
+    assert np.max(O.rel_err(z["S"], np.exp(lad.sum(0))[:, None] * S0)) < 1e-13
+
+
+def test_kda_segments_compose_with_the_dense_law():
+    rng = np.random.default_rng(63)
+    n, d = 300, 8
+    k, v, _, b, _ = _rand_chain(rng, n, d, 5, unit=True)
+    la = -0.05 - 0.2 * rng.random((n, d))
+    S0 = rng.standard_normal((d, 5))
+    full = O.kda_recurrence(k, v, la, b, S0=S0)
+    cuts = [0, 41, 42, 170, 300]
+    els = [_as_el(O.kda_recurrence(k[a:c], v[a:c], la[a:c], b[a:c], renorm_every=5)) for a, c in zip(cuts[:-1], cuts[1:])]
+    f = O.compose_fold("dense", els, S0=S0)
+    assert np.max(O.rel_err(f["S_final"], full["S"])) < 1e-12
+    assert np.max(O.rel_err_T("dense", f["T_hat"], f["T_exp"], full["T_hat"], full["T_exp"])) < 1e-12
