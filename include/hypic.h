@@ -82,7 +82,10 @@ typedef enum { HYPIC_F32 = 0, HYPIC_BF16 = 1 } hypic_dtype;
 typedef enum {
     HYPIC_DENSE_DELTA = 0, /* A_t = alpha_t (I - beta_t k_t k_t^T)  (GDN, DeltaNet) */
     HYPIC_DIAG = 1,        /* A_t = diag(alpha_t)                   (GLA)          */
-    HYPIC_SCALAR = 2       /* A_t = alpha_t I                       (RetNet, Mamba2) */
+    HYPIC_SCALAR = 2,      /* A_t = alpha_t I                       (RetNet, Mamba2) */
+    HYPIC_KDA = 3          /* A_t = diag(alpha_t) (I - beta_t k_t k_t^T), alpha_t per
+                              channel (KDA); T is a dense d_k x d_k matrix, so KDA
+                              elements compose exactly like HYPIC_DENSE_DELTA ones     */
 } hypic_kind;
 
 /* Order in which (segment, chain) build tasks are handed to the compute units.
@@ -137,7 +140,9 @@ typedef enum { HYPIC_ACT_NONE = 0, HYPIC_ACT_SILU = 1 } hypic_activation;
  * cached.  T_C is the ordered product of the segment's per-token transitions;
  * S(C|0) is the state after the segment from S = 0.  The dense kind uses the
  * chunked WY/UT form of the gated delta rule with T carried as extra state
- * columns; the diagonal and scalar kinds use their closed forms.
+ * columns; the diagonal and scalar kinds use their closed forms; KDA runs its
+ * token recurrence in float32 vector arithmetic, one thread per column of [T | S]
+ * (whatever precision is asked for; no qk_l2norm, no outputs, no RR schedule).
  *
  * Segment s covers tokens [cu_seqlens[s] + skip_head, cu_seqlens[s+1]) of the
  * packed token axis (skip_head >= 0 leaves the seam window out of the cache
@@ -146,10 +151,10 @@ typedef enum { HYPIC_ACT_NONE = 0, HYPIC_ACT_SILU = 1 } hypic_activation;
  * Layouts (B = n_batch, typically layers; N = n_tokens):
  *   k           [B, N, h_k, d_k]   in_dtype
  *   v           [B, N, h_v, d_v]   in_dtype
- *   log_alpha   float32, <= 0: DENSE/SCALAR [B, N, h_v]; DIAG [B, N, h_v, d_k]
- *   beta        float32 [B, N, h_v] (DENSE only; must be NULL otherwise)
+ *   log_alpha   float32, <= 0: DENSE/SCALAR [B, N, h_v]; DIAG/KDA [B, N, h_v, d_k]
+ *   beta        float32 [B, N, h_v] (DENSE and KDA; must be NULL otherwise)
  *   T_hat       float32 (NULL = skip T, plain state pass):
- *                 DENSE [n_seg, B, h_v, d_k, d_k]; DIAG [n_seg, B, h_v, d_k];
+ *                 DENSE/KDA [n_seg, B, h_v, d_k, d_k]; DIAG [n_seg, B, h_v, d_k];
  *                 SCALAR [n_seg, B, h_v]
  *   T_exp       int32 [n_seg, B, h_v] (required iff T_hat)
  *   S           float32 [n_seg, B, h_v, d_k, d_v]
@@ -209,7 +214,7 @@ size_t hypic_segment_build_workspace_bytes(const hypic_build_desc* desc);
  * Layouts (C = n_chain):
  *   slot        device int32 [n_elem], values in [0, n_slot); NULL = identity
  *               (then n_slot >= n_elem)
- *   T_hat       float32 element store: DENSE [n_slot, C, d_k, d_k];
+ *   T_hat       float32 element store: DENSE/KDA [n_slot, C, d_k, d_k];
  *               DIAG [n_slot, C, d_k]; SCALAR [n_slot, C]  (unused by NAIVE_ADD)
  *   T_exp       int32 [n_slot, C]
  *   S           float32 [n_slot, C, d_k, d_v]
@@ -376,7 +381,7 @@ size_t hypic_conv_warmup_workspace_bytes(const hypic_conv_desc* desc);
  * x_a sin + x_b cos) of the angle delta * theta_i; channels >= rotary_dim unchanged.
  * Its per-token transitions become R A_t R^T and its writes R k v^T, so
  *   S' = R S,   T' = R T R^T (DENSE; T_exp unchanged),   T' = T (SCALAR).
- * Per-channel (DIAG) gates do not commute with R: HYPIC_ERR_UNSUPPORTED.
+ * Per-channel (DIAG, KDA) gates do not commute with R: HYPIC_ERR_UNSUPPORTED.
  * Layouts (C = n_chain), float32, out may alias in (in-place update):
  *   S_in, S_out          [n_elem, C, d_k, d_v]
  *   T_hat_in, T_hat_out  [n_elem, C, d_k, d_k] (DENSE; NULL for SCALAR)

@@ -14,12 +14,12 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhypic.so
 # enums (values fixed by include/hypic.h)
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_DEVICE = range(5)
 F32, BF16 = 0, 1
-DENSE, DIAG, SCALAR = 0, 1, 2
+DENSE, DIAG, SCALAR, KDA = 0, 1, 2, 3
 SCHED = {"natural": 0, "lpt": 1, "rr": 2}
 PREC = {"auto": 0, "f32": 1, "f16": 2, "f16_precise_t": 3}
 COMPOSE = {"auto": 0, "fold": 1, "scan": 2, "naive_add": 3}
 ACT = {"none": 0, "silu": 1}
-KIND = {"dense": DENSE, "diag": DIAG, "scalar": SCALAR}
+KIND = {"dense": DENSE, "diag": DIAG, "scalar": SCALAR, "kda": KDA}
 INLINE_SEGS = 160          # segment tables up to this size need no workspace
 SEAM_SINK_DEFAULT = 8.0
 NOALLOC_SCRATCH_BYTES = 32 << 20   # fixed per-device scratch of hypic_compose_noalloc

@@ -123,14 +123,15 @@ def hypic_segment_build(k, v, log_alpha, cu_seqlens, beta=None, *, kind="dense",
     v = _as4(v, "v")
     h_v = v.shape[2]
     v = _check(v, "v", dtype=k.dtype, shape=(B, N, h_v, v.shape[3]))
-    la_numel = B * N * h_v * (d if kd == A.DIAG else 1)
+    per_channel = kd in (A.DIAG, A.KDA)
+    la_numel = B * N * h_v * (d if per_channel else 1)
     _check(log_alpha, "log_alpha", dtype=torch.float32, numel=la_numel)
-    if kd == A.DIAG and log_alpha.shape[-1] != d:
-        raise ValueError(f"diag log_alpha must have last dimension d = {d}, got shape {tuple(log_alpha.shape)}")
-    if kd == A.DENSE:
+    if per_channel and log_alpha.shape[-1] != d:
+        raise ValueError(f"{kind} log_alpha must have last dimension d = {d}, got shape {tuple(log_alpha.shape)}")
+    if kd in (A.DENSE, A.KDA):
         _check(beta, "beta", dtype=torch.float32, numel=B * N * h_v)
     elif beta is not None:
-        raise ValueError("beta is used by the dense kind only")
+        raise ValueError("beta is used by the dense and KDA kinds only")
     if want_o:
         if kd != A.DENSE:
             raise ValueError("per-token outputs are implemented for the dense kind only")
@@ -143,7 +144,7 @@ def hypic_segment_build(k, v, log_alpha, cu_seqlens, beta=None, *, kind="dense",
     dev = _gpu_device(k, "k")
     _check(v, "v", device=dev)
     _check(q, "q", device=dev, optional=True)
-    la = _check(log_alpha.reshape(B, N, h_v, d) if kd == A.DIAG else log_alpha.reshape(B, N, h_v), "log_alpha",
+    la = _check(log_alpha.reshape(B, N, h_v, d) if per_channel else log_alpha.reshape(B, N, h_v), "log_alpha",
                 device=dev)
     bt = _check(beta.reshape(B, N, h_v), "beta", device=dev) if beta is not None else None
     cu = _host_offsets(cu_seqlens)
@@ -151,7 +152,8 @@ def hypic_segment_build(k, v, log_alpha, cu_seqlens, beta=None, *, kind="dense",
     S = _out(out, "S", (n_seg, B, h_v, d, d), torch.float32, dev)
     T_hat = T_exp = None
     if with_T:
-        tshape = {A.DENSE: (n_seg, B, h_v, d, d), A.DIAG: (n_seg, B, h_v, d), A.SCALAR: (n_seg, B, h_v)}[kd]
+        tshape = {A.DENSE: (n_seg, B, h_v, d, d), A.KDA: (n_seg, B, h_v, d, d), A.DIAG: (n_seg, B, h_v, d),
+                  A.SCALAR: (n_seg, B, h_v)}[kd]
         T_hat = _out(out, "T_hat", tshape, torch.float32, dev)
         T_exp = _out(out, "T_exp", (n_seg, B, h_v), torch.int32, dev)
     o = _out(out, "o", (B, N, h_v, d), out_dtype, dev) if want_o else None
@@ -197,7 +199,8 @@ def hypic_compose(T_hat, T_exp, S, *, kind="dense", slot=None, S0=None, mode="au
     n_slot, n_chain, d = S.shape[0], S.shape[1], S.shape[2]
     _check(S, "S", dtype=torch.float32, shape=(n_slot, n_chain, d, d))
     naive = mode == "naive_add"
-    tshape = {A.DENSE: (n_slot, n_chain, d, d), A.DIAG: (n_slot, n_chain, d), A.SCALAR: (n_slot, n_chain)}[kd]
+    tshape = {A.DENSE: (n_slot, n_chain, d, d), A.KDA: (n_slot, n_chain, d, d), A.DIAG: (n_slot, n_chain, d),
+              A.SCALAR: (n_slot, n_chain)}[kd]
     _check(T_hat, "T_hat", dtype=torch.float32, shape=tshape, optional=naive)
     _check(T_exp, "T_exp", dtype=torch.int32, shape=(n_slot, n_chain), optional=naive)
     _check(S0, "S0", dtype=torch.float32, shape=(n_chain, d, d), optional=True)
@@ -216,7 +219,7 @@ def hypic_compose(T_hat, T_exp, S, *, kind="dense", slot=None, S0=None, mode="au
     S_prefix = torch.empty((n_elem, n_chain, d, d), dtype=torch.float32, device=dev) if want_prefix else None
     T_total = T_total_exp = None
     if want_T:
-        tout = {A.DENSE: (n_chain, d, d), A.DIAG: (n_chain, d), A.SCALAR: (n_chain,)}[kd]
+        tout = {A.DENSE: (n_chain, d, d), A.KDA: (n_chain, d, d), A.DIAG: (n_chain, d), A.SCALAR: (n_chain,)}[kd]
         T_total = torch.empty(tout, dtype=torch.float32, device=dev)
         T_total_exp = torch.empty((n_chain,), dtype=torch.int32, device=dev)
     desc = A.ComposeDesc(kind=kd, n_chain=n_chain, d_k=d, d_v=S.shape[3], n_elem=n_elem, n_slot=n_slot,

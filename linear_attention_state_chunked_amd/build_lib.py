@@ -19,7 +19,7 @@ OUT = os.path.join(PKG, "libhypic.so")
 BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["gdn_build.hip", "dense_engine.hip", "diag_build.hip", "compose.hip", "conv.hip", "seam.hip", "rope.hip",
+SOURCES = ["gdn_build.hip", "dense_engine.hip", "diag_build.hip", "compose.hip", "conv.hip", "seam.hip", "rope.hip", "kda_build.hip",
            "hypic_host.cpp"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

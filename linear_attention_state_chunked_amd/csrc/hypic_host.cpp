@@ -122,11 +122,14 @@ hypic_status check_workspace(const char* who, size_t need, void* ws, size_t have
 
 bool supported_d(int d) { return d == 64 || d == 128; }
 
+// kinds whose transition is a dense d_k x d_k matrix (composed alike)
+bool dense_T(hypic_kind k) { return k == HYPIC_DENSE_DELTA || k == HYPIC_KDA; }
+
 int64_t build_tasks(const hypic_build_desc* d) { return (int64_t)d->n_seg * d->n_batch * d->h_v; }
 
 hypic_status validate_build(const hypic_build_desc* d) {
     if (!d) return fail(HYPIC_ERR_INVALID_ARGUMENT, "build: desc is NULL");
-    if (d->kind < HYPIC_DENSE_DELTA || d->kind > HYPIC_SCALAR)
+    if (d->kind < HYPIC_DENSE_DELTA || d->kind > HYPIC_KDA)
         return fail(HYPIC_ERR_INVALID_ARGUMENT, "build: unknown kind %d", (int)d->kind);
     if (d->in_dtype != HYPIC_F32 && d->in_dtype != HYPIC_BF16)
         return fail(HYPIC_ERR_INVALID_ARGUMENT, "build: unknown in_dtype %d", (int)d->in_dtype);
@@ -143,6 +146,7 @@ hypic_status validate_build(const hypic_build_desc* d) {
         return fail(HYPIC_ERR_INVALID_ARGUMENT, "build: qk_l2norm=%d must be 0 or 1", d->qk_l2norm);
     if (d->qk_l2norm && d->kind != HYPIC_DENSE_DELTA)
         return fail(HYPIC_ERR_UNSUPPORTED, "build: qk_l2norm is supported for the dense kind only");
+    const bool has_beta = d->kind == HYPIC_DENSE_DELTA || d->kind == HYPIC_KDA;
     hypic_status st = check_offsets(d->cu_seqlens, d->n_seg, d->n_tokens, "build: cu_seqlens");
     if (st != HYPIC_OK) return st;
     for (int32_t i = 0; i < d->n_seg; ++i)
@@ -155,9 +159,9 @@ hypic_status validate_build(const hypic_build_desc* d) {
         if (!aligned16(d->k) || !aligned16(d->v))
             return fail(HYPIC_ERR_INVALID_ARGUMENT, "build: k and v must be 16-byte aligned");
     }
-    if (d->kind == HYPIC_DENSE_DELTA) {
+    if (has_beta) {
         if (d->n_seg > 0 && d->n_tokens > 0 && !d->beta)
-            return fail(HYPIC_ERR_INVALID_ARGUMENT, "build: beta is required for the dense kind");
+            return fail(HYPIC_ERR_INVALID_ARGUMENT, "build: beta is required for the dense and KDA kinds");
     } else if (d->beta) {
         return fail(HYPIC_ERR_INVALID_ARGUMENT, "build: beta must be NULL for the diagonal and scalar kinds");
     }
@@ -165,6 +169,7 @@ hypic_status validate_build(const hypic_build_desc* d) {
     if (d->o) {
         if (d->kind != HYPIC_DENSE_DELTA)
             return fail(HYPIC_ERR_UNSUPPORTED, "build: per-token outputs are implemented for the dense kind only");
+
         if (!d->q) return fail(HYPIC_ERR_INVALID_ARGUMENT, "build: o requested without q");
         if (!aligned16(d->q)) return fail(HYPIC_ERR_INVALID_ARGUMENT, "build: q must be 16-byte aligned");
         if (d->out_dtype != HYPIC_F32 && d->out_dtype != HYPIC_BF16)
@@ -418,6 +423,26 @@ hypic_status hypic_segment_build(const hypic_build_desc* d, hypic_stream_t strea
         }
         e = hypic::launch_gdn_build(a, d->d_k, build_prec_f32(d) ? 1 : 0, grid, s);
         if (e != hipSuccess) return device_fail("build: dense build launch", e);
+    } else if (d->kind == HYPIC_KDA) {
+        if (d->schedule == HYPIC_SCHED_RR)
+            return fail(HYPIC_ERR_UNSUPPORTED, "build: RR schedule is implemented for the dense kind only");
+        hypic::KdaArgs a{};
+        a.n_batch = d->n_batch;
+        a.n_tokens = d->n_tokens;
+        a.h_k = d->h_k;
+        a.h_v = d->h_v;
+        a.in_bf16 = d->in_dtype == HYPIC_BF16;
+        a.n_tasks = (int)n_tasks;
+        a.k = d->k;
+        a.v = d->v;
+        a.log_alpha = d->log_alpha;
+        a.beta = d->beta;
+        a.T_hat = d->T_hat;
+        a.T_exp = d->T_exp;
+        a.S = d->S;
+        a.seg = tab;
+        e = hypic::launch_kda_build(a, d->d_k, s);
+        if (e != hipSuccess) return device_fail("build: KDA build launch", e);
     } else {
         hypic::DiagArgs a{};
         a.n_batch = d->n_batch;
@@ -474,7 +499,7 @@ int64_t dense_scan_cost(const hypic_compose_desc* d, int64_t b, int cus) {
 int scan_block_size(const hypic_compose_desc* d, int cus) {
     if (d->scan_block > 0) return d->scan_block;
     const int64_t n = d->n_elem;
-    if (d->kind != HYPIC_DENSE_DELTA) {
+    if (!dense_T(d->kind)) {
         int b = 1;
         while ((int64_t)b * b < n) ++b;  // ~sqrt(n): balances the two sequential phases
         return std::max(b, 2);
@@ -493,7 +518,7 @@ int scan_block_size(const hypic_compose_desc* d, int cus) {
 
 hypic_compose_mode resolve_mode(const hypic_compose_desc* d, int cus) {
     if (d->mode != HYPIC_COMPOSE_AUTO) return d->mode;
-    if (d->kind == HYPIC_DENSE_DELTA)
+    if (dense_T(d->kind))
         return (d->n_elem >= 4 && dense_scan_cost(d, scan_block_size(d, cus), cus) < dense_fold_cost(d, cus))
                    ? HYPIC_COMPOSE_SCAN
                    : HYPIC_COMPOSE_FOLD;
@@ -507,7 +532,7 @@ struct ScanLayout {
 
 ScanLayout scan_layout(const hypic_compose_desc* d, int nblk) {
     const int64_t C = d->n_chain, D = d->d_k;
-    const int64_t tlen = d->kind == HYPIC_DENSE_DELTA ? D * D : (d->kind == HYPIC_DIAG ? D : 1);
+    const int64_t tlen = dense_T(d->kind) ? D * D : (d->kind == HYPIC_DIAG ? D : 1);
     ScanLayout L;
     L.aggT = 0;
     L.aggE = L.aggT + align_up(sizeof(float) * nblk * C * tlen);
@@ -519,7 +544,7 @@ ScanLayout scan_layout(const hypic_compose_desc* d, int nblk) {
 
 hypic_status validate_compose(const hypic_compose_desc* d) {
     if (!d) return fail(HYPIC_ERR_INVALID_ARGUMENT, "compose: desc is NULL");
-    if (d->kind < HYPIC_DENSE_DELTA || d->kind > HYPIC_SCALAR)
+    if (d->kind < HYPIC_DENSE_DELTA || d->kind > HYPIC_KDA)
         return fail(HYPIC_ERR_INVALID_ARGUMENT, "compose: unknown kind %d", (int)d->kind);
     if (d->mode < HYPIC_COMPOSE_AUTO || d->mode > HYPIC_COMPOSE_NAIVE_ADD)
         return fail(HYPIC_ERR_INVALID_ARGUMENT, "compose: unknown mode %d", (int)d->mode);
@@ -569,7 +594,7 @@ hypic_status compose_impl(const hypic_compose_desc* d, hypic_stream_t stream, vo
     if (st != HYPIC_OK) return st;
     const int cus = planner_cus();
     const hypic_compose_mode m = resolve_mode(d, cus);
-    const int kind = d->kind == HYPIC_DENSE_DELTA ? 0 : (d->kind == HYPIC_DIAG ? 1 : 2);
+    const int kind = dense_T(d->kind) ? 0 : (d->kind == HYPIC_DIAG ? 1 : 2);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const int D = d->d_k;
     const bool wantT = d->T_total != nullptr;
@@ -839,7 +864,7 @@ hypic_status hypic_seam_advance(const hypic_seam_desc* d, hypic_stream_t stream)
 
 hypic_status hypic_state_rerotate(const hypic_rerotate_desc* d, hypic_stream_t stream) {
     if (!d) return fail(HYPIC_ERR_INVALID_ARGUMENT, "rerotate: desc is NULL");
-    if (d->kind == HYPIC_DIAG)
+    if (d->kind == HYPIC_DIAG || d->kind == HYPIC_KDA)
         return fail(HYPIC_ERR_UNSUPPORTED,
                     "rerotate: per-channel gates do not commute with the RoPE rotation (only the dense and "
                     "scalar kinds re-rotate exactly)");

@@ -96,6 +96,25 @@ struct DiagArgs {
     SegTable seg;
 };
 
+// Per-channel gated delta rule (KDA) build: one workgroup per (segment, batch, value head),
+// one thread per column of X = [T | S] (T columns only when T_hat is set).
+struct KdaArgs {
+    int n_batch;
+    long long n_tokens;
+    int h_k, h_v;
+    int in_bf16;
+    int n_tasks;
+    const void* k;
+    const void* v;
+    const float* log_alpha;   // [B, N, h_v, d]
+    const float* beta;        // [B, N, h_v]
+    float* T_hat;
+    int* T_exp;
+    float* S;
+    SegTable seg;
+};
+hipError_t launch_kda_build(const KdaArgs& a, int d, hipStream_t s);
+
 // One fold launch: grid (chain, block).  Block `blk` folds elements
 // [blk*per_block, min(n_elem, (blk+1)*per_block)) in order, from the state
 // init_S[blk] (or zero) and transition I.

@@ -12,7 +12,8 @@ Distributions (the same for the device and the CPU reference):
   * gated-delta decay log(alpha) = -scale * softplus(N(0,1)), scale 0.05 (0.005 for
     the slow-decay workloads, 0 for the DeltaNet ones, alpha = 1), float32;
   * RetNet-style scalar decay gamma_h = 1 - 2**-(5 + 4h/15) for scalar head h;
-  * GLA per-channel gates alpha = sigmoid(N(2,1)) ** (1/16), stored as log(alpha);
+  * GLA per-channel gates alpha = sigmoid(N(2,1)) ** (1/16), stored as log(alpha)
+    (also the per-channel gates of the KDA workload, with beta as above);
   * pre-convolution activations N(0,1), depthwise conv taps N(0,1)/2.
 bf16 workloads round k, v, q (and the pre-conv activations) to bfloat16 with
 round-to-nearest-even; the rounded values are returned as float32 arrays that
@@ -120,6 +121,8 @@ WORKLOADS = {
                                 alpha_scale=0.0, fixed_lens=(1024,) * 16),
     "delta4x4k_bf16": Workload("delta4x4k_bf16", 8, 1, 16, 32, 128, "bf16", "dense",
                                alpha_scale=0.0, fixed_lens=(4096,) * 4),
+    # per-channel gated delta rule (KDA): 32 v-heads on 16 k-heads, 16 x 512 tokens
+    "kda_bf16": Workload("kda_bf16", 9, 1, 16, 32, 128, "bf16", "kda", fixed_lens=(512,) * 16),
 }
 
 
@@ -182,6 +185,12 @@ def _value_side(wl: Workload, layer: int, vhead: int, n: int) -> dict:
     elif wl.kind == "diag":
         x = 2.0 + stream(wl.seed, layer, vhead, "gla").standard_normal((n, wl.d))
         out["log_alpha"] = (-_softplus(-x) / 16.0).astype(np.float32)
+    elif wl.kind == "kda":
+        # per-channel gates as the GLA heads', write strength as the gated delta rule's
+        b = stream(wl.seed, layer, vhead, "beta").standard_normal(n)
+        out["beta"] = (1.0 / (1.0 + np.exp(-b))).astype(np.float32)
+        x = 2.0 + stream(wl.seed, layer, vhead, "gla").standard_normal((n, wl.d))
+        out["log_alpha"] = (-_softplus(-x) / 16.0).astype(np.float32)
     else:
         raise ValueError(wl.kind)
     return out
@@ -214,7 +223,7 @@ def layer_inputs(wl: Workload, layer: int, heads: range | None = None, with_q: b
     k = np.empty((n, wl.h_k, wl.d), np.float32)
     q = np.empty((n, wl.h_k, wl.d), np.float32) if with_q else None
     v = np.empty((n, wl.h_v, wl.d), np.float32)
-    la_shape = (n, wl.h_v, wl.d) if wl.kind == "diag" else (n, wl.h_v)
+    la_shape = (n, wl.h_v, wl.d) if wl.kind in ("diag", "kda") else (n, wl.h_v)
     la = np.zeros(la_shape, np.float32)
     beta = np.zeros((n, wl.h_v), np.float32)
 

@@ -569,3 +569,66 @@ def test_rerotate_end_to_end_at_new_offset(gpu):
     print(f"rerotated compose at the new offsets: S {eS:.2e}, T {eT:.2e} (without re-rotation {e_stale:.2e})")
     assert eS < TOL_F32 and eT < TOL_F32
     assert e_stale > 100 * TOL_F32
+
+
+# ----------------------------------------------------------------------------------------
+# per-channel gated delta rule (KDA): build, and composition through the dense law
+
+
+def _kda_segments(c, lens):
+    out, s0 = [], 0
+    for n in lens:
+        out.append(O.kda_recurrence(c["k"][s0:s0 + n], c["v"][s0:s0 + n], c["log_alpha"][s0:s0 + n],
+                                    c["beta"][s0:s0 + n]))
+        s0 += n
+    return out
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_kda_build_ragged_and_compose(gpu, dtype):
+    wl = WORKLOADS["kda_bf16"]
+    lens = [0, 1, 63, 64, 65, 200, 130, 300] if dtype == "bf16" else [1, 17, 129, 0, 90]
+    n, h_v = sum(lens), 4 if dtype == "bf16" else 2
+    dt, tol = (torch.bfloat16, TOL_BF16) if dtype == "bf16" else (torch.float32, TOL_F32)
+    chains = [chain_inputs(wl, 0, h, n) for h in range(h_v)]
+    h_k = h_v // 2
+    kk = np.stack([chains[2 * kh]["k"] for kh in range(h_k)], axis=1)
+    for h, c in enumerate(chains):
+        c["k"] = kk[:, h // 2]
+        if dtype == "f32":      # full-precision values (the workload's are bf16-exact)
+            c["v"] = c["v"] + np.float32(1e-3) * np.sin(np.arange(c["v"].size, dtype=np.float32)).reshape(c["v"].shape)
+    k = dev_tensor(kk[None], dt)
+    v = dev_tensor(np.stack([c["v"] for c in chains], 1)[None], dt)
+    la = dev_tensor(np.stack([c["log_alpha"] for c in chains], 1)[None])
+    bt = dev_tensor(np.stack([c["beta"] for c in chains], 1)[None])
+    out = H.hypic_segment_build(k, v, la, cu_of(lens), bt, kind="kda")
+    plain = H.hypic_segment_build(k, v, la, cu_of(lens), bt, kind="kda", with_T=False)
+    n_seg = len(lens)
+    E = (out["T_hat"].reshape(n_seg, h_v, 128, 128), out["T_exp"].reshape(n_seg, h_v),
+         out["S"].reshape(n_seg, h_v, 128, 128))
+    fold = H.hypic_compose(*E, kind="kda", mode="fold", want_T=True, want_prefix=True)
+    scan = H.hypic_compose(*E, kind="kda", mode="scan", want_T=True, scan_block=3)
+    torch.cuda.synchronize()
+    assert torch.equal(plain["S"], out["S"])       # the T columns never feed the state columns
+    wT = wS = wF = 0.0
+    for h, c in enumerate(chains):
+        refs = _kda_segments(c, lens)
+        for s, r in enumerate(refs):
+            S = out["S"][s, 0, h].cpu().numpy()
+            if lens[s] == 0:
+                Te = torch.ldexp(out["T_hat"][s, 0, h], out["T_exp"][s, 0, h].float())
+                assert torch.equal(Te, torch.eye(128, device=Te.device)) and not S.any()
+                continue
+            eT = float(O.rel_err_T("dense", out["T_hat"][s, 0, h].cpu().numpy(), int(out["T_exp"][s, 0, h]),
+                                   r["T_hat"], r["T_exp"]))
+            eS = float(O.rel_err(S, r["S"]))
+            assert eT < tol and eS < tol, f"{dtype} head {h} segment {s}: T {eT:.3e}, S {eS:.3e}"
+            wT, wS = max(wT, eT), max(wS, eS)
+        full = O.kda_recurrence(c["k"], c["v"], c["log_alpha"], c["beta"])
+        for lab, cc in (("fold", fold), ("scan", scan)):
+            eF = float(O.rel_err(cc["S_final"][h].cpu().numpy(), full["S"]))
+            eTT = float(O.rel_err_T("dense", cc["T_total"][h].cpu().numpy(), int(cc["T_total_exp"][h]),
+                                    full["T_hat"], full["T_exp"]))
+            assert eF < tol and eTT < tol, f"{dtype} {lab} head {h}: S_final {eF:.3e}, T_total {eTT:.3e}"
+            wF = max(wF, eF, eTT)
+    print(f"kda {dtype}: segment T {wT:.2e}, S {wS:.2e}; composed S_final / T_total {wF:.2e}")
