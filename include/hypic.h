@@ -271,6 +271,59 @@ size_t hypic_compose_workspace_bytes(const hypic_compose_desc* desc);
 hypic_status hypic_compose_noalloc(const hypic_compose_desc* desc, hypic_stream_t stream);
 
 /* ------------------------------------------------------------------------------------
+ * hypic_compose_seam -- the warm hit path in one pass: seam window and composition
+ * fused, the running state kept on chip (dense kind).
+ *
+ * [news], seam-window paragraph: on reuse the first w tokens of each segment are
+ * recomputed under the full prefix, advancing the running state and emitting their
+ * outputs; [news], linear-layer paragraph: the cached rest of the segment is composed
+ * by S <- T_C S + S(C|0).  For request positions i = 0 .. n_elem-1 in order, per chain:
+ *   S <- the gated delta rule over seam i's tokens from S, emitting o_t = S_t^T q_t;
+ *   S <- 2^T_exp[slot[i]] T_hat[slot[i]] S + S[slot[i]],
+ * from S0 (NULL = 0); writes S_final and, if asked, the state entering each request
+ * position before its seam (S_prefix).  Neither the seam's own (T, S) nor the prefix
+ * states need to go through memory, unlike hypic_seam_advance + hypic_compose.
+ * Layouts (C = n_chain = n_batch * h_v, chain = b * h_v + h):
+ *   slot, T_hat, T_exp, S, S0, S_final, S_prefix as in hypic_compose (dense kind)
+ *   seam tokens packed over request positions: position i owns tokens
+ *   [cu_seam[i], cu_seam[i+1]) (host int64 [n_elem + 1]), at most
+ *   HYPIC_COMPOSE_SEAM_MAX_W of them; q, k [B, N, h_k, d_k] and v [B, N, h_v, d_v]
+ *   in_dtype (q, k L2-normalised per token on load when qk_l2norm); log_alpha, beta
+ *   float32 [B, N, h_v]; o [B, N, h_v, d_v] out_dtype or NULL.
+ * Workspace: hypic_compose_seam_workspace_bytes() (0 for at most 160 positions).
+ * ---------------------------------------------------------------------------------- */
+#define HYPIC_COMPOSE_SEAM_MAX_W 8
+typedef struct {
+    int32_t n_batch;
+    int32_t h_k, h_v, d_k, d_v;
+    int32_t n_elem;
+    int32_t n_slot;
+    const int32_t* slot;
+    const float* T_hat;
+    const int32_t* T_exp;
+    const float* S;
+    const float* S0;
+    float* S_final;
+    float* S_prefix;
+    hypic_dtype in_dtype;
+    hypic_dtype out_dtype;
+    int64_t n_tokens;
+    const int64_t* cu_seam;     /* host [n_elem + 1] */
+    int32_t qk_l2norm;
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* log_alpha;
+    const float* beta;
+    void* o;
+    void* workspace;
+    size_t workspace_bytes;
+} hypic_seam_compose_desc;
+
+hypic_status hypic_compose_seam(const hypic_seam_compose_desc* desc, hypic_stream_t stream);
+size_t hypic_compose_seam_workspace_bytes(const hypic_seam_compose_desc* desc);
+
+/* ------------------------------------------------------------------------------------
  * hypic_seam_advance -- seam tokens through the running state (dense kind).
  *
  * [news], seam-window paragraph: the first w tokens of a reused segment are

@@ -9,6 +9,7 @@ and only marshal arguments, with torch providing device memory and streams.
 from .api import (  # noqa: F401
     hypic_compose,
     hypic_compose_noalloc,
+    hypic_compose_seam,
     hypic_conv_warmup,
     hypic_device_status,
     hypic_plan_schedule,

@@ -22,6 +22,7 @@ ACT = {"none": 0, "silu": 1}
 KIND = {"dense": DENSE, "diag": DIAG, "scalar": SCALAR, "kda": KDA}
 INLINE_SEGS = 160          # segment tables up to this size need no workspace
 SEAM_SINK_DEFAULT = 8.0
+COMPOSE_SEAM_MAX_W = 8
 NOALLOC_SCRATCH_BYTES = 32 << 20   # fixed per-device scratch of hypic_compose_noalloc
 
 _p = C.c_void_p
@@ -72,6 +73,16 @@ class ConvDesc(C.Structure):
     ]
 
 
+class SeamComposeDesc(C.Structure):
+    _fields_ = [
+        ("n_batch", _i32), ("h_k", _i32), ("h_v", _i32), ("d_k", _i32), ("d_v", _i32), ("n_elem", _i32),
+        ("n_slot", _i32), ("slot", _p), ("T_hat", _p), ("T_exp", _p), ("S", _p), ("S0", _p), ("S_final", _p),
+        ("S_prefix", _p), ("in_dtype", _enum), ("out_dtype", _enum), ("n_tokens", _i64), ("cu_seam", _p),
+        ("qk_l2norm", _i32), ("q", _p), ("k", _p), ("v", _p), ("log_alpha", _p), ("beta", _p), ("o", _p),
+        ("workspace", _p), ("workspace_bytes", C.c_size_t),
+    ]
+
+
 class RerotateDesc(C.Structure):
     _fields_ = [
         ("kind", _enum), ("n_elem", _i32), ("n_chain", _i32), ("d_k", _i32), ("d_v", _i32),
@@ -87,6 +98,8 @@ EXPORTS = {
     "hypic_compose_workspace_bytes": ([C.POINTER(ComposeDesc)], C.c_size_t),
     "hypic_compose_noalloc": ([C.POINTER(ComposeDesc), _p], _enum),
     "hypic_seam_advance": ([C.POINTER(SeamDesc), _p], _enum),
+    "hypic_compose_seam": ([C.POINTER(SeamComposeDesc), _p], _enum),
+    "hypic_compose_seam_workspace_bytes": ([C.POINTER(SeamComposeDesc)], C.c_size_t),
     "hypic_seam_advance_workspace_bytes": ([C.POINTER(SeamDesc)], C.c_size_t),
     "hypic_conv_warmup": ([C.POINTER(ConvDesc), _p], _enum),
     "hypic_conv_warmup_workspace_bytes": ([C.POINTER(ConvDesc)], C.c_size_t),

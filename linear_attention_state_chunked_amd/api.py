@@ -238,6 +238,64 @@ def hypic_compose(T_hat, T_exp, S, *, kind="dense", slot=None, S0=None, mode="au
             "_workspace": ws}
 
 
+def hypic_compose_seam(T_hat, T_exp, S, q, k, v, log_alpha, beta, cu_seam, *, slot=None, S0=None, want_o=True,
+                       want_prefix=False, out_dtype=None, qk_l2norm=False):
+    """The warm hit path in one pass: for each request position, the seam tokens run
+    through the running state (outputs emitted), then the cached element is composed.
+
+    Element store as hypic_compose (dense): S, T_hat [n_slot, C, d, d] float32, T_exp
+    [n_slot, C] int32 with C = B * h_v; slot device int32 [n_elem] or None; S0 [C, d, d]
+    or None.  Seam tokens packed over request positions (cu_seam host [n_elem + 1], each
+    at most 8): q, k [B, N, h_k, d], v [B, N, h_v, d] of one dtype; log_alpha, beta float32
+    [B, N, h_v].  Returns S_final [C, d, d], S_prefix [n_elem, C, d, d] or None (the state
+    entering each position, before its seam), o [B, N, h_v, d] or None.
+    """
+    if not isinstance(S, torch.Tensor) or S.dim() != 4:
+        raise ValueError("S must be a [n_slot, n_chain, d, d] tensor")
+    n_slot, n_chain, d = S.shape[0], S.shape[1], S.shape[2]
+    _check(S, "S", dtype=torch.float32, shape=(n_slot, n_chain, d, d))
+    _check(T_hat, "T_hat", dtype=torch.float32, shape=(n_slot, n_chain, d, d))
+    _check(T_exp, "T_exp", dtype=torch.int32, shape=(n_slot, n_chain))
+    _check(S0, "S0", dtype=torch.float32, shape=(n_chain, d, d), optional=True)
+    k = _check(_as4(k, "k"), "k", dtype=_FLOAT_IN)
+    B, N, h_k, dk = k.shape
+    q = _check(_as4(q, "q"), "q", dtype=k.dtype, shape=k.shape)
+    v = _as4(v, "v")
+    h_v = v.shape[2]
+    v = _check(v, "v", dtype=k.dtype, shape=(B, N, h_v, d))
+    if dk != d or B * h_v != n_chain:
+        raise ValueError(f"seam tokens [B={B}, h_v={h_v}, d={dk}] do not match the {n_chain} chains of d = {d}")
+    _check(log_alpha, "log_alpha", dtype=torch.float32, numel=B * N * h_v)
+    _check(beta, "beta", dtype=torch.float32, numel=B * N * h_v)
+    cu = _host_offsets(cu_seam)
+    n_elem = len(cu) - 1
+    if slot is not None:
+        _check(slot, "slot", dtype=torch.int32, numel=n_elem)
+    elif n_slot < n_elem:
+        raise ValueError(f"{n_elem} request positions but only {n_slot} slots and no slot map")
+    dev = _gpu_device(S, "S")
+    for t, nm in ((T_hat, "T_hat"), (T_exp, "T_exp"), (S0, "S0"), (slot, "slot"), (q, "q"), (k, "k"), (v, "v"),
+                  (log_alpha, "log_alpha"), (beta, "beta")):
+        _check(t, nm, device=dev, optional=True)
+    out_dtype = out_dtype or k.dtype
+    if out_dtype not in _FLOAT_IN:
+        raise ValueError(f"out_dtype must be bfloat16 or float32, got {out_dtype}")
+    S_final = torch.empty((n_chain, d, d), dtype=torch.float32, device=dev)
+    S_prefix = torch.empty((n_elem, n_chain, d, d), dtype=torch.float32, device=dev) if want_prefix else None
+    o = torch.empty((B, N, h_v, d), dtype=out_dtype, device=dev) if want_o else None
+    desc = A.SeamComposeDesc(n_batch=B, h_k=h_k, h_v=h_v, d_k=d, d_v=d, n_elem=n_elem, n_slot=n_slot,
+                             slot=_ptr(slot), T_hat=_ptr(T_hat), T_exp=_ptr(T_exp), S=_ptr(S), S0=_ptr(S0),
+                             S_final=_ptr(S_final), S_prefix=_ptr(S_prefix), in_dtype=_dtype(k),
+                             out_dtype=A.BF16 if out_dtype == torch.bfloat16 else A.F32, n_tokens=N,
+                             cu_seam=cu.ctypes.data, qk_l2norm=int(bool(qk_l2norm)), q=_ptr(q), k=_ptr(k),
+                             v=_ptr(v), log_alpha=_ptr(log_alpha), beta=_ptr(beta), o=_ptr(o))
+    L = A.lib()
+    ws = _workspace(L.hypic_compose_seam_workspace_bytes(C.byref(desc)), dev)
+    desc.workspace, desc.workspace_bytes = ws.data_ptr(), ws.numel()
+    A.check(L.hypic_compose_seam(C.byref(desc), _stream()))
+    return {"S_final": S_final, "S_prefix": S_prefix, "o": o, "_workspace": ws}
+
+
 def _state_numel(n_seam, stride, block):
     """Floats a seam-state array must hold: seam s at s * stride (stride 0: dense blocks)."""
     if n_seam == 0:

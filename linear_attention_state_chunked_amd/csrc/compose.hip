@@ -81,7 +81,12 @@ __device__ __forceinline__ halfx8 t_frag(const _Float16* base) {
 // loader waves hold the next element's (T_i, and for role 0 S_i) in registers, loaded
 // from HBM while the current element is multiplied, and write them into LDS (T_i as
 // hi/lo f16, S_i as fp32, row-major) between two workgroup barriers.
-template <int D>
+// SEAM: the fused warm path.  Loader wave t also loads seam token t of the next element
+// (q, k, v rows, gates) and stages it in LDS (float32, q and k L2-normalised on request);
+// before each element's product the compute waves run the gated delta rule over those tokens
+// on their accumulator-resident columns: u = k^T S (lane-local partial over its 64 rows plus
+// the other lane half's), S <- alpha (S - beta k u^T) + beta k v^T, o = S^T q.
+template <int D, bool SEAM>
 __global__ __launch_bounds__(D * 6) void fold_dense_kernel(FoldArgs a) {
     constexpr int NB = D / 32;                        // compute waves
     constexpr int NLT = 2 * NB * 64;                  // loader threads
@@ -93,6 +98,11 @@ __global__ __launch_bounds__(D * 6) void fold_dense_kernel(FoldArgs a) {
     __shared__ __align__(16) float sS[D * RSS];
     __shared__ int sE;
     __shared__ int sEw[NB];
+    constexpr int WS = SEAM ? kFusedSeamMax : 1;
+    __shared__ __align__(16) float sQk[WS][2][D];   // seam q, k rows
+    __shared__ __align__(16) float sVs[WS][D];      // seam v rows
+    __shared__ float sGb[WS][2];                    // alpha, beta
+    __shared__ int sW;                              // seam tokens of the staged element
 
     const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -112,6 +122,11 @@ __global__ __launch_bounds__(D * 6) void fold_dense_kernel(FoldArgs a) {
         typedef float f4 __attribute__((ext_vector_type(4)));
         f4 tr[TPL], ts[TPL];
         int ei = 0;
+        // seam tokens lw, lw + NLW, ... (loader wave lw): lane l holds channels l, l + 64, ...
+        constexpr int NLW = NLT / 64, TPW = (kFusedSeamMax + NLW - 1) / NLW, CPL = D / 64;
+        const int lw = lt >> 6, ll = lt & 63;
+        float sq[TPW][CPL], sk[TPW][CPL], sv[TPW][CPL], sal[TPW], sbe[TPW];
+        int swn = 0;
         auto load = [&](int el) __attribute__((always_inline)) {
             const long long so = elem(el);
             const f4* src = reinterpret_cast<const f4*>(a.T_hat + so * DD);
@@ -123,6 +138,34 @@ __global__ __launch_bounds__(D * 6) void fold_dense_kernel(FoldArgs a) {
                 for (int r = 0; r < TPL; ++r) ts[r] = srs[lt + NLT * r];
             }
             ei = a.T_exp[so];
+            if constexpr (SEAM) {
+                swn = seg_len(a.seam_tab, el);
+                const int bb = chain / a.h_v, hh = chain - (chain / a.h_v) * a.h_v;
+                const int hk = (hh * a.h_k) / a.h_v;
+#pragma unroll
+                for (int m = 0; m < TPW; ++m) {
+                    const int t = lw + NLW * m;
+                    if (t < swn) {
+                        const long long row = (long long)bb * a.n_tokens + seg_start(a.seam_tab, el) + t;
+                        const long long qi = (row * a.h_k + hk) * D, vi = (row * a.h_v + hh) * D;
+#pragma unroll
+                        for (int u = 0; u < CPL; ++u) {
+                            const int c = ll + 64 * u;
+                            if (a.in_bf16) {
+                                sq[m][u] = bf16_to_f32(reinterpret_cast<const uint16_t*>(a.q)[qi + c]);
+                                sk[m][u] = bf16_to_f32(reinterpret_cast<const uint16_t*>(a.k)[qi + c]);
+                                sv[m][u] = bf16_to_f32(reinterpret_cast<const uint16_t*>(a.v)[vi + c]);
+                            } else {
+                                sq[m][u] = reinterpret_cast<const float*>(a.q)[qi + c];
+                                sk[m][u] = reinterpret_cast<const float*>(a.k)[qi + c];
+                                sv[m][u] = reinterpret_cast<const float*>(a.v)[vi + c];
+                            }
+                        }
+                        sal[m] = expf(a.log_alpha[row * a.h_v + hh]);
+                        sbe[m] = a.beta[row * a.h_v + hh];
+                    }
+                }
+            }
         };
         auto stage = [&]() __attribute__((always_inline)) {
             typedef _Float16 half4 __attribute__((ext_vector_type(4)));
@@ -142,6 +185,38 @@ __global__ __launch_bounds__(D * 6) void fold_dense_kernel(FoldArgs a) {
                 if (!t_role) *reinterpret_cast<f4*>(&sS[row * RSS + col]) = ts[r];
             }
             if (lt == 0) sE = ei;
+            if constexpr (SEAM) {
+                if (lt == 0) sW = swn;
+#pragma unroll
+                for (int m = 0; m < TPW; ++m) {
+                    const int t = lw + NLW * m;
+                    if (t < swn) {   // uniform over the wave
+                        float fq = 1.f, fk = 1.f;
+                        if (a.qk_l2norm) {
+                            float nq = 0.f, nk = 0.f;
+#pragma unroll
+                            for (int u = 0; u < CPL; ++u) {
+                                nq += sq[m][u] * sq[m][u];
+                                nk += sk[m][u] * sk[m][u];
+                            }
+                            nq = wave_sum(nq);
+                            nk = wave_sum(nk);
+                            fq = nq > 0.f ? 1.f / sqrtf(nq) : 0.f;
+                            fk = nk > 0.f ? 1.f / sqrtf(nk) : 0.f;
+                        }
+#pragma unroll
+                        for (int u = 0; u < CPL; ++u) {
+                            sQk[t][0][ll + 64 * u] = sq[m][u] * fq;
+                            sQk[t][1][ll + 64 * u] = sk[m][u] * fk;
+                            sVs[t][ll + 64 * u] = sv[m][u];
+                        }
+                        if (ll == 0) {
+                            sGb[t][0] = sal[m];
+                            sGb[t][1] = sbe[m];
+                        }
+                    }
+                }
+            }
         };
         if (e0 < e1) load(e0);
         for (int el = e0; el < e1; ++el) {
@@ -187,6 +262,51 @@ __global__ __launch_bounds__(D * 6) void fold_dense_kernel(FoldArgs a) {
             }
         }
         __syncthreads();  // element el staged
+        if constexpr (SEAM) {
+            const int w = sW;
+            const int bb = chain / a.h_v, hh = chain - (chain / a.h_v) * a.h_v;
+            for (int t = 0; t < w; ++t) {
+                const float* kr = sQk[t][1];
+                const float* qr = sQk[t][0];
+                // u = k^T S for this lane's column: its 64 rows, then the other half's
+                float up[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int xb = 0; xb < NB; ++xb)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const floatx4 k4 = *reinterpret_cast<const floatx4*>(kr + 32 * xb + 8 * g + 4 * half);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) up[i] = fmaf(k4[i], X[xb][4 * g + i], up[i]);
+                    }
+                float u = (up[0] + up[1]) + (up[2] + up[3]);
+                u += __shfl_xor(u, 32, 64);
+                const float al = sGb[t][0], be = sGb[t][1];
+                // S <- al (S - be k u) + be k v  =  al S + k (be (v - al u))
+                const float cf = be * (sVs[t][col0 + l32] - al * u);
+                float op[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int xb = 0; xb < NB; ++xb)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const floatx4 k4 = *reinterpret_cast<const floatx4*>(kr + 32 * xb + 8 * g + 4 * half);
+                        const floatx4 q4 = *reinterpret_cast<const floatx4*>(qr + 32 * xb + 8 * g + 4 * half);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float x = fmaf(k4[i], cf, al * X[xb][4 * g + i]);
+                            X[xb][4 * g + i] = x;
+                            op[i] = fmaf(q4[i], x, op[i]);
+                        }
+                    }
+                float ov = (op[0] + op[1]) + (op[2] + op[3]);
+                ov += __shfl_xor(ov, 32, 64);
+                if (half == 0 && a.o) {
+                    const long long row = (long long)bb * a.n_tokens + seg_start(a.seam_tab, el) + t;
+                    const long long oi = (row * a.h_v + hh) * D + col0 + l32;
+                    if (a.out_bf16) reinterpret_cast<uint16_t*>(a.o)[oi] = f32_to_bf16(ov);
+                    else reinterpret_cast<float*>(a.o)[oi] = ov;
+                }
+            }
+        }
         const int ecur = sE;
         // scale this wave's columns to max |x| in [0.5, 1) before the hi/lo split
         float m = 0.f;
@@ -353,8 +473,14 @@ hipError_t launch_fold(const FoldArgs& a, int d, int with_T, hipStream_t s) {
     if (a.kind == 0 && !a.naive) {
         // role 1 (the composed transition) only when its outputs are wanted
         const dim3 g3(a.n_chain, a.n_block, (with_T && a.out_T) ? 2 : 1);
-        if (d == 128) hipLaunchKernelGGL((fold_dense_kernel<128>), g3, dim3(768), 0, s, a);
-        else if (d == 64) hipLaunchKernelGGL((fold_dense_kernel<64>), g3, dim3(384), 0, s, a);
+        if (a.seam) {
+            // the fused warm path: one block per chain, S only
+            if (a.n_block != 1 || with_T) return hipErrorInvalidValue;
+            if (d == 128) hipLaunchKernelGGL((fold_dense_kernel<128, true>), g3, dim3(768), 0, s, a);
+            else if (d == 64) hipLaunchKernelGGL((fold_dense_kernel<64, true>), g3, dim3(384), 0, s, a);
+            else return hipErrorInvalidValue;
+        } else if (d == 128) hipLaunchKernelGGL((fold_dense_kernel<128, false>), g3, dim3(768), 0, s, a);
+        else if (d == 64) hipLaunchKernelGGL((fold_dense_kernel<64, false>), g3, dim3(384), 0, s, a);
         else return hipErrorInvalidValue;
     } else {
         // naive addition of any kind, and the diagonal / scalar kinds

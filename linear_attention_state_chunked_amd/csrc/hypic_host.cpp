@@ -713,6 +713,100 @@ hypic_status hypic_compose_noalloc(const hypic_compose_desc* d, hypic_stream_t s
 }
 
 // ------------------------------------------------------------------------------------------
+// fused seam + compose (warm hit path)
+
+namespace {
+
+hypic_status validate_compose_seam(const hypic_seam_compose_desc* d) {
+    if (!d) return fail(HYPIC_ERR_INVALID_ARGUMENT, "compose_seam: desc is NULL");
+    if (d->n_batch < 1 || d->h_k < 1 || d->h_v < 1 || d->h_v % d->h_k || d->n_elem < 0 || d->n_slot < 0 ||
+        d->n_tokens < 0)
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "compose_seam: bad geometry");
+    if (d->d_k != d->d_v || !supported_d(d->d_k))
+        return fail(HYPIC_ERR_UNSUPPORTED, "compose_seam: d_k=%d d_v=%d (supported: d_k == d_v in {64, 128})",
+                    d->d_k, d->d_v);
+    if ((int64_t)d->n_batch * d->h_v > 65535 * 1024)
+        return fail(HYPIC_ERR_UNSUPPORTED, "compose_seam: too many chains");
+    if ((d->in_dtype != HYPIC_F32 && d->in_dtype != HYPIC_BF16) ||
+        (d->out_dtype != HYPIC_F32 && d->out_dtype != HYPIC_BF16))
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "compose_seam: unknown dtype");
+    if (d->qk_l2norm != 0 && d->qk_l2norm != 1)
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "compose_seam: qk_l2norm must be 0 or 1");
+    if (!d->S_final) return fail(HYPIC_ERR_INVALID_ARGUMENT, "compose_seam: S_final is NULL");
+    if (!d->slot && d->n_slot < d->n_elem)
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "compose_seam: slot is NULL but n_slot=%d < n_elem=%d", d->n_slot,
+                    d->n_elem);
+    hypic_status st = check_offsets(d->cu_seam, d->n_elem, d->n_tokens, "compose_seam: cu_seam");
+    if (st != HYPIC_OK) return st;
+    int64_t w_max = 0;
+    for (int32_t i = 0; i < d->n_elem; ++i) w_max = std::max<int64_t>(w_max, d->cu_seam[i + 1] - d->cu_seam[i]);
+    if (w_max > hypic::kFusedSeamMax)
+        return fail(HYPIC_ERR_UNSUPPORTED, "compose_seam: a seam of %lld tokens (at most %d fused; use "
+                    "hypic_seam_advance and hypic_compose)", (long long)w_max, hypic::kFusedSeamMax);
+    if (d->n_elem > 0 && (!d->S || !d->T_hat || !d->T_exp))
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "compose_seam: T_hat, T_exp and S are required");
+    if (d->T_hat && !aligned16(d->T_hat))
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "compose_seam: T_hat must be 16-byte aligned");
+    if (w_max > 0 && (!d->q || !d->k || !d->v || !d->log_alpha || !d->beta))
+        return fail(HYPIC_ERR_INVALID_ARGUMENT, "compose_seam: q, k, v, log_alpha and beta are required");
+    return HYPIC_OK;
+}
+
+}  // namespace
+
+size_t hypic_compose_seam_workspace_bytes(const hypic_seam_compose_desc* d) {
+    if (!d || d->n_elem < 0) return 0;
+    return seg_table_layout(d->n_elem).bytes;
+}
+
+hypic_status hypic_compose_seam(const hypic_seam_compose_desc* d, hypic_stream_t stream) {
+    hypic_status st = validate_compose_seam(d);
+    if (st != HYPIC_OK) return st;
+    const SegTableLayout L = seg_table_layout(d->n_elem);
+    st = check_workspace("compose_seam", L.bytes, d->workspace, d->workspace_bytes);
+    if (st != HYPIC_OK) return st;
+    std::vector<int64_t> start(d->n_elem);
+    std::vector<int32_t> len(d->n_elem);
+    for (int32_t i = 0; i < d->n_elem; ++i) {
+        start[i] = d->cu_seam[i];
+        len[i] = (int32_t)(d->cu_seam[i + 1] - d->cu_seam[i]);
+    }
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hypic::FoldArgs a{};
+    hipError_t e = fill_seg_table(a.seam_tab, L, d->workspace, start, len, {}, s);
+    if (e != hipSuccess) return device_fail("compose_seam: table upload", e);
+    a.kind = 0;
+    a.n_chain = d->n_batch * d->h_v;
+    a.n_elem = d->n_elem;
+    a.per_block = std::max(1, d->n_elem);
+    a.n_block = 1;
+    a.slot = d->slot;
+    a.T_hat = d->T_hat;
+    a.T_exp = d->T_exp;
+    a.S = d->S;
+    a.init_S = d->S0;
+    a.out_S = d->S_final;
+    a.prefix = d->S_prefix;
+    a.seam = 1;
+    a.n_batch = d->n_batch;
+    a.h_k = d->h_k;
+    a.h_v = d->h_v;
+    a.n_tokens = d->n_tokens;
+    a.in_bf16 = d->in_dtype == HYPIC_BF16;
+    a.out_bf16 = d->out_dtype == HYPIC_BF16;
+    a.qk_l2norm = d->qk_l2norm;
+    a.q = d->q;
+    a.k = d->k;
+    a.v = d->v;
+    a.log_alpha = d->log_alpha;
+    a.beta = d->beta;
+    a.o = d->o;
+    e = hypic::launch_fold(a, d->d_k, 0, s);
+    if (e != hipSuccess) return device_fail("compose_seam: launch", e);
+    return ok();
+}
+
+// ------------------------------------------------------------------------------------------
 // seam advance
 
 namespace {

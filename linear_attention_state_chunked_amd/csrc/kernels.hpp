@@ -134,7 +134,22 @@ struct FoldArgs {
     int* out_e;               // [n_block, n_chain] or null
     float* prefix;            // [n_elem, n_chain, dk, dv] or null
     int naive;                // 1: S <- S + S_i
+    // Fused seam (dense kind, one block per chain): before element el's product the running
+    // state goes through the seam tokens [start, start + len) of entry el of `seam_tab`
+    // (packed seam axis, at most kFusedSeamMax tokens), emitting o_t = S_t^T q_t.
+    int seam;
+    int n_batch, h_k, h_v;    // chain = b * h_v + h
+    long long n_tokens;       // packed seam tokens
+    int in_bf16, out_bf16, qk_l2norm;
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* log_alpha;
+    const float* beta;
+    void* o;                  // [B, n_tokens, h_v, dv]
+    SegTable seam_tab;
 };
+constexpr int kFusedSeamMax = 8;
 
 // One short-seam launch (every seam <= 16 tokens): one workgroup per (seam, batch,
 // value head); computes whichever of o, S_out, T_hat/T_exp, S_seam are non-null.

@@ -29,7 +29,7 @@ def L():
 def test_every_declared_symbol_is_exported(L):
     src = open(HEADER).read()
     declared = set(re.findall(r"^\s*(?:hypic_status|size_t|const char\*|int)\s+(hypic_\w+)\s*\(", src, re.M))
-    assert len(declared) == 15
+    assert len(declared) == 17
     assert declared == set(A.EXPORTS)
     out = subprocess.run(["nm", "-D", "--defined-only", A.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT (hypic_\w+)", out))
@@ -41,7 +41,8 @@ def test_every_declared_symbol_is_exported(L):
 def test_struct_layouts_match_the_header(tmp_path):
     lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "hypic.h"', "int main(void) {"]
     structs = {"hypic_build_desc": A.BuildDesc, "hypic_compose_desc": A.ComposeDesc,
-               "hypic_seam_desc": A.SeamDesc, "hypic_conv_desc": A.ConvDesc, "hypic_rerotate_desc": A.RerotateDesc}
+               "hypic_seam_desc": A.SeamDesc, "hypic_conv_desc": A.ConvDesc, "hypic_rerotate_desc": A.RerotateDesc,
+               "hypic_seam_compose_desc": A.SeamComposeDesc}
     for cname, cls in structs.items():
         lines.append(f'printf("{cname} %zu\\n", sizeof({cname}));')
         for f, _ in cls._fields_:
@@ -348,3 +349,24 @@ def test_rerotate_validation(L):
         assert msg in L.hypic_last_error().decode(), kw
     d = A.RerotateDesc(**{**base, "n_elem": 0})
     assert L.hypic_state_rerotate(C.byref(d), None) == A.OK      # nothing to do, nothing enqueued
+
+
+def test_compose_seam_validation(L):
+    cu = np.array([0, 8, 16], np.int64)
+    long = np.array([0, 9, 16], np.int64)
+    base = dict(n_batch=1, h_k=1, h_v=2, d_k=128, d_v=128, n_elem=2, n_slot=2, slot=None, T_hat=0x1000,
+                T_exp=0x2000, S=0x3000, S0=None, S_final=0x4000, S_prefix=None, in_dtype=A.BF16, out_dtype=A.F32,
+                n_tokens=16, cu_seam=cu.ctypes.data, qk_l2norm=0, q=0x5000, k=0x6000, v=0x7000,
+                log_alpha=0x8000, beta=0x9000, o=None, workspace=None, workspace_bytes=0)
+    for kw, status, msg in ((dict(cu_seam=long.ctypes.data), A.ERR_UNSUPPORTED, "at most 8"),
+                            (dict(S_final=None), A.ERR_INVALID_ARGUMENT, "S_final"),
+                            (dict(n_slot=1), A.ERR_INVALID_ARGUMENT, "n_slot"),
+                            (dict(T_hat=None), A.ERR_INVALID_ARGUMENT, "T_hat"),
+                            (dict(q=None), A.ERR_INVALID_ARGUMENT, "q, k, v"),
+                            (dict(h_k=3), A.ERR_INVALID_ARGUMENT, "geometry"),
+                            (dict(d_k=96, d_v=96), A.ERR_UNSUPPORTED, "d_k"),
+                            (dict(out_dtype=7), A.ERR_INVALID_ARGUMENT, "dtype")):
+        d = A.SeamComposeDesc(**{**base, **kw})
+        assert L.hypic_compose_seam(C.byref(d), None) == status, kw
+        assert msg in L.hypic_last_error().decode(), kw
+    assert L.hypic_compose_seam_workspace_bytes(C.byref(A.SeamComposeDesc(**base))) == 0

@@ -309,6 +309,10 @@ def test_warm30_full_conv_seam_compose(gpu):
     pre = c["S_prefix"]
     sa = H.hypic_seam_advance(sq, sk, sv, sl, sb, cu_seam, S_in=pre, state_stride=2 * n_chain * d * d,
                               S_out=None, qk_l2norm=True, out_dtype=torch.float32)
+    # the same warm path in one fused pass over the cached rest elements in request order
+    fu = H.hypic_compose_seam(E_T[:n_slot], E_e[:n_slot], E_S[:n_slot], sq, sk, sv, sl, sb, cu_seam,
+                              slot=torch.from_numpy(order.astype(np.int32)).to(DEV), want_prefix=True,
+                              out_dtype=torch.float32, qk_l2norm=True)
     torch.cuda.synchronize()
     idx = [layer * h_v + h for layer, h in chains]
     S_start = _host(pre[0::2][:, idx])                                  # [n_slot, 8, d, d]
@@ -316,14 +320,21 @@ def test_warm30_full_conv_seam_compose(gpu):
     o_s = np.stack([_host(o[layer, :, h]) for layer, h in chains], 1)    # [n_slot*w, 8, d]
     S_fin = _host(c["S_final"][idx])
     S_fin_fold = _host(cf["S_final"][idx])
-    del xq, xk, xv, E_T, E_S, c, cf, pre, sa
+    fu_start = _host(fu["S_prefix"][:, idx])
+    fu_o = np.stack([_host(fu["o"][layer, :, h]) for layer, h in chains], 1)
+    fu_fin = _host(fu["S_final"][idx])
+    del xq, xk, xv, E_T, E_S, c, cf, pre, sa, fu
     log("device done; waiting for the oracle")
     outs = _collect(pool, res)
     worst = [0.0, 0.0, 0.0]
     for j, ((layer, h), r) in enumerate(zip(chains, outs)):
         e_start = O.rel_err(S_start[:, j], r["S_start"])
         e_o = O.rel_err(o_s[:, j].reshape(n_slot, w, d), r["o_seam"])
-        e_f = max(float(O.rel_err(S_fin[j], r["S_final"])), float(O.rel_err(S_fin_fold[j], r["S_final"])))
+        e_f = max(float(O.rel_err(S_fin[j], r["S_final"])), float(O.rel_err(S_fin_fold[j], r["S_final"])),
+                  float(O.rel_err(fu_fin[j], r["S_final"])))
+        # the fused pass: states entering each position, seam outputs
+        e_start = np.maximum(e_start, O.rel_err(fu_start[:, j], r["S_start"]))
+        e_o = np.maximum(e_o, O.rel_err(fu_o[:, j].reshape(n_slot, w, d), r["o_seam"]))
         worst = [max(worst[0], float(np.max(e_start))), max(worst[1], float(np.max(e_o))), max(worst[2], e_f)]
         assert np.max(e_start) <= TOL, f"layer {layer} head {h}: segment-start state err {np.max(e_start):.3e}"
         assert np.max(e_o) <= TOL, f"layer {layer} head {h}: seam output err {np.max(e_o):.3e}"

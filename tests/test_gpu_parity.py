@@ -632,3 +632,60 @@ def test_kda_build_ragged_and_compose(gpu, dtype):
             assert eF < tol and eTT < tol, f"{dtype} {lab} head {h}: S_final {eF:.3e}, T_total {eTT:.3e}"
             wF = max(wF, eF, eTT)
     print(f"kda {dtype}: segment T {wT:.2e}, S {wS:.2e}; composed S_final / T_total {wF:.2e}")
+
+
+# ----------------------------------------------------------------------------------------
+# fused warm path: seam window + composition in one pass, state kept on chip
+
+
+@pytest.mark.parametrize("dtype,l2", [("f32", False), ("bf16", True)])
+def test_compose_seam_fused(gpu, dtype, l2):
+    from synth import random_elements, rne_bf16
+
+    rng = np.random.default_rng(77)
+    d, B, h_k, h_v = 128, 2, 1, 2
+    n_chain, n_slot = B * h_v, 6
+    el = random_elements(78, n_slot, n_chain, d)     # well-conditioned T: every cross term counts
+    slots = np.array([3, 0, 5, 0, 2, 4, 1], np.int32)
+    widths = [8, 3, 0, 8, 1, 5, 8]
+    cu = np.concatenate([[0], np.cumsum(widths)]).astype(np.int64)
+    N = int(cu[-1])
+    q = rng.standard_normal((B, N, h_k, d)).astype(np.float32)
+    k = rng.standard_normal((B, N, h_k, d)).astype(np.float32)
+    if not l2:
+        q /= np.linalg.norm(q, axis=-1, keepdims=True)
+        k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((B, N, h_v, d)).astype(np.float32)
+    beta = (1.0 / (1.0 + np.exp(-rng.standard_normal((B, N, h_v))))).astype(np.float32)
+    la = (-0.05 * np.logaddexp(0.0, rng.standard_normal((B, N, h_v)))).astype(np.float32)
+    if dtype == "bf16":
+        q, k, v = rne_bf16(q), rne_bf16(k), rne_bf16(v)
+    dt, tol = (torch.float32, TOL_F32) if dtype == "f32" else (torch.bfloat16, TOL_BF16)
+    S0 = rng.standard_normal((n_chain, d, d)).astype(np.float32)
+    r = H.hypic_compose_seam(dev_tensor(el["T_hat"]), torch.from_numpy(el["T_exp"]).to("cuda:0"),
+                             dev_tensor(el["S"]), dev_tensor(q, dt), dev_tensor(k, dt), dev_tensor(v, dt),
+                             dev_tensor(la), dev_tensor(beta), cu, slot=torch.from_numpy(slots).to("cuda:0"),
+                             S0=dev_tensor(S0), want_prefix=True, out_dtype=torch.float32, qk_l2norm=l2)
+    torch.cuda.synchronize()
+    o, Sf, Sp = r["o"].cpu().numpy(), r["S_final"].cpu().numpy(), r["S_prefix"].cpu().numpy()
+    worst = 0.0
+    for c in range(n_chain):
+        b, h = c // h_v, c % h_v
+        kk = O.l2_normalise(k[b, :, 0]) if l2 else k[b, :, 0]
+        qq = O.l2_normalise(q[b, :, 0]) if l2 else q[b, :, 0]
+        S = S0[c].astype(np.float64)
+        for i, s in enumerate(slots):
+            e = float(O.rel_err(Sp[i, c], S))
+            lo, hi = int(cu[i]), int(cu[i + 1])
+            if hi > lo:
+                run = O.dense_recurrence(kk[lo:hi], v[b, lo:hi, h], la[b, lo:hi, h], beta[b, lo:hi, h], S0=S,
+                                         q=qq[lo:hi])
+                e = max(e, float(O.rel_err(o[b, lo:hi, h], run["o"])))
+                S = run["S"]
+            S = O.apply_T("dense", el["T_hat"][s, c], el["T_exp"][s, c], S) + el["S"][s, c]
+            assert e < tol, f"chain {c} position {i}: err {e:.3e}"
+            worst = max(worst, e)
+        e = float(O.rel_err(Sf[c], S))
+        assert e < tol, f"chain {c}: final state err {e:.3e}"
+        worst = max(worst, e)
+    print(f"fused seam + compose {dtype}: max err {worst:.2e}")
