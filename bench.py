@@ -10,11 +10,14 @@ the timed region.  Prints one JSON line.
 Beside the headline line's fields, "rows" times every other step of the path on
 its own workload shape (inputs filled on the device; the timing does not depend on
 the values): the diagonal/scalar build (16 x 512 tokens, 16 RetNet + 16 GLA
-heads), the warm 30-layer path (conv warm-up of the seam tokens, seam advance,
-compose of 128 segments x 960 chains with prefix states), and the cold 100k-token
-30-layer build in LPT, round-robin and natural order with the single sequential
-pass beside it.  Each carries its algorithmic bytes or flops and the fraction of
-the matching MI355X peak.
+heads); the headline layer under the precise-T plan, as a plain state pass, as the
+output-fused build with and without T (the T overhead on the segment forward) and
+its re-rotation to new offsets; the per-channel gated delta (KDA) build; the warm
+30-layer path (conv warm-up of the seam tokens, seam advance, compose of 128
+segments x 960 chains with prefix states, and the same path fused into one pass);
+and the cold 100k-token 30-layer build in LPT, round-robin and natural order, with
+the precise-T plan and the single sequential pass beside it.  Each carries its
+algorithmic bytes or flops and the fraction of the matching MI355X peak.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-rows]
   python bench.py --calibrate-copy      (a plain 1 GiB device copy, for HBM counters)
@@ -38,6 +41,7 @@ sys.path.insert(0, ROOT)
 METRIC = "segment-build tokens/s for (T_C,S|0) + compose µs/segment, % MFMA/HBM peak"
 PEAK_MFMA_F16 = 2.5e15        # MI355X dense f16/bf16 matrix peak, FLOP/s
 PEAK_HBM = 8.0e12             # MI355X HBM3E, B/s
+PEAK_ALU_F32 = 157.3e12       # MI355X fp32 vector peak (packed fp32), FLOP/s
 D, CHUNK = 128, 64
 
 
@@ -274,15 +278,23 @@ def row_warm(dev):
     seam2 = lambda: H.hypic_seam_advance(sq, sk, sv, la, beta, cu_seam, S_in=pre, state_stride=2 * nc * d * d,
                                          S_out=None, qk_l2norm=True, out_dtype=torch.float32)
     t_seam2 = _median_time(seam2)
+    order_d = slot_d[1::2].contiguous()
+    fused = lambda: H.hypic_compose_seam(E_T[:n_slot], E_e[:n_slot], E_S[:n_slot], sq, sk, sv, la, beta, cu_seam,
+                                         slot=order_d, out_dtype=torch.float32, qk_l2norm=True)
+    t_fused = _median_time(fused, reps=3)
     tok_bytes = (2 * hk + hv) * d * 4 * L * nw + 2 * hv * 4 * L * nw
     seam1_bytes = tok_bytes + 2 * n_slot * nc * d * d * 4 + n_slot * nc * 4
     comp_bytes = 2 * n_slot * nc * (2 * d * d * 4 + 4) + 2 * n_slot * nc * d * d * 4
     seam2_bytes = tok_bytes + n_slot * nc * d * d * 4 + L * nw * hv * d * 4
+    # fused: read each cached (T_hat, S) once, the seam tokens, write the outputs and the final state
+    fused_bytes = n_slot * nc * (2 * d * d * 4 + 4) + tok_bytes + L * nw * hv * d * 4 + nc * d * d * 4
     return {"conv_warmup": _hbm(conv_bytes, t_conv),
             "seam_build": _hbm(seam1_bytes, t_seam1),
             "compose_fold_prefix": dict(_hbm(comp_bytes, t_comp), us_per_segment=t_comp * 1e6 / n_slot),
             "seam_outputs": _hbm(seam2_bytes, t_seam2),
-            "total_ms": (t_conv + t_seam1 + t_comp + t_seam2) * 1e3}
+            "total_ms": (t_conv + t_seam1 + t_comp + t_seam2) * 1e3,
+            "fused_seam_compose": dict(_hbm(fused_bytes, t_fused), us_per_segment=t_fused * 1e6 / n_slot),
+            "fused_total_ms": (t_conv + t_fused) * 1e3}
 
 
 def row_cold(dev):
@@ -319,10 +331,80 @@ def row_cold(dev):
         * ((N + CHUNK - 1) // CHUNK) * L * hv
     t = _median_time(lambda: H.hypic_segment_build(k, v, la, [0, N], beta, with_T=False), reps=3)
     res["single_pass_no_T"] = _mfma(single_flops, t)
+    t = _median_time(lambda: H.hypic_segment_build(k, v, la, cu, beta, schedule="lpt", out=out,
+                                                    precision="f16_precise_t"), reps=3)
+    res["lpt_precise_T"] = _mfma(flops, t)
     E = (out["T_hat"].view(n_seg, L * hv, d, d), out["T_exp"].view(n_seg, L * hv), out["S"].view(n_seg, L * hv, d, d))
     tc = _median_time(lambda: H.hypic_compose(*E, mode="scan"), reps=3)
     res["compose_scan"] = dict(_hbm(n_seg * L * hv * (2 * d * d * 4 + 4), tc), us_per_segment=tc * 1e6 / n_seg)
     return res
+
+
+def row_build_plans(dev):
+    """The 64k-token GDN layer of the headline step under the other build plans: the
+    precise-T plan (transition-only pass with hi/lo operands, then the state pass), the
+    output-fused build (per-token outputs from each segment's zero start, with and without
+    T: the T overhead on the segment forward), the plain state pass, and the RoPE
+    re-rotation of the layer's 2,048 cached (T, S) elements."""
+    import torch
+    import torch.nn.functional as F
+
+    from linear_attention_state_chunked_amd import api as H
+
+    wl, inp, cu = make_inputs(dev)
+    k, v, la, bt = inp["k"], inp["v"], inp["log_alpha"], inp["beta"]
+    N, h_v = k.shape[1], v.shape[2]
+    n_chunks = sum((int(cu[i + 1] - cu[i]) + 63) // 64 for i in range(len(cu) - 1))
+    flops = build_flops_per_chunk() * n_chunks * h_v
+    out = {}
+    t = _median_time(lambda: H.hypic_segment_build(k, v, la, cu, bt, precision="f16_precise_t"))
+    out["precise_T"] = _mfma(flops, t)
+    t = _median_time(lambda: H.hypic_segment_build(k, v, la, cu, bt, with_T=False))
+    # without T the carry covers the d state columns only: 4 C d d instead of 4 C d 2d
+    state_flops = flops - 4 * CHUNK * D * D * n_chunks * h_v
+    out["state_only"] = _mfma(state_flops, t)
+    g = torch.Generator(device=dev)
+    g.manual_seed(2)
+    q = F.normalize(torch.randn(k.shape, device=dev, generator=g), dim=-1).to(k.dtype)
+    t_to = _median_time(lambda: H.hypic_segment_build(k, v, la, cu, bt, q=q, want_o=True))
+    t_o = _median_time(lambda: H.hypic_segment_build(k, v, la, cu, bt, q=q, want_o=True, with_T=False))
+    # algorithmic flops of the outputs per chunk: Q K^T (r-shared) and the two output products
+    out_flops = (2 * CHUNK * CHUNK * D / 2 + 2 * CHUNK * D * D + 2 * CHUNK * CHUNK * D) * n_chunks * h_v
+    out["output_fused_with_T"] = _mfma(flops + out_flops, t_to)
+    out["output_fused_no_T"] = _mfma(flops - 4 * CHUNK * D * D * n_chunks * h_v + out_flops, t_o)
+    out["output_fused_T_overhead_pct"] = (t_to / t_o - 1.0) * 100.0
+    b = H.hypic_segment_build(k, v, la, cu, bt)
+    n_seg = len(cu) - 1
+    Tn, Sn = b["T_hat"].reshape(n_seg, h_v, D, D), b["S"].reshape(n_seg, h_v, D, D)
+    delta = np.arange(n_seg, dtype=np.int64) * 1000 - 31_000
+    t = _median_time(lambda: H.hypic_state_rerotate(Tn, Sn, delta, inplace=True))
+    out["rerotate_T_and_S"] = _hbm(2 * 2 * Tn.numel() * 4, t)     # read and write T and S
+    return out
+
+
+def row_kda(dev):
+    """Per-channel gated delta rule (KDA) build: 32 value heads on 16 key heads, d = 128,
+    16 segments x 512 tokens, bf16 inputs; token recurrence in float32 vector arithmetic
+    (bound: the vector ALUs; 157.3 TFLOP/s is the chip's fp32 vector peak with packed
+    fp32 math, which this build does not use)."""
+    import torch
+
+    from linear_attention_state_chunked_amd import api as H
+    from synth import WORKLOADS, layer_inputs, segment_lengths
+
+    wl = WORKLOADS["kda_bf16"]
+    x = layer_inputs(wl, 0, with_q=False)
+    t_ = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(dt)
+    k, v = t_(x["k"][None], torch.bfloat16), t_(x["v"][None], torch.bfloat16)
+    la, bt = t_(x["log_alpha"][None], torch.float32), t_(x["beta"][None], torch.float32)
+    lens = segment_lengths(wl)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    t = _median_time(lambda: H.hypic_segment_build(k, v, la, cu, bt, kind="kda"))
+    n_tok = int(cu[-1]) * wl.h_v
+    # per token and column of [T | S]: k^T X (2d), decay and rank-1 update (3d), write (2d for S)
+    flops = n_tok * (2 * D * (2 * D) + 3 * D * (2 * D) + 2 * D * D)
+    return {"s": t, "flops": flops, "TFLOP_per_s": flops / t / 1e12, "alu_frac": flops / t / PEAK_ALU_F32,
+            "tokens_per_s": int(cu[-1]) / t}
 
 
 def _oracle_chain(args):
@@ -446,7 +528,8 @@ def main():
         del path, inp
         torch.cuda.empty_cache()
         rows = {}
-        for name, fn in (("diag_scalar_build_16x512", row_diag), ("warm30_seam_compose", row_warm),
+        for name, fn in (("diag_scalar_build_16x512", row_diag), ("gdn64k_build_plans", row_build_plans),
+                         ("kda_build_16x512", row_kda), ("warm30_seam_compose", row_warm),
                          ("cold100k_build", row_cold)):
             rows[name] = fn(dev)
             torch.cuda.empty_cache()
