@@ -566,8 +566,9 @@ __global__ __launch_bounds__((gdn_carry_waves<D, WITH_T, WITH_S>() + 4) * 64) vo
                 };
                 reset_x();
                 int ew = 0;
-                // T columns: rescale by an exact power of two so that max |X_T| lies in [0.5, 1)
-                // (f16 operands never underflow).  The NaN-propagating maximum maps to gfx950's
+                // T columns: rescale by an exact power of two once max |X_T| leaves [1/4, 2), back
+                // into [0.5, 1) (f16 operands never underflow; inside the window f16 keeps its full
+                // relative precision, so most chunks skip the pass).  The NaN-propagating maximum maps to gfx950's
                 // three-input maximum with |.| source modifiers (fmaxf would first canonicalise
                 // every input: twice the instructions)
                 auto renorm = [&] {
@@ -578,7 +579,8 @@ __global__ __launch_bounds__((gdn_carry_waves<D, WITH_T, WITH_S>() + 4) * 64) vo
                         for (int j = 0; j < 16; j += 2)
                             m = __builtin_elementwise_maximum(
                                 m, __builtin_elementwise_maximum(__builtin_fabsf(X[xb][j]), __builtin_fabsf(X[xb][j + 1])));
-                    const int e = exp2_of(wave_max(m));
+                    const int e0 = exp2_of(wave_max(m));   // m in [2^(e0-1), 2^e0)
+                    const int e = (e0 < -1 || e0 > 1) ? e0 : 0;
                     if (e != 0) {
 #pragma unroll
                         for (int xb = 0; xb < NB; ++xb)
@@ -937,12 +939,18 @@ __global__ __launch_bounds__((gdn_carry_waves<D, WITH_T, WITH_S>() + 4) * 64) vo
                             dst[ks].zero();
                     }
                 };
-                auto store_rows = [&](const Raw8<IN_BF16>* src, E* dst, int blk, float sc, int ln) {
+                // scaled: rows multiplied by sc (the key L2 normalisation)
+                auto store_rows = [&](const Raw8<IN_BF16>* src, E* dst, int blk, float sc, int ln, auto scaled) {
                     E* row = dst + (16 * blk + (ln & 15)) * RK + 8 * (ln >> 4);
 #pragma unroll
                     for (int ks = 0; ks < KS; ++ks) {
                         float x[8];
                         src[ks].get(x);
+                        if constexpr (!decltype(scaled)::value) {
+                            *reinterpret_cast<u32x4*>(row + 32 * ks) =
+                                u32x4{pk_f16(x[0], x[1]), pk_f16(x[2], x[3]), pk_f16(x[4], x[5]), pk_f16(x[6], x[7])};
+                            continue;
+                        }
                         *reinterpret_cast<u32x4*>(row + 32 * ks) =
                             u32x4{pk_f16(x[0] * sc, x[1] * sc), pk_f16(x[2] * sc, x[3] * sc),
                                   pk_f16(x[4] * sc, x[5] * sc), pk_f16(x[6] * sc, x[7] * sc)};
@@ -989,7 +997,11 @@ __global__ __launch_bounds__((gdn_carry_waves<D, WITH_T, WITH_S>() + 4) * 64) vo
                         ss += __shfl_xor(ss, 32, 64);
                         sc = ss > 0.f ? 1.f / sqrtf(ss) : 0.f;
                     }
-                    store_rows(pk, reinterpret_cast<E*>(sm + LY::Kn + (cc % 3) * LY::sz_K), pw, sc, ln);
+                    E* kt = reinterpret_cast<E*>(sm + LY::Kn + (cc % 3) * LY::sz_K);
+                    if (a.qk_l2norm)
+                        store_rows(pk, kt, pw, sc, ln, std::true_type{});
+                    else
+                        store_rows(pk, kt, pw, sc, ln, std::false_type{});
                     if (pw == GW) {
                         float* sGl = reinterpret_cast<float*>(sm + LY::Gv + (cc & 1) * (3 * 64 * 4));
                         float* Scc = reinterpret_cast<float*>(sm + LY::Sc + (cc % 3) * LY::sz_Sc);
@@ -1004,7 +1016,7 @@ __global__ __launch_bounds__((gdn_carry_waves<D, WITH_T, WITH_S>() + 4) * 64) vo
                     }
                 };
                 auto stage_v = [&](int cc, unsigned char* sm, int ln) {
-                    store_rows(pv, reinterpret_cast<E*>(sm + LY::Vn + (cc & 1) * LY::sz_K), pw, 1.f, ln);
+                    store_rows(pv, reinterpret_cast<E*>(sm + LY::Vn + (cc & 1) * LY::sz_K), pw, 1.f, ln, std::false_type{});
                 };
                 auto pbar = [&](int ln) {
                     pb_target += NP;
