@@ -191,8 +191,11 @@ typedef struct {
      * segment also gets o_t = S_t^T q_t, S_t the segment's zero-start state after
      * token t -- the segment's own prefill outputs, with T and S(C|0) as side
      * outputs.  q [B, N, h_k, d_k] in_dtype; o [B, N, h_v, d_v] out_dtype (tokens
-     * outside the covered ranges are not written).  Runs on the general chunk
-     * engine (one workgroup per (segment, chain)). */
+     * outside the covered ranges are not written).  With 16-bit inputs under the
+     * f16 plans it runs on the segment-build engine: with T_hat, a transition-only
+     * pass (f16 operands; hi/lo under HYPIC_PREC_F16_PRECISE_T or for segments longer
+     * than 2,048 tokens) followed by the state pass with outputs.  Float32 inputs or
+     * operands run the general chunk engine (one workgroup per (segment, chain)). */
     const void* q;
     void* o;
     hypic_dtype out_dtype;

@@ -174,8 +174,8 @@ hypic_status validate_build(const hypic_build_desc* d) {
         if (!aligned16(d->q)) return fail(HYPIC_ERR_INVALID_ARGUMENT, "build: q must be 16-byte aligned");
         if (d->out_dtype != HYPIC_F32 && d->out_dtype != HYPIC_BF16)
             return fail(HYPIC_ERR_INVALID_ARGUMENT, "build: unknown out_dtype %d", (int)d->out_dtype);
-        if (d->precision == HYPIC_PREC_F16_PRECISE_T)
-            return fail(HYPIC_ERR_UNSUPPORTED, "build: the output-fused build has no precise-T plan");
+        if (d->precision == HYPIC_PREC_F16_PRECISE_T && d->in_dtype != HYPIC_BF16)
+            return fail(HYPIC_ERR_UNSUPPORTED, "build: the output-fused build's precise-T plan needs 16-bit inputs");
     }
     if ((d->T_hat == nullptr) != (d->T_exp == nullptr))
         return fail(HYPIC_ERR_INVALID_ARGUMENT, "build: T_hat and T_exp must be both set or both NULL");
@@ -332,8 +332,9 @@ hypic_status hypic_segment_build(const hypic_build_desc* d, hypic_stream_t strea
     hipError_t e = fill_seg_table(tab, L, d->workspace, start, len, order, s);
     if (e != hipSuccess) return device_fail("build: segment table upload", e);
 
-    if (d->kind == HYPIC_DENSE_DELTA && d->o) {
-        // output-fused build: the general chunk engine from a zero state, with q
+    if (d->kind == HYPIC_DENSE_DELTA && d->o && (d->in_dtype != HYPIC_BF16 || build_prec_f32(d))) {
+        // output-fused build with float32 inputs or operands: the general chunk engine from a
+        // zero state, with q
         hypic::EngineArgs a{};
         a.n_batch = d->n_batch;
         a.n_tokens = d->n_tokens;
@@ -410,11 +411,21 @@ hypic_status hypic_segment_build(const hypic_build_desc* d, hypic_stream_t strea
             a.stream_stride = stride;
             a.stream_len = len[0];
         }
-        if (d->precision == HYPIC_PREC_F16_PRECISE_T && d->T_hat) {
-            // the precise plan: a transition-only pass with hi/lo operands, then the state pass
+        const bool with_o = d->o != nullptr;   // 16-bit inputs here (the others took the general engine)
+        if (with_o) {
+            a.q = d->q;
+            a.o = d->o;
+            a.out_bf16 = d->out_dtype == HYPIC_BF16;
+        }
+        if (d->T_hat && (with_o || d->precision == HYPIC_PREC_F16_PRECISE_T)) {
+            // T from a transition-only pass: hi/lo operands under the precise plan (and, with
+            // outputs, for the long segments AUTO gives hi/lo T operands), else single f16 operands;
+            // then the state pass (with outputs, if asked)
             hypic::EngineArgs t = a;
-            t.precise_T = 2;
+            t.precise_T = (d->precision == HYPIC_PREC_F16_PRECISE_T || a.precise_T == 1) ? 2 : 3;
             t.S_out = nullptr;
+            t.q = nullptr;
+            t.o = nullptr;
             e = hypic::launch_gdn_build(t, d->d_k, 0, grid, s);
             if (e != hipSuccess) return device_fail("build: transition pass launch", e);
             a.T_hat = nullptr;

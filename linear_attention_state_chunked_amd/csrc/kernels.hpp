@@ -67,6 +67,7 @@ struct EngineArgs {
     int* T_exp;
     void* o;
     int precise_T;               // 0: single f16 operands; 1: T columns with hi/lo X and Vn (with S);
+                                 // 3: transition-only pass, single f16 operands;
                                  // 2: transition-only pass, hi/lo Tg, W', X, Vn (no S columns)
     // stream mode (persistent grid, equal segments, 16-bit inputs): segment s covers tokens
     // [stream_start0 + s * stream_stride, ... + stream_len); each workgroup streams the chunks

@@ -268,38 +268,50 @@ def test_schedules_are_bitwise_identical(ragged_dense):
         assert torch.equal(o["T_exp"], outs[0]["T_exp"])
 
 
-@pytest.mark.parametrize("variant", ["fast", "no_T_skip_head", "precise_T"])
+@pytest.mark.parametrize("variant", ["fast", "no_T_skip_head", "precise_T", "outputs", "outputs_no_T_skip_head"])
 def test_stream_build_matches_per_task_build(gpu, variant):
     """Equal segments take the stream path (one persistent workgroup per compute unit running
     the chunks of its tasks back to back); the same segments built with one workgroup per task
     (a ragged last segment turns the stream off) must agree bit for bit, and a block from a
     workgroup's second task must match the oracle.  Variants: the fast plan; the plain state
-    pass (no T) with a skipped head; segments over 2,048 tokens (hi/lo T operands)."""
+    pass (no T) with a skipped head; segments over 2,048 tokens (hi/lo T operands); the
+    output-fused build (per-token outputs, with T from its own pass, and without T with a
+    skipped head)."""
     wl = WORKLOADS["gdn64k_bf16"]
     h_v = wl.h_v
     seg = 2112 if variant == "precise_T" else 256
-    skip = 8 if variant == "no_T_skip_head" else 0
-    with_T = variant != "no_T_skip_head"
+    skip = 8 if variant.endswith("skip_head") else 0
+    with_T = "no_T" not in variant
+    outputs = variant.startswith("outputs")
     lens_u = [seg] * 16                      # 512 tasks: two per workgroup on 256 compute units
     lens_r = [seg] * 15 + [seg - 1]
     dev, chains = _dense_inputs(wl, sum(lens_u), h_v)
     kw = dict(beta=dev["beta"], with_T=with_T, skip_head=skip)
+    if outputs:
+        kw.update(q=dev["q"], want_o=True, out_dtype=torch.float32)
     uni = H.hypic_segment_build(dev["k"], dev["v"], dev["log_alpha"], cu_of(lens_u), **kw)
     rag = H.hypic_segment_build(dev["k"], dev["v"], dev["log_alpha"], cu_of(lens_r), **kw)
     torch.cuda.synchronize()
     for key in ("S", "T_hat", "T_exp") if with_T else ("S",):
         assert torch.equal(uni[key][:15], rag[key][:15]), key
+    if outputs:
+        covered = np.concatenate([np.arange(i * seg + skip, (i + 1) * seg) for i in range(15)])
+        cov = torch.from_numpy(covered).cuda()
+        assert torch.equal(uni["o"][:, cov], rag["o"][:, cov]), "o"
     s, h = 12, 5
     lo, hi = s * seg + skip, (s + 1) * seg
     c = chains[h]
-    r = O.dense_recurrence(c["k"][lo:hi], c["v"][lo:hi], c["log_alpha"][lo:hi], c["beta"][lo:hi])
+    r = O.dense_recurrence(c["k"][lo:hi], c["v"][lo:hi], c["log_alpha"][lo:hi], c["beta"][lo:hi],
+                           q=c["q"][lo:hi] if outputs else None)
     e_S = float(O.rel_err(uni["S"][s, 0, h].cpu().numpy(), r["S"]))
-    e_T = 0.0
+    e_T = e_o = 0.0
     if with_T:
         e_T = float(O.rel_err_T("dense", uni["T_hat"][s, 0, h].cpu().numpy(), int(uni["T_exp"][s, 0, h]),
                                 r["T_hat"], r["T_exp"]))
-    print(f"stream build ({variant}), segment {s} head {h}: S {e_S:.2e}, T {e_T:.2e}")
-    assert e_S < TOL_BF16 and e_T < TOL_BF16
+    if outputs:
+        e_o = float(O.rel_err(uni["o"][0, lo:hi, h].cpu().numpy(), r["o"]))
+    print(f"stream build ({variant}), segment {s} head {h}: S {e_S:.2e}, T {e_T:.2e}, o {e_o:.2e}")
+    assert e_S < TOL_BF16 and e_T < TOL_BF16 and e_o < TOL_BF16
 
 
 def test_stream_build_d64_bf16(gpu):
