@@ -871,20 +871,35 @@ __global__ __launch_bounds__((gdn_carry_waves<D, WITH_T, WITH_S>() + 4) * 64) vo
                                 }
                                 const int valid = min(64, len - 64 * cc);
                                 row += 64 * cc;
-                                const long long obase = (row * a.h_v + h) * D + col0 + (ln & 31);
-                                const long long ostride = (long long)a.h_v * D;
+                                // a wave-uniform base and 32-bit per-store offsets; the full-chunk and
+                                // dtype branches are uniform
+                                auto store_o = [&](auto bf, auto full) {
+                                    constexpr bool BF = decltype(bf)::value;
+                                    constexpr unsigned ES = BF ? 2 : 4;
+                                    unsigned char* ob = reinterpret_cast<unsigned char*>(a.o) + ((row * a.h_v + h) * D + col0) * ES;
+                                    const unsigned rs = (unsigned)a.h_v * D * ES;    // bytes between token rows
+                                    const unsigned lo = (unsigned)(ln & 31) * ES + (unsigned)(4 * hf) * rs;
 #pragma unroll
-                                for (int mt = 0; mt < 2; ++mt)
+                                    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                                    for (int j = 0; j < 16; ++j) {
-                                        const int t = 32 * mt + 8 * (j >> 2) + 4 * hf + (j & 3);
-                                        if (t < valid) {
-                                            if (a.out_bf16)
-                                                reinterpret_cast<uint16_t*>(a.o)[obase + t * ostride] = f32_to_bf16(Oq[mt][j]);
-                                            else
-                                                reinterpret_cast<float*>(a.o)[obase + t * ostride] = Oq[mt][j];
+                                        for (int j = 0; j < 16; ++j) {
+                                            const int tc = 32 * mt + 8 * (j >> 2) + (j & 3);   // token minus 4 hf
+                                            if (decltype(full)::value || tc + 4 * hf < valid) {
+                                                unsigned char* dst = ob + (lo + (unsigned)tc * rs);
+                                                if constexpr (BF)   // round to nearest even (v_cvt_pk_bf16_f32)
+                                                    *reinterpret_cast<__bf16*>(dst) = (__bf16)Oq[mt][j];
+                                                else
+                                                    *reinterpret_cast<float*>(dst) = Oq[mt][j];
+                                            }
                                         }
-                                    }
+                                };
+                                if (a.out_bf16) {
+                                    if (valid == 64) store_o(std::true_type{}, std::true_type{});
+                                    else store_o(std::true_type{}, std::false_type{});
+                                } else {
+                                    if (valid == 64) store_o(std::false_type{}, std::true_type{});
+                                    else store_o(std::false_type{}, std::false_type{});
+                                }
                             }
                             scale_vn();
                             // X <- Gamma X + K^T Vn in steps (mt, st, xb): consecutive products on
@@ -1002,13 +1017,6 @@ __global__ __launch_bounds__((gdn_carry_waves<D, WITH_T, WITH_S>() + 4) * 64) vo
                         }
                         // W'(c+1) formed (its Tg reads done): the forming waves count it on the
                         // W' hand-off counter and, with T, on the Tg-reuse counter
-                        if constexpr (WO) {
-                            // Q of chunk c+1 into the one Q tile (its last reader, the Q S0 products of
-                            // chunk c, ran before the barrier); ordered before the carry of c+1 by the
-                            // W' hand-off below
-                            cq_stage(sm, ln);
-                            if (c + 2 < nc) cq_prefetch(c + 2, ln);
-                        }
                         if (TR || !WITH_T) count_arrival(sCnt + 1, ln);
                         if (WITH_T && TR && ln == 0)
                             __hip_atomic_fetch_add(sCnt + 2, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -1028,14 +1036,22 @@ __global__ __launch_bounds__((gdn_carry_waves<D, WITH_T, WITH_S>() + 4) * 64) vo
                                 for (int mt = 0; mt < 2; ++mt)
                                     Vn[mt] = OpF16::mma(colfrag_nat(TgA, RT, 0, 32 * mt, kk, ln), fb, Vn[mt]);
                             }
+                            if constexpr (WO) {
+                                // Q of chunk c+1 into the one Q tile (its last reader, the Q S0 products
+                                // of chunk c, ran before the barrier); every S wave waits for this
+                                // counter (below) before its next carry
+                                cq_stage(sm, ln);
+                                if (c + 2 < nc) cq_prefetch(c + 2, ln);
+                            }
                             // Tg(c+1) consumed: the preparation of chunk c+2 may overwrite it
                             count_arrival(sCnt + 2, ln);
                             if constexpr (VS) {
-                                // V of chunk c+2 into the buffer that held V(c) (read by U(c),
-                                // formed before the previous barrier), then the loads of c+3
+                                // V of chunk c+2 into the buffer that held V(c) (read by U(c), formed
+                                // before the previous barrier), then the loads of c+3.  With outputs
+                                // there is one V buffer: first every S wave's U(c+1) has read it (and
+                                // staged its rows of Q(c+1))
+                                if constexpr (WO) wait_count(sCnt + 2, NC * (c + 2));
                                 if (c + 2 < nc) {
-                                    // one V buffer with outputs: every S wave's U(c+1) has read it
-                                    if constexpr (WO) wait_count(sCnt + 2, NC * (c + 2));
                                     cv_stage(c + 2, sm, ln);
                                     if (c + 3 < nc) cv_prefetch(c + 3, ln);
                                 }
