@@ -78,13 +78,8 @@ __device__ __forceinline__ floatx16 zero16() {
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-// round-to-nearest-even float -> bf16 (finite inputs; NaN kept quiet)
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
+// float32 -> bf16 bits, round to nearest even (gfx950's v_cvt_pk_bf16_f32; NaN stays NaN)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 // load 8 consecutive input elements (bf16 or f32) as floats; p must be 16-byte aligned
 // for bf16 and 32-byte aligned for f32.
