@@ -17,7 +17,8 @@ its re-rotation to new offsets; the per-channel gated delta (KDA) build; the war
 segments x 960 chains with prefix states, and the same path fused into one pass);
 and the cold 100k-token 30-layer build in LPT, round-robin and natural order, with
 the precise-T plan and the single sequential pass beside it.  Each carries its
-algorithmic bytes or flops and the fraction of the matching MI355X peak.
+algorithmic bytes or flops and the fraction of the matching MI355X peak; each row's
+launches are timed one by one after a 512 MiB cache flush, so they read from HBM.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-rows]
   python bench.py --calibrate-copy      (a plain 1 GiB device copy, for HBM counters)
@@ -170,13 +171,34 @@ def time_events(fn, reps, stream):
     return [e0.elapsed_time(e1) * 1e-3 for e0, e1 in evs]
 
 
+_FLUSH = None
+
+
+def _flush_caches():
+    """Write a 512 MiB buffer: evicts the L2 caches and the 256 MB MALL, so the next launch
+    reads its inputs from HBM."""
+    import torch
+
+    global _FLUSH
+    if _FLUSH is None:
+        _FLUSH = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
+    _FLUSH.fill_(1)
+
+
 def _median_time(fn, reps=5, warm=2):
+    """Median of `reps` launches, each timed with HIP events after a cache flush (outside the
+    events), so every row reads its inputs from HBM."""
     import torch
 
     for _ in range(warm):
         fn()
     torch.cuda.synchronize()
-    return float(np.median(time_events(fn, reps, torch.cuda.current_stream())))
+    stream = torch.cuda.current_stream()
+    ts = []
+    for _ in range(reps):
+        _flush_caches()
+        ts += time_events(fn, 1, stream)
+    return float(np.median(ts))
 
 
 def _hbm(nbytes, t):
