@@ -305,11 +305,17 @@ __device__ __forceinline__ HL4 ld_a(const _Float16* t, int lane) {
 // of (I + L)^-1 in accumulator layout, into the token-column-major Tg tiles (row stride 72);
 // bc, bgc: beta and beta gamma of this lane's column token 16 a + (lane & 15).
 __device__ __forceinline__ void st_tg(_Float16* TgAT, _Float16* TgGT, _Float16* TgGlT, bool pt, floatx4 v, int b,
-                                      int a, int lane, float bc, float bgc) {
+                                      int a, int lane, float bc, float bgc, const float* rr) {
     const int tc = 16 * a + (lane & 15);
     const int o = tc * (64 + 8) + 16 * b + 4 * (lane >> 4);
-    st4h(TgAT + o, __builtin_bit_cast(halfx4, u32x2{pk_f16(v[0] * bc, v[1] * bc), pk_f16(v[2] * bc, v[3] * bc)}));
-    const floatx4 gv = v * bgc;
+    floatx4 vr = v;
+    if (rr) {
+        // row factors Gamma / gamma_i of the lane's four row tokens
+        const float4 r = *reinterpret_cast<const float4*>(rr + 16 * b + 4 * (lane >> 4));
+        vr = v * floatx4{r.x, r.y, r.z, r.w};
+    }
+    st4h(TgAT + o, __builtin_bit_cast(halfx4, u32x2{pk_f16(vr[0] * bc, vr[1] * bc), pk_f16(vr[2] * bc, vr[3] * bc)}));
+    const floatx4 gv = vr * bgc;
     const HL4 x = split4v(gv);
     st4h(TgGT + o, x.hi);
     if (pt) st4h(TgGlT + o, x.lo);
@@ -334,8 +340,63 @@ __device__ __forceinline__ floatx4 inv16(floatx4 n, floatx4 nt, int lane) {
     return mm16(P8T, split4v(r), r);                                          // (I + N^8) ...
 }
 
-// Chunk-local UT transform, wave pw of four owning token block pw: from the staged K rows
-// (f16, row stride GLayout<D>::RK) and the gate vectors (G log2 e, beta, beta gamma),
+// The off-diagonal gram blocks of wave pw: rows block rb[i], columns block cb[i].
+__device__ __forceinline__ void gram_blocks_of(int pw, int& n_off, int (&rb)[2], int (&cb)[2]) {
+    n_off = (pw == 0 || pw == 2) ? 2 : 1;
+    rb[0] = rb[1] = 3;
+    cb[0] = 0;
+    cb[1] = 1;
+    if (pw == 1) { rb[0] = 1; cb[0] = 0; }
+    if (pw == 2) { rb[0] = 2; cb[0] = 0; rb[1] = 2; cb[1] = 1; }
+    if (pw == 3) { rb[0] = 3; cb[0] = 2; }
+}
+
+// Gram blocks of wave pw from the staged K rows of a chunk: the diagonal block (pw, pw) and the
+// off-diagonal blocks G_{rb[i], cb[i]} = K_rb K_cb^T in accumulator layout (rows: tokens of the
+// later block rb, columns: block cb).  Each K block is read once.
+template <int D>
+__device__ __forceinline__ void gram_blocks(const _Float16* Kn1, int pw, int ln, floatx4& gd, floatx4 (&gt)[2]) {
+    constexpr int KS = D / 32, RK = GLayout<D>::RK;
+    const int g = ln >> 4, cl = ln & 15;
+    auto krow = [&](int blk, int ks) { return ld8(Kn1 + (16 * blk + cl) * RK + 32 * ks + 8 * g); };
+    auto mma32 = [](halfx8 x, halfx8 y, floatx4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(x, y, c, 0, 0, 0); };
+    int n_off, rb[2], cb[2];
+    gram_blocks_of(pw, n_off, rb, cb);
+    halfx8 ka[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) ka[ks] = krow(pw, ks);
+    gd = zero4();
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) gd = mma32(ka[ks], ka[ks], gd);
+    gt[0] = gt[1] = zero4();
+    {
+        // the row block of the off-diagonal products is this wave's own (ka) except for wave 0
+        // (block 3, with block 0 = ka as the first column block): each block is read once
+        halfx8 kr[KS], kc[KS];
+        if (pw == 0) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                kr[ks] = krow(3, ks);
+                kc[ks] = ka[ks];
+            }
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                kr[ks] = ka[ks];
+                kc[ks] = krow(cb[0], ks);
+            }
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) gt[0] = mma32(kr[ks], kc[ks], gt[0]);
+        if (n_off > 1) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) gt[1] = mma32(kr[ks], krow(cb[1], ks), gt[1]);
+        }
+    }
+}
+
+// Chunk-local UT transform, wave pw of four owning token block pw: from the gram blocks of
+// gram_blocks (gd, gt) and the gate vectors (G log2 e, beta, beta gamma),
 // L = strictly-lower(beta_i e^{G_i - G_j} K K^T) and Tg = (I + L)^-1 diag(beta), written as
 // its ten lower 16x16 blocks.  With D_b = (I + L_bb)^-1 and Inv the blocks of (I + L)^-1:
 //   Inv_10 = -D_1 L_10 D_0,  Inv_32 = -D_3 L_32 D_2
@@ -343,24 +404,25 @@ __device__ __forceinline__ floatx4 inv16(floatx4 n, floatx4 nt, int lane) {
 //   Inv_2a = -D_2 Q_2a,  Inv_3a = -(Inv_32 Q_2a + D_3 Q_3a)
 // Phase 1, all four waves in parallel: the diagonal gram block (pw, pw) and D_pw, and the
 // off-diagonal blocks of L (0: L_30, L_31; 1: L_10; 2: L_20, L_21; 3: L_32).  Every D_b and
-// L_ba goes to an exchange slot; side() runs while the gram products are in flight, tg_wait()
+// L_ba goes to an exchange slot; side() (staging of later chunks) runs first, tg_wait()
 // holds the first Tg write until the previous Tg has been consumed.  One barrier (pbar) among
 // the four waves, then phase 2 without further hand-offs: wave 1 forms Inv_10, wave 2 block
 // row 2, wave 0 Inv_32 and Inv_31, wave 3 Inv_30; each recomputes the small shared factors
 // it needs (Inv_10, Inv_32, Q) instead of waiting for another wave's.
 template <int D, class Bar, class Wait, class Side>
-__device__ __forceinline__ void ut_blocks(const _Float16* Kn1, const float* sGl, const float* sBeta,
-                                          const float* sBG, _Float16* XB, _Float16* TgAT, _Float16* TgGT,
-                                          _Float16* TgGlT, bool pt, int pw, int ln, Bar&& pbar, Wait&& tg_wait,
-                                          Side&& side) {
-    constexpr int KS = D / 32, RK = GLayout<D>::RK;
+__device__ __forceinline__ void ut_blocks(const floatx4& gd, const floatx4 (&gt)[2], const float* sGl,
+                                          const float* sBeta, const float* sBG, _Float16* XB, _Float16* TgAT,
+                                          _Float16* TgGT, _Float16* TgGlT, bool pt, const float* rr, int pw, int ln,
+                                          Bar&& pbar, Wait&& tg_wait, Side&& side) {
     const int g = ln >> 4, cl = ln & 15;
     auto slot = [&](int i) { return XB + i * kXT; };
     // exchange slots: D_b in slot b; L_10, L_20, L_21, L_30, L_31, L_32 in slots 4..9; slots 10
     // and 11 are private to waves 0 and 3 (Inv_32 turned into an A operand)
     auto lslot = [](int rb, int cb) { return rb == 1 ? 4 : rb == 2 ? 5 + cb : rb == 3 ? (cb < 2 ? 7 + cb : 9) : -1; };
-    auto krow = [&](int blk, int ks) { return ld8(Kn1 + (16 * blk + cl) * RK + 32 * ks + 8 * g); };
-    auto mma32 = [](halfx8 x, halfx8 y, floatx4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(x, y, c, 0, 0, 0); };
+    int n_off, rb[2], cb[2];
+    gram_blocks_of(pw, n_off, rb, cb);
+    // independent work (staging of a later chunk) first
+    side();
     // beta and beta gamma of this lane's column token in each block
     float bcol[4], bgcol[4];
 #pragma unroll
@@ -368,27 +430,6 @@ __device__ __forceinline__ void ut_blocks(const _Float16* Kn1, const float* sGl,
         bcol[a] = sBeta[16 * a + cl];
         bgcol[a] = sBG[16 * a + cl];
     }
-    // ---- gram: diagonal block (pw, pw); off-diagonal blocks G_{rb[i], cb[i]} = K_rb K_cb^T
-    //      in accumulator layout (rows: tokens of the later block rb, columns: block cb)
-    halfx8 ka[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) ka[ks] = krow(pw, ks);
-    floatx4 gd = zero4();
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) gd = mma32(ka[ks], ka[ks], gd);
-    const int n_off = (pw == 0 || pw == 2) ? 2 : 1;
-    int rb[2] = {3, 3}, cb[2] = {0, 1};
-    if (pw == 1) { rb[0] = 1; cb[0] = 0; }
-    if (pw == 2) { rb[0] = 2; cb[0] = 0; rb[1] = 2; cb[1] = 1; }
-    if (pw == 3) { rb[0] = 3; cb[0] = 2; }
-    floatx4 gt[2] = {zero4(), zero4()};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        gt[0] = mma32(krow(rb[0], ks), krow(cb[0], ks), gt[0]);
-        if (n_off > 1) gt[1] = mma32(krow(rb[1], ks), krow(cb[1], ks), gt[1]);
-    }
-    // independent work (staging of a later chunk) while the gram products are in flight
-    side();
     // ---- gate factors: L_{rb, cb}[r][c] = beta_r e^{G_r - G_c} G[r][c] (r later than c);
     //      N = -L_{pw,pw} and N^T for the diagonal block
 #pragma unroll
@@ -422,7 +463,7 @@ __device__ __forceinline__ void ut_blocks(const _Float16* Kn1, const float* sGl,
     const floatx4 Dm = inv16(n, nt, ln);
     st_cm(slot(pw), Dm, ln);
     tg_wait();
-    st_tg(TgAT, TgGT, TgGlT, pt, Dm, pw, pw, ln, bcol[pw], bgcol[pw]);
+    st_tg(TgAT, TgGT, TgGlT, pt, Dm, pw, pw, ln, bcol[pw], bgcol[pw], rr);
     pbar(ln);
     // ---- phase 2.  A transposing read (ld_a) of a slot gives that tile as an A operand, a
     //      plain read (ld_b) as a B operand; an accumulator tile is a B operand as it is.
@@ -432,17 +473,17 @@ __device__ __forceinline__ void ut_blocks(const _Float16* Kn1, const float* sGl,
         const HL4 L21a = ld_a(slot(6), ln), L31a = ld_a(slot(8), ln), L32a = ld_a(slot(9), ln);
         const floatx4 inv32 = -mm16(D3a, split4v(mm16(L32a, D2b, zero4())), zero4());
         st_cm(slot(10), inv32, ln);
-        st_tg(TgAT, TgGT, TgGlT, pt, inv32, 3, 2, ln, bcol[2], bgcol[2]);
+        st_tg(TgAT, TgGT, TgGlT, pt, inv32, 3, 2, ln, bcol[2], bgcol[2], rr);
         const floatx4 q21 = mm16(L21a, D1b, zero4()), q31 = mm16(L31a, D1b, zero4());
         const floatx4 r1 = mm16(ld_a(slot(10), ln), split4v(q21), mm16(D3a, split4v(q31), zero4()));
-        st_tg(TgAT, TgGT, TgGlT, pt, -r1, 3, 1, ln, bcol[1], bgcol[1]);
+        st_tg(TgAT, TgGT, TgGlT, pt, -r1, 3, 1, ln, bcol[1], bgcol[1], rr);
         return;
     }
     const HL4 D0b = ld_b(slot(0), ln), D1a = ld_a(slot(1), ln), L10a = ld_a(slot(4), ln);
     // Inv_10 = -D_1 (L_10 D_0)
     const floatx4 inv10 = -mm16(D1a, split4v(mm16(L10a, D0b, zero4())), zero4());
     if (pw == 1) {
-        st_tg(TgAT, TgGT, TgGlT, pt, inv10, 1, 0, ln, bcol[0], bgcol[0]);
+        st_tg(TgAT, TgGT, TgGlT, pt, inv10, 1, 0, ln, bcol[0], bgcol[0], rr);
         return;
     }
     const HL4 L20a = ld_a(slot(5), ln), L21a = ld_a(slot(6), ln);
@@ -452,8 +493,8 @@ __device__ __forceinline__ void ut_blocks(const _Float16* Kn1, const float* sGl,
     if (pw == 2) {
         const HL4 D1b = ld_b(slot(1), ln), D2a = ld_a(slot(2), ln);
         const floatx4 q21 = mm16(L21a, D1b, zero4());
-        st_tg(TgAT, TgGT, TgGlT, pt, -mm16(D2a, split4v(q21), zero4()), 2, 1, ln, bcol[1], bgcol[1]);
-        st_tg(TgAT, TgGT, TgGlT, pt, -mm16(D2a, split4v(q20), zero4()), 2, 0, ln, bcol[0], bgcol[0]);
+        st_tg(TgAT, TgGT, TgGlT, pt, -mm16(D2a, split4v(q21), zero4()), 2, 1, ln, bcol[1], bgcol[1], rr);
+        st_tg(TgAT, TgGT, TgGlT, pt, -mm16(D2a, split4v(q20), zero4()), 2, 0, ln, bcol[0], bgcol[0], rr);
         return;
     }
     // wave 3: Inv_30 = -(Inv_32 Q_20 + D_3 Q_30), Q_30 = L_30 D_0 + L_31 Inv_10
@@ -463,7 +504,7 @@ __device__ __forceinline__ void ut_blocks(const _Float16* Kn1, const float* sGl,
     st_cm(slot(11), inv32, ln);
     const floatx4 q30 = mm16(L31a, I10, mm16(L30a, D0b, zero4()));
     const floatx4 r0 = mm16(ld_a(slot(11), ln), split4v(q20), mm16(D3a, split4v(q30), zero4()));
-    st_tg(TgAT, TgGT, TgGlT, pt, -r0, 3, 0, ln, bcol[0], bgcol[0]);
+    st_tg(TgAT, TgGT, TgGlT, pt, -r0, 3, 0, ln, bcol[0], bgcol[0], rr);
 }
 
 // Carry waves of a variant: D/32 per column kind present (T columns, S columns).
@@ -496,6 +537,9 @@ __global__ __launch_bounds__((gdn_carry_waves<D, WITH_T, WITH_S>() + 4) * 64) vo
     constexpr bool WLO = PT && !WITH_S;         // W' as hi/lo fragments (low half where V would be)
                                                 //     in their idle tail before the barrier
     constexpr int NT = (NC + NP) * 64;
+    // the row factors Gamma / gamma_i of Vn are folded into the Tg tiles (so into U and W'); the
+    // output variant keeps U - W' S0 unscaled for its outputs and scales Vn itself
+    constexpr bool FOLD_R = !WO;
     constexpr int RK = LY::RK, RT = LY::RT;
 
     __shared__ __align__(16) unsigned char smem[LY::total];
@@ -575,21 +619,32 @@ __global__ __launch_bounds__((gdn_carry_waves<D, WITH_T, WITH_S>() + 4) * 64) vo
                 };
                 reset_x();
                 int ew = 0;
-                // T columns: rescale by an exact power of two once max |X_T| leaves [1/4, 2), back
-                // into [0.5, 1) (f16 operands never underflow; inside the window f16 keeps its full
-                // relative precision, so most chunks skip the pass).  The NaN-propagating maximum maps to gfx950's
-                // three-input maximum with |.| source modifiers (fmaxf would first canonicalise
-                // every input: twice the instructions)
+                // T columns: rescale by an exact power of two once max |X_T| leaves [2^-8, 2) (the
+                // hi/lo operands of the precise plan: [1/4, 2)), back into [0.5, 1).  The f16 operands
+                // never underflow: an entry 2^-6 below the column maximum or more becomes an f16
+                // subnormal, with an absolute error under 2^-17 of that maximum.  A chunk decaying
+                // T by 2^-4 rescales every other chunk instead of every chunk.  The NaN-propagating
+                // maximum maps to gfx950's three-input maximum with |.| source modifiers (fmaxf
+                // would first canonicalise every input: twice the instructions)
                 auto renorm = [&] {
+                    // max |X_T| of this lane as a tree of three-input maxima (22 + 8 + 3 + 1 for
+                    // NB = 4): the first level takes |.| as source modifiers
+                    constexpr int NX = 16 * NB, N1 = (NX + 2) / 3, N2 = (N1 + 2) / 3;
+                    auto mx3 = [](float a, float b, float c) {
+                        return __builtin_elementwise_maximum(a, __builtin_elementwise_maximum(b, c));
+                    };
+                    auto xa = [&](int i) { return i < NX ? __builtin_fabsf(X[i >> 4][i & 15]) : 0.f; };
+                    float m1[N1], m2[N2];
+#pragma unroll
+                    for (int i = 0; i < N1; ++i) m1[i] = mx3(xa(3 * i), xa(3 * i + 1), xa(3 * i + 2));
+#pragma unroll
+                    for (int i = 0; i < N2; ++i)
+                        m2[i] = mx3(m1[3 * i], 3 * i + 1 < N1 ? m1[3 * i + 1] : 0.f, 3 * i + 2 < N1 ? m1[3 * i + 2] : 0.f);
                     float m = 0.f;
 #pragma unroll
-                    for (int xb = 0; xb < NB; ++xb)
-#pragma unroll
-                        for (int j = 0; j < 16; j += 2)
-                            m = __builtin_elementwise_maximum(
-                                m, __builtin_elementwise_maximum(__builtin_fabsf(X[xb][j]), __builtin_fabsf(X[xb][j + 1])));
+                    for (int i = 0; i < N2; i += 2) m = mx3(m, m2[i], i + 1 < N2 ? m2[i + 1] : 0.f);
                     const int e0 = exp2_of(wave_max(m));   // m in [2^(e0-1), 2^e0)
-                    const int e = (e0 < -1 || e0 > 1) ? e0 : 0;
+                    const int e = (e0 < (PT ? -1 : -7) || e0 > 1) ? e0 : 0;
                     if (e != 0) {
 #pragma unroll
                         for (int xb = 0; xb < NB; ++xb)
@@ -792,7 +847,7 @@ __global__ __launch_bounds__((gdn_carry_waves<D, WITH_T, WITH_S>() + 4) * 64) vo
                                     }
                                     __builtin_amdgcn_sched_barrier(0);
                                 }
-                            scale_vn();
+                            if constexpr (!FOLD_R) scale_vn();
 #pragma unroll
                             for (int xb = 0; xb < NB; ++xb) {
 #pragma unroll
@@ -901,7 +956,7 @@ __global__ __launch_bounds__((gdn_carry_waves<D, WITH_T, WITH_S>() + 4) * 64) vo
                                     else store_o(std::false_type{}, std::false_type{});
                                 }
                             }
-                            scale_vn();
+                            if constexpr (!FOLD_R) scale_vn();
                             // X <- Gamma X + K^T Vn in steps (mt, st, xb): consecutive products on
                             // different X blocks, each Vn operand converted once for its NB steps,
                             // the K column fragments read two steps ahead
@@ -946,7 +1001,23 @@ __global__ __launch_bounds__((gdn_carry_waves<D, WITH_T, WITH_S>() + 4) * 64) vo
                     // STREAM: the last chunk of a task ends here; exponent slots alternate by task
                     const bool task_end = STREAM && c >= 0 && (c + 1) % ncT == 0;
                     if (task_end && TR && lane == 0) sEw[4 * ((c / ncT) & 1) + wave] = ew;
+                    // the K fragments of W'(c+1) are read before the barrier, off the post-barrier
+                    // burst of LDS reads: K(c+1) was staged before the previous barrier (K(0) only
+                    // after this one)
+                    halfx8 fa_next[4];
+                    auto load_fa = [&] {
+                        const E* Kn1p = reinterpret_cast<const E*>(sm + LY::Kn + pn3 * LY::sz_K);
+#pragma unroll
+                        for (int kk = 0; kk < 4; ++kk) fa_next[kk] = colfrag_nat(Kn1p, RK, 0, 32 * wave, kk, ln);
+                    };
+                    constexpr bool FA = !PT;
+                    if constexpr (FA) {
+                        if ((TR || !WITH_T) && c >= 0 && c + 1 < nc) load_fa();
+                    }
                     __syncthreads();  // preparation of chunk c+1 is complete
+                    if constexpr (FA) {
+                        if ((TR || !WITH_T) && c < 0 && nc > 0) load_fa();
+                    }
                     if (task_end) {
                         const int k = c / ncT;
                         write_out(seg + k * dseg, chain_off, sEw + 4 * (k & 1));
@@ -999,12 +1070,10 @@ __global__ __launch_bounds__((gdn_carry_waves<D, WITH_T, WITH_S>() + 4) * 64) vo
                                 }
                             } else {
                                 // the fragments of the first half in flight before the products
-                                halfx8 fa[4], fb[4];
+                                halfx8 fb[4];
+                                const halfx8* fa = fa_next;
 #pragma unroll
-                                for (int kk = 0; kk < 4; ++kk) {
-                                    fa[kk] = colfrag_nat(Kn1, RK, 0, 32 * dt, kk, ln);
-                                    fb[kk] = colfrag_nat(TgG, RT, 0, 0, kk, ln);
-                                }
+                                for (int kk = 0; kk < 4; ++kk) fb[kk] = colfrag_nat(TgG, RT, 0, 0, kk, ln);
 #pragma unroll
                                 for (int mt = 0; mt < 2; ++mt) {
                                     floatx16 acc = zero16();
@@ -1253,6 +1322,9 @@ __global__ __launch_bounds__((gdn_carry_waves<D, WITH_T, WITH_S>() + 4) * 64) vo
                 // the preparation waves are the critical path of every chunk: let their few
                 // instructions issue ahead of the carry waves' (matrix-core bound) stream
                 __builtin_amdgcn_s_setprio(3);
+                // gram of the next chunk to solve, formed before the workgroup barrier that precedes
+                // its solve (its K rows are staged, and visible to all four waves, one barrier earlier)
+                floatx4 gd, gt[2];
                 if (nc > 0) {
                     prefetch_kg(0, lane);
                     if constexpr (PV) prefetch_v(0, lane);
@@ -1260,6 +1332,7 @@ __global__ __launch_bounds__((gdn_carry_waves<D, WITH_T, WITH_S>() + 4) * 64) vo
                     stage_kg(0, smem, lane);
                     if (nc > 1) prefetch_kg(1, lane);
                     pbar(lane);
+                    gram_blocks<D>(reinterpret_cast<const E*>(smem + LY::Kn), pw, lane, gd, gt);
                 }
                 for (int c = -1; c < nc; ++c) {
                     int lz = 0, lzv = 0;
@@ -1268,7 +1341,6 @@ __global__ __launch_bounds__((gdn_carry_waves<D, WITH_T, WITH_S>() + 4) * 64) vo
                     unsigned char* sm = smem + lz;
                     const int ln = lane + lzv;
                     if (c + 1 < nc) {
-                        const E* Kn1 = reinterpret_cast<const E*>(sm + LY::Kn + ((c + 1) % 3) * LY::sz_K);
                         E* XB = reinterpret_cast<E*>(sm + LY::XB);
                         E* TgAT = reinterpret_cast<E*>(sm + LY::TgA);
                         E* TgGT = reinterpret_cast<E*>(sm + LY::TgG);
@@ -1276,7 +1348,9 @@ __global__ __launch_bounds__((gdn_carry_waves<D, WITH_T, WITH_S>() + 4) * 64) vo
                         const float* sGl = reinterpret_cast<const float*>(sm + LY::Gv + ((c + 1) & 1) * (3 * 64 * 4));
                         // solve chunk c+1 (K and gates staged before the last workgroup barrier);
                         // meanwhile stage K and gates of chunk c+2 (buffers last read before it)
-                        ut_blocks<D>(Kn1, sGl, sGl + 64, sGl + 128, XB, TgAT, TgGT, TgGlT, PT, pw, ln, pbar,
+                        ut_blocks<D>(gd, gt, sGl, sGl + 64, sGl + 128, XB, TgAT, TgGT, TgGlT, PT,
+                                     FOLD_R ? reinterpret_cast<const float*>(sm + LY::Sc + ((c + 1) % 3) * LY::sz_Sc) : nullptr,
+                                     pw, ln, pbar,
                                      [&] {
                                          // Tg(c+1) overwrites Tg(c): wait until the carry waves
                                          // formed W'(c) and U(c)
@@ -1299,6 +1373,11 @@ __global__ __launch_bounds__((gdn_carry_waves<D, WITH_T, WITH_S>() + 4) * 64) vo
                             form_m(c + 1, sm, ln);
                             if (c + 2 < nc) prefetch_q(c + 2, ln);
                         }
+                    }
+                    // gram of chunk c+2: its K rows were staged before this chunk's prep barrier
+                    if (c + 2 < nc) {
+                        const E* Kn2 = reinterpret_cast<const E*>(sm + LY::Kn + ((c + 2) % 3) * LY::sz_K);
+                        gram_blocks<D>(Kn2, pw, ln, gd, gt);
                     }
                     __syncthreads();  // chunk c+1 prepared
                 }
