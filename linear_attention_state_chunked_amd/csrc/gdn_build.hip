@@ -1061,7 +1061,7 @@ __global__ __launch_bounds__((gdn_carry_waves<D, WITH_T, WITH_S>() + 4) * 64) vo
                                 for (int mt = 0; mt < 2; ++mt) {
                                     floatx16 acc = zero16();
 #pragma unroll
-                                    for (int kk = 0; kk < 4; ++kk) {
+                                    for (int kk = 0; kk < 2 + 2 * mt; ++kk) {   // Tg lower triangular
                                         const halfx8 fa = colfrag_nat(Kn1, RK, 0, 32 * dt, kk, ln);
                                         acc = OpF16::mma(fa, colfrag_nat(TgGl, RT, 0, 32 * mt, kk, ln), acc);
                                         acc = OpF16::mma(fa, colfrag_nat(TgG, RT, 0, 32 * mt, kk, ln), acc);
@@ -1069,16 +1069,17 @@ __global__ __launch_bounds__((gdn_carry_waves<D, WITH_T, WITH_S>() + 4) * 64) vo
                                     store_w(mt, acc);
                                 }
                             } else {
-                                // the fragments of the first half in flight before the products
-                                halfx8 fb[4];
+                                // the fragments of the first half in flight before the products; Tg is
+                                // lower triangular, so the first 32 tokens take keys 0..31 only
+                                halfx8 fb[2];
                                 const halfx8* fa = fa_next;
 #pragma unroll
-                                for (int kk = 0; kk < 4; ++kk) fb[kk] = colfrag_nat(TgG, RT, 0, 0, kk, ln);
+                                for (int kk = 0; kk < 2; ++kk) fb[kk] = colfrag_nat(TgG, RT, 0, 0, kk, ln);
 #pragma unroll
                                 for (int mt = 0; mt < 2; ++mt) {
                                     floatx16 acc = zero16();
 #pragma unroll
-                                    for (int kk = 0; kk < 4; ++kk)
+                                    for (int kk = 0; kk < 2 + 2 * mt; ++kk)
                                         acc = OpF16::mma(fa[kk], mt == 0 ? fb[kk] : colfrag_nat(TgG, RT, 0, 32, kk, ln), acc);
                                     store_w(mt, acc);
                                 }
@@ -1102,8 +1103,11 @@ __global__ __launch_bounds__((gdn_carry_waves<D, WITH_T, WITH_S>() + 4) * 64) vo
                             for (int kk = 0; kk < 4; ++kk) {
                                 const halfx8 fb = colfrag_nat(Vc, RK, 0, col0, kk, ln);
 #pragma unroll
-                                for (int mt = 0; mt < 2; ++mt)
+                                for (int mt = 0; mt < 2; ++mt) {
+                                    // Tg lower triangular: tokens 0..31 take values 0..31 only
+                                    if (mt == 0 && kk >= 2) continue;
                                     Vn[mt] = OpF16::mma(colfrag_nat(TgA, RT, 0, 32 * mt, kk, ln), fb, Vn[mt]);
+                                }
                             }
                             if constexpr (WO) {
                                 // Q of chunk c+1 into the one Q tile (its last reader, the Q S0 products
