@@ -322,7 +322,8 @@ def row_warm(dev):
 def row_cold(dev):
     """Cold 100,000-token request, 30 layers x 32 value heads (16 key heads), 20
     segments of uneven length: the build of all 19,200 segment-heads in LPT,
-    round-robin and natural task order, and the single sequential pass (no T)."""
+    round-robin and natural task order, and the single sequential pass (no T); then one
+    layer alone (640 segment-heads), where the task order and segment parallelism matter."""
     import torch
 
     from linear_attention_state_chunked_amd import api as H
@@ -359,6 +360,25 @@ def row_cold(dev):
     E = (out["T_hat"].view(n_seg, L * hv, d, d), out["T_exp"].view(n_seg, L * hv), out["S"].view(n_seg, L * hv, d, d))
     tc = _median_time(lambda: H.hypic_compose(*E, mode="scan"), reps=3)
     res["compose_scan"] = dict(_hbm(n_seg * L * hv * (2 * d * d * 4 + 4), tc), us_per_segment=tc * 1e6 / n_seg)
+    # one layer of the same request: 640 segment-heads of 512..8192 tokens on 256 compute units,
+    # where the task order decides the makespan, against the single pass over the whole prompt
+    # (32 chains: a long sequence alone cannot fill the device)
+    one = {key: torch.empty((n_seg, 1) + tuple(t.shape[2:]), dtype=t.dtype, device=dev) for key, t in out.items()}
+    k1, v1, la1, b1 = k[:1], v[:1], la[:1], beta[:1]
+    res1 = {}
+    for sched in ("lpt", "rr", "natural"):
+        t = _median_time(lambda: H.hypic_segment_build(k1, v1, la1, cu, b1, schedule=sched, out=one), reps=3)
+        res1[sched] = _mfma(flops / L, t)
+    # the same segment lengths in increasing order over the same tokens (the longest last): the
+    # order LPT protects against; the natural order then starts the longest tasks last
+    cu_asc = np.concatenate([[0], np.cumsum(sorted(lens))]).astype(np.int64)
+    t = _median_time(lambda: H.hypic_segment_build(k1, v1, la1, cu_asc, b1, schedule="natural", out=one), reps=3)
+    res1["natural_ascending"] = _mfma(flops / L, t)
+    t = _median_time(lambda: H.hypic_segment_build(k1, v1, la1, cu_asc, b1, schedule="lpt", out=one), reps=3)
+    res1["lpt_ascending"] = _mfma(flops / L, t)
+    t = _median_time(lambda: H.hypic_segment_build(k1, v1, la1, [0, N], b1, with_T=False), reps=3)
+    res1["single_pass_no_T"] = _mfma(single_flops / L, t)
+    res["one_layer"] = res1
     return res
 
 
