@@ -498,10 +498,10 @@ hypic_status hypic_seam_widths(const int64_t* seg_lens, int32_t n, double sink, 
 /* ------------------------------------------------------------------------------------
  * hypic_device_status -- device-side invariant check.
  *
- * Synchronises the current device, then reads and clears its sticky status word.  The
- * dense build's waves hand work to each other through bounded waits on LDS counters; a
- * wait that runs out (a hand-off that never came) lets the kernel finish and sets the
- * word.  Returns HYPIC_OK, or HYPIC_ERR_DEVICE (with a message) when any launch since
+ * Synchronises the current device, then reads and clears its sticky status words.  The
+ * waves of the dense build and of the dense compose hand work to each other through
+ * bounded waits on LDS counters; a wait that runs out (a hand-off that never came) lets
+ * the kernel finish and sets the word.  Returns HYPIC_OK, or HYPIC_ERR_DEVICE (with a message) when any launch since
  * the previous call set it: the outputs of those launches are unreliable.
  * ---------------------------------------------------------------------------------- */
 hypic_status hypic_device_status(void);

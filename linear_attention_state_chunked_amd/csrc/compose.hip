@@ -12,8 +12,9 @@
 // T) in matrix-core accumulators and computes T_i X with f16 hi/lo operand splits
 // (three products, ~22-bit operand precision) after scaling its column block by an
 // exact power of two (the column maximum uses the NaN-propagating three-input maximum
-// with |.| modifiers); T_i is staged row-major in LDS as hi/lo f16 by loader waves,
-// one element ahead.
+// with |.| modifiers); T_i is staged row-major in LDS as hi/lo f16 by loader waves in
+// two column halves, each as soon as the compute waves are done with that half of the
+// previous element (LDS counters, no workgroup barrier per element).
 // Diagonal / scalar kinds: elementwise, one thread per state entry stripe.
 #include <mutex>
 
@@ -46,6 +47,38 @@ hipError_t noalloc_scratch(void** ptr) {
     }
     *ptr = cached[dev];
     return hipSuccess;
+}
+
+// Sticky status word of the compose kernels (see take_compose_status): a bounded wait that ran
+// out sets it.
+__device__ unsigned int g_compose_status;
+
+hipError_t take_compose_status(unsigned* out) {
+    unsigned v = 0;
+    const unsigned z = 0;
+    hipError_t e = hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_compose_status), sizeof v, 0, hipMemcpyDeviceToHost);
+    if (e == hipSuccess && v) e = hipMemcpyToSymbol(HIP_SYMBOL(g_compose_status), &z, sizeof z, 0, hipMemcpyHostToDevice);
+    *out = v;
+    return e;
+}
+
+// One arrival per wave on an LDS counter, after the wave's earlier LDS accesses.
+__device__ __forceinline__ void fold_arrive(int* cnt, int lane) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    if (lane == 0) __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Bounded wait until an LDS counter reaches target; a wait that runs out sets the status word
+// and goes on, so the kernel still ends.
+__device__ __forceinline__ void fold_wait(int* cnt, int target) {
+    int spins = 0;
+    while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target) {
+        if (++spins > (1 << 20)) {
+            __hip_atomic_fetch_or(&g_compose_status, kStatusWaitExpired, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
 __device__ __forceinline__ void split_hilo(const floatx16& x, int st, float scale, halfx8& hi, halfx8& lo) {
@@ -103,6 +136,9 @@ __global__ __launch_bounds__(D * 6) void fold_dense_kernel(FoldArgs a) {
     __shared__ __align__(16) float sVs[WS][D];      // seam v rows
     __shared__ float sGb[WS][2];                    // alpha, beta
     __shared__ int sW;                              // seam tokens of the staged element
+    // hand-off counters: T_i column half A, half B and S_i staged (one arrival per loader wave),
+    // then consumed (one per compute wave)
+    __shared__ int sC[6];
 
     const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -117,26 +153,40 @@ __global__ __launch_bounds__(D * 6) void fold_dense_kernel(FoldArgs a) {
         return (long long)sl * a.n_chain + chain;
     };
 
+    constexpr int NLW = NLT / 64;                     // loader waves
+    if (tid < 6) sC[tid] = 0;
+    __syncthreads();
     if (loader) {
         const int lt = tid - NB * 64;
         typedef float f4 __attribute__((ext_vector_type(4)));
-        f4 tr[TPL], ts[TPL];
+        // T_i by column halves: float4 r of half h of loader thread lt is row (lt + NLT r) / (D / 8),
+        // columns h D / 2 + 4 ((lt + NLT r) % (D / 8)) .. + 3
+        constexpr int TPH = TPL / 2;
+        f4 th[2][TPH], ts[TPL];
         int ei = 0;
         // seam tokens lw, lw + NLW, ... (loader wave lw): lane l holds channels l, l + 64, ...
         constexpr int NLW = NLT / 64, TPW = (kFusedSeamMax + NLW - 1) / NLW, CPL = D / 64;
         const int lw = lt >> 6, ll = lt & 63;
         float sq[TPW][CPL], sk[TPW][CPL], sv[TPW][CPL], sal[TPW], sbe[TPW];
         int swn = 0;
-        auto load = [&](int el) __attribute__((always_inline)) {
-            const long long so = elem(el);
-            const f4* src = reinterpret_cast<const f4*>(a.T_hat + so * DD);
+        auto hrow = [&](int r) { return (lt + NLT * r) / (D / 8); };
+        auto hcol = [&](int r, int h) { return h * (D / 2) + 4 * ((lt + NLT * r) % (D / 8)); };
+        auto load_half = [&](int el, int h) __attribute__((always_inline)) {
+            const f4* src = reinterpret_cast<const f4*>(a.T_hat + elem(el) * DD);
 #pragma unroll
-            for (int r = 0; r < TPL; ++r) tr[r] = src[lt + NLT * r];
+            for (int r = 0; r < TPH; ++r) th[h][r] = src[(hrow(r) * D + hcol(r, h)) / 4];
+        };
+        auto load_s = [&](int el) __attribute__((always_inline)) {
             if (!t_role) {  // the transition role needs no S_i
-                const f4* srs = reinterpret_cast<const f4*>(a.S + so * DD);
+                const f4* srs = reinterpret_cast<const f4*>(a.S + elem(el) * DD);
 #pragma unroll
                 for (int r = 0; r < TPL; ++r) ts[r] = srs[lt + NLT * r];
             }
+        };
+        // half A comes with the exponent and the seam tokens
+        auto load = [&](int el) __attribute__((always_inline)) {
+            const long long so = elem(el);
+            load_half(el, 0);
             ei = a.T_exp[so];
             if constexpr (SEAM) {
                 swn = seg_len(a.seam_tab, el);
@@ -167,13 +217,12 @@ __global__ __launch_bounds__(D * 6) void fold_dense_kernel(FoldArgs a) {
                 }
             }
         };
-        auto stage = [&]() __attribute__((always_inline)) {
+        auto stage_half = [&](int hh) __attribute__((always_inline)) {
             typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-            for (int r = 0; r < TPL; ++r) {
-                const int f = 4 * (lt + NLT * r);
-                const int row = f / D, col = f % D;
-                const f4 v = tr[r];
+            for (int r = 0; r < TPH; ++r) {
+                const int row = hrow(r), col = hcol(r, hh);
+                const f4 v = th[hh][r];
                 half4 h, l;
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
@@ -182,8 +231,17 @@ __global__ __launch_bounds__(D * 6) void fold_dense_kernel(FoldArgs a) {
                 }
                 *reinterpret_cast<half4*>(&sT[0][row * RS + col]) = h;
                 *reinterpret_cast<half4*>(&sT[1][row * RS + col]) = l;
-                if (!t_role) *reinterpret_cast<f4*>(&sS[row * RSS + col]) = ts[r];
             }
+        };
+        auto stage_s = [&]() __attribute__((always_inline)) {
+#pragma unroll
+            for (int r = 0; r < TPL; ++r) {
+                const int f = 4 * (lt + NLT * r);
+                *reinterpret_cast<f4*>(&sS[(f / D) * RSS + f % D]) = ts[r];
+            }
+        };
+        auto stage = [&]() __attribute__((always_inline)) {
+            stage_half(0);
             if (lt == 0) sE = ei;
             if constexpr (SEAM) {
                 if (lt == 0) sW = swn;
@@ -218,12 +276,29 @@ __global__ __launch_bounds__(D * 6) void fold_dense_kernel(FoldArgs a) {
                 }
             }
         };
-        if (e0 < e1) load(e0);
+        if (e0 < e1) {
+            load(e0);
+            load_half(e0, 1);
+            load_s(e0);
+        }
+        // each part of element el goes into LDS once the compute waves are done with that part
+        // of element el - 1, and the loads of the same part of el + 1 follow it
         for (int el = e0; el < e1; ++el) {
-            stage();
-            __syncthreads();  // element el staged
+            const int k = el - e0;
+            fold_wait(sC + 3, NB * k);
+            stage();                        // T half A, exponent, seam tokens
+            fold_arrive(sC + 0, lane);
             if (el + 1 < e1) load(el + 1);
-            __syncthreads();  // element el consumed
+            fold_wait(sC + 4, NB * k);
+            stage_half(1);
+            fold_arrive(sC + 1, lane);
+            if (el + 1 < e1) load_half(el + 1, 1);
+            if (!t_role) {
+                fold_wait(sC + 5, NB * k);
+                stage_s();
+                fold_arrive(sC + 2, lane);
+                if (el + 1 < e1) load_s(el + 1);
+            }
         }
         __syncthreads();  // epilogue exponent exchange
         return;
@@ -261,7 +336,8 @@ __global__ __launch_bounds__(D * 6) void fold_dense_kernel(FoldArgs a) {
                     for (int j = 0; j < 16; ++j) dst[(32 * xb + acc_row(half, j)) * D + col0 + l32] = X[xb][j];
             }
         }
-        __syncthreads();  // element el staged
+        const int kel = el - e0;
+        fold_wait(sC + 0, NLW * (kel + 1));   // T half A, exponent and seam tokens of el staged
         if constexpr (SEAM) {
             const int w = sW;
             const int bb = chain / a.h_v, hh = chain - (chain / a.h_v) * a.h_v;
@@ -333,14 +409,18 @@ __global__ __launch_bounds__(D * 6) void fold_dense_kernel(FoldArgs a) {
         for (int i = 0; i < LA; ++i) tload(i, fh[i], fl[i]);
 #pragma unroll
         for (int i = 0; i < NSTEP; ++i) {
+            // steps NSTEP / 2 .. read T half B (contraction indices D / 2 ..)
+            if (i + LA == NSTEP / 2) fold_wait(sC + 1, NLW * (kel + 1));
             if (i + LA < NSTEP) tload(i + LA, fh[(i + LA) % NR], fl[(i + LA) % NR]);
             const int ob = i % NB, ks = i / NB;
             if (ob == 0) split_hilo(X[ks >> 1], ks & 1, sc, bh, bl);
             acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fl[i % NR], bh, acc[ob], 0, 0, 0);
             acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fh[i % NR], bl, acc[ob], 0, 0, 0);
             acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fh[i % NR], bh, acc[ob], 0, 0, 0);
+            if (i == NSTEP / 2 - 1) fold_arrive(sC + 3, lane);   // every half-A fragment read
             __builtin_amdgcn_sched_barrier(0);
         }
+        fold_arrive(sC + 4, lane);   // every half-B fragment read
         if (t_role) {
             // X = T_i (X 2^-sx): exponent += sx + e_i, then renormalise
             float mm = 0.f;
@@ -356,13 +436,14 @@ __global__ __launch_bounds__(D * 6) void fold_dense_kernel(FoldArgs a) {
                 for (int j = 0; j < 16; ++j) X[xb][j] = acc[xb][j] * r;
             ew += sx + ecur + e;
         } else {
+            fold_wait(sC + 2, NLW * (kel + 1));   // S_el staged
 #pragma unroll
             for (int xb = 0; xb < NB; ++xb)
 #pragma unroll
                 for (int j = 0; j < 16; ++j)
                     X[xb][j] = ldexpf(acc[xb][j], sx + ecur) + sS[(32 * xb + acc_row(half, j)) * RSS + col0 + l32];
+            fold_arrive(sC + 5, lane);
         }
-        __syncthreads();  // element el consumed
     }
 
     if (t_role && lane == 0) sEw[wave] = ew;

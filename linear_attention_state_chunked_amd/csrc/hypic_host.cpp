@@ -232,13 +232,17 @@ int hypic_version(void) { return HYPIC_VERSION; }
 hypic_status hypic_device_status(void) {
     hipError_t e = hipDeviceSynchronize();
     if (e != hipSuccess) return device_fail("device status: synchronize", e);
-    unsigned flags = 0;
+    unsigned flags = 0, cflags = 0;
     e = hypic::take_device_status(&flags);
     if (e != hipSuccess) return device_fail("device status: read", e);
-    if (flags & hypic::kStatusWaitExpired)
+    e = hypic::take_compose_status(&cflags);
+    if (e != hipSuccess) return device_fail("device status: read", e);
+    if ((flags | cflags) & hypic::kStatusWaitExpired)
         return fail(HYPIC_ERR_DEVICE,
-                    "device status: a bounded wait inside the dense build gave up (a hand-off between the "
-                    "waves of a workgroup never came); outputs since the last status call are unreliable");
+                    "device status: a bounded wait inside the %s gave up (a hand-off between the waves of a "
+                    "workgroup never came); outputs since the last status call are unreliable",
+                    (flags & hypic::kStatusWaitExpired) ? "dense build" : "compose");
+    flags |= cflags;
     if (flags) return fail(HYPIC_ERR_DEVICE, "device status: flags 0x%x", flags);
     return ok();
 }

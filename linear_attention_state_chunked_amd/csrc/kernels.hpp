@@ -38,7 +38,8 @@ __device__ __forceinline__ int task_at(const SegTable& t, int it, int per_seg) {
 // (an ordinary vector atomic), so a broken hand-off is reported instead of passing as
 // silently wrong data.  take_device_status() reads and clears it (synchronous).
 constexpr unsigned kStatusWaitExpired = 1u;
-hipError_t take_device_status(unsigned* out);
+hipError_t take_device_status(unsigned* out);    // the dense build's word
+hipError_t take_compose_status(unsigned* out);   // the compose kernels' word
 
 // One dense (gated delta rule) chunk-engine launch.  Each task is one
 // (segment, batch, value head) chain; it runs the segment's tokens chunk by chunk
