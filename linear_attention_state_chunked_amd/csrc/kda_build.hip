@@ -4,10 +4,14 @@
 // compose with the dense composition law of the HYPIC news article's linear-layer
 // paragraph, which names KDA among the families), S(C|0) the zero-start state.
 //
-// Token-sequential, float32 vector arithmetic.  Thread j owns column j of X = [T | S]
-// (d rows in registers); columns evolve independently under X <- A_t X + [0 | w_t], so a
-// token needs no exchange between threads: u_j = k_t^T X_j, then
+// Token-sequential, float32 vector arithmetic.  Four threads own column j of X = [T | S]
+// (a quarter of its d rows each, in registers; lanes l, l ^ 16, l ^ 32, l ^ 48 of one wave);
+// columns evolve independently under X <- A_t X + [0 | w_t], so a token needs only the sum of
+// the four partial dot products u_j = k_t^T X_j (two lane exchanges), then
 //   X_rj <- alpha_r X_rj - alpha_r k_r beta u_j (+ k_r beta v_j for the state columns).
+// Four threads per column give 16 waves per workgroup with d/4 rows each (107 VGPRs), so
+// every SIMD issues from four waves (one thread per column ran at 290 registers, one wave
+// per SIMD: 2.3 ms against 1.3 ms for the 16 x 512-token, 32-head layer).
 // The per-channel gates make the chunked WY/UT form need per-channel exponentials of gate
 // differences inside a chunk (overflow-prone in f16 operands); the token form has none.
 // Tokens are staged 16 at a time in LDS (k, alpha, alpha k, beta, v) and read as
@@ -21,8 +25,9 @@
 namespace hypic {
 
 template <int D, bool WITH_T, bool IN_BF16>
-__global__ __launch_bounds__((WITH_T ? 2 : 1) * D) void kda_build_kernel(KdaArgs a) {
-    constexpr int NT = (WITH_T ? 2 : 1) * D;
+__global__ __launch_bounds__((WITH_T ? 8 : 4) * D) void kda_build_kernel(KdaArgs a) {
+    constexpr int NT = (WITH_T ? 8 : 4) * D;
+    constexpr int DH = D / 4;   // rows per thread
     constexpr int CH = 16;
     __shared__ __align__(16) float sK[CH][D];
     __shared__ __align__(16) float sA[CH][D];
@@ -41,12 +46,17 @@ __global__ __launch_bounds__((WITH_T ? 2 : 1) * D) void kda_build_kernel(KdaArgs
     const long long start = seg_start(a.seg, seg);
     const int len = seg_len(a.seg, seg);
     const long long N = a.n_tokens;
-    const bool t_col = WITH_T && tid < D;
-    const int col = (WITH_T && tid >= D) ? tid - D : tid;
+    // wave w holds columns 32 w .. 32 w + 31 of [T | S]; lane l holds rows hf DH .. of column
+    // 32 w + (l & 31), hf = l >> 5
+    const int lane = tid & 63, wv = tid >> 6, hf = lane >> 4;
+    const int gcol = 16 * wv + (lane & 15);
+    const bool t_col = WITH_T && gcol < D;
+    const int col = (WITH_T && gcol >= D) ? gcol - D : gcol;
+    const int r0 = hf * DH;
 
-    float X[D];
+    float X[DH];
 #pragma unroll
-    for (int r = 0; r < D; ++r) X[r] = (t_col && r == col) ? 1.f : 0.f;
+    for (int r = 0; r < DH; ++r) X[r] = (t_col && r0 + r == col) ? 1.f : 0.f;
     int ex = 0;
 
     for (int c0 = 0; c0 < len; c0 += CH) {
@@ -85,28 +95,33 @@ __global__ __launch_bounds__((WITH_T ? 2 : 1) * D) void kda_build_kernel(KdaArgs
 #pragma unroll
             for (int i = 0; i < 8; ++i) up[i] = 0.f;
 #pragma unroll
-            for (int r = 0; r < D; ++r) up[r & 7] = fmaf(sK[t][r], X[r], up[r & 7]);
-            const float u = ((up[0] + up[1]) + (up[2] + up[3])) + ((up[4] + up[5]) + (up[6] + up[7]));
+            for (int r = 0; r < DH; ++r) up[r & 7] = fmaf(sK[t][r0 + r], X[r], up[r & 7]);
+            float u = ((up[0] + up[1]) + (up[2] + up[3])) + ((up[4] + up[5]) + (up[6] + up[7]));
+            u += __shfl_xor(u, 16, 64);   // the other row quarters of this column
+            u += __shfl_xor(u, 32, 64);
             const float bt = sB[t];
             const float w = bt * u;
             if (t_col) {
 #pragma unroll
-                for (int r = 0; r < D; ++r) X[r] = fmaf(-sAK[t][r], w, sA[t][r] * X[r]);
+                for (int r = 0; r < DH; ++r) X[r] = fmaf(-sAK[t][r0 + r], w, sA[t][r0 + r] * X[r]);
             } else {
-                const float wv = bt * sV[t][col];
+                const float wvv = bt * sV[t][col];
 #pragma unroll
-                for (int r = 0; r < D; ++r) X[r] = fmaf(sK[t][r], wv, fmaf(-sAK[t][r], w, sA[t][r] * X[r]));
+                for (int r = 0; r < DH; ++r)
+                    X[r] = fmaf(sK[t][r0 + r], wvv, fmaf(-sAK[t][r0 + r], w, sA[t][r0 + r] * X[r]));
             }
         }
         if (t_col) {
             // this column's largest magnitude back into [0.5, 1)
             float m = 0.f;
 #pragma unroll
-            for (int r = 0; r < D; ++r) m = fmaxf(m, fabsf(X[r]));
+            for (int r = 0; r < DH; ++r) m = fmaxf(m, fabsf(X[r]));
+            m = fmaxf(m, __shfl_xor(m, 16, 64));   // all row quarters
+            m = fmaxf(m, __shfl_xor(m, 32, 64));
             const int e = exp2_of(m);
             if (e != 0) {
 #pragma unroll
-                for (int r = 0; r < D; ++r) X[r] = ldexpf(X[r], -e);
+                for (int r = 0; r < DH; ++r) X[r] = ldexpf(X[r], -e);
                 ex += e;
             }
         }
@@ -121,24 +136,24 @@ __global__ __launch_bounds__((WITH_T ? 2 : 1) * D) void kda_build_kernel(KdaArgs
         if ((tid & 63) == 0) sE[tid >> 6] = em;
         __syncthreads();
         int emax = sE[0];
-        for (int w = 1; w < D / 64; ++w) emax = max(emax, sE[w]);
+        for (int w = 1; w < D / 16; ++w) emax = max(emax, sE[w]);   // the waves of T columns
         if (t_col) {
-            float* dst = a.T_hat + ((long long)seg * a.n_batch * a.h_v + chain) * D * D + col;
+            float* dst = a.T_hat + ((long long)seg * a.n_batch * a.h_v + chain) * D * D + (long long)r0 * D + col;
 #pragma unroll
-            for (int r = 0; r < D; ++r) dst[(long long)r * D] = ldexpf(X[r], ex - emax);
+            for (int r = 0; r < DH; ++r) dst[(long long)r * D] = ldexpf(X[r], ex - emax);
             if (tid == 0) a.T_exp[(long long)seg * a.n_batch * a.h_v + chain] = emax;
         }
     }
     if (!t_col) {
-        float* dst = a.S + ((long long)seg * a.n_batch * a.h_v + chain) * D * D + col;
+        float* dst = a.S + ((long long)seg * a.n_batch * a.h_v + chain) * D * D + (long long)r0 * D + col;
 #pragma unroll
-        for (int r = 0; r < D; ++r) dst[(long long)r * D] = X[r];
+        for (int r = 0; r < DH; ++r) dst[(long long)r * D] = X[r];
     }
 }
 
 template <int D, bool WITH_T>
 static hipError_t launch_kda_d(const KdaArgs& a, hipStream_t s) {
-    constexpr int nt = (WITH_T ? 2 : 1) * D;
+    constexpr int nt = (WITH_T ? 8 : 4) * D;
     if (a.in_bf16) hipLaunchKernelGGL((kda_build_kernel<D, WITH_T, true>), dim3(a.n_tasks), dim3(nt), 0, s, a);
     else hipLaunchKernelGGL((kda_build_kernel<D, WITH_T, false>), dim3(a.n_tasks), dim3(nt), 0, s, a);
     return hipGetLastError();
