@@ -619,13 +619,13 @@ __global__ __launch_bounds__((gdn_carry_waves<D, WITH_T, WITH_S>() + 4) * 64) vo
                 };
                 reset_x();
                 int ew = 0;
-                // T columns: rescale by an exact power of two once max |X_T| leaves [2^-8, 2) (the
-                // hi/lo operands of the precise plan: [1/4, 2)), back into [0.5, 1).  The f16 operands
-                // never underflow: an entry 2^-6 below the column maximum or more becomes an f16
-                // subnormal, with an absolute error under 2^-17 of that maximum.  A chunk decaying
-                // T by 2^-4 rescales every other chunk instead of every chunk.  The NaN-propagating
-                // maximum maps to gfx950's three-input maximum with |.| source modifiers (fmaxf
-                // would first canonicalise every input: twice the instructions)
+                // T columns: rescale by an exact power of two once max |X_T| leaves [2^-4, 2) (the
+                // hi/lo operands of the precise plan: [1/4, 2)), back into [0.5, 1), so the f16
+                // operands of X_T and of its Vn stay clear of the f16 subnormals (a window reaching
+                // down to 2^-8 raised the segment T error from 7.7e-4 to 1.2e-3).  A chunk decaying
+                // T by about 2^-4 rescales every other chunk.  The NaN-propagating maximum maps to
+                // gfx950's three-input maximum with |.| source modifiers (fmaxf would first
+                // canonicalise every input: twice the instructions)
                 auto renorm = [&] {
                     // max |X_T| of this lane as a tree of three-input maxima (22 + 8 + 3 + 1 for
                     // NB = 4): the first level takes |.| as source modifiers
@@ -644,7 +644,7 @@ __global__ __launch_bounds__((gdn_carry_waves<D, WITH_T, WITH_S>() + 4) * 64) vo
 #pragma unroll
                     for (int i = 0; i < N2; i += 2) m = mx3(m, m2[i], i + 1 < N2 ? m2[i + 1] : 0.f);
                     const int e0 = exp2_of(wave_max(m));   // m in [2^(e0-1), 2^e0)
-                    const int e = (e0 < (PT ? -1 : -7) || e0 > 1) ? e0 : 0;
+                    const int e = (e0 < (PT ? -1 : -3) || e0 > 1) ? e0 : 0;
                     if (e != 0) {
 #pragma unroll
                         for (int xb = 0; xb < NB; ++xb)
