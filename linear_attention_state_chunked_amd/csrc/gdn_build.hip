@@ -537,9 +537,11 @@ __global__ __launch_bounds__((gdn_carry_waves<D, WITH_T, WITH_S>() + 4) * 64) vo
     constexpr bool WLO = PT && !WITH_S;         // W' as hi/lo fragments (low half where V would be)
                                                 //     in their idle tail before the barrier
     constexpr int NT = (NC + NP) * 64;
-    // the row factors Gamma / gamma_i of Vn are folded into the Tg tiles (so into U and W'); the
-    // output variant keeps U - W' S0 unscaled for its outputs and scales Vn itself
-    constexpr bool FOLD_R = !WO;
+    // the row factors Gamma / gamma_i of Vn are folded into the Tg tiles (so into U and W') in the
+    // fast plan.  The output variant keeps U - W' S0 unscaled for its outputs, and the precise plan
+    // keeps the hi/lo Tg values unscaled (their low halves would sink further into the f16
+    // subnormals): both scale Vn themselves, in fp32
+    constexpr bool FOLD_R = !WO && !PT;
     constexpr int RK = LY::RK, RT = LY::RT;
 
     __shared__ __align__(16) unsigned char smem[LY::total];
