@@ -254,6 +254,35 @@ def test_dense_bf16_l2norm_on_load(gpu):
     _check_build(out, chains, lens, "dense", TOL_BF16, normalise=True)
 
 
+@pytest.mark.parametrize("shift", [-8, 10])
+@pytest.mark.parametrize("kind", ["dense", "diag"])
+def test_f16_plan_value_range(gpu, kind, shift):
+    """bf16 values scaled by 2^shift (exact in bf16): at |v| ~ 2^-8 the f16 operands stay
+    normal, at |v| ~ 2^10 (largest |v| and |S| near 2^13) they stay below the f16 maximum, and
+    the build holds the bf16 tolerance at both ends of the documented range."""
+    lens = [64, 130, 700]
+    if kind == "dense":
+        dev, chains = _dense_inputs(WORKLOADS["gdn64k_bf16"], sum(lens), 2)
+        k, la, beta = dev["k"], dev["log_alpha"], dev["beta"]
+        v = dev["v"] * (2.0 ** shift)
+    else:
+        wl = WORKLOADS["gla_bf16"]
+        chains = [chain_inputs(wl, 0, i, sum(lens)) for i in range(2)]
+        k = dev_tensor(np.stack([c["k"] for c in chains], 1)[None], torch.bfloat16)
+        v = dev_tensor(np.stack([c["v"] for c in chains], 1)[None], torch.bfloat16) * (2.0 ** shift)
+        la, beta = dev_tensor(np.stack([c["log_alpha"] for c in chains], 1)[None]), None
+    assert v.dtype == torch.bfloat16
+    for c in chains:
+        c["v"] = np.ldexp(c["v"], shift)
+    out = H.hypic_segment_build(k, v, la, cu_of(lens), beta=beta, kind=kind)
+    torch.cuda.synchronize()
+    H.hypic_device_status()
+    s_max = float(out["S"].abs().max())
+    assert 2.0 ** (shift - 6) < s_max < 2.0 ** 15, s_max
+    eT, eS = _check_build(out, chains, lens, kind, TOL_BF16)
+    print(f"{kind} v x 2^{shift}: max |S| {s_max:.3g}, T err {eT:.2e}, S err {eS:.2e}")
+
+
 def test_schedules_are_bitwise_identical(ragged_dense):
     wl, dev, chains = ragged_dense
     outs = []
