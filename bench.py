@@ -19,6 +19,8 @@ and the cold 100k-token 30-layer build in LPT, round-robin and natural order, wi
 the precise-T plan and the single sequential pass beside it.  Each carries its
 algorithmic bytes or flops and the fraction of the matching MI355X peak; each row's
 launches are timed one by one after a 512 MiB cache flush, so they read from HBM.
+The last row, "mfma_probe", measures the dense f16 matrix-core rate this GPU
+sustains on back-to-back products alone (libhypic_probe), with its clock.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-rows]
   python bench.py --calibrate-copy      (a plain 1 GiB device copy, for HBM counters)
@@ -207,6 +209,43 @@ def _hbm(nbytes, t):
 
 def _mfma(flops, t):
     return {"s": t, "flops": flops, "TFLOP_per_s": flops / t / 1e12, "mfma_frac": flops / t / PEAK_MFMA_F16}
+
+
+def row_mfma_probe(dev):
+    """Achievable dense f16 matrix-core rate of this GPU (libhypic_probe): 4 workgroups per CU of 8 waves,
+    each wave with 4 independent v_mfma_f32_32x32x16_f16 products in flight on register operands, 10
+    launches of about 4 ms back to back after 3 warm-up launches.  The clock is read inside the kernel
+    (core-clock cycles over 100 MHz real-time ticks), so the rate per cycle comes out as well."""
+    import torch
+
+    L = C.CDLL(os.path.join(ROOT, "linear_attention_state_chunked_amd", "libhypic_probe.so"))
+    L.hypic_probe_mfma_f16.argtypes = [C.c_int, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p]
+    L.hypic_probe_mfma_f16.restype = C.c_int
+    L.hypic_probe_mfma_f16_flops.argtypes = [C.c_int, C.c_int]
+    L.hypic_probe_mfma_f16_flops.restype = C.c_double
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    groups, iters = 4 * cus, 10000
+    sink = torch.empty(groups * 512, dtype=torch.float32, device=dev)
+    clocks = torch.empty(groups * 2, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream()
+    ts, ghz = [], []
+    for i in range(13):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        rc = L.hypic_probe_mfma_f16(groups, iters, C.c_void_p(sink.data_ptr()), C.c_void_p(clocks.data_ptr()),
+                                    C.c_void_p(stream.cuda_stream))
+        e1.record(stream)
+        if rc != 0:
+            raise RuntimeError(f"hypic_probe_mfma_f16 returned {rc}")
+        torch.cuda.synchronize()
+        if i >= 3:
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+            c = clocks.view(-1, 2).double().cpu().numpy()
+            ghz.append(float(np.median(c[:, 0] / (c[:, 1] * 10e-9))) * 1e-9)
+    flops = L.hypic_probe_mfma_f16_flops(groups, iters)
+    t, clk = float(np.median(ts)), float(np.median(ghz))
+    return {"flops": flops, "s": t, "TFLOP_per_s": flops / t / 1e12, "frac_of_spec_peak": flops / t / PEAK_MFMA_F16,
+            "clock_GHz": clk, "flop_per_cycle_per_cu": flops / (t * clk * 1e9 * cus), "compute_units": cus}
 
 
 def row_diag(dev):
@@ -572,7 +611,7 @@ def main():
         rows = {}
         for name, fn in (("diag_scalar_build_16x512", row_diag), ("gdn64k_build_plans", row_build_plans),
                          ("kda_build_16x512", row_kda), ("warm30_seam_compose", row_warm),
-                         ("cold100k_build", row_cold)):
+                         ("cold100k_build", row_cold), ("mfma_probe", row_mfma_probe)):
             rows[name] = fn(dev)
             torch.cuda.empty_cache()
         out["rows"] = rows

@@ -38,6 +38,26 @@ def test_every_declared_symbol_is_exported(L):
         assert getattr(L, name) is not None
 
 
+def test_probe_library_exports_its_declared_symbols():
+    """libhypic_probe (the matrix-core rate probe the benchmark reports beside the build's rate) exports
+    what include/hypic_probe.h declares; its flop count is the product count times 32 x 32 x 16 x 2."""
+    src = open(os.path.join(ROOT, "include", "hypic_probe.h")).read()
+    declared = set(re.findall(r"^\s*(?:int|double)\s+(hypic_probe_\w+)\s*\(", src, re.M))
+    assert declared == {"hypic_probe_mfma_f16", "hypic_probe_mfma_f16_flops"}
+    path = os.path.join(os.path.dirname(A.LIB_PATH), "libhypic_probe.so")
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True).stdout
+    assert declared <= set(re.findall(r"\bT (hypic_probe_\w+)", out))
+    P = C.CDLL(path)
+    P.hypic_probe_mfma_f16_flops.argtypes = [C.c_int, C.c_int]
+    P.hypic_probe_mfma_f16_flops.restype = C.c_double
+    assert P.hypic_probe_mfma_f16_flops(3, 5) == 3 * 8 * 5 * 4 * 32 * 32 * 16 * 2
+    # invalid arguments are rejected on the host, before any HIP call
+    P.hypic_probe_mfma_f16.argtypes = [C.c_int, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p]
+    P.hypic_probe_mfma_f16.restype = C.c_int
+    assert P.hypic_probe_mfma_f16(0, 5, None, None, None) == -1
+    assert P.hypic_probe_mfma_f16(4, 5, None, None, None) == -1
+
+
 def test_struct_layouts_match_the_header(tmp_path):
     lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "hypic.h"', "int main(void) {"]
     structs = {"hypic_build_desc": A.BuildDesc, "hypic_compose_desc": A.ComposeDesc,
