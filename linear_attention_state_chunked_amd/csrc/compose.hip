@@ -115,10 +115,13 @@ __device__ __forceinline__ halfx8 t_frag(const _Float16* base) {
 // from HBM while the current element is multiplied, and write them into LDS (T_i as
 // hi/lo f16, S_i as fp32, row-major) between two workgroup barriers.
 // SEAM: the fused warm path.  Loader wave t also loads seam token t of the next element
-// (q, k, v rows, gates) and stages it in LDS (float32, q and k L2-normalised on request);
-// before each element's product the compute waves run the gated delta rule over those tokens
-// on their accumulator-resident columns: u = k^T S (lane-local partial over its 64 rows plus
-// the other lane half's), S <- alpha (S - beta k u^T) + beta k v^T, o = S^T q.
+// (q, k, v rows, gates).  The seam window (w <= 8 tokens) is applied in the one-chunk form of
+// the gated delta rule: while the compute waves multiply element el, the loader waves turn
+// the window of el + 1 into its factors (the w x w gram and output mask, Tg = (I + L)^-1
+// diag(beta) by forward substitution, -Tg diag(gamma) K, diag(gamma) Q and K^T as hi/lo f16
+// tiles).  Before each element's product the compute waves then advance their accumulator-
+// resident columns on the matrix cores: Z = Tg V - Tg diag(gamma) K S, O = diag(gamma) Q S +
+// Mq Z (the window's outputs o_t = S_t^T q_t), S <- Gamma S + K^T diag(Gamma / gamma) Z.
 template <int D, bool SEAM>
 __global__ __launch_bounds__(D * 6) void fold_dense_kernel(FoldArgs a) {
     constexpr int NB = D / 32;                        // compute waves
@@ -132,13 +135,29 @@ __global__ __launch_bounds__(D * 6) void fold_dense_kernel(FoldArgs a) {
     __shared__ int sE;
     __shared__ int sEw[NB];
     constexpr int WS = SEAM ? kFusedSeamMax : 1;
-    __shared__ __align__(16) float sQk[WS][2][D];   // seam q, k rows
-    __shared__ __align__(16) float sVs[WS][D];      // seam v rows
-    __shared__ float sGb[WS][2];                    // alpha, beta
+    // seam window of the staged element (w <= kFusedSeamMax tokens), in the one-chunk form of the gated
+    // delta rule (rows = window tokens; row WS of each w-row tile stays zero for the padded rows of the
+    // 32-row matrix-core operands):
+    //   G_t = sum_{s<=t} log alpha_s, gamma_t = e^{G_t}, Gamma = gamma_{w-1}
+    //   L = strictly-lower(beta_t e^{G_t - G_s} k_t.k_s),  Tg = (I + L)^-1 diag(beta)
+    //   Z = Tg V - Tg diag(gamma) K S,  S' = Gamma S + K^T diag(Gamma / gamma) Z
+    //   O = diag(gamma) Q S + Mq Z,     Mq = lower(e^{G_t - G_s} q_t.k_s), diagonal included
+    constexpr int RW = D + 4;                       // row stride (halves) of the w x D operand tiles
+    constexpr int WK = SEAM ? D : 1;
+    __shared__ __align__(16) _Float16 sWh[WS + 1][RW], sWl[WS + 1][RW];   // -Tg diag(gamma) K, hi / lo
+    __shared__ __align__(16) _Float16 sQh[WS + 1][RW], sQl[WS + 1][RW];   // diag(gamma) Q, hi / lo
+    __shared__ __align__(16) _Float16 sKTh[WK][8], sKTl[WK][8];           // K^T, hi / lo
+    __shared__ __align__(16) _Float16 sTh[WS + 1][8], sTl[WS + 1][8];     // Tg, hi / lo
+    __shared__ __align__(16) _Float16 sMh[WS + 1][8], sMl[WS + 1][8];     // Mq, hi / lo
+    __shared__ __align__(16) float sKf[WS][D + 4];  // the window's keys (fp32, for the w x w products)
+    __shared__ __align__(16) float sVs[WS][D];      // the window's values
+    __shared__ float sLf[WS][WS], sTgf[WS][WS];     // L and Tg (fp32)
+    __shared__ float sGb[WS][2];                    // log alpha, beta
+    __shared__ float sGv[WS], sR[WS], sGam;         // gamma_t, Gamma / gamma_t, Gamma
     __shared__ int sW;                              // seam tokens of the staged element
     // hand-off counters: T_i column half A, half B and S_i staged (one arrival per loader wave),
     // then consumed (one per compute wave)
-    __shared__ int sC[6];
+    __shared__ int sC[9];
 
     const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -154,7 +173,14 @@ __global__ __launch_bounds__(D * 6) void fold_dense_kernel(FoldArgs a) {
     };
 
     constexpr int NLW = NLT / 64;                     // loader waves
-    if (tid < 6) sC[tid] = 0;
+    if (tid < 9) sC[tid] = 0;
+    if constexpr (SEAM) {
+        // the zero rows of the window's operand tiles
+        for (int i = tid; i < RW; i += D * 6) {
+            sWh[WS][i] = sWl[WS][i] = sQh[WS][i] = sQl[WS][i] = (_Float16)0.f;
+            if (i < 8) sTh[WS][i] = sTl[WS][i] = sMh[WS][i] = sMl[WS][i] = (_Float16)0.f;
+        }
+    }
     __syncthreads();
     if (loader) {
         const int lt = tid - NB * 64;
@@ -169,25 +195,29 @@ __global__ __launch_bounds__(D * 6) void fold_dense_kernel(FoldArgs a) {
         const int lw = lt >> 6, ll = lt & 63;
         float sq[TPW][CPL], sk[TPW][CPL], sv[TPW][CPL], sal[TPW], sbe[TPW];
         int swn = 0;
+        int lbar = 0;   // loader-barrier target
         auto hrow = [&](int r) { return (lt + NLT * r) / (D / 8); };
         auto hcol = [&](int r, int h) { return h * (D / 2) + 4 * ((lt + NLT * r) % (D / 8)); };
-        auto load_half = [&](int el, int h) __attribute__((always_inline)) {
-            const f4* src = reinterpret_cast<const f4*>(a.T_hat + elem(el) * DD);
+        // the element's slot offset, read once per element by load(): a slot read right before each
+        // part's loads would wait (vmcnt) for every load still in flight
+        long long so_ld = 0;
+        auto load_half = [&](int h) __attribute__((always_inline)) {
+            const f4* src = reinterpret_cast<const f4*>(a.T_hat + so_ld * DD);
 #pragma unroll
             for (int r = 0; r < TPH; ++r) th[h][r] = src[(hrow(r) * D + hcol(r, h)) / 4];
         };
-        auto load_s = [&](int el) __attribute__((always_inline)) {
+        auto load_s = [&]() __attribute__((always_inline)) {
             if (!t_role) {  // the transition role needs no S_i
-                const f4* srs = reinterpret_cast<const f4*>(a.S + elem(el) * DD);
+                const f4* srs = reinterpret_cast<const f4*>(a.S + so_ld * DD);
 #pragma unroll
                 for (int r = 0; r < TPL; ++r) ts[r] = srs[lt + NLT * r];
             }
         };
         // half A comes with the exponent and the seam tokens
         auto load = [&](int el) __attribute__((always_inline)) {
-            const long long so = elem(el);
-            load_half(el, 0);
-            ei = a.T_exp[so];
+            so_ld = elem(el);
+            load_half(0);
+            ei = a.T_exp[so_ld];
             if constexpr (SEAM) {
                 swn = seg_len(a.seam_tab, el);
                 const int bb = chain / a.h_v, hh = chain - (chain / a.h_v) * a.h_v;
@@ -211,7 +241,7 @@ __global__ __launch_bounds__(D * 6) void fold_dense_kernel(FoldArgs a) {
                                 sv[m][u] = reinterpret_cast<const float*>(a.v)[vi + c];
                             }
                         }
-                        sal[m] = expf(a.log_alpha[row * a.h_v + hh]);
+                        sal[m] = a.log_alpha[row * a.h_v + hh];
                         sbe[m] = a.beta[row * a.h_v + hh];
                     }
                 }
@@ -240,46 +270,175 @@ __global__ __launch_bounds__(D * 6) void fold_dense_kernel(FoldArgs a) {
                 *reinterpret_cast<f4*>(&sS[(f / D) * RSS + f % D]) = ts[r];
             }
         };
-        auto stage = [&]() __attribute__((always_inline)) {
-            stage_half(0);
-            if (lt == 0) sE = ei;
+        // the window's factors, by the loader waves (token t = lw + NLW m belongs to loader wave lw);
+        // tokens from w on are zeros in every factor
+        auto loader_barrier = [&]() __attribute__((always_inline)) {
+            lbar += NLW;
+            fold_arrive(sC + 6, lane);
+            fold_wait(sC + 6, lbar);
+        };
+        // sum over the 64 lanes with DPP row sums and four readlanes (no LDS round trips)
+        auto wsum = [](float v) {
+            v = group_sum<16>(v);
+            return (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)) +
+                    __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16))) +
+                   (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32)) +
+                    __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48)));
+        };
+        // the window's normalised q rows (fp32) live in the -W' tiles until -W' is formed: rows 0..3 in
+        // sWh, 4..7 in sWl, both below their zero row
+        auto qrow = [&](int t) __attribute__((always_inline)) {
+            return (t < 4 ? reinterpret_cast<float*>(&sWh[0][0]) : reinterpret_cast<float*>(&sWl[0][0])) +
+                   (t & 3) * (D + 4);
+        };
+        auto stage_window = [&]() __attribute__((always_inline)) {
             if constexpr (SEAM) {
-                if (lt == 0) sW = swn;
+            if (lt == 0) sW = swn;
+            // 1. each loader wave's tokens: normalised k (fp32 rows, hi/lo K^T) and q (fp32 rows), v rows,
+            //    gates
 #pragma unroll
-                for (int m = 0; m < TPW; ++m) {
-                    const int t = lw + NLW * m;
-                    if (t < swn) {   // uniform over the wave
-                        float fq = 1.f, fk = 1.f;
-                        if (a.qk_l2norm) {
-                            float nq = 0.f, nk = 0.f;
+            for (int m = 0; m < TPW; ++m) {
+                const int t = lw + NLW * m;
+                if (t >= WS) continue;
+                const bool live = t < swn;   // uniform over the wave
+                float fq = 1.f, fk = 1.f;
+                if (live && a.qk_l2norm) {
+                    float nq = 0.f, nk = 0.f;
 #pragma unroll
-                            for (int u = 0; u < CPL; ++u) {
-                                nq += sq[m][u] * sq[m][u];
-                                nk += sk[m][u] * sk[m][u];
-                            }
-                            nq = wave_sum(nq);
-                            nk = wave_sum(nk);
-                            fq = nq > 0.f ? 1.f / sqrtf(nq) : 0.f;
-                            fk = nk > 0.f ? 1.f / sqrtf(nk) : 0.f;
-                        }
+                    for (int u = 0; u < CPL; ++u) {
+                        nq += sq[m][u] * sq[m][u];
+                        nk += sk[m][u] * sk[m][u];
+                    }
+                    nq = wsum(nq);
+                    nk = wsum(nk);
+                    fq = nq > 0.f ? 1.f / sqrtf(nq) : 0.f;
+                    fk = nk > 0.f ? 1.f / sqrtf(nk) : 0.f;
+                }
+                float* qr = qrow(t);
 #pragma unroll
-                        for (int u = 0; u < CPL; ++u) {
-                            sQk[t][0][ll + 64 * u] = sq[m][u] * fq;
-                            sQk[t][1][ll + 64 * u] = sk[m][u] * fk;
-                            sVs[t][ll + 64 * u] = sv[m][u];
-                        }
-                        if (ll == 0) {
-                            sGb[t][0] = sal[m];
-                            sGb[t][1] = sbe[m];
-                        }
+                for (int u = 0; u < CPL; ++u) {
+                    const int c = ll + 64 * u;
+                    const float kk = live ? sk[m][u] * fk : 0.f;
+                    qr[c] = live ? sq[m][u] * fq : 0.f;
+                    sKf[t][c] = kk;
+                    sVs[t][c] = live ? sv[m][u] : 0.f;
+                    const _Float16 kh = (_Float16)kk;
+                    sKTh[c][t] = kh;
+                    sKTl[c][t] = (_Float16)(kk - (float)kh);
+                }
+                if (ll == 0) {
+                    sGb[t][0] = live ? sal[m] : 0.f;
+                    sGb[t][1] = live ? sbe[m] : 0.f;
+                }
+            }
+            loader_barrier();
+            // 2a. the 2 w^2 dot products k_t.k_s and q_t.k_s over all loader waves: LPP lanes per product,
+            //     32 channels per lane, summed with DPP lane permutations
+            auto gsum = [&](float x) {   // G_i of token i: the staged log gates summed in order
+                float g = 0.f;
+#pragma unroll
+                for (int r = 0; r < WS; ++r) g += r <= x ? sGb[r][0] : 0.f;
+                return g;
+            };
+            auto fexp2 = [](float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); };
+            {
+                constexpr int NPROD = 2 * WS * WS, PPW = NPROD / NLW, LPP = 64 / PPW, CPN = D / LPP;
+                static_assert(PPW * NLW == NPROD && LPP * PPW == 64 && (LPP == 2 || LPP == 4), "product split");
+                const int pi = PPW * lw + ll / LPP, part = ll % LPP;
+                const bool isq = pi >= WS * WS;
+                const int pq = isq ? pi - WS * WS : pi, t = pq / WS, s2 = pq % WS;
+                const float* x = isq ? qrow(t) : sKf[t];
+                const float* y = sKf[s2];
+                float acc4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int c = CPN * part; c < CPN * part + CPN; c += 4) {
+                    const float4 a4 = *reinterpret_cast<const float4*>(x + c);
+                    const float4 b4 = *reinterpret_cast<const float4*>(y + c);
+                    acc4[0] = fmaf(a4.x, b4.x, acc4[0]);
+                    acc4[1] = fmaf(a4.y, b4.y, acc4[1]);
+                    acc4[2] = fmaf(a4.z, b4.z, acc4[2]);
+                    acc4[3] = fmaf(a4.w, b4.w, acc4[3]);
+                }
+                float dp = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
+                dp += dpp_perm<0xb1>(dp);                     // quad_perm [1,0,3,2]
+                if constexpr (LPP == 4) dp += dpp_perm<0x4e>(dp);   // quad_perm [2,3,0,1]
+                if (part == 0) {
+                    const float dec = fexp2(gsum((float)t) - gsum((float)s2));
+                    if (isq) {
+                        const float mq = (t < swn && s2 <= t) ? dec * dp : 0.f;
+                        const _Float16 mh = (_Float16)mq;
+                        sMh[t][s2] = mh;
+                        sMl[t][s2] = (_Float16)(mq - (float)mh);
+                    } else {
+                        sLf[t][s2] = (t < swn && s2 < t) ? sGb[t][1] * dec * dp : 0.f;
                     }
                 }
             }
+            loader_barrier();
+            // 2b. wave 0: Tg = (I + L)^-1 diag(beta) by forward substitution (lane j one column); the other
+            //     waves: diag(gamma) Q rows; the last wave also Gamma / gamma and Gamma
+            if (lw == 0) {
+                if (ll < WS) {
+                    const int j = ll;
+                    float xs[WS];
+#pragma unroll
+                    for (int i = 0; i < WS; ++i) {
+                        float v = i == j ? sGb[j][1] : 0.f;
+#pragma unroll
+                        for (int s3 = 0; s3 < i; ++s3) v = fmaf(-sLf[i][s3], xs[s3], v);
+                        xs[i] = v;
+                    }
+#pragma unroll
+                    for (int i = 0; i < WS; ++i) {
+                        const float v = (i < swn && j < swn) ? xs[i] : 0.f;
+                        sTgf[i][j] = v;
+                        const _Float16 vh = (_Float16)v;
+                        sTh[i][j] = vh;
+                        sTl[i][j] = (_Float16)(v - (float)vh);
+                    }
+                }
+            } else {
+                for (int e = lt - 64; e < WS * D; e += NLT - 64) {
+                    const int t = e / D, c = e - (e / D) * D;
+                    const float x = t < swn ? fexp2(gsum((float)t)) * qrow(t)[c] : 0.f;
+                    const _Float16 xh = (_Float16)x;
+                    sQh[t][c] = xh;
+                    sQl[t][c] = (_Float16)(x - (float)xh);
+                }
+                if (lw == NLW - 1 && ll < WS) {
+                    const bool live = ll < swn;
+                    const float Glast = gsum((float)(swn > 0 ? swn - 1 : 0)), Gl = gsum((float)ll);
+                    sGv[ll] = live ? fexp2(Gl) : 0.f;
+                    sR[ll] = live ? fexp2(Glast - Gl) : 0.f;
+                    if (ll == 0) sGam = swn > 0 ? fexp2(Glast) : 1.f;
+                }
+            }
+            loader_barrier();
+            // 3. -Tg diag(gamma) K, hi / lo (over the borrowed q rows, read in phase 2 only)
+            for (int e = lt; e < WS * D; e += NLT) {
+                const int i = e / D, c = e - (e / D) * D;
+                float v = 0.f;
+#pragma unroll
+                for (int j = 0; j < WS; ++j) v = fmaf(sTgf[i][j] * sGv[j], sKf[j][c], v);
+                v = -v;
+                const _Float16 vh = (_Float16)v;
+                sWh[i][c] = vh;
+                sWl[i][c] = (_Float16)(v - (float)vh);
+            }
+            }
+        };
+        auto stage = [&]() __attribute__((always_inline)) {
+            stage_half(0);
+            if (lt == 0) sE = ei;
         };
         if (e0 < e1) {
             load(e0);
-            load_half(e0, 1);
-            load_s(e0);
+            load_half(1);
+            load_s();
+            if constexpr (SEAM) {
+                stage_window();                 // the window of the first element
+                fold_arrive(sC + 8, lane);
+            }
         }
         // each part of element el goes into LDS once the compute waves are done with that part
         // of element el - 1, and the loads of the same part of el + 1 follow it
@@ -292,12 +451,21 @@ __global__ __launch_bounds__(D * 6) void fold_dense_kernel(FoldArgs a) {
             fold_wait(sC + 4, NB * k);
             stage_half(1);
             fold_arrive(sC + 1, lane);
-            if (el + 1 < e1) load_half(el + 1, 1);
+            if (el + 1 < e1) load_half(1);
             if (!t_role) {
                 fold_wait(sC + 5, NB * k);
                 stage_s();
                 fold_arrive(sC + 2, lane);
-                if (el + 1 < e1) load_s(el + 1);
+                if (el + 1 < e1) load_s();
+            }
+            if constexpr (SEAM) {
+                // the window of el + 1, once the compute waves are done with the window of el (the
+                // product of el still runs)
+                if (el + 1 < e1) {
+                    fold_wait(sC + 7, NB * (k + 1));
+                    stage_window();
+                    fold_arrive(sC + 8, lane);
+                }
             }
         }
         __syncthreads();  // epilogue exponent exchange
@@ -339,49 +507,115 @@ __global__ __launch_bounds__(D * 6) void fold_dense_kernel(FoldArgs a) {
         const int kel = el - e0;
         fold_wait(sC + 0, NLW * (kel + 1));   // T half A, exponent and seam tokens of el staged
         if constexpr (SEAM) {
+            fold_wait(sC + 8, NLW * (kel + 1));   // the window of el staged
             const int w = sW;
-            const int bb = chain / a.h_v, hh = chain - (chain / a.h_v) * a.h_v;
-            for (int t = 0; t < w; ++t) {
-                const float* kr = sQk[t][1];
-                const float* qr = sQk[t][0];
-                // u = k^T S for this lane's column: its 64 rows, then the other half's
-                float up[4] = {0.f, 0.f, 0.f, 0.f};
+            if (w > 0) {   // uniform
+                // an opaque zero keeps the window's per-lane LDS offsets from being hoisted out of the
+                // element loop into long-lived registers
+                int oz = 0;
+                asm volatile("" : "+v"(oz));
+                const int wl = lane + oz, l32 = wl & 31, half = wl >> 5;
+                const int bb = chain / a.h_v, hh = chain - (chain / a.h_v) * a.h_v;
+                // the window's products take X 2^-sx (maximum in [0.5, 1)) as hi/lo f16 operands
+                float mx = 0.f;
 #pragma unroll
                 for (int xb = 0; xb < NB; ++xb)
 #pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const floatx4 k4 = *reinterpret_cast<const floatx4*>(kr + 32 * xb + 8 * g + 4 * half);
+                    for (int j = 0; j < 16; ++j) mx = __builtin_elementwise_maximum(mx, __builtin_fabsf(X[xb][j]));
+                const int wx = exp2_of(wave_max(mx));
+                const float wsc = ldexpf(1.f, -wx);
+                // operands over the window's tokens: lane half h supplies tokens 4h .. 4h + 3 (the
+                // other four contraction slots are zero); A rows past the window read the zero row
+                auto frag4 = [](const _Float16* p) {
+                    const halfx4 x = *reinterpret_cast<const halfx4*>(p);
+                    return halfx8{x[0], x[1], x[2], x[3], (_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
+                };
+                auto split4 = [](const float (&v)[4], halfx8& hi, halfx8& lo) {
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) up[i] = fmaf(k4[i], X[xb][4 * g + i], up[i]);
+                    for (int i = 0; i < 8; ++i) hi[i] = lo[i] = (_Float16)0.f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const _Float16 h = (_Float16)v[i];
+                        hi[i] = h;
+                        lo[i] = (_Float16)(v[i] - (float)h);
                     }
-                float u = (up[0] + up[1]) + (up[2] + up[3]);
-                u += __shfl_xor(u, 32, 64);
-                const float al = sGb[t][0], be = sGb[t][1];
-                // S <- al (S - be k u) + be k v  =  al S + k (be (v - al u))
-                const float cf = be * (sVs[t][col0 + l32] - al * u);
-                float op[4] = {0.f, 0.f, 0.f, 0.f};
+                };
+                auto mma3 = [](halfx8 ah, halfx8 al, halfx8 bh, halfx8 bl, floatx16 c) {
+                    c = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, bh, c, 0, 0, 0);
+                    c = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bl, c, 0, 0, 0);
+                    return __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bh, c, 0, 0, 0);
+                };
+                const int rr = l32 < WS ? l32 : WS;
+                floatx16 Z = zero16(), O = zero16();
+                {
+                    // Z = Tg V 2^-wx
+                    float vv[4];
 #pragma unroll
-                for (int xb = 0; xb < NB; ++xb)
+                    for (int i = 0; i < 4; ++i) vv[i] = sVs[4 * half + i][col0 + l32] * wsc;
+                    halfx8 bh, bl;
+                    split4(vv, bh, bl);
+                    Z = mma3(frag4(&sTh[rr][4 * half]), frag4(&sTl[rr][4 * half]), bh, bl, Z);
+                }
+                // Z -= Tg diag(gamma) K X 2^-wx,  O = diag(gamma) Q X 2^-wx; the operand fragments of a
+                // step are read one step ahead
+                halfx8 fw[2][4];
+                auto wload = [&](int ks, halfx8 (&f)[4]) {
+                    const int off = 16 * ks + 4 * half;
+                    f[0] = t_frag(&sWh[rr][off]);
+                    f[1] = t_frag(&sWl[rr][off]);
+                    f[2] = t_frag(&sQh[rr][off]);
+                    f[3] = t_frag(&sQl[rr][off]);
+                };
+                wload(0, fw[0]);
 #pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const floatx4 k4 = *reinterpret_cast<const floatx4*>(kr + 32 * xb + 8 * g + 4 * half);
-                        const floatx4 q4 = *reinterpret_cast<const floatx4*>(qr + 32 * xb + 8 * g + 4 * half);
+                for (int ks = 0; ks < 2 * NB; ++ks) {
+                    if (ks + 1 < 2 * NB) wload(ks + 1, fw[(ks + 1) & 1]);
+                    halfx8 bh, bl;
+                    split_hilo(X[ks >> 1], ks & 1, wsc, bh, bl);
+                    const halfx8(&f)[4] = fw[ks & 1];
+                    Z = mma3(f[0], f[1], bh, bl, Z);
+                    O = mma3(f[2], f[3], bh, bl, O);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                {
+                    // O += Mq Z
+                    const float zz[4] = {Z[0], Z[1], Z[2], Z[3]};
+                    halfx8 bh, bl;
+                    split4(zz, bh, bl);
+                    O = mma3(frag4(&sMh[rr][4 * half]), frag4(&sMl[rr][4 * half]), bh, bl, O);
+                }
+                if (a.o) {
+                    // o_t for the window tokens t = 4h + j of this lane's column
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const float x = fmaf(k4[i], cf, al * X[xb][4 * g + i]);
-                            X[xb][4 * g + i] = x;
-                            op[i] = fmaf(q4[i], x, op[i]);
+                    for (int j = 0; j < 4; ++j) {
+                        const int t = 4 * half + j;
+                        if (t < w) {
+                            const float ov = ldexpf(O[j], wx);
+                            const long long row = (long long)bb * a.n_tokens + seg_start(a.seam_tab, el) + t;
+                            const long long oi = (row * a.h_v + hh) * D + col0 + l32;
+                            if (a.out_bf16) reinterpret_cast<uint16_t*>(a.o)[oi] = f32_to_bf16(ov);
+                            else reinterpret_cast<float*>(a.o)[oi] = ov;
                         }
                     }
-                float ov = (op[0] + op[1]) + (op[2] + op[3]);
-                ov += __shfl_xor(ov, 32, 64);
-                if (half == 0 && a.o) {
-                    const long long row = (long long)bb * a.n_tokens + seg_start(a.seam_tab, el) + t;
-                    const long long oi = (row * a.h_v + hh) * D + col0 + l32;
-                    if (a.out_bf16) reinterpret_cast<uint16_t*>(a.o)[oi] = f32_to_bf16(ov);
-                    else reinterpret_cast<float*>(a.o)[oi] = ov;
+                }
+                {
+                    // S <- Gamma S + K^T diag(Gamma / gamma) Z
+                    float vn[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) vn[j] = ldexpf(Z[j], wx) * sR[4 * half + j];
+                    halfx8 bh, bl;
+                    split4(vn, bh, bl);
+                    const float Gm = sGam;
+#pragma unroll
+                    for (int rt = 0; rt < NB; ++rt) {
+#pragma unroll
+                        for (int j = 0; j < 16; ++j) X[rt][j] *= Gm;
+                        X[rt] = mma3(frag4(&sKTh[32 * rt + l32][4 * half]), frag4(&sKTl[32 * rt + l32][4 * half]), bh,
+                                     bl, X[rt]);
+                    }
                 }
             }
+            fold_arrive(sC + 7, lane);   // the window of el consumed
         }
         const int ecur = sE;
         // scale this wave's columns to max |x| in [0.5, 1) before the hi/lo split
