@@ -293,6 +293,8 @@ __global__ __launch_bounds__(D * 6) void fold_dense_kernel(FoldArgs a) {
         };
         auto stage_window = [&]() __attribute__((always_inline)) {
             if constexpr (SEAM) {
+            // the window is on the critical path of the next element: issue ahead of the compute waves
+            __builtin_amdgcn_s_setprio(2);
             if (lt == 0) sW = swn;
             // 1. each loader wave's tokens: normalised k (fp32 rows, hi/lo K^T) and q (fp32 rows), v rows,
             //    gates
@@ -425,6 +427,7 @@ __global__ __launch_bounds__(D * 6) void fold_dense_kernel(FoldArgs a) {
                 sWh[i][c] = vh;
                 sWl[i][c] = (_Float16)(v - (float)vh);
             }
+            __builtin_amdgcn_s_setprio(0);
             }
         };
         auto stage = [&]() __attribute__((always_inline)) {
