@@ -787,6 +787,265 @@ __global__ __launch_bounds__(256) void fold_diag_kernel(FoldArgs a) {
     }
 }
 
+// Dense kind, running state only (no composed transition, no seam window).  Under
+// S <- T_i S + S_i the columns of a chain's state never mix, so a chain's d columns are split
+// into d/16 parts of one workgroup each, and the part's rows into four compute waves (d/4 rows
+// each, 16-row tiles).  A step forms T_i X for the part with 16x16x32 f16 products on hi/lo
+// splits of both operands (three products per pair, the lo x lo term dropped): T_i is staged
+// row-major in LDS as hi/lo f16 by the loader waves (double buffered; the loads run two
+// elements ahead of use), the part's columns go through LDS transposed, as hi/lo f16 after a
+// per-column scaling by an exact power of two that the four waves agree on through LDS
+// (every column's maximum |x| lands in [0.5, 1)).  S_i is added in fp32 as read from HBM.
+// The workgroups of one chain are dealt to the same XCD, so T_i comes from HBM once and from
+// that XCD's L2 for the other parts.
+template <int D>
+constexpr int split_loader_waves() { return D == 128 ? 8 : 4; }
+
+template <int D>
+__global__ __launch_bounds__((4 + split_loader_waves<D>()) * 64) void fold_split_kernel(FoldArgs a) {
+    constexpr int NCW = 4;                       // compute waves
+    constexpr int NLW = split_loader_waves<D>(); // loader waves
+    constexpr int NLT = NLW * 64;
+    constexpr int NCP = D / 16;                  // column parts per chain
+    constexpr int RPW = D / NCW;                 // rows per compute wave
+    constexpr int NT = RPW / 16;                 // 16-row tiles per compute wave
+    constexpr int KS = D / 32;                   // 32-deep contraction steps
+    constexpr int RS = D + 8;                    // LDS row stride (halves)
+    constexpr int TPL = D * D / (4 * NLT);       // float4 of T_i per loader thread
+    static_assert(TPL * 4 * NLT == D * D && NT * 16 == RPW, "split");
+    __shared__ __align__(16) _Float16 sT[2][2][D * RS];   // [buffer][hi, lo], row-major
+    __shared__ __align__(16) _Float16 sX[2][16 * RS];     // [hi, lo][column][row]
+    __shared__ __align__(16) float sM[16][NCW * 4];       // [column][wave, lane group] partial maxima
+    // counters: T consumed (one arrival per compute wave and element), column maxima written,
+    // columns written (one per compute wave and step), T staged into buffer 0 and into buffer 1
+    // (one per loader wave and element).  The staged counts are kept per buffer: before its
+    // first wait for a consumed element a loader wave may stage elements 0 and 1 while another
+    // has not yet staged element 0, so one count over both buffers could reach a target early
+    __shared__ int sC[5];
+
+    // workgroup -> (chain, part): ids congruent mod 8 share an XCD
+    const int id = blockIdx.x, r8 = id >> 3;
+    const int cp = r8 % NCP;
+    const int chain = (r8 / NCP) * 8 + (id & 7);
+    if (chain >= a.n_chain) return;   // padding of the grid to whole groups of 8 chains
+    const int blk = blockIdx.y;
+    const int e0 = blk * a.per_block;
+    const int ne = max(0, min(a.n_elem, e0 + a.per_block) - e0);
+    const long long DD = (long long)D * D;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if (tid < 5) sC[tid] = 0;
+    __syncthreads();
+
+    // slots of the elements in batches of 64 (lane i: element b0 + i), one vector load per batch,
+    // so that no per-element slot read has to wait (vmcnt) for the loads in flight
+    int sl_b = 0, eb = -1;
+    auto slot_batch = [&](int k) __attribute__((always_inline)) {
+        const int b0 = k & ~63;
+        if (b0 != eb) {
+            eb = b0;
+            const int kk = b0 + lane;
+            sl_b = kk < ne ? (a.slot ? a.slot[e0 + kk] : e0 + kk) : 0;
+        }
+        return b0;
+    };
+
+    if (wave >= NCW) {
+        // ============================ loader waves ============================
+        typedef float f4 __attribute__((ext_vector_type(4)));
+        typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+        const int lt = tid - NCW * 64;
+        f4 tr[2][TPL];
+        auto load = [&](int k, f4 (&dst)[TPL]) __attribute__((always_inline)) {
+            const int b0 = slot_batch(k);
+            const int sl = __builtin_amdgcn_readlane(sl_b, k - b0);
+            const f4* src = reinterpret_cast<const f4*>(a.T_hat + ((long long)sl * a.n_chain + chain) * DD);
+#pragma unroll
+            for (int r = 0; r < TPL; ++r) dst[r] = src[lt + NLT * r];
+        };
+        auto stage = [&](const f4 (&src)[TPL], int buf) __attribute__((always_inline)) {
+#pragma unroll
+            for (int r = 0; r < TPL; ++r) {
+                const int f = lt + NLT * r, row = f / (D / 4), c = 4 * (f % (D / 4));
+                half4 h, l;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    h[u] = (_Float16)src[r][u];
+                    l[u] = (_Float16)(src[r][u] - (float)h[u]);
+                }
+                *reinterpret_cast<half4*>(&sT[buf][0][row * RS + c]) = h;
+                *reinterpret_cast<half4*>(&sT[buf][1][row * RS + c]) = l;
+            }
+        };
+        if (ne > 0) load(0, tr[0]);
+        if (ne > 1) load(1, tr[1]);
+        auto body = [&](auto bc, int k) __attribute__((always_inline)) {
+            constexpr int B = decltype(bc)::value;   // register set and LDS buffer of element k
+            if (k >= 2) fold_wait(sC + 0, NCW * (k - 1));   // element k - 2 (same buffer) consumed
+            stage(tr[B], B);
+            fold_arrive(sC + 3 + B, lane);
+            if (k + 2 < ne) load(k + 2, tr[B]);
+        };
+        for (int k = 0; k < ne; k += 2) {
+            body(std::integral_constant<int, 0>{}, k);
+            if (k + 1 < ne) body(std::integral_constant<int, 1>{}, k + 1);
+        }
+        return;
+    }
+
+    // ============================ compute waves ============================
+    typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+    const int w = wave, g = lane >> 4, cl = lane & 15;
+    const int col = 16 * cp + cl;
+    const int rbase = RPW * w + 4 * g;   // row of tile t, register j: rbase + 16 t + j
+    floatx4 X[NT];
+    if (a.init_S) {
+        const float* src = a.init_S + ((long long)blk * a.n_chain + chain) * DD + col;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) X[t][j] = src[(rbase + 16 * t + j) * D];
+    } else {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) X[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+    // exponents of the batch's elements (lane i: element b0 + i)
+    int ex_b = 0, ebx = -1;
+    floatx4 sr[2][NT];   // S_i of elements k and k + 1, read two elements ahead
+    auto load_s = [&](int k, floatx4 (&dst)[NT]) __attribute__((always_inline)) {
+        const int b0 = slot_batch(k);
+        const int sl = __builtin_amdgcn_readlane(sl_b, k - b0);
+        const float* src = a.S + ((long long)sl * a.n_chain + chain) * DD + col;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) dst[t][j] = src[(rbase + 16 * t + j) * D];
+    };
+    auto exponent = [&](int k) __attribute__((always_inline)) {
+        const int b0 = k & ~63;
+        if (b0 != ebx) {
+            ebx = b0;
+            slot_batch(k);
+            ex_b = b0 + lane < ne ? a.T_exp[(long long)sl_b * a.n_chain + chain] : 0;
+        }
+        return __builtin_amdgcn_readlane(ex_b, k - b0);
+    };
+    if (ne > 0) load_s(0, sr[0]);
+    if (ne > 1) load_s(1, sr[1]);
+    auto body = [&](auto bc, int k) __attribute__((always_inline)) {
+        constexpr int B = decltype(bc)::value;
+        const int el = e0 + k;
+        // 1. the columns' maxima over the four waves
+        float m = 0.f;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) m = __builtin_elementwise_maximum(m, __builtin_fabsf(X[t][j]));
+        sM[cl][4 * w + g] = m;
+        fold_arrive(sC + 1, lane);
+        fold_wait(sC + 1, NCW * (k + 1));
+        {
+            const float4* mv = reinterpret_cast<const float4*>(&sM[cl][0]);
+            float mm = 0.f;
+#pragma unroll
+            for (int q = 0; q < NCW; ++q) {
+                const float4 v = mv[q];
+                mm = __builtin_elementwise_maximum(
+                    mm, __builtin_elementwise_maximum(__builtin_elementwise_maximum(v.x, v.y),
+                                                      __builtin_elementwise_maximum(v.z, v.w)));
+            }
+            m = mm;
+        }
+        const int sx = exp2_of(m);
+        // 2. the columns as hi/lo f16, scaled by 2^-sx, transposed into LDS
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            half4 h, l;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float v = ldexpf(X[t][j], -sx);
+                h[j] = (_Float16)v;
+                l[j] = (_Float16)(v - (float)h[j]);
+            }
+            *reinterpret_cast<half4*>(&sX[0][cl * RS + rbase + 16 * t]) = h;
+            *reinterpret_cast<half4*>(&sX[1][cl * RS + rbase + 16 * t]) = l;
+        }
+        fold_arrive(sC + 2, lane);
+        // the T_el fragments of this wave's rows, read while the other waves write their columns
+        fold_wait(sC + 3 + B, NLW * (k / 2 + 1));   // T_el staged in buffer B
+        const _Float16* Th = &sT[B][0][0];
+        const _Float16* Tl = &sT[B][1][0];
+        halfx8 fah[KS][NT], fal[KS][NT];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const int ao = (RPW * w + 16 * t + cl) * RS + 32 * ks + 8 * g;
+                fah[ks][t] = *reinterpret_cast<const halfx8*>(Th + ao);
+                fal[ks][t] = *reinterpret_cast<const halfx8*>(Tl + ao);
+            }
+        if (a.prefix) {
+            float* dst = a.prefix + ((long long)el * a.n_chain + chain) * DD + col;
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) dst[(rbase + 16 * t + j) * D] = X[t][j];
+        }
+        const int ecur = exponent(k);
+        fold_wait(sC + 2, NCW * (k + 1));
+        // 3. T_el X: rows of this wave, the part's 16 columns; the cross terms and the main term
+        // in separate accumulators (four independent product chains)
+        floatx4 acc[NT], acs[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = acs[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int kof = 32 * ks + 8 * g;
+            const halfx8 bh = *reinterpret_cast<const halfx8*>(&sX[0][cl * RS + kof]);
+            const halfx8 bl = *reinterpret_cast<const halfx8*>(&sX[1][cl * RS + kof]);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                acs[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fal[ks][t], bh, acs[t], 0, 0, 0);
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fah[ks][t], bh, acc[t], 0, 0, 0);
+            }
+#pragma unroll
+            for (int t = 0; t < NT; ++t) acs[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fah[ks][t], bl, acs[t], 0, 0, 0);
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] += acs[t];
+        fold_arrive(sC + 0, lane);   // buffer B and the columns read
+        // 4. S <- 2^(e + sx) (T_el X 2^-sx) + S_el
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) X[t][j] = ldexpf(acc[t][j], ecur + sx) + sr[B][t][j];
+        if (k + 2 < ne) load_s(k + 2, sr[B]);
+    };
+    for (int k = 0; k < ne; k += 2) {
+        body(std::integral_constant<int, 0>{}, k);
+        if (k + 1 < ne) body(std::integral_constant<int, 1>{}, k + 1);
+    }
+    if (a.out_S) {
+        float* dst = a.out_S + ((long long)blk * a.n_chain + chain) * DD + col;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) dst[(rbase + 16 * t + j) * D] = X[t][j];
+    }
+}
+
+hipError_t launch_fold_split(const FoldArgs& a, int d, hipStream_t s) {
+    if (a.kind != 0 || a.naive || a.seam || a.out_T) return hipErrorInvalidValue;
+    const dim3 grid(((a.n_chain + 7) / 8) * 8 * (d / 16), a.n_block);
+    if (d == 128)
+        hipLaunchKernelGGL((fold_split_kernel<128>), grid, dim3((4 + split_loader_waves<128>()) * 64), 0, s, a);
+    else if (d == 64)
+        hipLaunchKernelGGL((fold_split_kernel<64>), grid, dim3((4 + split_loader_waves<64>()) * 64), 0, s, a);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
 hipError_t launch_fold(const FoldArgs& a, int d, int with_T, hipStream_t s) {
     if (a.kind == 0 && !a.naive) {
         // role 1 (the composed transition) only when its outputs are wanted

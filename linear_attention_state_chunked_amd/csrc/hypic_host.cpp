@@ -488,10 +488,12 @@ hypic_status hypic_segment_build(const hypic_build_desc* d, hypic_stream_t strea
 
 namespace {
 
-// Dense compose cost model in element steps, one workgroup per compute unit (LDS-bound):
-// FOLD runs one workgroup per chain (two with the composed T) for n steps; SCAN's block
-// reduce runs two per (chain, block) for B steps, the scan of the aggregates one (two)
-// per chain for n/B steps, and the optional re-fold one per (chain, block) for B steps.
+// Dense compose cost model in element steps of fold_dense_kernel, one workgroup per compute
+// unit: FOLD runs one workgroup per chain (two with the composed T) for n steps; SCAN's
+// block reduce runs two per (chain, block) for B steps, the scan of the aggregates one (two)
+// per chain for n/B steps, and the optional re-fold one per (chain, block) for B steps.  A
+// fold of the running state alone can instead run column-split (d/16 workgroups per chain),
+// whose step takes kSplitStepPct percent of a fold_dense_kernel step.
 // `cus` is the device's compute unit count, looked up once per call by the caller.
 int planner_cus() {
     const int n = device_cu_count();
@@ -500,14 +502,29 @@ int planner_cus() {
 
 int64_t dense_rounds(int64_t wgs, int cus) { return (wgs + cus - 1) / cus; }
 
+// 1.8 us against 3.5 us per element for 32 chains of d = 128 (the 64k-token layer's compose as FOLD)
+constexpr int64_t kSplitStepPct = 50;
+
+// a fold of the running state alone over `wgs` (chain, block) pairs: column-split or not
+bool split_fold_better(int64_t wgs, int d, int cus) {
+    return dense_rounds(wgs * (d / 16), cus) * kSplitStepPct < dense_rounds(wgs, cus) * 100;
+}
+
+// cost in percent of a fold_dense_kernel step of `steps` steps over `wgs` (chain, block) pairs
+int64_t state_fold_cost(int64_t wgs, int64_t steps, int d, int cus) {
+    return std::min(dense_rounds(wgs * (d / 16), cus) * kSplitStepPct, dense_rounds(wgs, cus) * 100) * steps;
+}
+
 int64_t dense_fold_cost(const hypic_compose_desc* d, int cus) {
-    return dense_rounds((int64_t)d->n_chain * (d->T_total ? 2 : 1), cus) * d->n_elem;
+    if (d->T_total) return dense_rounds((int64_t)d->n_chain * 2, cus) * d->n_elem * 100;
+    return state_fold_cost(d->n_chain, d->n_elem, d->d_k, cus);
 }
 
 int64_t dense_scan_cost(const hypic_compose_desc* d, int64_t b, int cus) {
     const int64_t C = d->n_chain, nb = (d->n_elem + b - 1) / b;
-    int64_t cost = dense_rounds(2 * C * nb, cus) * b + dense_rounds(C * (d->T_total ? 2 : 1), cus) * nb;
-    if (d->S_prefix) cost += dense_rounds(C * nb, cus) * b;
+    int64_t cost = dense_rounds(2 * C * nb, cus) * b * 100;
+    cost += d->T_total ? dense_rounds(2 * C, cus) * nb * 100 : state_fold_cost(C, nb, d->d_k, cus);
+    if (d->S_prefix) cost += state_fold_cost(C * nb, b, d->d_k, cus);
     return cost;
 }
 
@@ -653,7 +670,10 @@ hypic_status compose_impl(const hypic_compose_desc* d, hypic_stream_t stream, vo
         a.out_e = d->T_total_exp;
         a.prefix = d->S_prefix;
         a.naive = m == HYPIC_COMPOSE_NAIVE_ADD;
-        e = hypic::launch_fold(a, D, wantT ? 1 : 0, s);
+        if (kind == 0 && !a.naive && !wantT && d->n_elem > 0 && split_fold_better(d->n_chain, D, cus))
+            e = hypic::launch_fold_split(a, D, s);
+        else
+            e = hypic::launch_fold(a, D, wantT ? 1 : 0, s);
         if (e != hipSuccess) return device_fail("compose: fold launch", e);
         return ok();
     }
@@ -693,7 +713,10 @@ hypic_status compose_impl(const hypic_compose_desc* d, hypic_stream_t stream, vo
     b.out_T = d->T_total;
     b.out_e = d->T_total_exp;
     b.prefix = pre;
-    e = hypic::launch_fold(b, D, wantT ? 1 : 0, s);
+    if (kind == 0 && !wantT && split_fold_better(d->n_chain, D, cus))
+        e = hypic::launch_fold_split(b, D, s);
+    else
+        e = hypic::launch_fold(b, D, wantT ? 1 : 0, s);
     if (e != hipSuccess) return device_fail("compose: scan of block aggregates launch", e);
     // 3) re-fold each block from its entry state, writing the per-element states
     if (d->S_prefix) {
@@ -709,7 +732,10 @@ hypic_status compose_impl(const hypic_compose_desc* d, hypic_stream_t stream, vo
         c.S = d->S;
         c.init_S = pre;
         c.prefix = d->S_prefix;
-        e = hypic::launch_fold(c, D, 0, s);
+        if (kind == 0 && split_fold_better((int64_t)d->n_chain * nblk, D, cus))
+            e = hypic::launch_fold_split(c, D, s);
+        else
+            e = hypic::launch_fold(c, D, 0, s);
         if (e != hipSuccess) return device_fail("compose: scan re-fold launch", e);
     }
     return ok();

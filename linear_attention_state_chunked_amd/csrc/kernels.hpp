@@ -201,6 +201,8 @@ hipError_t launch_dense_engine(const EngineArgs& a, int d, int prec_f32, int gri
 hipError_t launch_gdn_build(const EngineArgs& a, int d, int prec_f32, int grid, hipStream_t s);
 hipError_t launch_diag_build(const DiagArgs& a, int d, hipStream_t s);
 hipError_t launch_fold(const FoldArgs& a, int d, int with_T, hipStream_t s);
+// dense kind, running state only: the columns of each chain split over d/16 workgroups
+hipError_t launch_fold_split(const FoldArgs& a, int d, hipStream_t s);
 // Device address of this device's fixed compose scratch (kNoAllocScratchBytes), looked up
 // once per device with that device current.
 constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;

@@ -134,6 +134,55 @@ def test_compose_random_elements(gpu, d):
 
 
 @pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("n_elem", [1, 2, 3, 70, 130])
+def test_compose_state_only_column_scales(gpu, d, n_elem):
+    """Running state alone (no composed transition), the path that splits each chain's columns
+    over workgroups: 9 chains (not a whole group of 8), slots, an initial state, element counts
+    on both sides of a 64-element batch, and S0 and every S_i scaled by powers of two in
+    [2^-40, 2^40].  The composition is linear in S, so each column of the result carries its
+    column's scale exactly and is compared on its own.  Every mode gets one scale per 32-column
+    block (the block width of the transition-carrying kernels, which scale a block as a whole);
+    FOLD, whose state-only form scales each column on its own, also gets one scale per column."""
+    from synth import random_elements
+
+    n_slot, n_chain = 23, 9
+    el = random_elements(31 + d + n_elem, n_slot, n_chain, d)
+    rng = np.random.default_rng([31, d, n_elem])
+    S1 = el["S"]
+    S01 = rng.standard_normal((n_chain, d, d)).astype(np.float32)
+    slot = rng.integers(0, n_slot, size=n_elem).astype(np.int32)
+    Td, ed, sd = dev_tensor(el["T_hat"]), dev_tensor(el["T_exp"], torch.int32), dev_tensor(slot, torch.int32)
+
+    def col_err(x, ref):
+        # relative error of every column on its own
+        return float(np.max(O.rel_err(np.swapaxes(x, -1, -2), np.swapaxes(ref, -1, -2), nd=1)))
+
+    blocks = np.repeat(rng.integers(-40, 41, size=d // 32), 32)
+    cols = rng.integers(-40, 41, size=d)
+    for ex, modes in ((blocks, (("fold", 0), ("scan", 0), ("scan", 5), ("auto", 0))), (cols, (("fold", 0),))):
+        cs = np.ldexp(1.0, ex).astype(np.float32)
+        S, S0 = S1 * cs, S01 * cs
+        refs = []
+        for c in range(n_chain):
+            elems = [{"T_hat": el["T_hat"][s, c], "T_exp": el["T_exp"][s, c], "S": S[s, c]} for s in slot]
+            refs.append(O.compose_fold("dense", elems, S0=S0[c]))
+        Sd, S0d = dev_tensor(S), dev_tensor(S0)
+        for mode, blk in modes:
+            if mode == "scan" and n_elem < 2:
+                continue
+            for want_prefix in (False, True):
+                r = H.hypic_compose(Td, ed, Sd, slot=sd, S0=S0d, mode=mode, want_prefix=want_prefix,
+                                    scan_block=blk)
+                torch.cuda.synchronize()
+                H.hypic_device_status()   # raises if a bounded wait ran out
+                for c in range(n_chain):
+                    ref = refs[c]
+                    eS = col_err(r["S_final"][c].cpu().numpy(), ref["S_final"])
+                    eP = col_err(r["S_prefix"][:, c].cpu().numpy(), ref["S_prefix"]) if want_prefix else 0.0
+                    assert max(eS, eP) < TOL_F32, (mode, blk, want_prefix, c, eS, eP)
+
+
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("kind", ["scalar", "diag"])
 def test_compose_random_elements_diag_scalar(gpu, d, kind):
     """Diagonal / scalar compose of random elements with slots, an initial state, prefix states
