@@ -14,7 +14,9 @@
 // exact power of two (the column maximum uses the NaN-propagating three-input maximum
 // with |.| modifiers); T_i is staged row-major in LDS as hi/lo f16 by loader waves in
 // two column halves, each as soon as the compute waves are done with that half of the
-// previous element (LDS counters, no workgroup barrier per element).
+// previous element (LDS counters, no workgroup barrier per element).  A fold that carries the
+// running state alone can instead split each chain's columns over d/16 workgroups
+// (fold_split_kernel), for few chains on many compute units.
 // Diagonal / scalar kinds: elementwise, one thread per state entry stripe.
 #include <mutex>
 
