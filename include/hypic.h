@@ -123,7 +123,7 @@ typedef enum {
 } hypic_precision;
 
 typedef enum {
-    HYPIC_COMPOSE_AUTO = 0,     /* FOLD for few elements per chain, else SCAN      */
+    HYPIC_COMPOSE_AUTO = 0,     /* FOLD or SCAN (and its block) by a cost model     */
     HYPIC_COMPOSE_FOLD = 1,     /* sequential S <- T_i S + S_i per chain            */
     HYPIC_COMPOSE_SCAN = 2,     /* blocked reduce, scan of block aggregates, re-fold */
     HYPIC_COMPOSE_NAIVE_ADD = 3 /* S <- S + S_i: the "addition" PIC mode of [readme],
@@ -212,7 +212,17 @@ size_t hypic_segment_build_workspace_bytes(const hypic_build_desc* desc);
  *   S <- T_{slot[i]} S + S_{slot[i]},  i = 0 .. n_elem-1,  starting from S0.
  * FOLD runs this sequentially per chain; SCAN uses the associative operator
  * (T2,S2) o (T1,S1) = (T2 T1, T2 S1 + S2) with identity (I, 0) in a blocked
- * reduce / scan / re-fold.  NAIVE_ADD is the straw-man S <- S + S_i.
+ * reduce / scan / re-fold.  NAIVE_ADD is the straw-man S <- S + S_i.  AUTO picks FOLD
+ * or SCAN, and SCAN's block size, from a cost model of element steps on the device's
+ * compute units.
+ *
+ * Dense arithmetic: each product T_i X takes f16 hi/lo splits of both operands (about
+ * 22-bit operands, fp32 accumulation) after scaling X by exact powers of two: per
+ * column where only the state is carried (FOLD, and SCAN's fold of the block
+ * aggregates and its re-fold, when T_total is NULL; each chain's columns are then
+ * spread over several workgroups when that is faster), per 32-column block otherwise.
+ * T_hat entries must lie within the f16 range (the builds emit them normalised to a
+ * maximum below 2).
  *
  * Layouts (C = n_chain):
  *   slot        device int32 [n_elem], values in [0, n_slot); NULL = identity
